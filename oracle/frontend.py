@@ -1,0 +1,62 @@
+"""Mask front-end oracle (numpy) -- TEST INFRASTRUCTURE.
+
+Two integer steps precede the attention kernel:
+
+``mask_to_csr``: exact expansion of a logical block mask to a finer physical
+tile shape, then the per-Q-tile list of selected KV tiles. It follows the
+FastVideo page (benchmarks/bench_vsa_blackwell.py): ``expand_exact256_mask``
+repeats every mask row 256/q_block times along Q and every column
+256/kv_block times along KV, which leaves the selected token pairs unchanged;
+``arm_fa4`` then lists, per physical Q tile, the ascending physical KV tile
+indices of the expanded mask (``arange(nkv).masked_select(mask)``) together
+with their count.
+
+``build_worklist``: the order in which Q tiles are processed. Items
+(b, h, p) are encoded as their flat index into kv_block_cnt and sorted by
+count, largest first, ties kept in ascending flat order (a stable sort), so
+that long rows start first (the work-list idea of the page
+"BlackwellMultiHeadLatentAttentionForwardFP8": a persistent grid walking a
+device list of work tiles instead of a plain grid).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def mask_to_csr(logical_mask, logical_block, physical_block, ld, fill=-1):
+    """Expand a logical mask and list its selected KV tiles per Q tile.
+
+    logical_mask: [B, H, NQ_l, NKV_l], nonzero = selected.
+    logical_block = (LQ, LKV) tokens per logical cell; physical_block =
+    (PQ, PKV) with LQ % PQ == 0 and LKV % PKV == 0.
+    Returns (idx [B, H, NQ_p, ld] int32, cnt [B, H, NQ_p] int32, overflow).
+    cnt is the true count; a row with cnt > ld keeps only its first ld
+    entries and sets ``overflow``. Slots past a row's count hold ``fill``.
+    """
+    m = np.asarray(logical_mask) != 0
+    lq, lkv = logical_block
+    pq, pkv = physical_block
+    if lq % pq or lkv % pkv:
+        raise ValueError("physical tile sizes must divide the logical block sizes")
+    phys = np.repeat(np.repeat(m, lq // pq, axis=2), lkv // pkv, axis=3)
+    B, H, NQ, NKV = phys.shape
+    idx = np.full((B, H, NQ, ld), fill, dtype=np.int32)
+    cnt = np.zeros((B, H, NQ), dtype=np.int32)
+    overflow = False
+    cols = np.arange(NKV, dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            for p in range(NQ):
+                sel = cols[phys[b, h, p]]
+                cnt[b, h, p] = sel.size
+                n = min(sel.size, ld)
+                idx[b, h, p, :n] = sel[:n]
+                overflow |= sel.size > ld
+    return idx, cnt, bool(overflow)
+
+
+def build_worklist(kv_block_cnt, ld):
+    """Flat (b, h, p) indices sorted by clamp(cnt, 0, ld) descending, stable."""
+    c = np.clip(np.asarray(kv_block_cnt, dtype=np.int64).reshape(-1), 0, ld)
+    return np.argsort(-c, kind="stable").astype(np.int32)

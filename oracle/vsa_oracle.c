@@ -1,0 +1,231 @@
+/*
+ * Block-sparse masked SDPA oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, obviously correct CPU implementation of the forward pass that
+ * the GPU library computes. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library; the product
+ * path never does. It shares no code with the GPU library.
+ *
+ * Definition followed (FastVideo page "[perf] Add fine-grained FA4 VSA
+ * kernels", benchmarks/bench_vsa_blackwell.py, function ref_masked_sdpa_fp32):
+ * per head, fp32 scores (Q K^T) * scale; every query token i may attend to the
+ * key tokens of the KV tiles its Q tile selects (a boolean token mask made by
+ * repeating the block mask over the tile sizes); unselected scores become
+ * -inf; a row softmax; then the product with V. True fp32 arithmetic is used
+ * (the page disables TF32 for this reference). Row log-sum-exp is the natural
+ * log of the sum of exp over the same masked fp32 scores (cf. page
+ * "BlackwellMultiHeadLatentAttentionForwardFP8", write_empty_output: a row
+ * with no selected key gives O = 0 and LSE = -inf).
+ *
+ * Block mask input is the per-Q-tile list form used by FA4's block-sparse
+ * interface (page 3, block_sparsity.py, BlockSparseTensorsTorch full_block_*):
+ * kv_block_idx [B,H,NQ,ld] int32 (row p uses entries [0, cnt)), kv_block_cnt
+ * [B,H,NQ] int32. Entries may be in any order; they must be distinct and in
+ * [0, S/block_kv).
+ *
+ * Evaluation order is fixed and independent of the tile shape: the selected
+ * key tokens of a row are visited in ascending token order and every sum over
+ * the head dimension runs d = 0..D-1. Hence two masks that select the same
+ * token pairs (for example a 256x256 mask and its exact expansion to 128x64 or
+ * 64x64 tiles) give bit-identical results.
+ *
+ * Built with plain gcc -O2 (no -ffast-math); OpenMP parallelises over rows.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG (-1)
+#define ORACLE_ERR_IDX_RANGE (-2)
+#define ORACLE_ERR_IDX_DUP (-3)
+#define ORACLE_ERR_CNT (-4)
+#define ORACLE_ERR_NOMEM (-5)
+
+static float bf16_to_f32(uint16_t b) {
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Mark the KV tiles selected by one CSR row; returns an error code. */
+static int mark_tiles(const int32_t* idx_row, int32_t n, int32_t ld, int32_t nkv, unsigned char* mark) {
+    if (n < 0 || n > ld) return ORACLE_ERR_CNT;
+    memset(mark, 0, (size_t)nkv);
+    for (int32_t e = 0; e < n; ++e) {
+        int32_t t = idx_row[e];
+        if (t < 0 || t >= nkv) return ORACLE_ERR_IDX_RANGE;
+        if (mark[t]) return ORACLE_ERR_IDX_DUP;
+        mark[t] = 1;
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Softmax weights of one query row over the key tokens (ascending order).
+ * On return: s[j] holds the weight of key token j for every selected j, keys
+ * that are not selected hold 0, *m the row max of the scores, *l the sum of
+ * exp(score - max). Returns the number of selected keys.
+ */
+static int64_t row_weights(const uint16_t* q, const uint16_t* k, int S, int H, int D, int b, int h, int i,
+                           const unsigned char* mark, int nkv, int block_kv, float scale, float* qf, float* s,
+                           float* m_out, float* l_out) {
+    const int64_t tok = (int64_t)H * D;
+    const uint16_t* qrow = q + ((int64_t)b * S + i) * tok + (int64_t)h * D;
+    for (int d = 0; d < D; ++d) qf[d] = bf16_to_f32(qrow[d]);
+
+    /* scores = (q . k) * scale over selected keys; masked keys -> -inf */
+    float m = -INFINITY;
+    int64_t nsel = 0;
+    for (int t = 0; t < nkv; ++t) {
+        for (int jj = 0; jj < block_kv; ++jj) {
+            int j = t * block_kv + jj;
+            if (!mark[t]) {
+                s[j] = -INFINITY;
+                continue;
+            }
+            const uint16_t* krow = k + ((int64_t)b * S + j) * tok + (int64_t)h * D;
+            float acc = 0.0f;
+            for (int d = 0; d < D; ++d) acc += qf[d] * bf16_to_f32(krow[d]);
+            s[j] = acc * scale;
+            if (s[j] > m) m = s[j];
+            ++nsel;
+        }
+    }
+    /* softmax along the row: exp(s - max) / sum */
+    float l = 0.0f;
+    if (nsel > 0) {
+        for (int j = 0; j < S; ++j) {
+            if (!mark[j / block_kv]) {
+                s[j] = 0.0f;
+                continue;
+            }
+            s[j] = expf(s[j] - m);
+            l += s[j];
+        }
+        for (int j = 0; j < S; ++j)
+            if (mark[j / block_kv]) s[j] = s[j] / l;
+    } else {
+        for (int j = 0; j < S; ++j) s[j] = 0.0f;
+    }
+    *m_out = m;
+    *l_out = l;
+    return nsel;
+}
+
+/*
+ * Forward pass for a list of query rows.
+ *   q, k, v : bf16 bit patterns, [B, S, H, D] contiguous
+ *   kv_block_idx / kv_block_cnt : block CSR at tile shape block_q x block_kv
+ *   rows    : flat row ids (b*H + h)*S + i, or NULL for all B*H*S rows in
+ *             that order
+ *   o       : [n_rows, D] fp32 output; lse : [n_rows] fp32 output
+ *   n_threads <= 0 uses the OpenMP default
+ * Returns 0, or a negative error code if any row's CSR entry is invalid.
+ */
+int vsa_oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* kv_block_idx,
+                         const int32_t* kv_block_cnt, int B, int S, int H, int D, int ld, int block_q, int block_kv,
+                         float scale, const int64_t* rows, int64_t n_rows, float* o, float* lse, int n_threads) {
+    if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || block_q <= 0 || block_kv <= 0 || ld < 0) return ORACLE_ERR_ARG;
+    if (S % block_q || S % block_kv) return ORACLE_ERR_ARG;
+    const int nq = S / block_q, nkv = S / block_kv;
+    const int64_t total = (int64_t)B * H * S;
+    if (rows == NULL) n_rows = total;
+    int status = ORACLE_OK;
+#ifdef _OPENMP
+    if (n_threads <= 0) n_threads = omp_get_max_threads();
+#else
+    (void)n_threads;
+#endif
+
+#pragma omp parallel num_threads(n_threads)
+    {
+        float* s = (float*)malloc(sizeof(float) * (size_t)S);
+        float* qf = (float*)malloc(sizeof(float) * (size_t)D);
+        unsigned char* mark = (unsigned char*)malloc((size_t)nkv);
+        if (!s || !qf || !mark) {
+#pragma omp critical
+            status = ORACLE_ERR_NOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 8)
+            for (int64_t r = 0; r < n_rows; ++r) {
+                int64_t flat = rows ? rows[r] : r;
+                float* orow = o + r * D;
+                if (flat < 0 || flat >= total) {
+#pragma omp critical
+                    status = ORACLE_ERR_ARG;
+                    continue;
+                }
+                int i = (int)(flat % S);
+                int h = (int)((flat / S) % H);
+                int b = (int)(flat / ((int64_t)S * H));
+                int p = i / block_q;
+                int64_t crow = ((int64_t)b * H + h) * nq + p;
+                int rc = mark_tiles(kv_block_idx + crow * ld, kv_block_cnt[crow], ld, nkv, mark);
+                if (rc != ORACLE_OK) {
+#pragma omp critical
+                    status = rc;
+                    continue;
+                }
+                float m, l;
+                int64_t nsel = row_weights(q, k, S, H, D, b, h, i, mark, nkv, block_kv, scale, qf, s, &m, &l);
+                /* out = softmax(scores) @ v, keys in ascending order */
+                for (int d = 0; d < D; ++d) orow[d] = 0.0f;
+                if (nsel > 0) {
+                    const int64_t tok = (int64_t)H * D;
+                    for (int j = 0; j < S; ++j) {
+                        if (!mark[j / block_kv]) continue;
+                        const uint16_t* vrow = v + ((int64_t)b * S + j) * tok + (int64_t)h * D;
+                        float w = s[j];
+                        for (int d = 0; d < D; ++d) orow[d] += w * bf16_to_f32(vrow[d]);
+                    }
+                    lse[r] = m + logf(l);
+                } else {
+                    lse[r] = -INFINITY;
+                }
+            }
+        }
+        free(s);
+        free(qf);
+        free(mark);
+    }
+    return status;
+}
+
+/*
+ * Softmax weights of one query row (flat id (b*H + h)*S + i) over all S key
+ * tokens: probs[j] = 0 for unselected keys. Used to check the oracle's own
+ * invariants (rows sum to one, zero outside the mask).
+ */
+int vsa_oracle_probs_row(const uint16_t* q, const uint16_t* k, const int32_t* kv_block_idx,
+                         const int32_t* kv_block_cnt, int B, int S, int H, int D, int ld, int block_q, int block_kv,
+                         float scale, int64_t flat_row, float* probs) {
+    if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || block_q <= 0 || block_kv <= 0 || ld < 0) return ORACLE_ERR_ARG;
+    if (S % block_q || S % block_kv) return ORACLE_ERR_ARG;
+    if (flat_row < 0 || flat_row >= (int64_t)B * H * S) return ORACLE_ERR_ARG;
+    const int nq = S / block_q, nkv = S / block_kv;
+    int i = (int)(flat_row % S);
+    int h = (int)((flat_row / S) % H);
+    int b = (int)(flat_row / ((int64_t)S * H));
+    int64_t crow = ((int64_t)b * H + h) * nq + i / block_q;
+    unsigned char* mark = (unsigned char*)malloc((size_t)nkv);
+    float* qf = (float*)malloc(sizeof(float) * (size_t)D);
+    if (!mark || !qf) {
+        free(mark);
+        free(qf);
+        return ORACLE_ERR_NOMEM;
+    }
+    int rc = mark_tiles(kv_block_idx + crow * ld, kv_block_cnt[crow], ld, nkv, mark);
+    if (rc == ORACLE_OK) {
+        float m, l;
+        row_weights(q, k, S, H, D, b, h, i, mark, nkv, block_kv, scale, qf, probs, &m, &l);
+    }
+    free(mark);
+    free(qf);
+    return rc;
+}

@@ -1,0 +1,98 @@
+"""Pins for the mask front-end oracle (exact expansion + CSR, work list)."""
+
+import numpy as np
+import pytest
+
+from oracle import frontend
+from workloads import anchor_count_mask, anchor_topk_mask
+
+
+def _selected_by_logical(mask, lblock, S):
+    """Brute force over tokens: pairs (i, j) the logical mask selects."""
+    B, H, _, _ = mask.shape
+    i = np.arange(S)
+    return mask[:, :, i[:, None] // lblock[0], i[None, :] // lblock[1]] != 0  # [B,H,S,S]
+
+
+def _selected_by_csr(idx, cnt, pblock, S):
+    B, H, NQ, _ = idx.shape
+    out = np.zeros((B, H, S, S), dtype=bool)
+    for b in range(B):
+        for h in range(H):
+            for p in range(NQ):
+                for t in idx[b, h, p, :cnt[b, h, p]]:
+                    out[b, h, p * pblock[0]:(p + 1) * pblock[0], t * pblock[1]:(t + 1) * pblock[1]] = True
+    return out
+
+
+@pytest.mark.parametrize("lblock,pblock", [((256, 256), (256, 128)), ((256, 256), (128, 64)),
+                                           ((256, 256), (64, 64)), ((256, 256), (256, 256)),
+                                           ((64, 64), (64, 64)), ((128, 64), (32, 16))])
+def test_csr_selects_exactly_the_logical_token_pairs(lblock, pblock):
+    S = 1024
+    rng = np.random.default_rng(lblock[0] + pblock[1])
+    mask = (rng.random((2, 2, S // lblock[0], S // lblock[1])) < 0.4).astype(np.uint8)
+    ld = S // pblock[1]
+    idx, cnt, ovf = frontend.mask_to_csr(mask, lblock, pblock, ld)
+    assert not ovf
+    assert idx.shape == (2, 2, S // pblock[0], ld) and cnt.shape == (2, 2, S // pblock[0])
+    assert np.array_equal(_selected_by_csr(idx, cnt, pblock, S), _selected_by_logical(mask, lblock, S))
+    # rows list distinct tiles in ascending order; unused slots hold the fill
+    for pos in np.ndindex(cnt.shape):
+        row = idx[pos][:cnt[pos]]
+        assert np.all(np.diff(row) > 0)
+        assert np.all(idx[pos][cnt[pos]:] == -1)
+    # counts scale by the KV expansion factor
+    e = lblock[1] // pblock[1]
+    assert np.all(cnt % e == 0)
+
+
+def test_overflow_truncates_and_flags():
+    mask = np.ones((1, 1, 2, 8), dtype=np.uint8)
+    idx, cnt, ovf = frontend.mask_to_csr(mask, (64, 64), (64, 32), ld=10)
+    assert ovf and np.all(cnt == 16)
+    assert np.array_equal(idx[0, 0, 0], np.arange(10))
+
+
+def test_coarser_physical_tile_rejected():
+    with pytest.raises(ValueError):
+        frontend.mask_to_csr(np.ones((1, 1, 4, 4), np.uint8), (64, 64), (128, 64), 4)
+
+
+def test_worklist_is_a_stable_descending_count_order():
+    rng = np.random.default_rng(3)
+    cnt = rng.integers(0, 20, size=(2, 3, 50)).astype(np.int32)
+    cnt[0, 0, 5] = 99  # beyond ld: clamped to ld for ordering
+    ld = 25
+    w = frontend.build_worklist(cnt, ld)
+    flat = np.clip(cnt.reshape(-1), 0, ld)
+    assert sorted(w.tolist()) == list(range(flat.size))
+    keys = flat[w]
+    assert np.all(np.diff(keys) <= 0)
+    for a, b in zip(w[:-1], w[1:]):
+        if flat[a] == flat[b]:
+            assert a < b
+    # same order as an explicit comparison sort on (-count, index)
+    assert w.tolist() == sorted(range(flat.size), key=lambda i: (-flat[i], i))
+
+
+def test_page_mask_generator_invariants():
+    m = anchor_topk_mask(3, 16, 16, 8, seed=1566)
+    assert m.shape == (3, 16, 16)
+    assert np.all(m.sum(-1) == 8)
+    rows = np.arange(16)
+    assert np.all(m[:, rows, rows] == 1)  # anchor floor(q*nkv/nq) = q on a square grid
+    m2 = anchor_topk_mask(3, 16, 16, 8, seed=1566)
+    assert np.array_equal(m, m2)
+    # rectangular grid anchor
+    m3 = anchor_topk_mask(2, 8, 32, 3, seed=5)
+    assert np.all(m3[:, np.arange(8), np.arange(8) * 4] == 1)
+
+
+def test_count_mask_generator_invariants():
+    m = anchor_count_mask(4, 512, 512, 10, 92, seed=9)
+    c = m.sum(-1)
+    assert c.min() >= 10 and c.max() <= 92
+    assert abs(c.mean() - 51) < 1.0
+    rows = np.arange(512)
+    assert np.all(m[:, rows, rows] == 1)

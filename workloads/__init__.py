@@ -1,0 +1,202 @@
+"""Seeded synthetic inputs for block-sparse attention: Q/K/V and block masks.
+
+This module is shared by the oracle tests, the GPU parity tests and the
+benchmark. It holds only input recipes (random draws and the mask sampler);
+none of the attention arithmetic, the mask expansion, the CSR build or the
+work-list ordering lives here.
+
+Recipes follow the FastVideo "[perf] Add fine-grained FA4 VSA kernels" page,
+file ``benchmarks/bench_vsa_blackwell.py``:
+
+* Q/K/V are i.i.d. standard normal values rounded to bf16, one draw per tensor
+  in the order q, k, v (section ``main``, the per-sequence-length draw). The
+  page draws on the CUDA device; here the draw is on a CPU generator so the
+  values do not depend on the GPU vendor's RNG stream.
+* A logical block mask keeps, in every Q-block row, the "diagonal anchor"
+  KV block floor(q*NKV/NQ) plus ``keep-1`` further blocks chosen uniformly
+  without replacement, by taking the top-k of i.i.d. U(0,1) scores with the
+  anchor's score forced above every other (function ``make_logical_mask``).
+* The mask seed is ``seed + seq_len + int(keep_fraction*1000)``, plus
+  ``q_block*1_000_003 + kv_block*9_176`` when a shape is sampled natively
+  rather than expanded from a 256x256 base (section ``main``).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+DEFAULT_SEED = 42
+
+# Keep fractions by sparsity label (bench_vsa_blackwell.py, table KEEP_FRAC).
+KEEP_FRAC = {
+    "dense": 1.0,
+    "50": 0.5,
+    "60": 0.4,
+    "70": 0.3,
+    "75": 0.25,
+    "80": 0.2,
+    "87.5": 0.125,
+    "90": 0.1,
+}
+
+
+def qkv(batch: int, seqlen: int, heads: int, head_dim: int, seed: int = DEFAULT_SEED):
+    """Return bf16 CPU tensors q, k, v of shape [B, S, H, D], i.i.d. N(0,1)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    out = []
+    for _ in range(3):
+        t = torch.randn(batch, seqlen, heads, head_dim, dtype=torch.float32, generator=g)
+        out.append(t.to(torch.bfloat16))
+    return tuple(out)
+
+
+def anchor_topk_mask(heads: int, nq: int, nkv: int, keep: int, seed: int) -> np.ndarray:
+    """[H, NQ, NKV] uint8 mask: diagonal anchor plus keep-1 uniform others.
+
+    Mirrors the sampling of ``make_logical_mask`` on the FastVideo page: one
+    U(0,1) score per block on a seeded CPU generator, the anchor
+    floor(q*NKV/NQ) forced to score 2, and the top ``keep`` scores per row.
+    """
+    if not 1 <= keep <= nkv:
+        raise ValueError(f"keep must be in [1, {nkv}], got {keep}")
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    scores = torch.rand(heads, nq, nkv, generator=g)
+    rows = torch.arange(nq)
+    anchor = torch.div(rows * nkv, nq, rounding_mode="floor").clamp_max(nkv - 1)
+    scores[:, rows, anchor] = 2.0
+    sel = torch.topk(scores, keep, dim=-1).indices
+    m = torch.zeros(heads, nq, nkv, dtype=torch.bool)
+    m.scatter_(-1, sel, True)
+    return m.to(torch.uint8).numpy()
+
+
+def anchor_count_mask(heads: int, nq: int, nkv: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """[H, NQ, NKV] uint8 mask whose per-row kept count is U{lo..hi}.
+
+    The count of every (head, Q-block) row is drawn independently and
+    uniformly from the integers lo..hi inclusive; the row then keeps its
+    diagonal anchor plus count-1 further blocks chosen uniformly without
+    replacement (the anchor/top-k mechanism above with a per-row keep).
+    Ties among equal U(0,1) scores are broken by block index (stable sort).
+    """
+    if not 1 <= lo <= hi <= nkv:
+        raise ValueError(f"need 1 <= lo <= hi <= {nkv}, got {lo}..{hi}")
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    counts = torch.randint(lo, hi + 1, (heads, nq), generator=g)
+    scores = torch.rand(heads, nq, nkv, generator=g)
+    rows = torch.arange(nq)
+    anchor = torch.div(rows * nkv, nq, rounding_mode="floor").clamp_max(nkv - 1)
+    scores[:, rows, anchor] = 2.0
+    order = torch.sort(scores, dim=-1, descending=True, stable=True).indices
+    rank = torch.empty_like(order)
+    rank.scatter_(-1, order, torch.arange(nkv).expand_as(order).contiguous())
+    return (rank < counts[..., None]).to(torch.uint8).numpy()
+
+
+def mask_seed(seed: int, seqlen: int, keep_fraction: float, native_shape=None) -> int:
+    """Mask seed rule of the FastVideo benchmark (section ``main``)."""
+    s = seed + seqlen + int(keep_fraction * 1000)
+    if native_shape is not None:
+        qb, kb = native_shape
+        s += qb * 1_000_003 + kb * 9_176
+    return s
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One synthetic problem: sizes, the logical mask grid and physical tiles.
+
+    ``logical_block`` is the (Q, KV) token size of one logical mask cell;
+    ``physical`` lists the (block_q, block_kv) tile shapes the forward pass
+    runs this mask at (each must divide the logical block).
+    """
+
+    name: str
+    batch: int
+    heads: int
+    seqlen: int
+    head_dim: int
+    logical_block: tuple
+    physical: tuple
+    mask_kind: str            # "topk", "dense" or "count"
+    keep: int = 0             # for "topk"
+    count_range: tuple = (0, 0)  # for "count"
+    keep_fraction: float = 1.0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    @property
+    def nq_logical(self) -> int:
+        return self.seqlen // self.logical_block[0]
+
+    @property
+    def nkv_logical(self) -> int:
+        return self.seqlen // self.logical_block[1]
+
+    def mask_seed(self, seed: int = DEFAULT_SEED) -> int:
+        native = None if self.logical_block == (256, 256) else self.logical_block
+        return mask_seed(seed, self.seqlen, self.keep_fraction, native)
+
+    def logical_mask(self, seed: int = DEFAULT_SEED) -> np.ndarray:
+        """[B, H, NQ_l, NKV_l] uint8 logical mask (same pattern for every b)."""
+        nq, nkv = self.nq_logical, self.nkv_logical
+        if self.mask_kind == "dense":
+            m = np.ones((self.heads, nq, nkv), dtype=np.uint8)
+        elif self.mask_kind == "topk":
+            m = anchor_topk_mask(self.heads, nq, nkv, self.keep, self.mask_seed(seed))
+        elif self.mask_kind == "count":
+            lo, hi = self.count_range
+            m = anchor_count_mask(self.heads, nq, nkv, lo, hi, self.mask_seed(seed))
+        else:
+            raise ValueError(self.mask_kind)
+        return np.ascontiguousarray(np.broadcast_to(m[None], (self.batch,) + m.shape))
+
+    def qkv(self, seed: int = DEFAULT_SEED):
+        return qkv(self.batch, self.seqlen, self.heads, self.head_dim, seed)
+
+
+# The five workloads of the block-sparse forward (tiny, dense, VSA-256 on its
+# own tiles and on finer tiles, native Q64/KV64 with skewed counts).
+TINY = Workload("tiny_64x64_b1h2s1024d64", 1, 2, 1024, 64, (64, 64), ((64, 64),),
+                "topk", keep=8, keep_fraction=0.5)
+DENSE = Workload("dense_b1h8s4096d128", 1, 8, 4096, 128, (128, 128), ((128, 128),),
+                 "dense", keep_fraction=1.0)
+VSA256 = Workload("vsa256_b1h24s32768d128_keep13", 1, 24, 32768, 128, (256, 256),
+                  ((256, 128),), "topk", keep=13, keep_fraction=0.1)
+VSA256_FINE = Workload("vsa256_fine_b1h24s32768d128_keep13", 1, 24, 32768, 128, (256, 256),
+                       ((128, 64), (64, 64)), "topk", keep=13, keep_fraction=0.1)
+NATIVE64 = Workload("native64_b1h24s32768d128_cnt10to92", 1, 24, 32768, 128, (64, 64),
+                    ((64, 64),), "count", count_range=(10, 92), keep_fraction=0.1)
+
+WORKLOADS = {w.name: w for w in (TINY, DENSE, VSA256, VSA256_FINE, NATIVE64)}
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """View a contiguous bf16 CPU tensor as a numpy uint16 array of raw bits."""
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def random_csr(batch, heads, nq, nkv, ld, count_lo, count_hi, seed, shuffle=True):
+    """Random block CSR (idx [B,H,NQ,ld] int32, cnt [B,H,NQ] int32) for tests.
+
+    Row counts are U{count_lo..count_hi}; each row holds distinct tile
+    indices, in random order when ``shuffle``; unused slots hold -1.
+    """
+    rng = np.random.default_rng(seed)
+    cnt = rng.integers(count_lo, count_hi + 1, size=(batch, heads, nq)).astype(np.int32)
+    idx = np.full((batch, heads, nq, ld), -1, dtype=np.int32)
+    for b in range(batch):
+        for h in range(heads):
+            for p in range(nq):
+                c = int(cnt[b, h, p])
+                sel = rng.choice(nkv, size=c, replace=False)
+                if not shuffle:
+                    sel = np.sort(sel)
+                idx[b, h, p, :c] = sel
+    return idx, cnt

@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse attention forward on one MI355X.
+
+One step = the whole forward path over one batch of synthetic input that is
+already resident in HBM: logical mask -> physical block CSR (exact
+expansion), the count-sorted work list, then the fused attention kernel.
+
+Default workload: VSA-256 mask, B=1 H=24 S=32768 D=128, Q256/KV256 logical
+blocks keeping 13 of 128 per row (~90% sparse), run on physical 256x128
+tiles. Throughput is sparse-aware: 4*D*(selected token pairs) per step.
+
+Prints one JSON line. The `roofline` object rates the attention kernel alone
+(HIP events around its launches on the stream it runs on) against the dense
+bf16 MFMA peak; `cpu_baseline` times the CPU oracle on a bounded sample of
+the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA (published figure)
+METRIC = "sparse-aware TFLOP/s and % of bf16 MFMA peak, block-sparse attn fwd S=32k"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="vsa256_b1h24s32768d128_keep13")
+    ap.add_argument("--tile", default=None, help="physical QxKV tile, e.g. 128x64 (default: workload's first)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per kernel launch (from rocprofv3 counters)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (for counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (sharding is a design note).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import block_sparse_attention_flashattention_amd as vsa
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n}), flush=True)
+        return 0
+
+    wl = W.WORKLOADS[args.workload]
+    if args.tile:
+        tile = tuple(int(x) for x in args.tile.lower().split("x"))
+    else:
+        tile = wl.physical[0]
+    bq, bkv = tile
+    lq, lkv = wl.logical_block
+    B, H, S, D = wl.batch, wl.heads, wl.seqlen, wl.head_dim
+
+    # ---- inputs, resident in HBM before timing ----
+    q_cpu, k_cpu, v_cpu = wl.qkv()
+    mask_cpu = wl.logical_mask()
+    q, k, v = (t.to(dev) for t in (q_cpu, k_cpu, v_cpu))
+    mask = torch.from_numpy(mask_cpu).to(dev)
+    nq = S // bq
+    ld = int(mask_cpu.sum(-1).max()) * (lkv // bkv)
+    idx = torch.zeros((B, H, nq, ld), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, H, nq), dtype=torch.int32, device=dev)
+    work = torch.empty((B * H * nq,), dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    scale = wl.scale
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev0=None, ev1=None):
+        vsa.vsa_mask_to_csr(mask, (lq, lkv), (bq, bkv), ld, idx, cnt, stream=stream)
+        vsa.vsa_build_worklist(cnt, ld, work, stream=stream)
+        if ev0 is not None:
+            ev0.record(stream)
+        vsa.vsa_attn_fwd_worklist(q, k, v, idx, cnt, bq, bkv, work, scale, o, lse, stream=stream)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    step()
+    torch.cuda.synchronize()
+    pairs = int(cnt.to(torch.int64).sum().item()) * bq * bkv
+    flops = 4.0 * D * pairs
+    for _ in range(args.warmup):
+        step()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in events:
+        step(e0, e1)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kernel_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in events]))
+    value = flops / (ms_step * 1e-3) / 1e12
+    kernel_tflops = flops / (kernel_ms * 1e-3) / 1e12
+
+    # Algorithmic HBM bytes of one kernel launch: Q, K, V read once, O and
+    # LSE written once, CSR indices and counts read once.
+    alg_bytes = (3 * B * S * H * D + B * S * H * D) * 2 + B * H * S * 4 + (B * H * nq) * (ld + 2) * 4
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "batch": B, "heads": H, "seq_len": S, "head_dim": D,
+            "logical_block": f"{lq}x{lkv}", "tile": f"{bq}x{bkv}",
+            "selected_pairs": pairs,
+            "density": round(pairs / (B * H * S * S), 5),
+            "parallelism": "single_gpu",
+        },
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "kernel_ms": round(kernel_ms, 4),
+        "kernel_tflops": round(kernel_tflops, 2),
+        "frontend_ms": round(ms_step - kernel_ms, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(kernel_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": alg_bytes,
+            "kernel": f"vsa_fwd_kernel<{bq},{bkv},{D}>",
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, q_cpu, k_cpu, v_cpu, idx, cnt, bq, bkv, ld, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(wl, q, k, v, idx, cnt, bq, bkv, ld, seconds):
+    """Time the CPU oracle on a bounded sample of query rows of this workload."""
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+    threads = min(threads, 16)
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    B, S, H, D = q.shape
+    nq = S // bq
+
+    def rows_for(n_tiles):
+        # whole query tiles, spread over heads, in a fixed pseudo-random order
+        order = np.random.default_rng(0).permutation(B * H * nq)[:n_tiles]
+        rows = []
+        for item in order:
+            bh, p = divmod(int(item), nq)
+            rows.append(bh * S + p * bq + np.arange(bq))
+        return np.concatenate(rows).astype(np.int64), order
+
+    def run(n_tiles):
+        rows, items = rows_for(n_tiles)
+        t0 = time.perf_counter()
+        oracle.attn_rows(q, k, v, idx_h, cnt_h, bq, bkv, wl.scale, rows, threads)
+        dt = time.perf_counter() - t0
+        flops = 4.0 * D * float(cnt_h.reshape(-1)[items].sum()) * bq * bkv
+        return dt, flops, rows.size
+
+    dt, fl, _ = run(max(1, threads // 4))
+    n_tiles = max(1, min(B * H * nq, int(max(1, threads // 4) * seconds / max(dt, 1e-3))))
+    dt, fl, n_rows = run(n_tiles)
+    return {
+        "value": round(fl / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n_tiles} of {B * H * nq} query tiles ({n_rows} rows, {fl:.3e} sparse-aware flops) "
+                  f"in {dt:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,225 @@
+"""Block-sparse attention forward for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over ``libvsa_attn.so`` (C ABI in ``include/vsa_attn.h``).
+Functions carry the C names and only marshal arguments: they check tensor
+placement, dtypes and shapes, allocate outputs when none are given, and pass
+raw device pointers plus the current HIP stream. Every step of the forward
+pass runs in the library's HIP kernels; there is no fallback path.
+
+Layouts: q, k, v, o ``[B, S, H, D]`` bf16; lse ``[B, H, S]`` fp32;
+kv_block_idx ``[B, H, S/block_q, ld]`` int32; kv_block_cnt
+``[B, H, S/block_q]`` int32; logical masks ``[B, H, NQ, NKV]`` uint8.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libvsa_attn.so")
+
+VSA_OK = 0
+VSA_ERR_INVALID_ARG = -1
+VSA_ERR_UNSUPPORTED = -2
+VSA_ERR_HIP = -3
+
+# Exported symbols of the C ABI (checked by the test suite against the header).
+SYMBOLS = (
+    "vsa_abi_version",
+    "vsa_status_string",
+    "vsa_last_error",
+    "vsa_mask_to_csr",
+    "vsa_build_worklist",
+    "vsa_attn_fwd",
+    "vsa_attn_fwd_worklist",
+    "vsa_release",
+)
+
+
+class VsaError(RuntimeError):
+    """A library call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_string(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libvsa_attn.so (built by ``build.py``); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} not found: build it with `python -m block_sparse_attention_flashattention_amd.build`")
+    lib = ctypes.CDLL(path)
+    p, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    lib.vsa_abi_version.argtypes = []
+    lib.vsa_abi_version.restype = i32
+    lib.vsa_status_string.argtypes = [i32]
+    lib.vsa_status_string.restype = ctypes.c_char_p
+    lib.vsa_last_error.argtypes = []
+    lib.vsa_last_error.restype = ctypes.c_char_p
+    lib.vsa_mask_to_csr.argtypes = [p, i32, i32, i32, i32, i32, i32, i32, i32, p, i32, p, p, p]
+    lib.vsa_mask_to_csr.restype = i32
+    lib.vsa_build_worklist.argtypes = [p, i32, i32, p, p]
+    lib.vsa_build_worklist.restype = i32
+    lib.vsa_attn_fwd.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p, p, p]
+    lib.vsa_attn_fwd.restype = i32
+    lib.vsa_attn_fwd_worklist.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p, i32, p, p,
+                                          p]
+    lib.vsa_attn_fwd_worklist.restype = i32
+    lib.vsa_release.argtypes = []
+    lib.vsa_release.restype = None
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().vsa_status_string(int(status)).decode()
+
+
+def _check(rc: int) -> None:
+    if rc != VSA_OK:
+        raise VsaError(rc, load_library().vsa_last_error().decode())
+
+
+def _stream_ptr(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, torch.bfloat16, 4)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share the shape [B, S, H, D]")
+    B, S, H, D = q.shape
+    _dev(kv_block_idx, "kv_block_idx", torch.int32, 4)
+    _dev(kv_block_cnt, "kv_block_cnt", torch.int32, 3)
+    if S % block_q or S % block_kv:
+        raise ValueError(f"seqlen {S} must be divisible by block_q {block_q} and block_kv {block_kv}")
+    nq = S // block_q
+    if tuple(kv_block_idx.shape[:3]) != (B, H, nq) or tuple(kv_block_cnt.shape) != (B, H, nq):
+        raise ValueError(f"kv_block_idx must be [B,H,{nq},ld] and kv_block_cnt [B,H,{nq}]")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    _dev(o, "o", torch.bfloat16, 4)
+    _dev(lse, "lse", torch.float32, 3)
+    if o.shape != q.shape or tuple(lse.shape) != (B, H, S):
+        raise ValueError("o must be [B,S,H,D] and lse [B,H,S]")
+    for name, t in (("k", k), ("v", v), ("kv_block_idx", kv_block_idx), ("kv_block_cnt", kv_block_cnt),
+                    ("o", o), ("lse", lse)):
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
+    return B, S, H, D, o, lse
+
+
+def vsa_attn_fwd(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale=None, o=None, lse=None,
+                 stream=None):
+    """Block-sparse attention forward; returns (o, lse).
+
+    Builds the count-sorted work list internally, then runs the fused
+    kernel. ``scale`` defaults to 1/sqrt(D).
+    """
+    B, S, H, D, o, lse = _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = load_library().vsa_attn_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(), B, S, H, D,
+        kv_block_idx.shape[3], block_q, block_kv, float(scale), o.data_ptr(), lse.data_ptr(),
+        _stream_ptr(stream, q.device))
+    _check(rc)
+    return o, lse
+
+
+def vsa_attn_fwd_worklist(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, work_list, scale=None, o=None,
+                          lse=None, stream=None):
+    """The fused kernel alone over a caller-built work list; returns (o, lse)."""
+    B, S, H, D, o, lse = _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse)
+    _dev(work_list, "work_list", torch.int32, 1)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = load_library().vsa_attn_fwd_worklist(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(), B, S, H, D,
+        kv_block_idx.shape[3], block_q, block_kv, float(scale), work_list.data_ptr(), work_list.numel(),
+        o.data_ptr(), lse.data_ptr(), _stream_ptr(stream, q.device))
+    _check(rc)
+    return o, lse
+
+
+def vsa_mask_to_csr(mask, logical_block, block, idx_ld, kv_block_idx=None, kv_block_cnt=None, overflow=None,
+                    stream=None):
+    """Exact expansion of a logical mask to ``block`` tiles + block CSR.
+
+    Returns (kv_block_idx, kv_block_cnt). Slots past a row's count are left
+    as allocated (zero when allocated here). ``overflow`` (optional int32
+    [1] GPU tensor) is set to 1 if some row holds more than ``idx_ld`` tiles.
+    """
+    _dev(mask, "mask", torch.uint8, 4)
+    B, H, NQL, NKVL = mask.shape
+    lq, lkv = logical_block
+    pq, pkv = block
+    if lq % pq or lkv % pkv:
+        raise ValueError("physical tile sizes must divide the logical block sizes")
+    nqp = NQL * (lq // pq)
+    if kv_block_idx is None:
+        kv_block_idx = torch.zeros((B, H, nqp, idx_ld), dtype=torch.int32, device=mask.device)
+    if kv_block_cnt is None:
+        kv_block_cnt = torch.empty((B, H, nqp), dtype=torch.int32, device=mask.device)
+    _dev(kv_block_idx, "kv_block_idx", torch.int32, 4)
+    _dev(kv_block_cnt, "kv_block_cnt", torch.int32, 3)
+    if tuple(kv_block_idx.shape) != (B, H, nqp, idx_ld) or tuple(kv_block_cnt.shape) != (B, H, nqp):
+        raise ValueError("output CSR shapes do not match the mask and tile shape")
+    ovf_ptr = None
+    if overflow is not None:
+        _dev(overflow, "overflow", torch.int32, 1)
+        ovf_ptr = overflow.data_ptr()
+    rc = load_library().vsa_mask_to_csr(mask.data_ptr(), B, H, NQL, NKVL, lq, lkv, pq, pkv,
+                                        kv_block_idx.data_ptr(), idx_ld, kv_block_cnt.data_ptr(), ovf_ptr,
+                                        _stream_ptr(stream, mask.device))
+    _check(rc)
+    return kv_block_idx, kv_block_cnt
+
+
+def vsa_build_worklist(kv_block_cnt, max_cnt, work_list=None, stream=None):
+    """Count-sorted work list (largest count first, stable) as int32 [n]."""
+    if not kv_block_cnt.is_cuda or kv_block_cnt.dtype != torch.int32 or not kv_block_cnt.is_contiguous():
+        raise ValueError("kv_block_cnt must be a contiguous int32 GPU tensor")
+    n = kv_block_cnt.numel()
+    if work_list is None:
+        work_list = torch.empty((n,), dtype=torch.int32, device=kv_block_cnt.device)
+    _dev(work_list, "work_list", torch.int32, 1)
+    if work_list.numel() != n:
+        raise ValueError("work_list must hold one entry per count")
+    rc = load_library().vsa_build_worklist(kv_block_cnt.data_ptr(), n, int(max_cnt), work_list.data_ptr(),
+                                           _stream_ptr(stream, kv_block_cnt.device))
+    _check(rc)
+    return work_list
+
+
+def vsa_release() -> None:
+    load_library().vsa_release()

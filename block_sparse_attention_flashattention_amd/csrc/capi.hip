@@ -1,0 +1,230 @@
+// C ABI of libvsa_attn.so: argument validation, dispatch and the per-device
+// work-list buffer. The operations are specified in include/vsa_attn.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <mutex>
+#include <vector>
+
+#include "vsa_attn.h"
+#include "vsa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int32_t hip_fail(hipError_t e, const char* what) {
+    return fail(VSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define VSA_REQUIRE(cond, code, ...)          \
+    do {                                      \
+        if (!(cond)) return fail(code, __VA_ARGS__); \
+    } while (0)
+
+// Validation shared by both forward entry points.
+int32_t check_fwd(const void* q, const void* k, const void* v, const int32_t* idx, const int32_t* cnt, int32_t batch,
+                  int32_t seqlen, int32_t heads, int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv,
+                  float scale, const void* o, const float* lse) {
+    VSA_REQUIRE(q && k && v && idx && cnt && o && lse, VSA_ERR_INVALID_ARG, "null tensor pointer");
+    VSA_REQUIRE(batch >= 1 && seqlen >= 1 && heads >= 1 && head_dim >= 1, VSA_ERR_INVALID_ARG,
+                "batch, seqlen, heads and head_dim must be >= 1");
+    VSA_REQUIRE(block_q >= 1 && block_kv >= 1, VSA_ERR_INVALID_ARG, "block sizes must be >= 1");
+    VSA_REQUIRE(seqlen % block_q == 0 && seqlen % block_kv == 0, VSA_ERR_INVALID_ARG,
+                "seqlen %d must be divisible by block_q %d and block_kv %d", seqlen, block_q, block_kv);
+    VSA_REQUIRE(idx_ld >= 1, VSA_ERR_INVALID_ARG, "idx_ld must be >= 1");
+    VSA_REQUIRE(isfinite(scale) && scale > 0.0f, VSA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    VSA_REQUIRE(vsa::fwd_supported(block_q, block_kv, head_dim), VSA_ERR_UNSUPPORTED,
+                "no kernel for block_q=%d block_kv=%d head_dim=%d (supported: block_q in {64,128,256}, "
+                "block_kv in {64,128}, head_dim in {64,128})",
+                block_q, block_kv, head_dim);
+    VSA_REQUIRE(aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(o, 16), VSA_ERR_INVALID_ARG,
+                "q, k, v, o must be 16-byte aligned");
+    VSA_REQUIRE(aligned(lse, 4) && aligned(idx, 4) && aligned(cnt, 4), VSA_ERR_INVALID_ARG,
+                "lse, kv_block_idx, kv_block_cnt must be 4-byte aligned");
+    const int64_t n_items = (int64_t)batch * heads * (seqlen / block_q);
+    VSA_REQUIRE(n_items <= INT32_MAX, VSA_ERR_INVALID_ARG, "batch*heads*seqlen/block_q exceeds int32");
+    VSA_REQUIRE((int64_t)batch * seqlen <= INT32_MAX, VSA_ERR_INVALID_ARG, "batch*seqlen exceeds int32");
+    return VSA_OK;
+}
+
+vsa::FwdParams make_params(const void* q, const void* k, const void* v, const int32_t* idx, const int32_t* cnt,
+                           int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim, int32_t idx_ld,
+                           int32_t block_q, int32_t block_kv, float scale, const int32_t* work, int32_t n_work,
+                           void* o, float* lse) {
+    (void)head_dim;
+    vsa::FwdParams p;
+    p.q = (const uint16_t*)q;
+    p.k = (const uint16_t*)k;
+    p.v = (const uint16_t*)v;
+    p.idx = idx;
+    p.cnt = cnt;
+    p.work = work;
+    p.o = (uint16_t*)o;
+    p.lse = lse;
+    p.n_work = n_work;
+    p.S = seqlen;
+    p.H = heads;
+    p.nq = seqlen / block_q;
+    p.nkv = seqlen / block_kv;
+    p.ld = idx_ld;
+    p.n_items = batch * heads * p.nq;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    return p;
+}
+
+// Library-owned work-list buffer, one per device, grown on demand.
+struct DeviceBuffer {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_buf_mutex;
+std::vector<DeviceBuffer> g_bufs;
+
+int32_t worklist_buffer(size_t bytes, int32_t** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_buf_mutex);
+    if ((int)g_bufs.size() <= dev) g_bufs.resize(dev + 1);
+    DeviceBuffer& b = g_bufs[dev];
+    if (b.bytes < bytes) {
+        if (b.ptr) {
+            e = hipFree(b.ptr);  // implicitly waits for work still using it
+            b.ptr = nullptr;
+            b.bytes = 0;
+            if (e != hipSuccess) return hip_fail(e, "hipFree");
+        }
+        e = hipMalloc(&b.ptr, bytes);
+        if (e != hipSuccess) return hip_fail(e, "hipMalloc(work list)");
+        b.bytes = bytes;
+    }
+    *out = (int32_t*)b.ptr;
+    return VSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t vsa_abi_version(void) { return 1; }
+
+const char* vsa_status_string(int32_t status) {
+    switch (status) {
+        case VSA_OK: return "VSA_OK";
+        case VSA_ERR_INVALID_ARG: return "VSA_ERR_INVALID_ARG";
+        case VSA_ERR_UNSUPPORTED: return "VSA_ERR_UNSUPPORTED";
+        case VSA_ERR_HIP: return "VSA_ERR_HIP";
+        default: return "VSA_ERR_UNKNOWN";
+    }
+}
+
+const char* vsa_last_error(void) { return g_last_error; }
+
+int32_t vsa_mask_to_csr(const uint8_t* mask, int32_t batch, int32_t heads, int32_t nq_logical, int32_t nkv_logical,
+                        int32_t logical_block_q, int32_t logical_block_kv, int32_t block_q, int32_t block_kv,
+                        int32_t* kv_block_idx, int32_t idx_ld, int32_t* kv_block_cnt, int32_t* overflow,
+                        void* stream) {
+    g_last_error[0] = 0;
+    VSA_REQUIRE(mask && kv_block_idx && kv_block_cnt, VSA_ERR_INVALID_ARG, "null pointer");
+    VSA_REQUIRE(batch >= 1 && heads >= 1 && nq_logical >= 1 && nkv_logical >= 1, VSA_ERR_INVALID_ARG,
+                "batch, heads, nq_logical, nkv_logical must be >= 1");
+    VSA_REQUIRE(logical_block_q >= 1 && logical_block_kv >= 1 && block_q >= 1 && block_kv >= 1,
+                VSA_ERR_INVALID_ARG, "block sizes must be >= 1");
+    VSA_REQUIRE(logical_block_q % block_q == 0 && logical_block_kv % block_kv == 0, VSA_ERR_INVALID_ARG,
+                "physical tile %dx%d must divide the logical block %dx%d", block_q, block_kv, logical_block_q,
+                logical_block_kv);
+    VSA_REQUIRE((int64_t)nq_logical * logical_block_q == (int64_t)nkv_logical * logical_block_kv,
+                VSA_ERR_INVALID_ARG, "query and key sequence lengths differ");
+    VSA_REQUIRE(idx_ld >= 1, VSA_ERR_INVALID_ARG, "idx_ld must be >= 1");
+    VSA_REQUIRE(aligned(kv_block_idx, 4) && aligned(kv_block_cnt, 4) && aligned(overflow, 4), VSA_ERR_INVALID_ARG,
+                "index buffers must be 4-byte aligned");
+    const int64_t q_ratio = logical_block_q / block_q, kv_ratio = logical_block_kv / block_kv;
+    const int64_t nq_phys = (int64_t)nq_logical * q_ratio;
+    const int64_t rows = (int64_t)batch * heads * nq_phys;
+    VSA_REQUIRE(rows <= INT32_MAX / 4 && (int64_t)nkv_logical * kv_ratio <= INT32_MAX, VSA_ERR_INVALID_ARG,
+                "problem too large");
+    hipError_t e = vsa::launch_mask_to_csr(mask, batch, heads, nq_logical, nkv_logical, (int)q_ratio, (int)kv_ratio,
+                                           (int)nq_phys, kv_block_idx, idx_ld, kv_block_cnt, overflow,
+                                           (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "mask_to_csr launch");
+    return VSA_OK;
+}
+
+int32_t vsa_build_worklist(const int32_t* kv_block_cnt, int32_t n_items, int32_t max_cnt, int32_t* work_list,
+                           void* stream) {
+    g_last_error[0] = 0;
+    VSA_REQUIRE(n_items >= 0, VSA_ERR_INVALID_ARG, "n_items must be >= 0");
+    VSA_REQUIRE(max_cnt >= 0 && max_cnt <= vsa::kWorklistMaxCnt, VSA_ERR_INVALID_ARG, "max_cnt must be in [0, %d]",
+                vsa::kWorklistMaxCnt);
+    if (n_items == 0) return VSA_OK;
+    VSA_REQUIRE(kv_block_cnt && work_list, VSA_ERR_INVALID_ARG, "null pointer");
+    VSA_REQUIRE(aligned(kv_block_cnt, 4) && aligned(work_list, 4), VSA_ERR_INVALID_ARG, "buffers must be 4-byte aligned");
+    hipError_t e = vsa::launch_build_worklist(kv_block_cnt, n_items, max_cnt, work_list, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
+    return VSA_OK;
+}
+
+int32_t vsa_attn_fwd_worklist(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
+                              const int32_t* kv_block_cnt, int32_t batch, int32_t seqlen, int32_t heads,
+                              int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv, float scale,
+                              const int32_t* work_list, int32_t n_work, void* o, float* lse, void* stream) {
+    g_last_error[0] = 0;
+    int32_t rc = check_fwd(q, k, v, kv_block_idx, kv_block_cnt, batch, seqlen, heads, head_dim, idx_ld, block_q,
+                           block_kv, scale, o, lse);
+    if (rc != VSA_OK) return rc;
+    VSA_REQUIRE(n_work >= 0, VSA_ERR_INVALID_ARG, "n_work must be >= 0");
+    if (n_work == 0) return VSA_OK;
+    VSA_REQUIRE(work_list && aligned(work_list, 4), VSA_ERR_INVALID_ARG, "work_list must be a 4-byte aligned pointer");
+    vsa::FwdParams p = make_params(q, k, v, kv_block_idx, kv_block_cnt, batch, seqlen, heads, head_dim, idx_ld,
+                                   block_q, block_kv, scale, work_list, n_work, o, lse);
+    hipError_t e = vsa::launch_fwd(block_q, block_kv, head_dim, p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    return VSA_OK;
+}
+
+int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
+                     const int32_t* kv_block_cnt, int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim,
+                     int32_t idx_ld, int32_t block_q, int32_t block_kv, float scale, void* o, float* lse,
+                     void* stream) {
+    g_last_error[0] = 0;
+    int32_t rc = check_fwd(q, k, v, kv_block_idx, kv_block_cnt, batch, seqlen, heads, head_dim, idx_ld, block_q,
+                           block_kv, scale, o, lse);
+    if (rc != VSA_OK) return rc;
+    VSA_REQUIRE(idx_ld <= vsa::kWorklistMaxCnt, VSA_ERR_UNSUPPORTED,
+                "idx_ld %d exceeds the work-list sort limit %d; use vsa_attn_fwd_worklist", idx_ld,
+                vsa::kWorklistMaxCnt);
+    const int32_t n_items = batch * heads * (seqlen / block_q);
+    int32_t* work = nullptr;
+    rc = worklist_buffer((size_t)n_items * sizeof(int32_t), &work);
+    if (rc != VSA_OK) return rc;
+    hipError_t e = vsa::launch_build_worklist(kv_block_cnt, n_items, idx_ld, work, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
+    vsa::FwdParams p = make_params(q, k, v, kv_block_idx, kv_block_cnt, batch, seqlen, heads, head_dim, idx_ld,
+                                   block_q, block_kv, scale, work, n_items, o, lse);
+    e = vsa::launch_fwd(block_q, block_kv, head_dim, p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    return VSA_OK;
+}
+
+void vsa_release(void) {
+    std::lock_guard<std::mutex> lock(g_buf_mutex);
+    for (auto& b : g_bufs) {
+        if (b.ptr) (void)hipFree(b.ptr);
+        b.ptr = nullptr;
+        b.bytes = 0;
+    }
+}
+
+}  // extern "C"

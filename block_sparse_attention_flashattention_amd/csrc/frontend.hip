@@ -1,0 +1,163 @@
+// Mask front-end for gfx950: logical block mask -> physical block CSR, and
+// the count-sorted work list.
+//
+// Exact expansion (FastVideo page "[perf] Add fine-grained FA4 VSA kernels",
+// benchmarks/bench_vsa_blackwell.py, expand_exact256_mask and arm_fa4):
+// physical Q tile p reads logical row floor(p / q_ratio); every selected
+// logical KV cell t becomes physical tiles t*kv_ratio .. t*kv_ratio +
+// kv_ratio-1, listed in ascending order. The selected token pairs are exactly
+// those of the logical mask.
+#include "vsa_internal.h"
+
+namespace vsa {
+namespace {
+
+// One wave per physical CSR row: 64 mask bytes per step, ballot + prefix
+// popcount to place each selected cell.
+__global__ __launch_bounds__(256) void mask_to_csr_kernel(const uint8_t* __restrict__ mask, int n_rows,
+                                                          int nq_logical, int nkv_logical, int q_ratio,
+                                                          int kv_ratio, int nq_physical, int32_t* __restrict__ idx,
+                                                          int ld, int32_t* __restrict__ cnt,
+                                                          int32_t* __restrict__ overflow) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= n_rows) return;
+    const int p = row % nq_physical;
+    const int bh = row / nq_physical;
+    const uint8_t* mrow = mask + ((int64_t)bh * nq_logical + p / q_ratio) * nkv_logical;
+    int32_t* orow = idx + (int64_t)row * ld;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int running = 0;  // selected logical cells so far
+    for (int base = 0; base < nkv_logical; base += 64) {
+        const int t = base + lane;
+        const bool sel = t < nkv_logical && mrow[t] != 0;
+        const uint64_t bal = __ballot(sel);
+        if (sel) {
+            const int pos = (running + __popcll(bal & below)) * kv_ratio;
+            for (int r = 0; r < kv_ratio; ++r)
+                if (pos + r < ld) orow[pos + r] = t * kv_ratio + r;
+        }
+        running += __popcll(bal);
+    }
+    if (lane == 0) {
+        const int c = running * kv_ratio;
+        cnt[row] = c;
+        if (c > ld && overflow) *overflow = 1;
+    }
+}
+
+// Lanes of the wave whose key equals this lane's key (among active lanes).
+template <int KEY_BITS>
+__device__ __forceinline__ uint64_t same_key_lanes(int key, bool active) {
+    uint64_t m = __ballot(active);
+#pragma unroll
+    for (int bit = 0; bit < KEY_BITS; ++bit) {
+        const bool set = (key >> bit) & 1;
+        const uint64_t bb = __ballot(set);
+        m &= set ? bb : ~bb;
+    }
+    return m;
+}
+
+// Stable counting sort of item indices by count, largest count first, in a
+// single workgroup of WAVES waves. Wave w owns a contiguous segment of the
+// items; per-wave histograms give each wave its own output offsets, and
+// within a wave the rank among equal keys comes from ballots, so the result
+// is deterministic and equal keys keep ascending item order.
+template <int WAVES, int BINS, int KEY_BITS>
+__global__ __launch_bounds__(WAVES * 64) void worklist_kernel(const int32_t* __restrict__ cnt, int n,
+                                                             int max_cnt, int32_t* __restrict__ work) {
+    __shared__ int hist[WAVES][BINS];
+    __shared__ int wave_total[WAVES];
+    constexpr int NT = WAVES * 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nbins = max_cnt + 1;
+    for (int i = tid; i < WAVES * BINS; i += NT) (&hist[0][0])[i] = 0;
+    __syncthreads();
+
+    const int seg = (n + WAVES - 1) / WAVES;
+    const int beg = min(n, wave * seg);
+    const int end = min(n, beg + seg);
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    // Phase 1: per-wave histogram of clamped counts.
+    for (int base = beg; base < end; base += 64) {
+        const int i = base + lane;
+        const bool act = i < end;
+        int key = act ? cnt[i] : 0;
+        key = key < 0 ? 0 : (key > max_cnt ? max_cnt : key);
+        const uint64_t same = same_key_lanes<KEY_BITS>(key, act);
+        if (act && (same & below) == 0) hist[wave][key] += __popcll(same);
+    }
+    __syncthreads();
+
+    // Phase 2: exclusive scan over keys in descending order; each thread owns
+    // PER consecutive positions (position o <-> key max_cnt - o).
+    constexpr int PER = (BINS + NT - 1) / NT;
+    int local_sum = 0;
+    for (int k = 0; k < PER; ++k) {
+        const int o = tid * PER + k;
+        if (o < nbins) {
+            const int key = max_cnt - o;
+            for (int w = 0; w < WAVES; ++w) local_sum += hist[w][key];
+        }
+    }
+    int incl = local_sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) wave_total[wave] = incl;
+    __syncthreads();
+    int run = incl - local_sum;
+    for (int w = 0; w < wave; ++w) run += wave_total[w];
+    for (int k = 0; k < PER; ++k) {
+        const int o = tid * PER + k;
+        if (o < nbins) {
+            const int key = max_cnt - o;
+            for (int w = 0; w < WAVES; ++w) {
+                const int c = hist[w][key];
+                hist[w][key] = run;
+                run += c;
+            }
+        }
+    }
+    __syncthreads();
+
+    // Phase 3: scatter in item order.
+    for (int base = beg; base < end; base += 64) {
+        const int i = base + lane;
+        const bool act = i < end;
+        int key = act ? cnt[i] : 0;
+        key = key < 0 ? 0 : (key > max_cnt ? max_cnt : key);
+        const uint64_t same = same_key_lanes<KEY_BITS>(key, act);
+        const int pos = act ? hist[wave][key] + __popcll(same & below) : 0;
+        if (act) work[pos] = i;
+        if (act && (same & below) == 0) hist[wave][key] += __popcll(same);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mask_to_csr(const uint8_t* mask, int batch, int heads, int nq_logical, int nkv_logical,
+                              int q_ratio, int kv_ratio, int nq_physical, int32_t* idx, int ld, int32_t* cnt,
+                              int32_t* overflow, hipStream_t stream) {
+    const int n_rows = batch * heads * nq_physical;
+    if (n_rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(mask_to_csr_kernel, dim3((n_rows + 3) / 4), dim3(256), 0, stream, mask, n_rows, nq_logical,
+                       nkv_logical, q_ratio, kv_ratio, nq_physical, idx, ld, cnt, overflow);
+    return hipGetLastError();
+}
+
+hipError_t launch_build_worklist(const int32_t* cnt, int n_items, int max_cnt, int32_t* work, hipStream_t stream) {
+    if (n_items <= 0) return hipSuccess;
+    if (max_cnt < 2048) {
+        hipLaunchKernelGGL((worklist_kernel<4, 2048, 11>), dim3(1), dim3(256), 0, stream, cnt, n_items, max_cnt, work);
+    } else {
+        hipLaunchKernelGGL((worklist_kernel<1, 8192, 13>), dim3(1), dim3(64), 0, stream, cnt, n_items, max_cnt, work);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace vsa

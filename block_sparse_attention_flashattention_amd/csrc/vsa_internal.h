@@ -1,0 +1,41 @@
+// Internal declarations shared by the translation units of libvsa_attn.so.
+// Not part of the public ABI (that is include/vsa_attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vsa {
+
+// Arguments of the fused forward kernel. All pointers are device pointers.
+struct FwdParams {
+    const uint16_t* q;       // [B, S, H, D] bf16 bits
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* idx;      // [B, H, nq, ld]
+    const int32_t* cnt;      // [B, H, nq]
+    const int32_t* work;     // [n_work] flat (b*H + h)*nq + p; may be null = identity
+    uint16_t* o;             // [B, S, H, D] bf16 bits
+    float* lse;              // [B, H, S]
+    int32_t n_work;
+    int32_t n_items;         // B * H * nq
+    int32_t S, H, nq, nkv, ld;
+    float scale_log2;        // softmax scale * log2(e)
+};
+
+// Launch the forward kernel for one (block_q, block_kv, head_dim); returns
+// hipSuccess or the launch error. Shapes are validated by the caller.
+hipError_t launch_fwd(int block_q, int block_kv, int head_dim, const FwdParams& p, hipStream_t stream);
+
+// Whether launch_fwd has a kernel for this configuration.
+bool fwd_supported(int block_q, int block_kv, int head_dim);
+
+// Front-end launches (frontend.hip).
+hipError_t launch_mask_to_csr(const uint8_t* mask, int batch, int heads, int nq_logical, int nkv_logical,
+                              int q_ratio, int kv_ratio, int nq_physical, int32_t* idx, int ld, int32_t* cnt,
+                              int32_t* overflow, hipStream_t stream);
+hipError_t launch_build_worklist(const int32_t* cnt, int n_items, int max_cnt, int32_t* work, hipStream_t stream);
+
+constexpr int kWorklistMaxCnt = 8191;
+
+}  // namespace vsa

@@ -1,0 +1,158 @@
+/*
+ * vsa_attn.h -- block-sparse attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libvsa_attn.so. Every entry point takes plain pointers and sizes;
+ * no framework types cross this boundary.
+ *
+ * The operation (FastVideo page "[perf] Add fine-grained FA4 VSA kernels",
+ * benchmarks/bench_vsa_blackwell.py, functions ref_masked_sdpa_fp32 and
+ * arm_fa4): for every batch b, head h and query token i,
+ *
+ *     A(i)  = union over selected KV tiles t of query tile floor(i/block_q)
+ *             of the key tokens [t*block_kv, (t+1)*block_kv)
+ *     O_i   = softmax_j in A(i) (scale * q_i . k_j) applied to v_j
+ *     LSE_i = ln sum_{j in A(i)} exp(scale * q_i . k_j)
+ *
+ * Dense attention is the case where every query tile selects every KV tile.
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ *  - Tensors are dense, row-major and contiguous:
+ *      q, k, v, o      [batch, seqlen, heads, head_dim]  bf16 (raw 16-bit)
+ *      lse             [batch, heads, seqlen]            fp32
+ *      kv_block_idx    [batch, heads, seqlen/block_q, idx_ld]  int32
+ *      kv_block_cnt    [batch, heads, seqlen/block_q]          int32
+ *    This is the per-query-tile list form of FA4's block-sparse tensors
+ *    (page 3, block_sparsity.py, BlockSparseTensorsTorch full_block_cnt /
+ *    full_block_idx, including the "compact" last dimension idx_ld that
+ *    only needs to hold the largest count).
+ *  - Pointers named in a signature are DEVICE pointers unless stated. The
+ *    caller owns every buffer; the library never frees or retains them.
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream). All
+ *    GPU work is enqueued asynchronously on it; no call synchronises the
+ *    host with the device.
+ *  - Arguments are validated on the host before anything is launched. A
+ *    call returns VSA_OK, or a negative vsa_status_t and enqueues nothing.
+ *    vsa_last_error() then returns a message naming the failed check.
+ *  - Device-data contract: row (b,h,p) uses kv_block_idx entries
+ *    [0, min(cnt, idx_ld)); entries must be distinct tile indices in
+ *    [0, seqlen/block_kv), in any order. Kernels never read outside
+ *    [0, idx_ld) and skip tile indices outside [0, seqlen/block_kv) rather
+ *    than read out of bounds; a row with count 0 yields O = 0 and
+ *    LSE = -inf (as the split-KV epilogue on page
+ *    "BlackwellMultiHeadLatentAttentionForwardFP8", write_empty_output).
+ *    Duplicate entries are counted twice.
+ */
+#ifndef VSA_ATTN_H
+#define VSA_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    VSA_OK = 0,
+    VSA_ERR_INVALID_ARG = -1, /* null pointer, bad size, non-divisible shape */
+    VSA_ERR_UNSUPPORTED = -2, /* valid but not implemented (tile shape, head_dim) */
+    VSA_ERR_HIP = -3          /* a HIP runtime call or kernel launch failed */
+} vsa_status_t;
+
+/* Version of this ABI; bumped on any signature change. */
+int32_t vsa_abi_version(void);
+
+/* Static string for a status code. */
+const char* vsa_status_string(int32_t status);
+
+/* Message of the last failed call on the calling host thread ("" if none). */
+const char* vsa_last_error(void);
+
+/*
+ * vsa_mask_to_csr -- mask front-end, step 1: exact expansion + block CSR.
+ *
+ * Source: page 3, bench_vsa_blackwell.py, expand_exact256_mask (repeat every
+ * logical row block_q-fold and column block_kv-fold, which keeps the
+ * selected token pairs) and arm_fa4 (per physical Q tile, the ascending
+ * indices of its selected physical KV tiles, and their count).
+ *
+ *   mask           [batch, heads, nq_logical, nkv_logical] uint8, nonzero =
+ *                  selected; logical cells are logical_block_q x
+ *                  logical_block_kv tokens.
+ *   block_q/kv     physical tile shape; must divide the logical block sizes.
+ *                  seqlen = nq_logical*logical_block_q must equal
+ *                  nkv_logical*logical_block_kv.
+ *   kv_block_idx   out [batch, heads, seqlen/block_q, idx_ld]: ascending
+ *                  physical KV tile indices; slots past the count are not
+ *                  written.
+ *   kv_block_cnt   out [batch, heads, seqlen/block_q]: number of selected
+ *                  physical KV tiles (the true count, even if > idx_ld).
+ *   overflow       optional out (device int32, may be NULL): set to 1 if
+ *                  any row's count exceeds idx_ld (that row then keeps only
+ *                  its first idx_ld tiles); never cleared by this call.
+ */
+int32_t vsa_mask_to_csr(const uint8_t* mask, int32_t batch, int32_t heads, int32_t nq_logical,
+                        int32_t nkv_logical, int32_t logical_block_q, int32_t logical_block_kv,
+                        int32_t block_q, int32_t block_kv, int32_t* kv_block_idx, int32_t idx_ld,
+                        int32_t* kv_block_cnt, int32_t* overflow, void* stream);
+
+/*
+ * vsa_build_worklist -- mask front-end, step 2: count-sorted work list.
+ *
+ * Source: page "BlackwellMultiHeadLatentAttentionForwardFP8" (persistent
+ * tile scheduling over a device work list instead of a plain grid); the
+ * order here is longest-first for load balance.
+ *
+ *   kv_block_cnt  [n_items] int32 (the flattened [batch, heads, nq] counts)
+ *   max_cnt       counts are clamped to [0, max_cnt] for ordering (pass the
+ *                 idx_ld the counts belong to); 0 <= max_cnt <= 8191.
+ *   work_list     out [n_items] int32: the flat indices (b*heads + h)*nq + p
+ *                 sorted by clamped count, largest first; equal counts keep
+ *                 ascending index order. Deterministic.
+ */
+int32_t vsa_build_worklist(const int32_t* kv_block_cnt, int32_t n_items, int32_t max_cnt,
+                           int32_t* work_list, void* stream);
+
+/*
+ * vsa_attn_fwd -- fused block-sparse attention forward (O and LSE).
+ *
+ * Source: page 3, bench_vsa_blackwell.py, ref_masked_sdpa_fp32 (what is
+ * computed) and arm_fa4 / the _flash_attn_fwd call (the tile-list input and
+ * outputs). Online softmax in base 2 with scale*log2(e) folded into one
+ * multiply (page "BlackwellMultiHeadLatentAttentionForwardFP8", softmax
+ * and correction warps). bf16 inputs, fp32 accumulation, bf16 O rounded to
+ * nearest even, fp32 LSE in natural log.
+ *
+ *   block_q x block_kv in {64,128,256} x {64,128}; head_dim in {64, 128};
+ *   seqlen divisible by both; 0 < scale < inf; 1 <= idx_ld.
+ *   Builds the count-sorted work list in a library-owned device buffer
+ *   (grown on demand per device, released by vsa_release) and then runs
+ *   the kernel in that order; see vsa_attn_fwd_worklist for the kernel alone.
+ */
+int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
+                     const int32_t* kv_block_cnt, int32_t batch, int32_t seqlen, int32_t heads,
+                     int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv, float scale,
+                     void* o, float* lse, void* stream);
+
+/*
+ * vsa_attn_fwd_worklist -- the attention kernel alone, over a caller-built
+ * work list (for example from vsa_build_worklist). Each entry is a flat
+ * index (b*heads + h)*(seqlen/block_q) + p in [0, batch*heads*seqlen/block_q);
+ * entries outside that range are skipped. Only the Q tiles listed are
+ * written, once per listing. n_work >= 0.
+ */
+int32_t vsa_attn_fwd_worklist(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
+                              const int32_t* kv_block_cnt, int32_t batch, int32_t seqlen, int32_t heads,
+                              int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv,
+                              float scale, const int32_t* work_list, int32_t n_work, void* o, float* lse,
+                              void* stream);
+
+/* Free the library-owned work-list buffers on every device. Not thread-safe
+ * with concurrent vsa_attn_fwd calls. */
+void vsa_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_ATTN_H */

@@ -1,0 +1,118 @@
+"""Host-side checks of libvsa_attn.so (no GPU needed).
+
+The library must load, export every function ``include/vsa_attn.h``
+declares, and reject invalid arguments during host validation, before any
+HIP call is made.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_flashattention_amd as vsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vsa_attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(vsa_[a-z0-9_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return vsa.load_library()
+
+
+def test_header_declares_the_binding_symbols():
+    assert _declared_functions() == sorted(vsa.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.vsa_abi_version() == 1
+
+
+def test_status_strings(lib):
+    assert lib.vsa_status_string(0) == b"VSA_OK"
+    assert lib.vsa_status_string(-1) == b"VSA_ERR_INVALID_ARG"
+    assert lib.vsa_status_string(-2) == b"VSA_ERR_UNSUPPORTED"
+    assert lib.vsa_status_string(-3) == b"VSA_ERR_HIP"
+
+
+# Fake device addresses: validation must reject each call before any launch,
+# so these are never dereferenced.
+A = 0x10000
+
+
+def _fwd(lib, **kw):
+    args = dict(q=A, k=A, v=A, idx=A, cnt=A, B=1, S=1024, H=2, D=128, ld=16, bq=128, bkv=64, scale=0.1, o=A, lse=A)
+    args.update(kw)
+    return lib.vsa_attn_fwd(args["q"], args["k"], args["v"], args["idx"], args["cnt"], args["B"], args["S"],
+                            args["H"], args["D"], args["ld"], args["bq"], args["bkv"], args["scale"], args["o"],
+                            args["lse"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), -1, "null"),
+    (dict(lse=None), -1, "null"),
+    (dict(B=0), -1, ">= 1"),
+    (dict(S=1000), -1, "divisible"),
+    (dict(ld=0), -1, "idx_ld"),
+    (dict(scale=0.0), -1, "scale"),
+    (dict(scale=float("nan")), -1, "scale"),
+    (dict(scale=-1.0), -1, "scale"),
+    (dict(D=96), -2, "head_dim"),
+    (dict(bq=32), -2, "block_q"),
+    (dict(bkv=256), -2, "block_kv"),
+    (dict(q=A + 2), -1, "aligned"),
+    (dict(lse=A + 2), -1, "aligned"),
+    (dict(ld=9000), -2, "work-list"),
+])
+def test_attn_fwd_rejects_invalid_arguments(lib, kw, status, needle):
+    assert _fwd(lib, **kw) == status
+    assert needle in lib.vsa_last_error().decode()
+
+
+def test_attn_fwd_worklist_rejects_bad_work_list(lib):
+    rc = lib.vsa_attn_fwd_worklist(A, A, A, A, A, 1, 1024, 2, 128, 16, 128, 64, 0.1, None, 5, A, A, None)
+    assert rc == -1 and "work_list" in lib.vsa_last_error().decode()
+    rc = lib.vsa_attn_fwd_worklist(A, A, A, A, A, 1, 1024, 2, 128, 16, 128, 64, 0.1, A, -1, A, A, None)
+    assert rc == -1
+    # n_work == 0 is a no-op that succeeds without touching the device
+    assert lib.vsa_attn_fwd_worklist(A, A, A, A, A, 1, 1024, 2, 128, 16, 128, 64, 0.1, None, 0, A, A, None) == 0
+
+
+def test_mask_to_csr_rejects_invalid_arguments(lib):
+    f = lib.vsa_mask_to_csr
+    assert f(None, 1, 1, 4, 4, 256, 256, 128, 64, A, 8, A, None, None) == -1
+    # physical tile must divide the logical block
+    assert f(A, 1, 1, 4, 4, 256, 256, 96, 64, A, 8, A, None, None) == -1
+    assert "divide" in lib.vsa_last_error().decode()
+    # query and key lengths must agree
+    assert f(A, 1, 1, 4, 8, 256, 256, 128, 64, A, 8, A, None, None) == -1
+    assert f(A, 1, 1, 4, 4, 256, 256, 128, 64, A, 0, A, None, None) == -1
+
+
+def test_build_worklist_validation(lib):
+    assert lib.vsa_build_worklist(A, -1, 10, A, None) == -1
+    assert lib.vsa_build_worklist(A, 10, -1, A, None) == -1
+    assert lib.vsa_build_worklist(A, 10, 9000, A, None) == -1
+    assert lib.vsa_build_worklist(None, 10, 10, A, None) == -1
+    assert lib.vsa_build_worklist(None, 0, 10, None, None) == 0  # empty list: nothing to do
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 128, 1, 64, dtype=torch.bfloat16)
+    idx = torch.zeros(1, 1, 2, 2, dtype=torch.int32)
+    cnt = torch.zeros(1, 1, 2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        vsa.vsa_attn_fwd(q, q, q, idx, cnt, 64, 64)

@@ -1,0 +1,302 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances for the forward pass (bf16 O compared after conversion to fp32,
+fp32 LSE): max |dO| <= 2e-2, mean |dO| <= 2e-3, |dLSE| <= 1e-3*max(1, |LSE|).
+Integer front-end outputs must be bit-exact.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import frontend as ofront
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+O_MAX_ABS = 2e-2
+O_MEAN_ABS = 2e-3
+LSE_REL = 1e-3
+
+
+def say(msg):
+    line = f"[gpu-parity] {msg}"
+    print(line, flush=True)
+    path = os.environ.get("VSA_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(line + "\n")
+
+
+@pytest.fixture(scope="module")
+def vsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_flashattention_amd as m
+
+    m.load_library()
+    return m
+
+
+def dev(x):
+    if isinstance(x, np.ndarray):
+        x = torch.from_numpy(np.ascontiguousarray(x))
+    return x.contiguous().to("cuda")
+
+
+def check_rows(o_gpu, lse_gpu, rows, o_ref, lse_ref, S, H, label):
+    """Compare GPU O [B,S,H,D] / LSE [B,H,S] at flat rows against oracle rows."""
+    rows = np.asarray(rows, dtype=np.int64)
+    i = rows % S
+    h = (rows // S) % H
+    b = rows // (S * H)
+    og = o_gpu.float().cpu().numpy()[b, i, h]
+    lg = lse_gpu.cpu().numpy()[b, h, i]
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(fin, np.isfinite(lg)), f"{label}: LSE finiteness differs"
+    assert np.all(lg[~fin] == -np.inf), f"{label}: empty rows must have LSE=-inf"
+    assert np.all(og[~fin] == 0.0), f"{label}: empty rows must have O=0"
+    d = np.abs(og - o_ref)
+    max_abs, mean_abs = float(d.max()), float(d.mean())
+    lse_err = float((np.abs(lg[fin] - lse_ref[fin]) / np.maximum(1.0, np.abs(lse_ref[fin]))).max()) if fin.any() else 0.0
+    say(f"{label}: rows={rows.size} max|dO|={max_abs:.3e} mean|dO|={mean_abs:.3e} LSE rel={lse_err:.3e}")
+    assert np.isfinite(og).all()
+    assert max_abs <= O_MAX_ABS, f"{label}: max |dO| {max_abs}"
+    assert mean_abs <= O_MEAN_ABS, f"{label}: mean |dO| {mean_abs}"
+    assert lse_err <= LSE_REL, f"{label}: LSE rel err {lse_err}"
+
+
+def sample_rows(B, H, S, bq, tiles_per_head=3, seed=0):
+    rng = np.random.default_rng(seed)
+    nq = S // bq
+    out = []
+    for b in range(B):
+        for h in range(H):
+            tiles = {0, nq - 1} | set(rng.integers(0, nq, size=tiles_per_head).tolist())
+            for p in sorted(tiles):
+                local = {0, 1, 31, 32, 33, bq - 1} | set(rng.integers(0, bq, size=2).tolist())
+                for r in sorted(local):
+                    out.append((b * H + h) * S + p * bq + r)
+    return np.array(out, dtype=np.int64)
+
+
+# ----------------------------------------------------------------- front-end
+
+FRONT_CASES = [
+    ("tiny", W.TINY, (64, 64), 16),
+    ("vsa256->256x128", W.VSA256, (256, 128), 26),
+    ("vsa256->128x64", W.VSA256, (128, 64), 52),
+    ("vsa256->64x64", W.VSA256, (64, 64), 52),
+    ("vsa256->256x256", W.VSA256, (256, 256), 128),
+    ("native64 compact", W.NATIVE64, (64, 64), 92),
+    ("native64 full", W.NATIVE64, (64, 64), 512),
+    ("dense->128x128", W.DENSE, (128, 128), 32),
+]
+
+
+@pytest.mark.parametrize("label,wl,shape,ld", FRONT_CASES, ids=[c[0] for c in FRONT_CASES])
+def test_mask_to_csr_bit_exact(vsa, label, wl, shape, ld):
+    say(f"mask_to_csr {label}")
+    mask = wl.logical_mask()
+    idx_ref, cnt_ref, ovf_ref = ofront.mask_to_csr(mask, wl.logical_block, shape, ld)
+    ovf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    idx, cnt = vsa.vsa_mask_to_csr(dev(mask), wl.logical_block, shape, ld, overflow=ovf)
+    torch.cuda.synchronize()
+    cnt_h, idx_h = cnt.cpu().numpy(), idx.cpu().numpy()
+    assert np.array_equal(cnt_h, cnt_ref)
+    valid = np.arange(ld)[None, None, None, :] < np.minimum(cnt_ref, ld)[..., None]
+    assert np.array_equal(np.where(valid, idx_h, -1), np.where(valid, idx_ref, -1))
+    assert bool(ovf.item()) == ovf_ref
+
+
+def test_mask_to_csr_overflow_flag(vsa):
+    say("mask_to_csr overflow")
+    rng = np.random.default_rng(5)
+    mask = (rng.random((2, 3, 8, 16)) < 0.3).astype(np.uint8)
+    mask[1, 2, 3, :] = 1  # a full row: 16 cells -> 32 tiles at kv_ratio 2
+    ld = 20
+    idx_ref, cnt_ref, ovf_ref = ofront.mask_to_csr(mask, (128, 64), (64, 32), ld)
+    assert ovf_ref
+    ovf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    idx, cnt = vsa.vsa_mask_to_csr(dev(mask), (128, 64), (64, 32), ld, overflow=ovf)
+    torch.cuda.synchronize()
+    assert np.array_equal(cnt.cpu().numpy(), cnt_ref)
+    valid = np.arange(ld)[None, None, None, :] < np.minimum(cnt_ref, ld)[..., None]
+    assert np.array_equal(np.where(valid, idx.cpu().numpy(), -1), np.where(valid, idx_ref, -1))
+    assert ovf.item() == 1
+
+
+WL_CASES = [
+    ("native64 counts", None, 92),
+    ("random clamp", (-3, 100, 12345), 90),
+    ("single", (0, 5, 1), 5),
+    ("ragged 65", (0, 3, 65), 3),
+    ("many", (0, 600, 100000), 600),
+    ("wide bins", (0, 5000, 7777), 5000),
+    ("all equal", (7, 7, 3000), 7),
+]
+
+
+@pytest.mark.parametrize("label,spec,ld", WL_CASES, ids=[c[0] for c in WL_CASES])
+def test_worklist_bit_exact(vsa, label, spec, ld):
+    say(f"worklist {label}")
+    if spec is None:
+        mask = W.NATIVE64.logical_mask()
+        _, cnt, _ = ofront.mask_to_csr(mask, (64, 64), (64, 64), ld)
+        cnt = cnt.reshape(-1)
+    else:
+        lo, hi, n = spec
+        cnt = np.random.default_rng(n).integers(lo, hi + 1, size=n).astype(np.int32)
+    ref = ofront.build_worklist(cnt, ld)
+    got = vsa.vsa_build_worklist(dev(cnt), ld)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------ forward pass
+
+def _run_fwd(vsa, q, k, v, idx, cnt, bq, bkv, scale):
+    o, lse = vsa.vsa_attn_fwd(q, k, v, idx, cnt, bq, bkv, scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def test_tiny_workload_all_rows(vsa):
+    wl = W.TINY
+    say(f"forward {wl.name} (all rows)")
+    q, k, v = wl.qkv()
+    idx, cnt, _ = ofront.mask_to_csr(wl.logical_mask(), wl.logical_block, (64, 64), 16)
+    o_ref, lse_ref = oracle.attn_full(q, k, v, idx, cnt, 64, 64, wl.scale)
+    o, lse = _run_fwd(vsa, dev(q), dev(k), dev(v), dev(idx), dev(cnt), 64, 64, wl.scale)
+    B, S, H, D = q.shape
+    rows = np.arange(B * H * S)
+    check_rows(o, lse, rows, o_ref.transpose(0, 2, 1, 3).reshape(-1, D), lse_ref.reshape(-1), S, H, wl.name)
+
+
+SHAPES = [(bq, bkv, d) for bq in (64, 128, 256) for bkv in (64, 128) for d in (64, 128)]
+
+
+@pytest.mark.parametrize("bq,bkv,D", SHAPES, ids=[f"{a}x{b}_d{c}" for a, b, c in SHAPES])
+def test_every_tile_shape_all_rows(vsa, bq, bkv, D):
+    """Random shuffled CSR with empty and full rows, compact ld, B=2."""
+    B, H, S = 2, 2, 1024
+    say(f"forward shapes {bq}x{bkv} D={D}")
+    q, k, v = W.qkv(B, S, H, D, seed=bq + bkv + D)
+    nq, nkv = S // bq, S // bkv
+    idx, cnt = W.random_csr(B, H, nq, nkv, nkv, 0, nkv, seed=bq * 7 + bkv + D)
+    cnt[0, 0, 0] = 0
+    cnt[1, 1, nq - 1] = nkv
+    idx[1, 1, nq - 1] = np.random.default_rng(1).permutation(nkv)
+    ld = int(cnt.max())
+    idx = np.ascontiguousarray(idx[..., :ld])
+    scale = 1.0 / math.sqrt(D)
+    o_ref, lse_ref = oracle.attn_full(q, k, v, idx, cnt, bq, bkv, scale)
+    o, lse = _run_fwd(vsa, dev(q), dev(k), dev(v), dev(idx), dev(cnt), bq, bkv, scale)
+    rows = np.arange(B * H * S)
+    check_rows(o, lse, rows, o_ref.transpose(0, 2, 1, 3).reshape(-1, D), lse_ref.reshape(-1), S, H,
+               f"{bq}x{bkv} D={D}")
+
+
+def test_invalid_entries_are_skipped_and_counts_clamped(vsa):
+    """Out-of-range tile indices are skipped; counts above ld use ld entries."""
+    B, H, S, D, bq, bkv = 1, 2, 1024, 128, 128, 64
+    say("forward invalid entries")
+    q, k, v = W.qkv(B, S, H, D, seed=99)
+    nq, nkv = S // bq, S // bkv
+    idx, cnt = W.random_csr(B, H, nq, nkv, 8, 3, 6, seed=98)
+    idx[0, 0, 1, 1] = -5          # skipped
+    idx[0, 1, 2, 0] = nkv         # skipped
+    cnt[0, 1, 3] = 50             # clamped to ld = 8 (slots 6..7 hold -1: skipped)
+    idx_clean = np.full_like(idx, -1)
+    cnt_clean = np.zeros_like(cnt)
+    for pos in np.ndindex(cnt.shape):
+        ent = [t for t in idx[pos][:min(cnt[pos], 8)] if 0 <= t < nkv]
+        idx_clean[pos][:len(ent)] = ent
+        cnt_clean[pos] = len(ent)
+    o_ref, lse_ref = oracle.attn_full(q, k, v, idx_clean, cnt_clean, bq, bkv, 1 / math.sqrt(D))
+    o, lse = _run_fwd(vsa, dev(q), dev(k), dev(v), dev(idx), dev(cnt), bq, bkv, 1 / math.sqrt(D))
+    check_rows(o, lse, np.arange(B * H * S), o_ref.transpose(0, 2, 1, 3).reshape(-1, D), lse_ref.reshape(-1),
+               S, H, "invalid entries")
+
+
+def test_worklist_subset_writes_only_listed_tiles(vsa):
+    B, H, S, D, bq, bkv = 1, 2, 512, 64, 64, 64
+    say("forward work-list subset")
+    q, k, v = W.qkv(B, S, H, D, seed=5)
+    nq, nkv = S // bq, S // bkv
+    idx, cnt = W.random_csr(B, H, nq, nkv, nkv, 1, nkv, seed=6)
+    work = np.array([3, 0, 9, 15], dtype=np.int32)  # flat (h*nq + p)
+    o = torch.full((B, S, H, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, S), 7.0, dtype=torch.float32, device="cuda")
+    vsa.vsa_attn_fwd_worklist(dev(q), dev(k), dev(v), dev(idx), dev(cnt), bq, bkv, dev(work), o=o, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_full(q, k, v, idx, cnt, bq, bkv, 1 / math.sqrt(D))
+    listed = np.zeros((H, nq), dtype=bool)
+    listed.reshape(-1)[work] = True
+    rows = [(h * S + p * bq + r) for h in range(H) for p in range(nq) if listed[h, p] for r in range(bq)]
+    check_rows(o, lse, rows, o_ref.transpose(0, 2, 1, 3).reshape(-1, D)[rows], lse_ref.reshape(-1)[rows], S, H,
+               "subset")
+    on = o.float().cpu().numpy()
+    ln = lse.cpu().numpy()
+    for h in range(H):
+        for p in range(nq):
+            if not listed[h, p]:
+                assert np.all(on[0, p * bq:(p + 1) * bq, h] == 7.0)
+                assert np.all(ln[0, h, p * bq:(p + 1) * bq] == 7.0)
+
+
+def test_deterministic_and_stream_aware(vsa):
+    B, H, S, D, bq, bkv = 1, 3, 2048, 128, 128, 64
+    say("forward determinism + side stream")
+    q, k, v = (dev(t) for t in W.qkv(B, S, H, D, seed=3))
+    idx, cnt = W.random_csr(B, H, S // bq, S // bkv, S // bkv, 1, 20, seed=4)
+    idx, cnt = dev(idx), dev(cnt)
+    o1, l1 = _run_fwd(vsa, q, k, v, idx, cnt, bq, bkv, 0.09)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o2, l2 = vsa.vsa_attn_fwd(q, k, v, idx, cnt, bq, bkv, 0.09)
+    s.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------ full-size workloads
+
+def _full_size(vsa, wl, shape, ld, label, tiles_per_head=2):
+    say(f"forward {label}: generating inputs")
+    q, k, v = wl.qkv()
+    mask = wl.logical_mask()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    idx, cnt = vsa.vsa_mask_to_csr(dev(mask), wl.logical_block, shape, ld)
+    say(f"forward {label}: kernel {shape[0]}x{shape[1]}")
+    o, lse = _run_fwd(vsa, qd, kd, vd, idx, cnt, shape[0], shape[1], wl.scale)
+    B, S, H, D = q.shape
+    rows = sample_rows(B, H, S, shape[0], tiles_per_head, seed=shape[0] + shape[1])
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    o_ref, lse_ref = oracle.attn_rows(q, k, v, idx_h, cnt_h, shape[0], shape[1], wl.scale, rows)
+    check_rows(o, lse, rows, o_ref, lse_ref, S, H, label)
+    return o, lse
+
+
+def test_dense_workload_sampled(vsa):
+    _full_size(vsa, W.DENSE, (128, 128), 32, "dense 128x128")
+
+
+def test_vsa256_workload_sampled_and_cross_shape(vsa):
+    o0, l0 = _full_size(vsa, W.VSA256, (256, 128), 26, "vsa256 256x128")
+    for shape in ((128, 64), (64, 64)):
+        o1, l1 = _full_size(vsa, W.VSA256_FINE, shape, 52, f"vsa256 {shape[0]}x{shape[1]}")
+        d = (o1.float() - o0.float()).abs()
+        lrel = ((l1 - l0).abs() / l0.abs().clamp_min(1.0)).max().item()
+        say(f"cross-shape {shape}: max|dO|={d.max().item():.3e} mean|dO|={d.mean().item():.3e} LSE rel={lrel:.3e}")
+        assert d.max().item() <= O_MAX_ABS and d.mean().item() <= O_MEAN_ABS and lrel <= LSE_REL
+        del o1, l1
+    torch.cuda.empty_cache()
+
+
+def test_native64_workload_sampled(vsa):
+    _full_size(vsa, W.NATIVE64, (64, 64), 92, "native64 64x64", tiles_per_head=3)
+    torch.cuda.empty_cache()

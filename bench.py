@@ -91,7 +91,7 @@ def main():
     q_cpu, k_cpu, v_cpu = wl.qkv()
     mask_cpu = wl.logical_mask()
     q, k, v = (t.to(dev) for t in (q_cpu, k_cpu, v_cpu))
-    mask = torch.from_numpy(mask_cpu).to(dev)
+    mask = torch.from_numpy(np.ascontiguousarray(mask_cpu).copy()).to(dev)
     nq = S // bq
     ld = int(mask_cpu.sum(-1).max()) * (lkv // bkv)
     idx = torch.zeros((B, H, nq, ld), dtype=torch.int32, device=dev)
@@ -172,7 +172,7 @@ def main():
             "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "algorithmic_bytes": alg_bytes,
-            "kernel": f"vsa_fwd_kernel<{bq},{bkv},{D}>",
+            "kernel": kernel_name(bq, bkv, D),
         },
     }
 
@@ -181,6 +181,13 @@ def main():
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def kernel_name(bq, bkv, d):
+    """Name of the forward kernel the library dispatches for this tile shape."""
+    if bq == 256:
+        return f"vsa_fwd_pp_kernel<{bkv},{d}>"
+    return f"vsa_fwd_kernel<{bq},{bkv},{d}>"
 
 
 def cpu_baseline(wl, q, k, v, idx, cnt, bq, bkv, ld, seconds):

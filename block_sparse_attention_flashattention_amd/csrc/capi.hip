@@ -44,6 +44,8 @@ int32_t check_fwd(const void* q, const void* k, const void* v, const int32_t* id
     VSA_REQUIRE(seqlen % block_q == 0 && seqlen % block_kv == 0, VSA_ERR_INVALID_ARG,
                 "seqlen %d must be divisible by block_q %d and block_kv %d", seqlen, block_q, block_kv);
     VSA_REQUIRE(idx_ld >= 1, VSA_ERR_INVALID_ARG, "idx_ld must be >= 1");
+    VSA_REQUIRE(idx_ld <= vsa::kMaxIdxLd, VSA_ERR_UNSUPPORTED, "idx_ld %d exceeds the supported maximum %d", idx_ld,
+                vsa::kMaxIdxLd);
     VSA_REQUIRE(isfinite(scale) && scale > 0.0f, VSA_ERR_INVALID_ARG, "scale must be finite and > 0");
     VSA_REQUIRE(vsa::fwd_supported(block_q, block_kv, head_dim), VSA_ERR_UNSUPPORTED,
                 "no kernel for block_q=%d block_kv=%d head_dim=%d (supported: block_q in {64,128,256}, "

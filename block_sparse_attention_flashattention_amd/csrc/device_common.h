@@ -1,0 +1,72 @@
+// Device-side helpers shared by the forward kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vsa {
+namespace dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr float kLn2 = 0.6931471805599453f;
+// A stale row max is kept while a tile's max exceeds it by at most this many
+// powers of two, so un-normalised probabilities stay <= 2^8 (exact in math;
+// the final division by the row sum uses the same stale max).
+constexpr float kRescaleThreshold = 8.0f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two floats -> two bf16 (round to nearest even) in one 32-bit word.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Value of x held by lane (l ^ 32), combined with x: returns op(x, other).
+__device__ __forceinline__ float halfwave_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halfwave_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// LDS barrier across the workgroup: waits for this wave's LDS operations and
+// keeps the compiler from moving memory accesses across it. Outstanding
+// global loads (including loads into LDS) are NOT waited for.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// 16-byte direct-to-LDS load: lane l reads 16 bytes at base + voff and writes
+// them to LDS byte address lds + 16*l (lds and base wave-uniform). Issued
+// through inline asm so that the compiler's conservative wait on later LDS
+// reads of other buffers is not inserted; completion is awaited explicitly
+// with wait_global_loads() before the barrier that publishes the data.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(base), "s"(lds)
+        : "memory", "m0");
+}
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
+}
+
+// Wait for every outstanding global load of this wave (data landed in LDS).
+__device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+}  // namespace dev
+}  // namespace vsa

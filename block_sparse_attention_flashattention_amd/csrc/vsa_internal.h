@@ -27,6 +27,9 @@ struct FwdParams {
 // hipSuccess or the launch error. Shapes are validated by the caller.
 hipError_t launch_fwd(int block_q, int block_kv, int head_dim, const FwdParams& p, hipStream_t stream);
 
+// 256-row query tiles: the two-group ping-pong kernel (attn_fwd_pp.hip).
+hipError_t launch_fwd_pp(int block_kv, int head_dim, const FwdParams& p, hipStream_t stream);
+
 // Whether launch_fwd has a kernel for this configuration.
 bool fwd_supported(int block_q, int block_kv, int head_dim);
 
@@ -37,5 +40,7 @@ hipError_t launch_mask_to_csr(const uint8_t* mask, int batch, int heads, int nq_
 hipError_t launch_build_worklist(const int32_t* cnt, int n_items, int max_cnt, int32_t* work, hipStream_t stream);
 
 constexpr int kWorklistMaxCnt = 8191;
+// Largest CSR row length the forward kernels accept (rows are staged in LDS).
+constexpr int kMaxIdxLd = 8191;
 
 }  // namespace vsa

@@ -124,7 +124,7 @@ int32_t vsa_build_worklist(const int32_t* kv_block_cnt, int32_t n_items, int32_t
  * nearest even, fp32 LSE in natural log.
  *
  *   block_q x block_kv in {64,128,256} x {64,128}; head_dim in {64, 128};
- *   seqlen divisible by both; 0 < scale < inf; 1 <= idx_ld.
+ *   seqlen divisible by both; 0 < scale < inf; 1 <= idx_ld <= 8191.
  *   Builds the count-sorted work list in a library-owned device buffer
  *   (grown on demand per device, released by vsa_release) and then runs
  *   the kernel in that order; see vsa_attn_fwd_worklist for the kernel alone.

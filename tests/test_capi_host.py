@@ -73,7 +73,7 @@ def _fwd(lib, **kw):
     (dict(bkv=256), -2, "block_kv"),
     (dict(q=A + 2), -1, "aligned"),
     (dict(lse=A + 2), -1, "aligned"),
-    (dict(ld=9000), -2, "work-list"),
+    (dict(ld=9000), -2, "maximum"),
 ])
 def test_attn_fwd_rejects_invalid_arguments(lib, kw, status, needle):
     assert _fwd(lib, **kw) == status

@@ -29,6 +29,8 @@
 // of a 16-lane group addressing row (kv0 + j/4), columns d0 + 4*(j%4) .. +3,
 // lane i receives column d0 + i of rows kv0 .. kv0+3. The V swizzle spreads
 // the 8 rows x 64 bytes of one such read over all 64 banks.
+#include <type_traits>
+
 #include "device_common.h"
 #include "vsa_internal.h"
 
@@ -71,6 +73,31 @@ __device__ __forceinline__ int swz_v(int row) {
     else return ((row >> 1) & 1) << 2;
 }
 
+// Scheduling pins for one MFMA phase (see mfma_phase in the kernel): the LDS
+// reads of the first RING steps, then per step its MFMA followed by the reads
+// of the step RING ahead. Masks: 0x100 LDS read, 0x008 MFMA.
+template <bool PV, bool QK>
+constexpr int step_reads(int st) {
+    return (PV && (!QK || (st & 1) == 0)) ? 2 : 1;  // PV: two 8-byte transposing reads
+}
+template <bool PV, bool QK, int RING, int NS, int ST = 0>
+__device__ __forceinline__ void pin_mfma_schedule() {
+    if constexpr (ST == 0) {
+        constexpr int pre = step_reads<PV, QK>(0) + step_reads<PV, QK>(1) + step_reads<PV, QK>(2) +
+                            step_reads<PV, QK>(3);
+        static_assert(RING == 4, "prefetch count assumes a ring of 4");
+        __builtin_amdgcn_sched_group_barrier(0x100, pre, 0);
+    }
+    if constexpr (ST < NS) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (ST + RING < NS) {
+            constexpr int r = step_reads<PV, QK>(ST + RING);
+            __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+        }
+        pin_mfma_schedule<PV, QK, RING, NS, ST + 1>();
+    }
+}
+
 template <int BKV, int D>
 __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     using C = PP<BKV, D>;
@@ -83,7 +110,15 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
-    const int wi = blockIdx.x;
+    // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs;
+    // give each XCD a contiguous run of the work list instead, so that the
+    // tiles it works on concurrently share K/V tiles in its own L2.
+    int wi;
+    {
+        const int nwg = gridDim.x, xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+        const int per = nwg / 8, rem = nwg % 8;
+        wi = (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+    }
     if (wi >= prm.n_work) return;
     const int item = prm.work ? prm.work[wi] : wi;
     if (item < 0 || item >= prm.n_items) return;
@@ -174,33 +209,63 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
         }
     }
 
-    // O^T += V^T P^T over the V tile at LDS offset vb
-    auto pv = [&](int vb) {
+    // MFMA phase. Steps are O^T += V^T P^T products (PV, over the V tile at
+    // LDS offset vb) and S^T = K Q^T products (QK, over the K tile at kb);
+    // when both run they alternate 1:1 so consecutive MFMAs use independent
+    // accumulators. Each step's A operand (two transposing 8-byte reads for
+    // PV, one 16-byte read for QK) is fetched RING steps ahead into a
+    // register ring, so LDS latency is hidden behind the MFMAs in flight.
+    constexpr int RING = 4;
+    auto mfma_phase = [&](auto pv_on, auto qk_on, int vb, int kb) {
+        constexpr bool PV = decltype(pv_on)::value;
+        constexpr bool QK = decltype(qk_on)::value;
+        constexpr int NPV = PV ? C::DB * C::KC : 0;
+        constexpr int NQK = QK ? C::NB * C::DC : 0;
+        constexpr int NS = NPV + NQK;
+        // step s -> (is_pv, item); PV item i = (g = i / DB, db = i % DB),
+        // QK item i = (c = i / NB, nb = i % NB)
+        auto is_pv = [](int st) { return PV && (!QK || (st & 1) == 0); };
+        auto item = [](int st) { return (PV && QK) ? (st >> 1) : st; };
+        auto load = [&](int st) -> bf16x8 {
+            const int i = item(st);
+            if (is_pv(st)) {
+                const int g = i / C::DB, db = i % C::DB;
+                const char* base = smem + vb + voff[db] + (g * 16) * C::ROW_BYTES;
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)base);
+                const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 8 * C::ROW_BYTES));
+                return __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+            } else {
+                const int c = i / C::NB, nb = i % C::NB;
+                return *(const bf16x8*)(smem + kb + koff[c] + nb * 32 * C::ROW_BYTES);
+            }
+        };
+        if constexpr (QK) {
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-            const char* base = smem + vb + voff[db];
+            for (int nb = 0; nb < C::NB; ++nb) sacc[nb] = f32x16{};
+        }
+        bf16x8 ring[RING];
 #pragma unroll
-            for (int g = 0; g < C::KC; ++g) {
-                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + (g * 16) * C::ROW_BYTES));
-                const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + (g * 16 + 8) * C::ROW_BYTES));
-                const bf16x8 av = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pk[g], oacc[db], 0, 0, 0);
+        for (int st = 0; st < RING && st < NS; ++st) ring[st] = load(st);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            const bf16x8 a = ring[st % RING];
+            if (st + RING < NS) ring[st % RING] = load(st + RING);
+            const int i = item(st);
+            if (is_pv(st)) {
+                const int g = i / C::DB, db = i % C::DB;
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[g], oacc[db], 0, 0, 0);
+            } else {
+                const int c = i / C::NB, nb = i % C::NB;
+                sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[c], sacc[nb], 0, 0, 0);
             }
         }
+        pin_mfma_schedule<PV, QK, RING, NS>();
     };
-
-    // S^T = K Q^T over the K tile at LDS offset kb
-    auto qk = [&](int kb) {
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-            sacc[nb] = f32x16{};
-#pragma unroll
-            for (int c = 0; c < C::DC; ++c) {
-                const char* a = smem + kb + koff[c] + nb * 32 * C::ROW_BYTES;
-                sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)a, qreg[c], sacc[nb], 0, 0, 0);
-            }
-        }
-    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    auto pv = [&](int vb) { mfma_phase(yes{}, no{}, vb, 0); };
+    auto qk = [&](int kb) { mfma_phase(no{}, yes{}, 0, kb); };
+    auto pv_qk = [&](int vb, int kb) { mfma_phase(yes{}, yes{}, vb, kb); };
 
     // softmax of S_j into pk (bf16), with the lazy rescale of O and l
     auto softmax = [&](bool ok) {
@@ -251,24 +316,48 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
 
     // Both groups pass 2(n+1) barriers. Each group has its own loop so that
     // S (live from M_j to V_j) and P (live from V_j to M_{j+1}) never both
-    // cross a loop back-edge.
+    // cross a loop back-edge, and the first and last tiles are peeled so the
+    // steady-state MFMA phase (PV_{j-1} then QK_j) is one basic block whose
+    // two independent accumulator sets the scheduler can interleave.
     if (grp == 0) {
-        for (int j = 0; j <= n; ++j) {
-            if (j >= 1) pv(vbuf(j - 1));       // phase 2j: M_j
-            if (j < n) qk(kbuf(j));
+        if (n > 0) {
+            qk(kbuf(0));                                   // M_0
             lds_barrier();
-            if (j < n) softmax(valid(tile_of(j)));   // phase 2j+1: V_j
+            softmax(valid(tile_of(0)));                    // V_0
             lds_barrier();
+            for (int j = 1; j < n; ++j) {
+                pv_qk(vbuf(j - 1), kbuf(j));               // M_j
+                lds_barrier();
+                softmax(valid(tile_of(j)));                // V_j
+                lds_barrier();
+            }
+            pv(vbuf(n - 1));                               // M_n
         }
+        lds_barrier();
+        lds_barrier();
     } else {
-        for (int j = 0; j <= n; ++j) {
-            if (j + 1 < n) issue_tile(kbase, kbuf(j + 1), tile_of(j + 1), false);   // phase 2j
-            if (j < n) issue_tile(vbase, vbuf(j), tile_of(j), true);
-            if (j >= 1) softmax(valid(tile_of(j - 1)));                                 // V_{j-1}
+        if (n > 0) {
+            if (n > 1) issue_tile(kbase, kbuf(1), tile_of(1), false);
+            issue_tile(vbase, vbuf(0), tile_of(0), true);
             lds_barrier();
-            if (j >= 1) pv(vbuf(j - 1));                                          // phase 2j+1: M_j
-            if (j < n) qk(kbuf(j));
+            qk(kbuf(0));                                   // M_0
             wait_global_loads();
+            lds_barrier();
+            for (int j = 1; j < n; ++j) {
+                if (j + 1 < n) issue_tile(kbase, kbuf(j + 1), tile_of(j + 1), false);
+                issue_tile(vbase, vbuf(j), tile_of(j), true);
+                softmax(valid(tile_of(j - 1)));            // V_{j-1}
+                lds_barrier();
+                pv_qk(vbuf(j - 1), kbuf(j));               // M_j
+                wait_global_loads();
+                lds_barrier();
+            }
+            softmax(valid(tile_of(n - 1)));                // V_{n-1}
+            lds_barrier();
+            pv(vbuf(n - 1));                               // M_n
+            lds_barrier();
+        } else {
+            lds_barrier();
             lds_barrier();
         }
     }

@@ -52,6 +52,12 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // reads of other buffers is not inserted; completion is awaited explicitly
 // with wait_global_loads() before the barrier that publishes the data.
 __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint32_t lds) {
+    // both operands are uniform; pin them to scalar registers
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t bhi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    base = (const void*)(uintptr_t)(((uint64_t)bhi << 32) | blo);
+    lds = __builtin_amdgcn_readfirstlane(lds);
     asm volatile(
         "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"

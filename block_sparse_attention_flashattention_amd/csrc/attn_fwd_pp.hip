@@ -19,10 +19,10 @@
 //     group 0:  M_0   V_0   M_1   V_1   M_2 ...  M_n
 //     group 1:  -     M_0   V_0   M_1   V_1 ...  V_n-1 M_n
 //
-// K and V tiles are double-buffered in LDS and fetched by group 1 with
-// direct-to-LDS 16-byte loads (global_load_lds_dwordx4) at the start of its
-// VALU phases: loads issued in phase 2j (K_{j+1}, V_j) are waited for at the
-// end of phase 2j+1, two phases before first use. Both tiles are stored
+// K and V tiles are double-buffered in LDS and fetched with direct-to-LDS
+// 16-byte loads (global_load_lds_dwordx4): K_{j+1} by group 1 and V_j by
+// group 0, both issued at the start of phase 2j and waited for at the end of
+// phase 2j+1, two phases before first use. Both tiles are stored
 // row-major with 16-byte chunks XOR-swizzled on the global side. K rows feed
 // the A operand of S^T = K Q^T with ds_read_b128; V feeds the A operand of
 // O^T = V^T P^T through the transposing read ds_read_b64_tr_b16: with lane j
@@ -47,7 +47,7 @@ struct PP {
     static constexpr int NC = D / 8;               // 16-byte chunks per row
     static constexpr int TILE = BKV * ROW_BYTES;   // bytes per K (or V) tile
     static constexpr int ROWS_PER_KB = 1024 / ROW_BYTES;
-    static constexpr int BLOCKS_PER_WAVE = TILE / 1024 / 4;   // 1 KB loads per group-1 wave
+    static constexpr int BLOCKS_PER_WAVE = TILE / 1024 / 4;   // 1 KB loads per wave of a group
     static constexpr int DC = D / 16;              // QK^T k-steps
     static constexpr int NB = BKV / 32;            // 32-key blocks of S^T
     static constexpr int DB = D / 32;              // 32-wide d blocks of O^T
@@ -161,12 +161,13 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     auto tile_of = [&](int j) { return __builtin_amdgcn_readfirstlane(lidx[j]); };
     auto valid = [&](int t) { return t >= 0 && t < nkv; };
 
-    // One group-1 wave's share of a tile: BLOCKS_PER_WAVE 1 KB direct-to-LDS
-    // loads, each from a uniform row base plus a 32-bit per-lane offset.
+    // One wave's share of a tile fetched by its group: BLOCKS_PER_WAVE 1 KB
+    // direct-to-LDS loads, each from a uniform row base plus a 32-bit
+    // per-lane offset.
     const int tok_bytes = (int)(tok_stride * 2);
     auto issue_tile = [&](const uint16_t* base, int dst, int t, bool v_layout) {
         const char* tile = (const char*)base + (int64_t)(valid(t) ? t : 0) * BKV * tok_bytes;
-        const int gw = wave - 4;
+        const int gw = wave & 3;
         const int rl = lane / C::NC, pos = lane % C::NC;
 #pragma unroll
         for (int i = 0; i < C::BLOCKS_PER_WAVE; ++i) {
@@ -319,16 +320,24 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     // cross a loop back-edge, and the first and last tiles are peeled so the
     // steady-state MFMA phase (PV_{j-1} then QK_j) is one basic block whose
     // two independent accumulator sets the scheduler can interleave.
+    // Tile fetches: group 1 issues K_{j+1} at the start of phase 2j (its
+    // softmax phase), group 0 issues V_j at the start of phase 2j (its MFMA
+    // phase); both wait at the end of phase 2j+1, so every load has two
+    // phases to land before its first use in phase 2j+2.
     if (grp == 0) {
         if (n > 0) {
+            issue_tile(vbase, vbuf(0), tile_of(0), true);
             qk(kbuf(0));                                   // M_0
             lds_barrier();
             softmax(valid(tile_of(0)));                    // V_0
+            wait_global_loads();
             lds_barrier();
             for (int j = 1; j < n; ++j) {
+                issue_tile(vbase, vbuf(j), tile_of(j), true);
                 pv_qk(vbuf(j - 1), kbuf(j));               // M_j
                 lds_barrier();
                 softmax(valid(tile_of(j)));                // V_j
+                wait_global_loads();
                 lds_barrier();
             }
             pv(vbuf(n - 1));                               // M_n
@@ -338,14 +347,12 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     } else {
         if (n > 0) {
             if (n > 1) issue_tile(kbase, kbuf(1), tile_of(1), false);
-            issue_tile(vbase, vbuf(0), tile_of(0), true);
             lds_barrier();
             qk(kbuf(0));                                   // M_0
             wait_global_loads();
             lds_barrier();
             for (int j = 1; j < n; ++j) {
                 if (j + 1 < n) issue_tile(kbase, kbuf(j + 1), tile_of(j + 1), false);
-                issue_tile(vbase, vbuf(j), tile_of(j), true);
                 softmax(valid(tile_of(j - 1)));            // V_{j-1}
                 lds_barrier();
                 pv_qk(vbuf(j - 1), kbuf(j));               // M_j

@@ -313,11 +313,8 @@ hipError_t launch_fwd(int block_q, int block_kv, int head_dim, const FwdParams& 
     VSA_CASE(64, 64, 128)
     VSA_CASE(64, 128, 64)
     VSA_CASE(64, 128, 128)
-    VSA_CASE(128, 64, 64)
-    VSA_CASE(128, 64, 128)
-    VSA_CASE(128, 128, 64)
-    VSA_CASE(128, 128, 128)
 #undef VSA_CASE
+    if (block_q == 128) return launch_fwd_2s(block_kv, head_dim, p, stream);
     if (block_q == 256) return launch_fwd_pp(block_kv, head_dim, p, stream);
     return hipErrorInvalidValue;
 }

@@ -1,0 +1,168 @@
+// Fused block-sparse attention forward for 128-row query tiles on gfx950:
+// two KV streams per query tile, one per wave group, in alternating phases.
+//
+// What is computed: FastVideo page "[perf] Add fine-grained FA4 VSA kernels",
+// ref_masked_sdpa_fp32 (per-wave arithmetic in wave_engine.h). The split of
+// one query tile's KV list into two streams whose (max, sum, O) partials are
+// merged in fp32 follows that page's fork notes (single-Q-block, two-KV-stream
+// schedule with an FP32 online-softmax merge); the merge itself is the
+// split-KV combination of page "BlackwellMultiHeadLatentAttentionForwardFP8"
+// (reduction_kernel: rescale each partial to the larger max).
+//
+// Schedule. All eight waves work on the same 128 query rows: wave w and wave
+// w+4 own rows [32*(w%4), +32). The tile's KV list, cut into 64-key
+// sub-tiles, is split in two halves: group 0 (waves 0-3) takes the first,
+// group 1 (waves 4-7) the second. Each group runs MFMA phases (PV of its
+// previous sub-tile, QK of its current one) and softmax phases; group 1 is
+// one phase behind group 0 and every phase ends in a workgroup barrier, so on
+// each SIMD one wave issues MFMAs while the other runs the softmax. Each group
+// has its own double-buffered K/V sub-tiles in LDS and fetches them itself
+// with direct-to-LDS loads issued at the start of its MFMA phase M_j (K_{j+1},
+// V_j) and waited for at the end of its softmax phase V_j. At the end group 1
+// hands its partial rows to group 0 through LDS, which merges and writes O and
+// LSE.
+#include "device_common.h"
+#include "vsa_internal.h"
+#include "wave_engine.h"
+
+namespace vsa {
+namespace {
+
+using namespace dev;
+
+constexpr int kIdxCap2s = 8192;  // CSR row entries staged in LDS (>= the largest idx_ld)
+
+template <int D>
+__global__ __launch_bounds__(512) void vsa_fwd_2s_kernel(FwdParams prm) {
+    constexpr int BQ = 128;
+    constexpr int SUB = 64;  // keys per sub-tile
+    using E = WaveEngine<SUB, D>;
+    using G = TileGeom<SUB, D>;
+    constexpr int GROUP_LDS = 4 * G::TILE;  // K[2], V[2] of one group
+    static_assert(4 * E::STATE_WORDS * 64 * 4 <= 2 * GROUP_LDS, "merge exchange must fit in the tile buffers");
+    __shared__ __attribute__((aligned(1024))) char smem[2 * GROUP_LDS + kIdxCap2s * 4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int grp = wave >> 2;
+    const int l32 = lane & 31;
+
+    const int wi = xcd_contiguous_block();
+    if (wi >= prm.n_work) return;
+    const int item = prm.work ? prm.work[wi] : wi;
+    if (item < 0 || item >= prm.n_items) return;
+
+    const int p = item % prm.nq;
+    const int bh = item / prm.nq;
+    const int h = bh % prm.H;
+    const int b = bh / prm.H;
+    const int S = prm.S;
+    const int64_t tok_stride = (int64_t)prm.H * D;
+    const int tok_bytes = (int)(tok_stride * 2);
+    int n = prm.cnt[item];
+    n = n < 0 ? 0 : (n > prm.ld ? prm.ld : n);
+    n = n > kIdxCap2s ? kIdxCap2s : n;
+    const int32_t* irow = prm.idx + (int64_t)item * prm.ld;
+    const int nkv = prm.nkv;
+    const int block_kv = prm.block_kv;
+    const int R = block_kv / SUB;  // sub-tiles per CSR tile (1 or 2)
+    const int q0 = p * BQ + (wave & 3) * 32;
+
+    // this group's stream: sub-tiles [first, first + ng)
+    const int N = n * R;
+    const int N0 = (N + 1) / 2, N1 = N - N0;
+    const int first = grp ? N0 : 0;
+    const int ng = grp ? N1 : N0;
+
+    E e;
+    e.init(smem, lane, prm.scale_log2);
+    e.load_q(prm.q + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D);
+
+    int* lidx = (int*)(smem + 2 * GROUP_LDS);
+    for (int i = tid; i < n; i += 512) lidx[i] = irow[i];
+    lds_barrier();
+
+    // sub-tile j of this stream -> CSR entry and 64-key offset inside it
+    auto tile_of = [&](int j) { return __builtin_amdgcn_readfirstlane(lidx[(first + j) / R]); };
+    auto valid = [&](int t) { return t >= 0 && t < nkv; };
+    const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    auto issue = [&](const char* base, int dst, int j, bool v_layout) {
+        const int t = tile_of(j);
+        const int64_t row0 = (int64_t)(valid(t) ? t : 0) * block_kv + ((first + j) % R) * SUB;
+        issue_tile<SUB, D>(smem, dst, base + row0 * tok_bytes, tok_bytes, v_layout, wave & 3, lane);
+    };
+    const int gbase = grp * GROUP_LDS;
+    auto kbuf = [&](int j) { return gbase + (j & 1) * G::TILE; };
+    auto vbuf = [&](int j) { return gbase + (2 + (j & 1)) * G::TILE; };
+    auto qk = [&](int j) { e.template mfma_phase<false, true>(0, kbuf(j)); };
+    auto pv = [&](int j) { e.template mfma_phase<true, false>(vbuf(j), 0); };
+    auto pv_qk = [&](int jv, int jk) { e.template mfma_phase<true, true>(vbuf(jv), kbuf(jk)); };
+    auto softmax = [&](int j) { e.softmax(valid(tile_of(j))); };
+
+    // Every wave passes the same number of barriers: group 0 uses 2*N0 + 2,
+    // group 1 (one phase later) 2*N1 + 3; the shorter one pads at the end.
+    const int total = max(2 * N0 + 2, 2 * N1 + 3);
+    int nbar = 0;
+    auto bar = [&]() {
+        lds_barrier();
+        ++nbar;
+    };
+
+    if (ng > 0) {
+        issue(kbase, kbuf(0), 0, false);
+        wait_global_loads();
+    }
+    bar();
+    if (grp == 1) bar();
+    if (ng > 0) {
+        if (ng > 1) issue(kbase, kbuf(1), 1, false);
+        issue(vbase, vbuf(0), 0, true);
+        qk(0);                                   // M_0
+        bar();
+        softmax(0);                              // V_0
+        wait_global_loads();
+        bar();
+        for (int j = 1; j < ng; ++j) {
+            if (j + 1 < ng) issue(kbase, kbuf(j + 1), j + 1, false);
+            issue(vbase, vbuf(j), j, true);
+            pv_qk(j - 1, j);                     // M_j
+            bar();
+            softmax(j);                          // V_j
+            wait_global_loads();
+            bar();
+        }
+        pv(ng - 1);                              // M_n
+        bar();
+    }
+    while (nbar < total) bar();
+
+    // merge the two streams' partial rows; the tile buffers are free now
+    float* xch = (float*)smem + (wave & 3) * E::STATE_WORDS * 64;
+    if (grp == 1) e.export_state(xch);
+    lds_barrier();
+    if (grp == 0) {
+        e.merge_state(xch);
+        e.store(prm.o + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D,
+                prm.lse + ((int64_t)b * prm.H + h) * S + q0 + l32);
+    }
+}
+
+template <int D>
+hipError_t launch_2s(const FwdParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL((vsa_fwd_2s_kernel<D>), dim3(p.n_work), dim3(512), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_2s(int block_kv, int head_dim, const FwdParams& p, hipStream_t stream) {
+    if (p.n_work <= 0) return hipSuccess;
+    if (block_kv != 64 && block_kv != 128) return hipErrorInvalidValue;
+    if (head_dim == 128) return launch_2s<128>(p, stream);
+    if (head_dim == 64) return launch_2s<64>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace vsa

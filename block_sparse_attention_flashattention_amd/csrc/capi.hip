@@ -81,6 +81,7 @@ vsa::FwdParams make_params(const void* q, const void* k, const void* v, const in
     p.nq = seqlen / block_q;
     p.nkv = seqlen / block_kv;
     p.ld = idx_ld;
+    p.block_kv = block_kv;
     p.n_items = batch * heads * p.nq;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);
     return p;

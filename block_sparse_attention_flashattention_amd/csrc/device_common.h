@@ -74,5 +74,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Wait for every outstanding global load of this wave (data landed in LDS).
 __device__ __forceinline__ void wait_global_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Consecutive workgroup ids are dispatched round-robin over the 8 XCDs. Map
+// them so each XCD takes a contiguous run of [0, gridDim.x) instead: the
+// work-list entries it processes concurrently then share K/V tiles in its own
+// L2. A bijection for any grid size.
+__device__ __forceinline__ int xcd_contiguous_block() {
+    const int nwg = gridDim.x, xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    const int per = nwg / 8, rem = nwg % 8;
+    return (xcd < rem) ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
 }  // namespace dev
 }  // namespace vsa

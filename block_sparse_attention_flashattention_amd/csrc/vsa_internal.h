@@ -20,6 +20,7 @@ struct FwdParams {
     int32_t n_work;
     int32_t n_items;         // B * H * nq
     int32_t S, H, nq, nkv, ld;
+    int32_t block_kv;        // tokens per KV tile of the CSR
     float scale_log2;        // softmax scale * log2(e)
 };
 
@@ -29,6 +30,8 @@ hipError_t launch_fwd(int block_q, int block_kv, int head_dim, const FwdParams& 
 
 // 256-row query tiles: the two-group ping-pong kernel (attn_fwd_pp.hip).
 hipError_t launch_fwd_pp(int block_kv, int head_dim, const FwdParams& p, hipStream_t stream);
+// 128-row query tiles: the two-KV-stream ping-pong kernel (attn_fwd_2s.hip).
+hipError_t launch_fwd_2s(int block_kv, int head_dim, const FwdParams& p, hipStream_t stream);
 
 // Whether launch_fwd has a kernel for this configuration.
 bool fwd_supported(int block_q, int block_kv, int head_dim);

@@ -1,0 +1,307 @@
+// Per-wave machinery of the phase-alternating ("ping-pong") forward kernels
+// on gfx950: one wave owns 32 query rows and accumulates
+//     S^T = K Q^T   and   O^T += V^T P^T
+// with v_mfma_f32_32x32x16_bf16 over KV tiles staged in LDS.
+//
+// Layout facts used throughout (32x32x16 MFMA, wave64; l = lane):
+//  * A operand: lane l supplies row (l % 32), 8 consecutive k slots of half
+//    (l / 32); B operand: lane l supplies column (l % 32), same k slots.
+//  * Result: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, column
+//    (l % 32).
+// With S^T (keys x queries) each lane therefore holds 16 scores of query row
+// (l % 32) per 32-key block, so the row max/sum is an in-lane reduction plus
+// one exchange between the half-waves, and the bf16-packed probabilities are
+// directly the B operand of O^T = V^T P^T, whose accumulator is again indexed
+// by query column, making the per-row rescale lane-uniform.
+//
+// Online softmax in base 2 with scale*log2(e) folded into one FMA, a running
+// row max and row sum, and a correction of O that is skipped while the max
+// grows by at most kRescaleThreshold (page "BlackwellMultiHeadLatentAttention
+// ForwardFP8", softmax / correction / skip_correction_threshold; what is
+// computed: FastVideo page "[perf] Add fine-grained FA4 VSA kernels",
+// ref_masked_sdpa_fp32).
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.h"
+
+namespace vsa {
+namespace dev {
+
+// 16-byte-chunk XOR swizzles (involutions: LDS position <-> global chunk).
+template <int NC>
+__device__ __forceinline__ int swz_k(int row) {
+    // 16 consecutive rows of one chunk column land in 16 distinct bank groups
+    if constexpr (NC == 16) return row & 15;
+    else return (row >> 1) & 7;
+}
+template <int NC>
+__device__ __forceinline__ int swz_v(int row) {
+    // the 8 rows x 4 chunks of one transposing read cover every bank group twice
+    if constexpr (NC == 16) return (row & 3) << 2;
+    else return ((row >> 1) & 1) << 2;
+}
+
+// Scheduling pins for one MFMA phase: the LDS reads of the first RING steps,
+// then per step its MFMA followed by the reads of the step RING ahead.
+// Masks: 0x100 LDS read, 0x008 MFMA.
+template <bool PV, bool QK>
+constexpr int step_reads(int st) {
+    return (PV && (!QK || (st & 1) == 0)) ? 2 : 1;  // PV: two 8-byte transposing reads
+}
+template <bool PV, bool QK, int RING, int NS, int ST = 0>
+__device__ __forceinline__ void pin_mfma_schedule() {
+    if constexpr (ST == 0) {
+        static_assert(RING == 4, "prefetch count assumes a ring of 4");
+        constexpr int pre = (NS > 0 ? step_reads<PV, QK>(0) : 0) + (NS > 1 ? step_reads<PV, QK>(1) : 0) +
+                            (NS > 2 ? step_reads<PV, QK>(2) : 0) + (NS > 3 ? step_reads<PV, QK>(3) : 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, pre, 0);
+    }
+    if constexpr (ST < NS) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (ST + RING < NS) {
+            constexpr int r = step_reads<PV, QK>(ST + RING);
+            __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+        }
+        pin_mfma_schedule<PV, QK, RING, NS, ST + 1>();
+    }
+}
+
+// K/V tile geometry in LDS: BKV rows of D bf16, row-major, 16-byte chunks
+// swizzled with swz_k (K) or swz_v (V).
+template <int BKV, int D>
+struct TileGeom {
+    static constexpr int ROW_BYTES = D * 2;
+    static constexpr int NC = D / 8;               // 16-byte chunks per row
+    static constexpr int TILE = BKV * ROW_BYTES;   // bytes per tile
+    static constexpr int ROWS_PER_KB = 1024 / ROW_BYTES;
+    static constexpr int BLOCKS_PER_WAVE = TILE / 1024 / 4;   // 1 KB loads per wave of a 4-wave group
+    static_assert(NC == 8 || NC == 16, "head_dim 64 or 128");
+    static_assert(BLOCKS_PER_WAVE >= 1 && TILE % 4096 == 0, "tile must split over four waves");
+};
+
+// One wave's share (gw = 0..3 within its 4-wave group) of fetching a tile:
+// BLOCKS_PER_WAVE direct-to-LDS 1 KB loads, each from a uniform row base plus
+// a 32-bit per-lane offset. `tile` points at row 0 of the tile for this head;
+// consecutive rows are tok_bytes apart.
+template <int BKV, int D>
+__device__ __forceinline__ void issue_tile(char* smem, int dst, const char* tile, int tok_bytes, bool v_layout, int gw,
+                                           int lane) {
+    using G = TileGeom<BKV, D>;
+    const int rl = lane / G::NC, pos = lane % G::NC;
+#pragma unroll
+    for (int i = 0; i < G::BLOCKS_PER_WAVE; ++i) {
+        const int blk = gw * G::BLOCKS_PER_WAVE + i;
+        const int row = blk * G::ROWS_PER_KB + rl;
+        const int c = pos ^ (v_layout ? swz_v<G::NC>(row) : swz_k<G::NC>(row));
+        const char* src = tile + (int64_t)(blk * G::ROWS_PER_KB) * tok_bytes;
+        const uint32_t off = (uint32_t)(rl * tok_bytes + c * 16);
+        lds_dma16(src, off, lds_addr(smem + dst + blk * 1024));
+    }
+}
+
+template <int BKV, int D>
+struct WaveEngine {
+    using G = TileGeom<BKV, D>;
+    static constexpr int DC = D / 16;    // QK^T k-steps
+    static constexpr int NB = BKV / 32;  // 32-key blocks of S^T
+    static constexpr int DB = D / 32;    // 32-wide d blocks of O^T
+    static constexpr int KC = BKV / 16;  // PV k-steps
+    static constexpr int RING = 4;       // operand prefetch distance (MFMA steps)
+    // fp32 words per lane exchanged when two waves merge their partial rows
+    static constexpr int STATE_WORDS = DB * 16 + 2;
+
+    char* smem;
+    int lane, l32, hi;
+    float scale_log2;
+    bf16x8 qreg[DC];
+    f32x16 oacc[DB];
+    f32x16 sacc[NB];
+    bf16x8 pk[KC];
+    int koff[DC];  // K operand: row l32, chunk 2c+hi (+ nb*32 rows)
+    int voff[DB];  // V transposing read of d-block db (+ (g*16 + r*8) rows)
+    float m_run, l_run;
+
+    __device__ __forceinline__ void init(char* smem_, int lane_, float scale_log2_) {
+        smem = smem_;
+        lane = lane_;
+        l32 = lane & 31;
+        hi = lane >> 5;
+        scale_log2 = scale_log2_;
+        // Within one operand loop the swizzle depends on the lane only (row
+        // offsets of a 32-key block or a 16-key chunk are multiples of the
+        // swizzle period), so every read is buffer + per-lane offset + constant.
+#pragma unroll
+        for (int c = 0; c < DC; ++c) koff[c] = l32 * G::ROW_BYTES + (((2 * c + hi) ^ swz_k<G::NC>(l32)) << 4);
+        // Transposing read: lane j of a 16-lane group addresses row
+        // (kv0 + j/4), columns d0 + 4*(j%4) .. +3; lane i then receives column
+        // d0 + i of rows kv0 .. kv0+3. Rows kv0 = g*16 + r*8 + 4*(l/32) give
+        // the k slots the S^T accumulator holds for half-wave l/32.
+        {
+            const int grp16 = lane >> 4, i = lane & 15;
+            const int row = (grp16 >> 1) * 4 + (i >> 2);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int d = db * 32 + (grp16 & 1) * 16 + 4 * (i & 3);
+                voff[db] = row * G::ROW_BYTES + (((d >> 3) ^ swz_v<G::NC>(row)) << 4) + (d & 7) * 2;
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) sacc[nb] = f32x16{};
+#pragma unroll
+        for (int g = 0; g < KC; ++g) pk[g] = bf16x8{};
+        m_run = -__builtin_inff();
+        l_run = 0.0f;
+    }
+
+    // Q^T operand: qrow points at d = 0 of this lane's query row (l32 of the
+    // wave's 32 rows) for this head.
+    __device__ __forceinline__ void load_q(const uint16_t* qrow) {
+        const uint16_t* qp = qrow + hi * 8;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) qreg[c] = *(const bf16x8*)(qp + c * 16);
+    }
+
+    // MFMA phase: PV steps (O^T += V^T P^T over the V tile at LDS offset vb)
+    // and/or QK steps (S^T = K Q^T over the K tile at kb). When both run they
+    // alternate 1:1 so consecutive MFMAs use independent accumulators; each
+    // step's A operand is fetched RING steps ahead into a register ring.
+    template <bool PV, bool QK>
+    __device__ __forceinline__ void mfma_phase(int vb, int kb) {
+        constexpr int NPV = PV ? DB * KC : 0;
+        constexpr int NQK = QK ? NB * DC : 0;
+        constexpr int NS = NPV + NQK;
+        // step -> (is_pv, item); PV item i = (g = i / DB, db = i % DB), QK
+        // item i = (c = i / NB, nb = i % NB)
+        auto is_pv = [](int st) { return PV && (!QK || (st & 1) == 0); };
+        auto item = [](int st) { return (PV && QK) ? (st >> 1) : st; };
+        auto load = [&](int st) -> bf16x8 {
+            const int i = item(st);
+            if (is_pv(st)) {
+                const int g = i / DB, db = i % DB;
+                const char* base = smem + vb + voff[db] + (g * 16) * G::ROW_BYTES;
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)base);
+                const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 8 * G::ROW_BYTES));
+                return __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+            } else {
+                const int c = i / NB, nb = i % NB;
+                return *(const bf16x8*)(smem + kb + koff[c] + nb * 32 * G::ROW_BYTES);
+            }
+        };
+        if constexpr (QK) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) sacc[nb] = f32x16{};
+        }
+        bf16x8 ring[RING];
+#pragma unroll
+        for (int st = 0; st < RING && st < NS; ++st) ring[st] = load(st);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+            const bf16x8 a = ring[st % RING];
+            if (st + RING < NS) ring[st % RING] = load(st + RING);
+            const int i = item(st);
+            if (is_pv(st)) {
+                const int g = i / DB, db = i % DB;
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[g], oacc[db], 0, 0, 0);
+            } else {
+                const int c = i / NB, nb = i % NB;
+                sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[c], sacc[nb], 0, 0, 0);
+            }
+        }
+        pin_mfma_schedule<PV, QK, RING, NS>();
+    }
+
+    // Softmax of the scores in sacc into pk (bf16), with the lazy rescale of
+    // O and l. A tile whose list entry was out of range (ok == false)
+    // contributes nothing.
+    __device__ __forceinline__ void softmax(bool ok) {
+        if (!ok) {
+#pragma unroll
+            for (int g = 0; g < KC; ++g) pk[g] = bf16x8{};
+            return;
+        }
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
+        mx = halfwave_max(mx);
+        const float m_new = fmaxf(m_run, mx * scale_log2);
+        if (__any(m_new > m_run + kRescaleThreshold)) {
+            const float alpha = fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        }
+        float lsum = 0.0f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p0 = fast_exp2(fmaf(sacc[nb][half * 8 + 2 * e], scale_log2, -m_run));
+                    const float p1 = fast_exp2(fmaf(sacc[nb][half * 8 + 2 * e + 1], scale_log2, -m_run));
+                    lsum += p0 + p1;
+                    w[e] = pack_bf16x2(p0, p1);
+                }
+                pk[nb * 2 + half] = __builtin_bit_cast(bf16x8, w);
+            }
+        }
+        l_run += lsum;
+    }
+
+    // Partial-row exchange between two waves that own the same rows (same
+    // lane -> row/column mapping): words[e * 64 + lane], e < STATE_WORDS.
+    __device__ __forceinline__ void export_state(float* words) const {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) words[(db * 16 + r) * 64 + lane] = oacc[db][r];
+        words[(DB * 16) * 64 + lane] = m_run;
+        words[(DB * 16 + 1) * 64 + lane] = l_run;
+    }
+    // Merge another wave's partial state (exported above) into this one:
+    // both sums are rescaled to the larger of the two (stale) maxima.
+    __device__ __forceinline__ void merge_state(const float* words) {
+        const float m1 = words[(DB * 16) * 64 + lane];
+        const float l1 = words[(DB * 16 + 1) * 64 + lane];
+        const float m = fmaxf(m_run, m1);
+        const float a0 = m == -__builtin_inff() ? 0.0f : fast_exp2(m_run - m);
+        const float a1 = m == -__builtin_inff() ? 0.0f : fast_exp2(m1 - m);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + words[(db * 16 + r) * 64 + lane] * a1;
+        l_run = l_run * a0 + l1 * a1;
+        m_run = m;
+    }
+
+    // Epilogue: O = O^T / l (bf16, RNE) into orow (d = 0 of this lane's query
+    // row), LSE = (m + log2 l) ln 2 into *lse_row (lanes of half-wave 0).
+    // A row with no selected key gives O = 0 and LSE = -inf.
+    __device__ __forceinline__ void store(uint16_t* orow, float* lse_row) const {
+        const float l_tot = halfwave_sum(l_run);
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int jg = 0; jg < 4; ++jg) {
+                const int d0 = db * 32 + jg * 8 + hi * 4;
+                u32x2 w;
+                w[0] = pack_bf16x2(oacc[db][jg * 4 + 0] * inv, oacc[db][jg * 4 + 1] * inv);
+                w[1] = pack_bf16x2(oacc[db][jg * 4 + 2] * inv, oacc[db][jg * 4 + 3] * inv);
+                *(u32x2*)(orow + d0) = w;
+            }
+        }
+        if (hi == 0) *lse_row = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
+    }
+};
+
+}  // namespace dev
+}  // namespace vsa

@@ -104,7 +104,7 @@ def main():
 
     def step(ev0=None, ev1=None):
         vsa.vsa_mask_to_csr(mask, (lq, lkv), (bq, bkv), ld, idx, cnt, stream=stream)
-        vsa.vsa_build_worklist(cnt, ld, work, stream=stream)
+        vsa.vsa_build_worklist(cnt, ld, work, segment=nq, stream=stream)
         if ev0 is not None:
             ev0.record(stream)
         vsa.vsa_attn_fwd_worklist(q, k, v, idx, cnt, bq, bkv, work, scale, o, lse, stream=stream)

@@ -69,7 +69,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vsa_last_error.restype = ctypes.c_char_p
     lib.vsa_mask_to_csr.argtypes = [p, i32, i32, i32, i32, i32, i32, i32, i32, p, i32, p, p, p]
     lib.vsa_mask_to_csr.restype = i32
-    lib.vsa_build_worklist.argtypes = [p, i32, i32, p, p]
+    lib.vsa_build_worklist.argtypes = [p, i32, i32, i32, p, p]
     lib.vsa_build_worklist.restype = i32
     lib.vsa_attn_fwd.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p, p, p]
     lib.vsa_attn_fwd.restype = i32
@@ -205,18 +205,25 @@ def vsa_mask_to_csr(mask, logical_block, block, idx_ld, kv_block_idx=None, kv_bl
     return kv_block_idx, kv_block_cnt
 
 
-def vsa_build_worklist(kv_block_cnt, max_cnt, work_list=None, stream=None):
-    """Count-sorted work list (largest count first, stable) as int32 [n]."""
+def vsa_build_worklist(kv_block_cnt, max_cnt, work_list=None, segment=None, stream=None):
+    """Count-sorted work list as int32 [n]: largest count first (stable)
+    within each segment of ``segment`` consecutive items. The default
+    segment is the last dimension of ``kv_block_cnt`` (one segment per batch
+    and head); ``segment = numel`` sorts the whole list."""
     if not kv_block_cnt.is_cuda or kv_block_cnt.dtype != torch.int32 or not kv_block_cnt.is_contiguous():
         raise ValueError("kv_block_cnt must be a contiguous int32 GPU tensor")
     n = kv_block_cnt.numel()
+    if segment is None:
+        segment = kv_block_cnt.shape[-1] if kv_block_cnt.dim() > 0 else n
+    if n and (segment < 1 or n % segment):
+        raise ValueError("segment must divide the number of items")
     if work_list is None:
         work_list = torch.empty((n,), dtype=torch.int32, device=kv_block_cnt.device)
     _dev(work_list, "work_list", torch.int32, 1)
     if work_list.numel() != n:
         raise ValueError("work_list must hold one entry per count")
-    rc = load_library().vsa_build_worklist(kv_block_cnt.data_ptr(), n, int(max_cnt), work_list.data_ptr(),
-                                           _stream_ptr(stream, kv_block_cnt.device))
+    rc = load_library().vsa_build_worklist(kv_block_cnt.data_ptr(), n, int(max(segment, 1)), int(max_cnt),
+                                           work_list.data_ptr(), _stream_ptr(stream, kv_block_cnt.device))
     _check(rc)
     return work_list
 

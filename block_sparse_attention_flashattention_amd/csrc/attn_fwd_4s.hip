@@ -1,0 +1,171 @@
+// Fused block-sparse attention forward for 64-row query tiles on gfx950:
+// four KV streams per query tile in two alternating wave groups.
+//
+// What is computed: FastVideo page "[perf] Add fine-grained FA4 VSA kernels",
+// ref_masked_sdpa_fp32 (per-wave arithmetic in wave_engine.h). The KV list
+// of one query tile is split into streams whose (max, sum, O) partials are
+// merged in fp32, as in that page's fork notes (two-KV-stream traversal and
+// merge, also used for the native Q64/KV64 tiles) and the split-KV
+// combination of page "BlackwellMultiHeadLatentAttentionForwardFP8".
+//
+// Schedule. Wave w owns query rows [32*(w%2), +32) of the 64-row tile and
+// works on stream s = w/2; the tile's KV list, cut into 32-key sub-tiles, is
+// split into four nearly equal consecutive parts, one per stream. Streams 0
+// and 1 (waves 0-3) form group 0, streams 2 and 3 (waves 4-7) group 1; each
+// SIMD runs one wave of each group, group 1 runs one phase behind group 0 and
+// every phase ends in a workgroup barrier, so one wave per SIMD issues MFMAs
+// while the other runs the softmax. Each stream's two waves fetch its own
+// double-buffered K/V sub-tiles (4 x 8 KB at head_dim 128) with direct-to-LDS
+// loads issued at the start of the MFMA phase M_j (K_{j+1}, V_j) and waited
+// for at the end of the softmax phase V_j. At the end streams 1-3 hand their
+// partial rows to stream 0 through LDS, which merges them and writes O and LSE.
+#include "device_common.h"
+#include "vsa_internal.h"
+#include "wave_engine.h"
+
+namespace vsa {
+namespace {
+
+using namespace dev;
+
+constexpr int kIdxCap4s = 8192;  // CSR row entries staged in LDS (>= the largest idx_ld)
+
+template <int D>
+__global__ __launch_bounds__(512) void vsa_fwd_4s_kernel(FwdParams prm) {
+    constexpr int BQ = 64;
+    constexpr int SUB = 32;  // keys per sub-tile
+    constexpr int NSTREAM = 4;
+    using E = WaveEngine<SUB, D>;
+    using G = TileGeom<SUB, D>;
+    constexpr int STREAM_LDS = 4 * G::TILE;  // K[2], V[2] of one stream
+    static_assert(6 * E::STATE_WORDS * 64 * 4 <= NSTREAM * STREAM_LDS, "merge exchange must fit in the tile buffers");
+    __shared__ __attribute__((aligned(1024))) char smem[NSTREAM * STREAM_LDS + kIdxCap4s * 4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int st = wave >> 1;                                  // stream
+    const int rb = wave & 1;                                   // 32-row block
+    const int grp = wave >> 2;
+    const int l32 = lane & 31;
+
+    const int wi = xcd_contiguous_block();
+    if (wi >= prm.n_work) return;
+    const int item = prm.work ? prm.work[wi] : wi;
+    if (item < 0 || item >= prm.n_items) return;
+
+    const int p = item % prm.nq;
+    const int bh = item / prm.nq;
+    const int h = bh % prm.H;
+    const int b = bh / prm.H;
+    const int S = prm.S;
+    const int64_t tok_stride = (int64_t)prm.H * D;
+    const int tok_bytes = (int)(tok_stride * 2);
+    int n = prm.cnt[item];
+    n = n < 0 ? 0 : (n > prm.ld ? prm.ld : n);
+    n = n > kIdxCap4s ? kIdxCap4s : n;
+    const int32_t* irow = prm.idx + (int64_t)item * prm.ld;
+    const int nkv = prm.nkv;
+    const int block_kv = prm.block_kv;
+    const int R = block_kv / SUB;  // sub-tiles per CSR tile (2 or 4)
+    const int q0 = p * BQ + rb * 32;
+
+    // stream s takes sub-tiles [first(s), first(s) + len(s))
+    const int N = n * R;
+    const int base_len = N / NSTREAM, extra = N % NSTREAM;
+    auto len_of = [&](int s) { return base_len + (s < extra ? 1 : 0); };
+    const int first = st * base_len + min(st, extra);
+    const int ng = len_of(st);
+
+    E e;
+    e.init(smem, lane, prm.scale_log2);
+    e.load_q(prm.q + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D);
+
+    int* lidx = (int*)(smem + NSTREAM * STREAM_LDS);
+    for (int i = tid; i < n; i += 512) lidx[i] = irow[i];
+    lds_barrier();
+
+    auto tile_of = [&](int j) { return __builtin_amdgcn_readfirstlane(lidx[(first + j) / R]); };
+    auto valid = [&](int t) { return t >= 0 && t < nkv; };
+    const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    auto issue = [&](const char* base, int dst, int j, bool v_layout) {
+        const int t = tile_of(j);
+        const int64_t row0 = (int64_t)(valid(t) ? t : 0) * block_kv + ((first + j) % R) * SUB;
+        issue_tile<SUB, D, 2>(smem, dst, base + row0 * tok_bytes, tok_bytes, v_layout, rb, lane);
+    };
+    const int sbase = st * STREAM_LDS;
+    auto kbuf = [&](int j) { return sbase + (j & 1) * G::TILE; };
+    auto vbuf = [&](int j) { return sbase + (2 + (j & 1)) * G::TILE; };
+    auto qk = [&](int j) { e.template mfma_phase<false, true>(0, kbuf(j)); };
+    auto pv = [&](int j) { e.template mfma_phase<true, false>(vbuf(j), 0); };
+    auto pv_qk = [&](int jv, int jk) { e.template mfma_phase<true, true>(vbuf(jv), kbuf(jk)); };
+    auto softmax = [&](int j) { e.softmax(valid(tile_of(j))); };
+
+    // Every wave passes the same number of barriers: a stream of length L in
+    // group g uses 2L + 2 + g; shorter streams pad at the end.
+    const int total = max(max(2 * len_of(0) + 2, 2 * len_of(1) + 2), max(2 * len_of(2) + 3, 2 * len_of(3) + 3));
+    int nbar = 0;
+    auto bar = [&]() {
+        lds_barrier();
+        ++nbar;
+    };
+
+    if (ng > 0) {
+        issue(kbase, kbuf(0), 0, false);
+        wait_global_loads();
+    }
+    bar();
+    if (grp == 1) bar();
+    if (ng > 0) {
+        if (ng > 1) issue(kbase, kbuf(1), 1, false);
+        issue(vbase, vbuf(0), 0, true);
+        qk(0);                                   // M_0
+        bar();
+        softmax(0);                              // V_0
+        wait_global_loads();
+        bar();
+        for (int j = 1; j < ng; ++j) {
+            if (j + 1 < ng) issue(kbase, kbuf(j + 1), j + 1, false);
+            issue(vbase, vbuf(j), j, true);
+            pv_qk(j - 1, j);                     // M_j
+            bar();
+            softmax(j);                          // V_j
+            wait_global_loads();
+            bar();
+        }
+        pv(ng - 1);                              // M_n
+        bar();
+    }
+    while (nbar < total) bar();
+
+    // merge streams 1..3 into stream 0 (same rows: waves rb, rb+2, rb+4, rb+6)
+    float* xch = (float*)smem;
+    auto slot = [&](int s) { return xch + ((s - 1) * 2 + rb) * E::STATE_WORDS * 64; };
+    if (st > 0) e.export_state(slot(st));
+    lds_barrier();
+    if (st == 0) {
+#pragma unroll
+        for (int s = 1; s < NSTREAM; ++s) e.merge_state(slot(s));
+        e.store(prm.o + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D,
+                prm.lse + ((int64_t)b * prm.H + h) * S + q0 + l32);
+    }
+}
+
+template <int D>
+hipError_t launch_4s(const FwdParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL((vsa_fwd_4s_kernel<D>), dim3(p.n_work), dim3(512), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_4s(int block_kv, int head_dim, const FwdParams& p, hipStream_t stream) {
+    if (p.n_work <= 0) return hipSuccess;
+    if (block_kv != 64 && block_kv != 128) return hipErrorInvalidValue;
+    if (head_dim == 128) return launch_4s<128>(p, stream);
+    if (head_dim == 64) return launch_4s<64>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace vsa

@@ -121,7 +121,7 @@ int32_t worklist_buffer(size_t bytes, int32_t** out) {
 
 extern "C" {
 
-int32_t vsa_abi_version(void) { return 1; }
+int32_t vsa_abi_version(void) { return 2; }
 
 const char* vsa_status_string(int32_t status) {
     switch (status) {
@@ -165,16 +165,18 @@ int32_t vsa_mask_to_csr(const uint8_t* mask, int32_t batch, int32_t heads, int32
     return VSA_OK;
 }
 
-int32_t vsa_build_worklist(const int32_t* kv_block_cnt, int32_t n_items, int32_t max_cnt, int32_t* work_list,
-                           void* stream) {
+int32_t vsa_build_worklist(const int32_t* kv_block_cnt, int32_t n_items, int32_t segment, int32_t max_cnt,
+                           int32_t* work_list, void* stream) {
     g_last_error[0] = 0;
     VSA_REQUIRE(n_items >= 0, VSA_ERR_INVALID_ARG, "n_items must be >= 0");
+    VSA_REQUIRE(segment >= 1 && (n_items == 0 || n_items % segment == 0), VSA_ERR_INVALID_ARG,
+                "segment must be >= 1 and divide n_items");
     VSA_REQUIRE(max_cnt >= 0 && max_cnt <= vsa::kWorklistMaxCnt, VSA_ERR_INVALID_ARG, "max_cnt must be in [0, %d]",
                 vsa::kWorklistMaxCnt);
     if (n_items == 0) return VSA_OK;
     VSA_REQUIRE(kv_block_cnt && work_list, VSA_ERR_INVALID_ARG, "null pointer");
     VSA_REQUIRE(aligned(kv_block_cnt, 4) && aligned(work_list, 4), VSA_ERR_INVALID_ARG, "buffers must be 4-byte aligned");
-    hipError_t e = vsa::launch_build_worklist(kv_block_cnt, n_items, max_cnt, work_list, (hipStream_t)stream);
+    hipError_t e = vsa::launch_build_worklist(kv_block_cnt, n_items, segment, max_cnt, work_list, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
     return VSA_OK;
 }
@@ -212,7 +214,9 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
     int32_t* work = nullptr;
     rc = worklist_buffer((size_t)n_items * sizeof(int32_t), &work);
     if (rc != VSA_OK) return rc;
-    hipError_t e = vsa::launch_build_worklist(kv_block_cnt, n_items, idx_ld, work, (hipStream_t)stream);
+    // one segment per (batch, head): heads stay contiguous in the list
+    hipError_t e = vsa::launch_build_worklist(kv_block_cnt, n_items, seqlen / block_q, idx_ld, work,
+                                              (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
     vsa::FwdParams p = make_params(q, k, v, kv_block_idx, kv_block_cnt, batch, seqlen, heads, head_dim, idx_ld,
                                    block_q, block_kv, scale, work, n_items, o, lse);

@@ -59,14 +59,20 @@ __device__ __forceinline__ uint64_t same_key_lanes(int key, bool active) {
     return m;
 }
 
-// Stable counting sort of item indices by count, largest count first, in a
-// single workgroup of WAVES waves. Wave w owns a contiguous segment of the
-// items; per-wave histograms give each wave its own output offsets, and
+// Stable counting sort of item indices by count, largest count first, within
+// one segment of `seg` consecutive items per workgroup (segment blockIdx.x
+// covers items [blockIdx.x*seg, +seg) and is written to the same positions
+// of the work list). Wave w of the WAVES waves owns a contiguous part of the
+// segment; per-wave histograms give each wave its own output offsets, and
 // within a wave the rank among equal keys comes from ballots, so the result
 // is deterministic and equal keys keep ascending item order.
 template <int WAVES, int BINS, int KEY_BITS>
-__global__ __launch_bounds__(WAVES * 64) void worklist_kernel(const int32_t* __restrict__ cnt, int n,
-                                                             int max_cnt, int32_t* __restrict__ work) {
+__global__ __launch_bounds__(WAVES * 64) void worklist_kernel(const int32_t* __restrict__ cnt_all, int seg,
+                                                             int max_cnt, int32_t* __restrict__ work_all) {
+    const int32_t* cnt = cnt_all + (int64_t)blockIdx.x * seg;
+    int32_t* work = work_all + (int64_t)blockIdx.x * seg;
+    const int first_item = blockIdx.x * seg;
+    const int n = seg;
     __shared__ int hist[WAVES][BINS];
     __shared__ int wave_total[WAVES];
     constexpr int NT = WAVES * 64;
@@ -75,9 +81,9 @@ __global__ __launch_bounds__(WAVES * 64) void worklist_kernel(const int32_t* __r
     for (int i = tid; i < WAVES * BINS; i += NT) (&hist[0][0])[i] = 0;
     __syncthreads();
 
-    const int seg = (n + WAVES - 1) / WAVES;
-    const int beg = min(n, wave * seg);
-    const int end = min(n, beg + seg);
+    const int part = (n + WAVES - 1) / WAVES;
+    const int beg = min(n, wave * part);
+    const int end = min(n, beg + part);
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
     // Phase 1: per-wave histogram of clamped counts.
@@ -133,7 +139,7 @@ __global__ __launch_bounds__(WAVES * 64) void worklist_kernel(const int32_t* __r
         key = key < 0 ? 0 : (key > max_cnt ? max_cnt : key);
         const uint64_t same = same_key_lanes<KEY_BITS>(key, act);
         const int pos = act ? hist[wave][key] + __popcll(same & below) : 0;
-        if (act) work[pos] = i;
+        if (act) work[pos] = first_item + i;
         if (act && (same & below) == 0) hist[wave][key] += __popcll(same);
     }
 }
@@ -150,12 +156,16 @@ hipError_t launch_mask_to_csr(const uint8_t* mask, int batch, int heads, int nq_
     return hipGetLastError();
 }
 
-hipError_t launch_build_worklist(const int32_t* cnt, int n_items, int max_cnt, int32_t* work, hipStream_t stream) {
+hipError_t launch_build_worklist(const int32_t* cnt, int n_items, int segment, int max_cnt, int32_t* work,
+                                 hipStream_t stream) {
     if (n_items <= 0) return hipSuccess;
+    const int n_seg = n_items / segment;
     if (max_cnt < 2048) {
-        hipLaunchKernelGGL((worklist_kernel<4, 2048, 11>), dim3(1), dim3(256), 0, stream, cnt, n_items, max_cnt, work);
+        hipLaunchKernelGGL((worklist_kernel<4, 2048, 11>), dim3(n_seg), dim3(256), 0, stream, cnt, segment, max_cnt,
+                           work);
     } else {
-        hipLaunchKernelGGL((worklist_kernel<1, 8192, 13>), dim3(1), dim3(64), 0, stream, cnt, n_items, max_cnt, work);
+        hipLaunchKernelGGL((worklist_kernel<1, 8192, 13>), dim3(n_seg), dim3(64), 0, stream, cnt, segment, max_cnt,
+                           work);
     }
     return hipGetLastError();
 }

@@ -32,6 +32,8 @@ hipError_t launch_fwd(int block_q, int block_kv, int head_dim, const FwdParams& 
 hipError_t launch_fwd_pp(int block_kv, int head_dim, const FwdParams& p, hipStream_t stream);
 // 128-row query tiles: the two-KV-stream ping-pong kernel (attn_fwd_2s.hip).
 hipError_t launch_fwd_2s(int block_kv, int head_dim, const FwdParams& p, hipStream_t stream);
+// 64-row query tiles: the four-KV-stream ping-pong kernel (attn_fwd_4s.hip).
+hipError_t launch_fwd_4s(int block_kv, int head_dim, const FwdParams& p, hipStream_t stream);
 
 // Whether launch_fwd has a kernel for this configuration.
 bool fwd_supported(int block_q, int block_kv, int head_dim);
@@ -40,7 +42,8 @@ bool fwd_supported(int block_q, int block_kv, int head_dim);
 hipError_t launch_mask_to_csr(const uint8_t* mask, int batch, int heads, int nq_logical, int nkv_logical,
                               int q_ratio, int kv_ratio, int nq_physical, int32_t* idx, int ld, int32_t* cnt,
                               int32_t* overflow, hipStream_t stream);
-hipError_t launch_build_worklist(const int32_t* cnt, int n_items, int max_cnt, int32_t* work, hipStream_t stream);
+hipError_t launch_build_worklist(const int32_t* cnt, int n_items, int segment, int max_cnt, int32_t* work,
+                                 hipStream_t stream);
 
 constexpr int kWorklistMaxCnt = 8191;
 // Largest CSR row length the forward kernels accept (rows are staged in LDS).

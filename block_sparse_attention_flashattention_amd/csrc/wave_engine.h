@@ -76,23 +76,24 @@ struct TileGeom {
     static constexpr int NC = D / 8;               // 16-byte chunks per row
     static constexpr int TILE = BKV * ROW_BYTES;   // bytes per tile
     static constexpr int ROWS_PER_KB = 1024 / ROW_BYTES;
-    static constexpr int BLOCKS_PER_WAVE = TILE / 1024 / 4;   // 1 KB loads per wave of a 4-wave group
     static_assert(NC == 8 || NC == 16, "head_dim 64 or 128");
-    static_assert(BLOCKS_PER_WAVE >= 1 && TILE % 4096 == 0, "tile must split over four waves");
+    static_assert(TILE % 1024 == 0, "tiles are fetched in 1 KB blocks");
 };
 
-// One wave's share (gw = 0..3 within its 4-wave group) of fetching a tile:
-// BLOCKS_PER_WAVE direct-to-LDS 1 KB loads, each from a uniform row base plus
-// a 32-bit per-lane offset. `tile` points at row 0 of the tile for this head;
-// consecutive rows are tok_bytes apart.
-template <int BKV, int D>
+// One wave's share (gw = 0..WPF-1 of the WPF waves that fetch the tile) of
+// fetching a tile: direct-to-LDS 1 KB loads, each from a uniform row base
+// plus a 32-bit per-lane offset. `tile` points at row 0 of the tile for this
+// head; consecutive rows are tok_bytes apart.
+template <int BKV, int D, int WPF = 4>
 __device__ __forceinline__ void issue_tile(char* smem, int dst, const char* tile, int tok_bytes, bool v_layout, int gw,
                                            int lane) {
     using G = TileGeom<BKV, D>;
+    constexpr int BLOCKS_PER_WAVE = G::TILE / 1024 / WPF;
+    static_assert(BLOCKS_PER_WAVE >= 1 && G::TILE % (1024 * WPF) == 0, "tile must split evenly over the waves");
     const int rl = lane / G::NC, pos = lane % G::NC;
 #pragma unroll
-    for (int i = 0; i < G::BLOCKS_PER_WAVE; ++i) {
-        const int blk = gw * G::BLOCKS_PER_WAVE + i;
+    for (int i = 0; i < BLOCKS_PER_WAVE; ++i) {
+        const int blk = gw * BLOCKS_PER_WAVE + i;
         const int row = blk * G::ROWS_PER_KB + rl;
         const int c = pos ^ (v_layout ? swz_v<G::NC>(row) : swz_k<G::NC>(row));
         const char* src = tile + (int64_t)(blk * G::ROWS_PER_KB) * tok_bytes;

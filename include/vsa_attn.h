@@ -100,17 +100,22 @@ int32_t vsa_mask_to_csr(const uint8_t* mask, int32_t batch, int32_t heads, int32
  * vsa_build_worklist -- mask front-end, step 2: count-sorted work list.
  *
  * Source: page "BlackwellMultiHeadLatentAttentionForwardFP8" (persistent
- * tile scheduling over a device work list instead of a plain grid); the
- * order here is longest-first for load balance.
+ * tile scheduling over a device work list instead of a plain grid). The
+ * order is longest-first for load balance, within segments: with
+ * segment = nq (one segment per batch and head) each head's query tiles stay
+ * together, so the K/V tiles they share stay cached; segment = n_items sorts
+ * the whole list.
  *
  *   kv_block_cnt  [n_items] int32 (the flattened [batch, heads, nq] counts)
+ *   segment       items per segment; must divide n_items
  *   max_cnt       counts are clamped to [0, max_cnt] for ordering (pass the
  *                 idx_ld the counts belong to); 0 <= max_cnt <= 8191.
- *   work_list     out [n_items] int32: the flat indices (b*heads + h)*nq + p
- *                 sorted by clamped count, largest first; equal counts keep
- *                 ascending index order. Deterministic.
+ *   work_list     out [n_items] int32: entry i of segment s is the flat index
+ *                 (b*heads + h)*nq + p of the segment's item with the i-th
+ *                 largest clamped count; equal counts keep ascending index
+ *                 order. Segments stay in ascending order. Deterministic.
  */
-int32_t vsa_build_worklist(const int32_t* kv_block_cnt, int32_t n_items, int32_t max_cnt,
+int32_t vsa_build_worklist(const int32_t* kv_block_cnt, int32_t n_items, int32_t segment, int32_t max_cnt,
                            int32_t* work_list, void* stream);
 
 /*
@@ -125,9 +130,10 @@ int32_t vsa_build_worklist(const int32_t* kv_block_cnt, int32_t n_items, int32_t
  *
  *   block_q x block_kv in {64,128,256} x {64,128}; head_dim in {64, 128};
  *   seqlen divisible by both; 0 < scale < inf; 1 <= idx_ld <= 8191.
- *   Builds the count-sorted work list in a library-owned device buffer
- *   (grown on demand per device, released by vsa_release) and then runs
- *   the kernel in that order; see vsa_attn_fwd_worklist for the kernel alone.
+ *   Builds the work list (count-sorted within each batch and head, segment
+ *   = seqlen/block_q) in a library-owned device buffer (grown on demand per
+ *   device, released by vsa_release) and then runs the kernel in that
+ *   order; see vsa_attn_fwd_worklist for the kernel alone.
  */
 int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
                      const int32_t* kv_block_cnt, int32_t batch, int32_t seqlen, int32_t heads,

@@ -12,11 +12,13 @@ indices of the expanded mask (``arange(nkv).masked_select(mask)``) together
 with their count.
 
 ``build_worklist``: the order in which Q tiles are processed. Items
-(b, h, p) are encoded as their flat index into kv_block_cnt and sorted by
-count, largest first, ties kept in ascending flat order (a stable sort), so
-that long rows start first (the work-list idea of the page
-"BlackwellMultiHeadLatentAttentionForwardFP8": a persistent grid walking a
-device list of work tiles instead of a plain grid).
+(b, h, p) are encoded as their flat index into kv_block_cnt. Within each
+segment of ``segment`` consecutive items (one segment per batch and head when
+segment = nq) they are sorted by count, largest first, ties kept in
+ascending flat order (a stable sort), so that long rows start first (the
+work-list idea of the page "BlackwellMultiHeadLatentAttentionForwardFP8": a
+grid walking a device list of work tiles instead of a plain grid); segments
+keep their order.
 """
 
 from __future__ import annotations
@@ -56,7 +58,15 @@ def mask_to_csr(logical_mask, logical_block, physical_block, ld, fill=-1):
     return idx, cnt, bool(overflow)
 
 
-def build_worklist(kv_block_cnt, ld):
-    """Flat (b, h, p) indices sorted by clamp(cnt, 0, ld) descending, stable."""
+def build_worklist(kv_block_cnt, ld, segment=None):
+    """Flat (b, h, p) indices; within each segment sorted by clamp(cnt, 0, ld)
+    descending, stable. segment defaults to the whole list."""
     c = np.clip(np.asarray(kv_block_cnt, dtype=np.int64).reshape(-1), 0, ld)
-    return np.argsort(-c, kind="stable").astype(np.int32)
+    n = c.size
+    segment = n if segment is None else segment
+    if n and n % segment:
+        raise ValueError("segment must divide the number of items")
+    out = np.empty(n, dtype=np.int32)
+    for s0 in range(0, n, segment):
+        out[s0:s0 + segment] = s0 + np.argsort(-c[s0:s0 + segment], kind="stable")
+    return out

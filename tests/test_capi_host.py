@@ -36,7 +36,7 @@ def test_header_declares_the_binding_symbols():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.vsa_abi_version() == 1
+    assert lib.vsa_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -101,11 +101,14 @@ def test_mask_to_csr_rejects_invalid_arguments(lib):
 
 
 def test_build_worklist_validation(lib):
-    assert lib.vsa_build_worklist(A, -1, 10, A, None) == -1
-    assert lib.vsa_build_worklist(A, 10, -1, A, None) == -1
-    assert lib.vsa_build_worklist(A, 10, 9000, A, None) == -1
-    assert lib.vsa_build_worklist(None, 10, 10, A, None) == -1
-    assert lib.vsa_build_worklist(None, 0, 10, None, None) == 0  # empty list: nothing to do
+    assert lib.vsa_build_worklist(A, -1, 1, 10, A, None) == -1
+    assert lib.vsa_build_worklist(A, 10, 10, -1, A, None) == -1
+    assert lib.vsa_build_worklist(A, 10, 10, 9000, A, None) == -1
+    assert lib.vsa_build_worklist(None, 10, 10, 10, A, None) == -1
+    assert lib.vsa_build_worklist(A, 10, 3, 10, A, None) == -1  # segment must divide n_items
+    assert "segment" in lib.vsa_last_error().decode()
+    assert lib.vsa_build_worklist(A, 10, 0, 10, A, None) == -1
+    assert lib.vsa_build_worklist(None, 0, 1, 10, None, None) == 0  # empty list: nothing to do
 
 
 def test_binding_refuses_cpu_tensors():

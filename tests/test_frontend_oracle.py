@@ -76,6 +76,24 @@ def test_worklist_is_a_stable_descending_count_order():
     assert w.tolist() == sorted(range(flat.size), key=lambda i: (-flat[i], i))
 
 
+def test_segmented_worklist_sorts_within_segments_only():
+    rng = np.random.default_rng(4)
+    cnt = rng.integers(0, 12, size=(2, 3, 40)).astype(np.int32)
+    ld = 10
+    seg = 40
+    w = frontend.build_worklist(cnt, ld, segment=seg)
+    flat = np.clip(cnt.reshape(-1), 0, ld)
+    assert sorted(w.tolist()) == list(range(flat.size))
+    for s0 in range(0, flat.size, seg):
+        part = w[s0:s0 + seg]
+        assert np.all((part >= s0) & (part < s0 + seg))  # items stay in their segment
+        assert part.tolist() == sorted(range(s0, s0 + seg), key=lambda i: (-flat[i], i))
+    # one segment = the global order; segment must divide the item count
+    assert np.array_equal(frontend.build_worklist(cnt, ld, segment=flat.size), frontend.build_worklist(cnt, ld))
+    with pytest.raises(ValueError):
+        frontend.build_worklist(cnt, ld, segment=7)
+
+
 def test_page_mask_generator_invariants():
     m = anchor_topk_mask(3, 16, 16, 8, seed=1566)
     assert m.shape == (3, 16, 16)

@@ -131,18 +131,22 @@ def test_mask_to_csr_overflow_flag(vsa):
 
 
 WL_CASES = [
-    ("native64 counts", None, 92),
-    ("random clamp", (-3, 100, 12345), 90),
-    ("single", (0, 5, 1), 5),
-    ("ragged 65", (0, 3, 65), 3),
-    ("many", (0, 600, 100000), 600),
-    ("wide bins", (0, 5000, 7777), 5000),
-    ("all equal", (7, 7, 3000), 7),
+    # label, (lo, hi, n) or None for the native Q64 counts, ld, segment (None = whole list)
+    ("native64 per head", None, 92, 512),
+    ("native64 global", None, 92, None),
+    ("random clamp", (-3, 100, 12345), 90, None),
+    ("random clamp segmented", (-3, 100, 12345), 90, 823),
+    ("single", (0, 5, 1), 5, None),
+    ("ragged 65", (0, 3, 65), 3, 13),
+    ("many", (0, 600, 100000), 600, 5000),
+    ("wide bins", (0, 5000, 7777), 5000, None),
+    ("wide bins segmented", (0, 5000, 7777), 5000, 7777 // 7),
+    ("all equal", (7, 7, 3000), 7, 100),
 ]
 
 
-@pytest.mark.parametrize("label,spec,ld", WL_CASES, ids=[c[0] for c in WL_CASES])
-def test_worklist_bit_exact(vsa, label, spec, ld):
+@pytest.mark.parametrize("label,spec,ld,segment", WL_CASES, ids=[c[0] for c in WL_CASES])
+def test_worklist_bit_exact(vsa, label, spec, ld, segment):
     say(f"worklist {label}")
     if spec is None:
         mask = W.NATIVE64.logical_mask()
@@ -151,8 +155,9 @@ def test_worklist_bit_exact(vsa, label, spec, ld):
     else:
         lo, hi, n = spec
         cnt = np.random.default_rng(n).integers(lo, hi + 1, size=n).astype(np.int32)
-    ref = ofront.build_worklist(cnt, ld)
-    got = vsa.vsa_build_worklist(dev(cnt), ld)
+    seg = cnt.size if segment is None else segment
+    ref = ofront.build_worklist(cnt, ld, segment=seg)
+    got = vsa.vsa_build_worklist(dev(cnt), ld, segment=seg)
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy(), ref)
 

@@ -88,17 +88,32 @@ __global__ __launch_bounds__(512) void vsa_fwd_2s_kernel(FwdParams prm) {
     auto valid = [&](int t) { return t >= 0 && t < nkv; };
     const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
     const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
-    auto issue = [&](const char* base, int dst, int j, bool v_layout) {
+    using F = TileFetch<SUB, D, 4>;
+    const int fw = wave & 3;  // this wave's index among the waves fetching its stream's tiles
+    auto tile_ptr = [&](const char* base, int j) {
         const int t = tile_of(j);
         const int64_t row0 = (int64_t)(valid(t) ? t : 0) * block_kv + ((first + j) % R) * SUB;
-        issue_tile<SUB, D>(smem, dst, base + row0 * tok_bytes, tok_bytes, v_layout, wave & 3, lane);
+        return base + row0 * tok_bytes;
     };
     const int gbase = grp * GROUP_LDS;
     auto kbuf = [&](int j) { return gbase + (j & 1) * G::TILE; };
     auto vbuf = [&](int j) { return gbase + (2 + (j & 1)) * G::TILE; };
-    auto qk = [&](int j) { e.template mfma_phase<false, true>(0, kbuf(j)); };
+    // The loads of M_j (K_{j+1} if it exists, then V_j) are spread over the
+    // MFMA phase, one 1 KB block per hook.
+    auto loads = [&](int j) {
+        const bool more = j + 1 < ng;
+        const char* kt = more ? tile_ptr(kbase, j + 1) : kbase;
+        const char* vt = tile_ptr(vbase, j);
+        const int kd = kbuf(j + 1), vd = vbuf(j);
+        return [=, &lane](int i) {
+            if (i < F::BPW) {
+                if (more) F::block(smem, kd, kt, tok_bytes, false, fw, lane, i);
+            } else {
+                F::block(smem, vd, vt, tok_bytes, true, fw, lane, i - F::BPW);
+            }
+        };
+    };
     auto pv = [&](int j) { e.template mfma_phase<true, false>(vbuf(j), 0); };
-    auto pv_qk = [&](int jv, int jk) { e.template mfma_phase<true, true>(vbuf(jv), kbuf(jk)); };
     auto softmax = [&](int j) { e.softmax(valid(tile_of(j))); };
 
     // Every wave passes the same number of barriers: group 0 uses 2*N0 + 2,
@@ -111,23 +126,19 @@ __global__ __launch_bounds__(512) void vsa_fwd_2s_kernel(FwdParams prm) {
     };
 
     if (ng > 0) {
-        issue(kbase, kbuf(0), 0, false);
+        F::all(smem, kbuf(0), tile_ptr(kbase, 0), tok_bytes, false, fw, lane);
         wait_global_loads();
     }
     bar();
     if (grp == 1) bar();
     if (ng > 0) {
-        if (ng > 1) issue(kbase, kbuf(1), 1, false);
-        issue(vbase, vbuf(0), 0, true);
-        qk(0);                                   // M_0
+        e.template mfma_phase<false, true, 2 * F::BPW>(0, kbuf(0), loads(0));               // M_0
         bar();
         softmax(0);                              // V_0
         wait_global_loads();
         bar();
         for (int j = 1; j < ng; ++j) {
-            if (j + 1 < ng) issue(kbase, kbuf(j + 1), j + 1, false);
-            issue(vbase, vbuf(j), j, true);
-            pv_qk(j - 1, j);                     // M_j
+            e.template mfma_phase<true, true, 2 * F::BPW>(vbuf(j - 1), kbuf(j), loads(j));  // M_j
             bar();
             softmax(j);                          // V_j
             wait_global_loads();

@@ -81,22 +81,32 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     auto valid = [&](int t) { return t >= 0 && t < nkv; };
     const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
     const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
-    auto issue = [&](const char* base, int dst, int j, bool v_layout) {
+    using F = TileFetch<BKV, D, 4>;  // a tile is fetched by the four waves of one group
+    auto tile_ptr = [&](const char* base, int j) {
         const int t = tile_of(j);
-        const char* tile = base + (int64_t)(valid(t) ? t : 0) * BKV * tok_bytes;
-        issue_tile<BKV, D>(smem, dst, tile, tok_bytes, v_layout, wave & 3, lane);
+        return base + (int64_t)(valid(t) ? t : 0) * BKV * tok_bytes;
     };
     // LDS byte offsets of the K and V buffers used for list entry j
     auto kbuf = [](int j) { return (j & 1) * G::TILE; };
     auto vbuf = [](int j) { return (2 + (j & 1)) * G::TILE; };
-    auto qk = [&](int j) { e.template mfma_phase<false, true>(0, kbuf(j)); };
+    // Tile loads are spread over a phase (one 1 KB block per hook) so that
+    // the eight waves' loads do not queue up at the start of the phase.
+    auto v_loads = [&](int j) {
+        const char* tile = tile_ptr(vbase, j);
+        return [=, &lane](int i) { F::block(smem, vbuf(j), tile, tok_bytes, true, wave & 3, lane, i); };
+    };
+    auto k_loads = [&](int j, bool on) {
+        const char* tile = on ? tile_ptr(kbase, j) : kbase;
+        return [=, &lane](int i) {
+            if (on) F::block(smem, kbuf(j), tile, tok_bytes, false, wave & 3, lane, i);
+        };
+    };
     auto pv = [&](int j) { e.template mfma_phase<true, false>(vbuf(j), 0); };
-    auto pv_qk = [&](int jv, int jk) { e.template mfma_phase<true, true>(vbuf(jv), kbuf(jk)); };
     auto softmax = [&](int j) { e.softmax(valid(tile_of(j))); };
 
     // prologue: group 1 fetches K_0
     if (grp == 1 && n > 0) {
-        issue(kbase, kbuf(0), 0, false);
+        F::all(smem, kbuf(0), tile_ptr(kbase, 0), tok_bytes, false, wave & 3, lane);
         wait_global_loads();
     }
     lds_barrier();
@@ -107,15 +117,13 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     // steady-state MFMA phase (PV_{j-1} then QK_j) is one basic block.
     if (grp == 0) {
         if (n > 0) {
-            issue(vbase, vbuf(0), 0, true);
-            qk(0);                               // M_0
+            e.template mfma_phase<false, true, F::BPW>(0, kbuf(0), v_loads(0));                // M_0
             lds_barrier();
             softmax(0);                          // V_0
             wait_global_loads();
             lds_barrier();
             for (int j = 1; j < n; ++j) {
-                issue(vbase, vbuf(j), j, true);
-                pv_qk(j - 1, j);                 // M_j
+                e.template mfma_phase<true, true, F::BPW>(vbuf(j - 1), kbuf(j), v_loads(j));   // M_j
                 lds_barrier();
                 softmax(j);                      // V_j
                 wait_global_loads();
@@ -127,16 +135,15 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
         lds_barrier();
     } else {
         if (n > 0) {
-            if (n > 1) issue(kbase, kbuf(1), 1, false);
+            if (n > 1) F::all(smem, kbuf(1), tile_ptr(kbase, 1), tok_bytes, false, wave & 3, lane);
             lds_barrier();
-            qk(0);                               // M_0
+            e.template mfma_phase<false, true>(0, kbuf(0));                                    // M_0
             wait_global_loads();
             lds_barrier();
             for (int j = 1; j < n; ++j) {
-                if (j + 1 < n) issue(kbase, kbuf(j + 1), j + 1, false);
-                softmax(j - 1);                  // V_{j-1}
+                e.template softmax<F::BPW>(valid(tile_of(j - 1)), k_loads(j + 1, j + 1 < n)); // V_{j-1}
                 lds_barrier();
-                pv_qk(j - 1, j);                 // M_j
+                e.template mfma_phase<true, true>(vbuf(j - 1), kbuf(j));                       // M_j
                 wait_global_loads();
                 lds_barrier();
             }

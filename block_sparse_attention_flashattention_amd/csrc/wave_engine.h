@@ -23,6 +23,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 
@@ -43,28 +44,31 @@ __device__ __forceinline__ int swz_v(int row) {
     else return ((row >> 1) & 1) << 2;
 }
 
-// Scheduling pins for one MFMA phase: the LDS reads of the first RING steps,
-// then per step its MFMA followed by the reads of the step RING ahead.
+// Scheduling pins for MFMA steps [S0, S1) of one MFMA phase of NS steps:
+// per step its MFMA followed by the LDS reads of the step RING ahead; with
+// PRE, first the reads of the first RING steps (the ring fill). The pins of
+// one scheduling region must describe exactly that region's reads and MFMAs.
 // Masks: 0x100 LDS read, 0x008 MFMA.
 template <bool PV, bool QK>
 constexpr int step_reads(int st) {
     return (PV && (!QK || (st & 1) == 0)) ? 2 : 1;  // PV: two 8-byte transposing reads
 }
-template <bool PV, bool QK, int RING, int NS, int ST = 0>
-__device__ __forceinline__ void pin_mfma_schedule() {
-    if constexpr (ST == 0) {
-        static_assert(RING == 4, "prefetch count assumes a ring of 4");
-        constexpr int pre = (NS > 0 ? step_reads<PV, QK>(0) : 0) + (NS > 1 ? step_reads<PV, QK>(1) : 0) +
-                            (NS > 2 ? step_reads<PV, QK>(2) : 0) + (NS > 3 ? step_reads<PV, QK>(3) : 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, pre, 0);
-    }
-    if constexpr (ST < NS) {
+template <bool PV, bool QK, int RING, int NS>
+constexpr int ring_fill_reads() {
+    int r = 0;
+    for (int st = 0; st < RING && st < NS; ++st) r += step_reads<PV, QK>(st);
+    return r;
+}
+template <bool PV, bool QK, int RING, int NS, int S0, int S1, bool PRE>
+__device__ __forceinline__ void pin_mfma_steps() {
+    if constexpr (PRE) __builtin_amdgcn_sched_group_barrier(0x100, ring_fill_reads<PV, QK, RING, NS>(), 0);
+    if constexpr (S0 < S1) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if constexpr (ST + RING < NS) {
-            constexpr int r = step_reads<PV, QK>(ST + RING);
+        if constexpr (S0 + RING < NS) {
+            constexpr int r = step_reads<PV, QK>(S0 + RING);
             __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
         }
-        pin_mfma_schedule<PV, QK, RING, NS, ST + 1>();
+        pin_mfma_steps<PV, QK, RING, NS, S0 + 1, S1, false>();
     }
 }
 
@@ -80,27 +84,40 @@ struct TileGeom {
     static_assert(TILE % 1024 == 0, "tiles are fetched in 1 KB blocks");
 };
 
-// One wave's share (gw = 0..WPF-1 of the WPF waves that fetch the tile) of
-// fetching a tile: direct-to-LDS 1 KB loads, each from a uniform row base
-// plus a 32-bit per-lane offset. `tile` points at row 0 of the tile for this
-// head; consecutive rows are tok_bytes apart.
-template <int BKV, int D, int WPF = 4>
-__device__ __forceinline__ void issue_tile(char* smem, int dst, const char* tile, int tok_bytes, bool v_layout, int gw,
-                                           int lane) {
+// Tile fetch: the tile is split into 1 KB blocks shared out over the WPF
+// waves that fetch it (wave gw takes blocks [gw*BPW, (gw+1)*BPW)); each block
+// is one direct-to-LDS 16-byte-per-lane load from a uniform row base plus a
+// 32-bit per-lane offset. `tile` points at row 0 of the tile for this head;
+// consecutive rows are tok_bytes apart.
+template <int BKV, int D, int WPF>
+struct TileFetch {
     using G = TileGeom<BKV, D>;
-    constexpr int BLOCKS_PER_WAVE = G::TILE / 1024 / WPF;
-    static_assert(BLOCKS_PER_WAVE >= 1 && G::TILE % (1024 * WPF) == 0, "tile must split evenly over the waves");
-    const int rl = lane / G::NC, pos = lane % G::NC;
-#pragma unroll
-    for (int i = 0; i < BLOCKS_PER_WAVE; ++i) {
-        const int blk = gw * BLOCKS_PER_WAVE + i;
+    static constexpr int BPW = G::TILE / 1024 / WPF;  // blocks per wave
+    static_assert(BPW >= 1 && G::TILE % (1024 * WPF) == 0, "tile must split evenly over the waves");
+
+    // block i (0 <= i < BPW) of wave gw's share
+    static __device__ __forceinline__ void block(char* smem, int dst, const char* tile, int tok_bytes, bool v_layout,
+                                                 int gw, int lane, int i) {
+        const int rl = lane / G::NC, pos = lane % G::NC;
+        const int blk = gw * BPW + i;
         const int row = blk * G::ROWS_PER_KB + rl;
         const int c = pos ^ (v_layout ? swz_v<G::NC>(row) : swz_k<G::NC>(row));
         const char* src = tile + (int64_t)(blk * G::ROWS_PER_KB) * tok_bytes;
         const uint32_t off = (uint32_t)(rl * tok_bytes + c * 16);
         lds_dma16(src, off, lds_addr(smem + dst + blk * 1024));
     }
-}
+    // wave gw's whole share
+    static __device__ __forceinline__ void all(char* smem, int dst, const char* tile, int tok_bytes, bool v_layout,
+                                               int gw, int lane) {
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) block(smem, dst, tile, tok_bytes, v_layout, gw, lane, i);
+    }
+};
+
+// Hook that issues nothing (phases without interleaved loads).
+struct NoHook {
+    __device__ __forceinline__ void operator()(int) const {}
+};
 
 template <int BKV, int D>
 struct WaveEngine {
@@ -170,11 +187,14 @@ struct WaveEngine {
     // and/or QK steps (S^T = K Q^T over the K tile at kb). When both run they
     // alternate 1:1 so consecutive MFMAs use independent accumulators; each
     // step's A operand is fetched RING steps ahead into a register ring.
-    template <bool PV, bool QK>
-    __device__ __forceinline__ void mfma_phase(int vb, int kb) {
+    // hook(0..NH-1) is called at evenly spaced step boundaries (hook 0 before
+    // the first MFMA) to spread other work, such as tile loads, over the phase.
+    template <bool PV, bool QK, int NH = 0, typename Hook = NoHook>
+    __device__ __forceinline__ void mfma_phase(int vb, int kb, Hook&& hook = Hook{}) {
         constexpr int NPV = PV ? DB * KC : 0;
         constexpr int NQK = QK ? NB * DC : 0;
         constexpr int NS = NPV + NQK;
+        static_assert(NH <= NS, "at most one hook per MFMA step");
         // step -> (is_pv, item); PV item i = (g = i / DB, db = i % DB), QK
         // item i = (c = i / NB, nb = i % NB)
         auto is_pv = [](int st) { return PV && (!QK || (st & 1) == 0); };
@@ -199,29 +219,46 @@ struct WaveEngine {
         bf16x8 ring[RING];
 #pragma unroll
         for (int st = 0; st < RING && st < NS; ++st) ring[st] = load(st);
+        // steps [S0, S1)
+        auto steps = [&]<int S0, int S1, bool PRE>() {
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-            const bf16x8 a = ring[st % RING];
-            if (st + RING < NS) ring[st % RING] = load(st + RING);
-            const int i = item(st);
-            if (is_pv(st)) {
-                const int g = i / DB, db = i % DB;
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[g], oacc[db], 0, 0, 0);
-            } else {
-                const int c = i / NB, nb = i % NB;
-                sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[c], sacc[nb], 0, 0, 0);
+            for (int st = S0; st < S1; ++st) {
+                const bf16x8 a = ring[st % RING];
+                if (st + RING < NS) ring[st % RING] = load(st + RING);
+                const int i = item(st);
+                if (is_pv(st)) {
+                    const int g = i / DB, db = i % DB;
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[g], oacc[db], 0, 0, 0);
+                } else {
+                    const int c = i / NB, nb = i % NB;
+                    sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[c], sacc[nb], 0, 0, 0);
+                }
             }
+            pin_mfma_steps<PV, QK, RING, NS, S0, S1, PRE>();
+        };
+        if constexpr (NH == 0) {
+            steps.template operator()<0, NS, true>();
+        } else {
+            // the ring fill forms its own scheduling region before hook 0
+            pin_mfma_steps<PV, QK, RING, NS, 0, 0, true>();
+            [&]<int... H>(std::integer_sequence<int, H...>) {
+                ((hook(H), steps.template operator()<H * NS / NH, (H + 1) * NS / NH, false>()), ...);
+            }(std::make_integer_sequence<int, NH>{});
         }
-        pin_mfma_schedule<PV, QK, RING, NS>();
     }
 
     // Softmax of the scores in sacc into pk (bf16), with the lazy rescale of
     // O and l. A tile whose list entry was out of range (ok == false)
-    // contributes nothing.
-    __device__ __forceinline__ void softmax(bool ok) {
+    // contributes nothing. hook(0..NH-1) is spread over the exponentials
+    // (and is called on skipped tiles too).
+    template <int NH = 0, typename Hook = NoHook>
+    __device__ __forceinline__ void softmax(bool ok, Hook&& hook = Hook{}) {
+        constexpr int CHUNKS = NB * 2;  // 8-score blocks per lane
         if (!ok) {
 #pragma unroll
             for (int g = 0; g < KC; ++g) pk[g] = bf16x8{};
+#pragma unroll
+            for (int i = 0; i < NH; ++i) hook(i);
             return;
         }
         float mx = sacc[0][0];
@@ -240,19 +277,21 @@ struct WaveEngine {
         }
         float lsum = 0.0f;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+        for (int ch = 0; ch < CHUNKS; ++ch) {
+            // hooks h with floor(h * CHUNKS / NH) == ch run before chunk ch
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                u32x4 w;
+            for (int h = 0; h < NH; ++h)
+                if (h * CHUNKS / NH == ch) hook(h);
+            const int nb = ch >> 1, half = ch & 1;
+            u32x4 w;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float p0 = fast_exp2(fmaf(sacc[nb][half * 8 + 2 * e], scale_log2, -m_run));
-                    const float p1 = fast_exp2(fmaf(sacc[nb][half * 8 + 2 * e + 1], scale_log2, -m_run));
-                    lsum += p0 + p1;
-                    w[e] = pack_bf16x2(p0, p1);
-                }
-                pk[nb * 2 + half] = __builtin_bit_cast(bf16x8, w);
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = fast_exp2(fmaf(sacc[nb][half * 8 + 2 * e], scale_log2, -m_run));
+                const float p1 = fast_exp2(fmaf(sacc[nb][half * 8 + 2 * e + 1], scale_log2, -m_run));
+                lsum += p0 + p1;
+                w[e] = pack_bf16x2(p0, p1);
             }
+            pk[ch] = __builtin_bit_cast(bf16x8, w);
         }
         l_run += lsum;
     }

@@ -44,7 +44,16 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per kernel launch (from rocprofv3 counters)")
+                    help="JSON file with measured HBM bytes per kernel launch (default: the one under profiles/ "
+                         "for this kernel and workload, used only if the kernel sources are unchanged)")
+    ap.add_argument("--clock-seconds", type=float, default=2.0,
+                    help="seconds of extra steps during which amd-smi samples the gfx clock (0: skip)")
+    ap.add_argument("--flush-steps", type=int, default=10,
+                    help="kernel launches timed after writing a buffer larger than the last-level cache")
+    ap.add_argument("--traffic-from-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                                  "COPY_WRITE_DIR"), default=None,
+                    help="write the traffic JSON from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE output directories "
+                         "of this workload and of --copy-calibration, then exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter calibration)")
     return ap.parse_args()
@@ -56,6 +65,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path (sharding is a design note).",
               file=sys.stderr)
         return 2
+
+    if args.traffic_from_counters:
+        return write_traffic(args)
 
     import torch
 
@@ -131,13 +143,47 @@ def main():
     value = flops / (ms_step * 1e-3) / 1e12
     kernel_tflops = flops / (kernel_ms * 1e-3) / 1e12
 
+    # Wrapper scope: mask front-end + the entry point that builds its own
+    # work list (what a caller without a cached work list pays).
+    def wrapper():
+        vsa.vsa_mask_to_csr(mask, (lq, lkv), (bq, bkv), ld, idx, cnt, stream=stream)
+        vsa.vsa_attn_fwd(q, k, v, idx, cnt, bq, bkv, scale, o, lse, stream=stream)
+
+    for _ in range(2):
+        wrapper()
+    torch.cuda.synchronize()
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for _ in range(args.steps):
+        wrapper()
+    w1.record(stream)
+    torch.cuda.synchronize()
+    wrapper_ms = w0.elapsed_time(w1) / args.steps
+
+    # Post-flush: the kernel alone after overwriting a buffer larger than the
+    # 256 MB last-level cache, so Q/K/V start cold.
+    kernel_ms_flush = None
+    if args.flush_steps > 0:
+        junk = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        fl_events = []
+        for i in range(args.flush_steps):
+            junk.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            vsa.vsa_attn_fwd_worklist(q, k, v, idx, cnt, bq, bkv, work, scale, o, lse, stream=stream)
+            e1.record(stream)
+            fl_events.append((e0, e1))
+        torch.cuda.synchronize()
+        kernel_ms_flush = float(np.mean([e0.elapsed_time(e1) for e0, e1 in fl_events]))
+        del junk
+
+    clock = sample_clock(step, args.clock_seconds) if args.clock_seconds > 0 else None
+
     # Algorithmic HBM bytes of one kernel launch: Q, K, V read once, O and
     # LSE written once, CSR indices and counts read once.
     alg_bytes = (3 * B * S * H * D + B * S * H * D) * 2 + B * H * S * 4 + (B * H * nq) * (ld + 2) * 4
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+    kname = kernel_name(bq, bkv, D)
+    traffic = read_traffic(args.traffic or default_traffic_path(kname, wl.name, bq, bkv))
 
     result = {
         "metric": METRIC,
@@ -164,6 +210,11 @@ def main():
         "kernel_ms": round(kernel_ms, 4),
         "kernel_tflops": round(kernel_tflops, 2),
         "frontend_ms": round(ms_step - kernel_ms, 4),
+        "wrapper_ms": round(wrapper_ms, 4),
+        "wrapper_tflops": round(flops / (wrapper_ms * 1e-3) / 1e12, 2),
+        "kernel_ms_post_flush": None if kernel_ms_flush is None else round(kernel_ms_flush, 4),
+        "kernel_tflops_post_flush": None if kernel_ms_flush is None else round(flops / (kernel_ms_flush * 1e-3) / 1e12, 2),
+        "clock": clock,
         "roofline": {
             "bound": "mfma",
             "achieved": round(kernel_tflops, 2),
@@ -172,7 +223,7 @@ def main():
             "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "algorithmic_bytes": alg_bytes,
-            "kernel": kernel_name(bq, bkv, D),
+            "kernel": kname,
         },
     }
 
@@ -187,7 +238,123 @@ def kernel_name(bq, bkv, d):
     """Name of the forward kernel the library dispatches for this tile shape."""
     if bq == 256:
         return f"vsa_fwd_pp_kernel<{bkv},{d}>"
-    return f"vsa_fwd_kernel<{bq},{bkv},{d}>"
+    if bq == 128:
+        return f"vsa_fwd_2s_kernel<{d}>"
+    return f"vsa_fwd_4s_kernel<{d}>"
+
+
+CSRC = os.path.join(ROOT, "block_sparse_attention_flashattention_amd", "csrc")
+
+
+def kernel_source_hash():
+    """sha256 over the HIP sources the library is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def default_traffic_path(kname, workload, bq, bkv):
+    stem = kname.split("<")[0]
+    return os.path.join(ROOT, "profiles", f"traffic_{stem}_{bq}x{bkv}_{workload}.json")
+
+
+def read_traffic(path):
+    """HBM bytes per launch from a traffic JSON, or None if it is missing or
+    was measured on other kernel sources."""
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def _counter_mean(d, counter, kernel_prefix):
+    import csv
+    vals = []
+    with open(os.path.join(d, "run_counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and kernel_prefix in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for {kernel_prefix!r} in {d}")
+    return sum(vals) / len(vals)
+
+
+def write_traffic(args):
+    """Traffic JSON from FETCH_SIZE / WRITE_SIZE passes (KiB per dispatch),
+    each scaled by what the same counter reads for a plain copy of known size."""
+    import workloads as W
+    wl = W.WORKLOADS[args.workload]
+    bq, bkv = (int(x) for x in args.tile.lower().split("x")) if args.tile else wl.physical[0]
+    kname = kernel_name(bq, bkv, wl.head_dim)
+    stem = kname.split("<")[0]
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_from_counters
+    copy_bytes = 1 << 30
+    fetch_scale = copy_bytes / (1024.0 * _counter_mean(cfetch_dir, "FETCH_SIZE", "copy"))
+    write_scale = copy_bytes / (1024.0 * _counter_mean(cwrite_dir, "WRITE_SIZE", "copy"))
+    fetch = _counter_mean(fetch_dir, "FETCH_SIZE", stem) * 1024.0 * fetch_scale
+    write = _counter_mean(write_dir, "WRITE_SIZE", stem) * 1024.0 * write_scale
+    out = {
+        "kernel": kname, "workload": wl.name, "tile": f"{bq}x{bkv}",
+        "bytes_per_launch": round(fetch + write),
+        "fetch_bytes": round(fetch), "write_bytes": round(write),
+        "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
+        "source_hash": kernel_source_hash(),
+    }
+    path = args.traffic or default_traffic_path(kname, wl.name, bq, bkv)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+    return 0
+
+
+def sample_clock(step, seconds):
+    """Run steps back to back for about `seconds` while amd-smi reads the gfx
+    clock of every XCD once, half-way through."""
+    import subprocess
+    import threading
+
+    import torch
+    box = {}
+
+    def query():
+        try:
+            r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True,
+                               timeout=30)
+            d = json.loads(r.stdout)
+            d = d["gpu_data"][0] if isinstance(d, dict) and "gpu_data" in d else d[0]
+            clk = d["clock"]
+            box["mhz"] = [float(clk[k]["clk"]["value"]) for k in sorted(clk) if k.startswith("gfx_")]
+        except Exception as e:  # best effort: the tool may be missing or print another layout
+            box["error"] = f"{type(e).__name__}: {e}"[:200]
+
+    t_end = time.perf_counter() + seconds
+    th = None
+    while True:
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+        now = time.perf_counter()
+        if th is None and now > t_end - seconds / 2:
+            th = threading.Thread(target=query)
+            th.start()
+        if now > t_end and th is not None and not th.is_alive():
+            break
+        if now > t_end + 40:
+            break
+    if "mhz" not in box:
+        return {"gfx_mhz_mean": None, "error": box.get("error", "no sample")}
+    mhz = box["mhz"]
+    return {"gfx_mhz_mean": round(sum(mhz) / len(mhz), 1), "gfx_mhz": mhz,
+            "source": "amd-smi metric --clock, sampled while steps ran back to back"}
 
 
 def cpu_baseline(wl, q, k, v, idx, cnt, bq, bkv, ld, seconds):

@@ -60,10 +60,12 @@ __global__ __launch_bounds__(512) void vsa_fwd_2s_kernel(FwdParams prm) {
     const int S = prm.S;
     const int64_t tok_stride = (int64_t)prm.H * D;
     const int tok_bytes = (int)(tok_stride * 2);
-    int n = prm.cnt[item];
-    n = n < 0 ? 0 : (n > prm.ld ? prm.ld : n);
-    n = n > kIdxCap2s ? kIdxCap2s : n;
+    // The count, the CSR row and Q are fetched at once; the row is read up
+    // to its allocated length ld, so it does not wait for the count.
     const int32_t* irow = prm.idx + (int64_t)item * prm.ld;
+    const int ldc = prm.ld < kIdxCap2s ? prm.ld : kIdxCap2s;
+    int n = prm.cnt[item];
+    n = n < 0 ? 0 : (n > ldc ? ldc : n);
     const int nkv = prm.nkv;
     const int block_kv = prm.block_kv;
     const int R = block_kv / SUB;  // sub-tiles per CSR tile (1 or 2)
@@ -80,8 +82,7 @@ __global__ __launch_bounds__(512) void vsa_fwd_2s_kernel(FwdParams prm) {
     e.load_q(prm.q + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D);
 
     int* lidx = (int*)(smem + 2 * GROUP_LDS);
-    for (int i = tid; i < n; i += 512) lidx[i] = irow[i];
-    lds_barrier();
+    for (int i = tid; i < ldc; i += 512) lidx[i] = irow[i];
 
     // sub-tile j of this stream -> CSR entry and 64-key offset inside it
     auto tile_of = [&](int j) { return __builtin_amdgcn_readfirstlane(lidx[(first + j) / R]); };
@@ -90,11 +91,13 @@ __global__ __launch_bounds__(512) void vsa_fwd_2s_kernel(FwdParams prm) {
     const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
     using F = TileFetch<SUB, D, 4>;
     const int fw = wave & 3;  // this wave's index among the waves fetching its stream's tiles
-    auto tile_ptr = [&](const char* base, int j) {
-        const int t = tile_of(j);
+    // sub-tile j of this stream in CSR tile t; out-of-range tiles load tile 0
+    // and contribute nothing
+    auto sub_ptr = [&](const char* base, int t, int j) {
         const int64_t row0 = (int64_t)(valid(t) ? t : 0) * block_kv + ((first + j) % R) * SUB;
         return base + row0 * tok_bytes;
     };
+    auto tile_ptr = [&](const char* base, int j) { return sub_ptr(base, tile_of(j), j); };
     const int gbase = grp * GROUP_LDS;
     auto kbuf = [&](int j) { return gbase + (j & 1) * G::TILE; };
     auto vbuf = [&](int j) { return gbase + (2 + (j & 1)) * G::TILE; };
@@ -125,10 +128,13 @@ __global__ __launch_bounds__(512) void vsa_fwd_2s_kernel(FwdParams prm) {
         ++nbar;
     };
 
+    // K_0 of this stream, addressed straight from the CSR row in memory; the
+    // barrier then publishes both it and the staged row.
     if (ng > 0) {
-        F::all(smem, kbuf(0), tile_ptr(kbase, 0), tok_bytes, false, fw, lane);
-        wait_global_loads();
+        const int t0 = __builtin_amdgcn_readfirstlane(irow[first / R]);
+        F::all(smem, kbuf(0), sub_ptr(kbase, t0, 0), tok_bytes, false, fw, lane);
     }
+    wait_global_loads();
     bar();
     if (grp == 1) bar();
     if (ng > 0) {

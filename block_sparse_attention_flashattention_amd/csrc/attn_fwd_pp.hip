@@ -58,12 +58,21 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     const int S = prm.S;
     const int64_t tok_stride = (int64_t)prm.H * D;
     const int tok_bytes = (int)(tok_stride * 2);
-    int n = prm.cnt[item];
-    n = n < 0 ? 0 : (n > prm.ld ? prm.ld : n);
-    n = n > kIdxCap ? kIdxCap : n;
+    // The count, the CSR row, Q and the first K tile are all fetched at once
+    // (none of these loads waits for another; the row is read up to its
+    // allocated length ld, so it does not need the count first).
     const int32_t* irow = prm.idx + (int64_t)item * prm.ld;
+    const int ldc = prm.ld < kIdxCap ? prm.ld : kIdxCap;
+    const int first_tile = __builtin_amdgcn_readfirstlane(irow[0]);
+    int n = prm.cnt[item];
     const int nkv = prm.nkv;
     const int q0 = p * BQ + wave * 32;
+    auto valid = [&](int t) { return t >= 0 && t < nkv; };
+    const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    using F = TileFetch<BKV, D, 4>;  // a tile is fetched by the four waves of one group
+    // out-of-range entries load tile 0 and contribute nothing
+    auto tile_at = [&](const char* base, int t) { return base + (int64_t)(valid(t) ? t : 0) * BKV * tok_bytes; };
 
     E e;
     e.init(smem, lane, prm.scale_log2);
@@ -72,20 +81,16 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     // Stage this tile's CSR row in LDS: list entries are then read with
     // uniform LDS loads, which do not wait on outstanding global loads.
     int* lidx = (int*)(smem + LDS_TILES);
-    for (int i = tid; i < n; i += 512) lidx[i] = irow[i];
+    for (int i = tid; i < ldc; i += 512) lidx[i] = irow[i];
+    // group 1 fetches K_0 (buffer 0 is free); an empty row fetches it too
+    if (grp == 1) F::all(smem, 0, tile_at(kbase, first_tile), tok_bytes, false, wave & 3, lane);
+    n = n < 0 ? 0 : (n > ldc ? ldc : n);
+    wait_global_loads();
     lds_barrier();
 
-    // Tile index of list entry j (uniform); out-of-range entries load tile 0
-    // and contribute nothing.
+    // Tile index of list entry j (uniform).
     auto tile_of = [&](int j) { return __builtin_amdgcn_readfirstlane(lidx[j]); };
-    auto valid = [&](int t) { return t >= 0 && t < nkv; };
-    const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
-    const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
-    using F = TileFetch<BKV, D, 4>;  // a tile is fetched by the four waves of one group
-    auto tile_ptr = [&](const char* base, int j) {
-        const int t = tile_of(j);
-        return base + (int64_t)(valid(t) ? t : 0) * BKV * tok_bytes;
-    };
+    auto tile_ptr = [&](const char* base, int j) { return tile_at(base, tile_of(j)); };
     // LDS byte offsets of the K and V buffers used for list entry j
     auto kbuf = [](int j) { return (j & 1) * G::TILE; };
     auto vbuf = [](int j) { return (2 + (j & 1)) * G::TILE; };
@@ -104,14 +109,7 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     auto pv = [&](int j) { e.template mfma_phase<true, false>(vbuf(j), 0); };
     auto softmax = [&](int j) { e.softmax(valid(tile_of(j))); };
 
-    // prologue: group 1 fetches K_0
-    if (grp == 1 && n > 0) {
-        F::all(smem, kbuf(0), tile_ptr(kbase, 0), tok_bytes, false, wave & 3, lane);
-        wait_global_loads();
-    }
-    lds_barrier();
-
-    // Both groups pass 2(n+1) barriers. Each group has its own loop so that
+    // Both groups pass 2(n+1) barriers after the prologue. Each group has its own loop so that
     // S (live from M_j to V_j) and P (live from V_j to M_{j+1}) never both
     // cross a loop back-edge, and the first and last tiles are peeled so the
     // steady-state MFMA phase (PV_{j-1} then QK_j) is one basic block.

@@ -46,6 +46,9 @@ def parse_args():
     ap.add_argument("--traffic", default=None,
                     help="JSON file with measured HBM bytes per kernel launch (default: the one under profiles/ "
                          "for this kernel and workload, used only if the kernel sources are unchanged)")
+    ap.add_argument("--prewarm-seconds", type=float, default=0.5,
+                    help="run steps back to back for this long before the warmup steps, so that the timed "
+                         "steps see the sustained clock rather than the ramp out of idle")
     ap.add_argument("--clock-seconds", type=float, default=2.0,
                     help="seconds of extra steps during which amd-smi samples the gfx clock (0: skip)")
     ap.add_argument("--flush-steps", type=int, default=10,
@@ -127,6 +130,11 @@ def main():
     torch.cuda.synchronize()
     pairs = int(cnt.to(torch.int64).sum().item()) * bq * bkv
     flops = 4.0 * D * pairs
+    t_pre = time.perf_counter() + args.prewarm_seconds
+    while time.perf_counter() < t_pre:
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
 

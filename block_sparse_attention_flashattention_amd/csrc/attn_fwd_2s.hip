@@ -83,6 +83,7 @@ __global__ __launch_bounds__(512) void vsa_fwd_2s_kernel(FwdParams prm) {
 
     int* lidx = (int*)(smem + 2 * GROUP_LDS);
     for (int i = tid; i < ldc; i += 512) lidx[i] = irow[i];
+    e.q_ready();
 
     // sub-tile j of this stream -> CSR entry and 64-key offset inside it
     auto tile_of = [&](int j) { return __builtin_amdgcn_readfirstlane(lidx[(first + j) / R]); };
@@ -91,11 +92,12 @@ __global__ __launch_bounds__(512) void vsa_fwd_2s_kernel(FwdParams prm) {
     const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
     using F = TileFetch<SUB, D, 4>;
     const int fw = wave & 3;  // this wave's index among the waves fetching its stream's tiles
+    const F fetch(fw, lane, tok_bytes);
     // sub-tile j of this stream in CSR tile t; out-of-range tiles load tile 0
     // and contribute nothing
     auto sub_ptr = [&](const char* base, int t, int j) {
         const int64_t row0 = (int64_t)(valid(t) ? t : 0) * block_kv + ((first + j) % R) * SUB;
-        return base + row0 * tok_bytes;
+        return uniform_ptr(base + row0 * tok_bytes);
     };
     auto tile_ptr = [&](const char* base, int j) { return sub_ptr(base, tile_of(j), j); };
     const int gbase = grp * GROUP_LDS;
@@ -104,17 +106,18 @@ __global__ __launch_bounds__(512) void vsa_fwd_2s_kernel(FwdParams prm) {
     // The loads of M_j (K_{j+1} if it exists, then V_j) are spread over the
     // MFMA phase, one 1 KB block per hook.
     auto loads = [&](int j) {
-        const bool more = j + 1 < ng;
-        const char* kt = more ? tile_ptr(kbase, j + 1) : kbase;
+        const char* kt = tile_ptr(kbase, j + 1);
         const char* vt = tile_ptr(vbase, j);
         const int kd = kbuf(j + 1), vd = vbuf(j);
-        return [=, &lane](int i) {
-            if (i < F::BPW) {
-                if (more) F::block(smem, kd, kt, tok_bytes, false, fw, lane, i);
-            } else {
-                F::block(smem, vd, vt, tok_bytes, true, fw, lane, i - F::BPW);
-            }
+        return [=, &fetch](int i) {
+            if (i < F::BPW) fetch.block(smem, kd, kt, tok_bytes, false, i);
+            else fetch.block(smem, vd, vt, tok_bytes, true, i - F::BPW);
         };
+    };
+    auto v_loads = [&](int j) {
+        const char* vt = tile_ptr(vbase, j);
+        const int vd = vbuf(j);
+        return [=, &fetch](int i) { fetch.block(smem, vd, vt, tok_bytes, true, i); };
     };
     auto pv = [&](int j) { e.template mfma_phase<true, false>(vbuf(j), 0); };
     auto softmax = [&](int j) { e.softmax(valid(tile_of(j))); };
@@ -132,21 +135,31 @@ __global__ __launch_bounds__(512) void vsa_fwd_2s_kernel(FwdParams prm) {
     // barrier then publishes both it and the staged row.
     if (ng > 0) {
         const int t0 = __builtin_amdgcn_readfirstlane(irow[first / R]);
-        F::all(smem, kbuf(0), sub_ptr(kbase, t0, 0), tok_bytes, false, fw, lane);
+        fetch.all(smem, kbuf(0), sub_ptr(kbase, t0, 0), tok_bytes, false);
     }
     wait_global_loads();
     bar();
     if (grp == 1) bar();
+    // M_j fetches K_{j+1} and V_j; the last M_j has no K to fetch and is peeled
+    // so that the loop body has no branch per load.
     if (ng > 0) {
-        e.template mfma_phase<false, true, 2 * F::BPW>(0, kbuf(0), loads(0));               // M_0
+        if (ng > 1) e.template mfma_phase<false, true, 2 * F::BPW>(0, kbuf(0), loads(0));   // M_0
+        else e.template mfma_phase<false, true, F::BPW>(0, kbuf(0), v_loads(0));
         bar();
         softmax(0);                              // V_0
         wait_global_loads();
         bar();
-        for (int j = 1; j < ng; ++j) {
+        for (int j = 1; j < ng - 1; ++j) {
             e.template mfma_phase<true, true, 2 * F::BPW>(vbuf(j - 1), kbuf(j), loads(j));  // M_j
             bar();
             softmax(j);                          // V_j
+            wait_global_loads();
+            bar();
+        }
+        if (ng > 1) {
+            e.template mfma_phase<true, true, F::BPW>(vbuf(ng - 2), kbuf(ng - 1), v_loads(ng - 1));
+            bar();
+            softmax(ng - 1);
             wait_global_loads();
             bar();
         }

@@ -71,8 +71,11 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
     const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
     using F = TileFetch<BKV, D, 4>;  // a tile is fetched by the four waves of one group
+    const F fetch(wave & 3, lane, tok_bytes);
     // out-of-range entries load tile 0 and contribute nothing
-    auto tile_at = [&](const char* base, int t) { return base + (int64_t)(valid(t) ? t : 0) * BKV * tok_bytes; };
+    auto tile_at = [&](const char* base, int t) {
+        return uniform_ptr(base + (int64_t)(valid(t) ? t : 0) * BKV * tok_bytes);
+    };
 
     E e;
     e.init(smem, lane, prm.scale_log2);
@@ -82,8 +85,9 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     // uniform LDS loads, which do not wait on outstanding global loads.
     int* lidx = (int*)(smem + LDS_TILES);
     for (int i = tid; i < ldc; i += 512) lidx[i] = irow[i];
+    e.q_ready();
     // group 1 fetches K_0 (buffer 0 is free); an empty row fetches it too
-    if (grp == 1) F::all(smem, 0, tile_at(kbase, first_tile), tok_bytes, false, wave & 3, lane);
+    if (grp == 1) fetch.all(smem, 0, tile_at(kbase, first_tile), tok_bytes, false);
     n = n < 0 ? 0 : (n > ldc ? ldc : n);
     wait_global_loads();
     lds_barrier();
@@ -98,13 +102,11 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     // the eight waves' loads do not queue up at the start of the phase.
     auto v_loads = [&](int j) {
         const char* tile = tile_ptr(vbase, j);
-        return [=, &lane](int i) { F::block(smem, vbuf(j), tile, tok_bytes, true, wave & 3, lane, i); };
+        return [=, &fetch](int i) { fetch.block(smem, vbuf(j), tile, tok_bytes, true, i); };
     };
-    auto k_loads = [&](int j, bool on) {
-        const char* tile = on ? tile_ptr(kbase, j) : kbase;
-        return [=, &lane](int i) {
-            if (on) F::block(smem, kbuf(j), tile, tok_bytes, false, wave & 3, lane, i);
-        };
+    auto k_loads = [&](int j) {
+        const char* tile = tile_ptr(kbase, j);
+        return [=, &fetch](int i) { fetch.block(smem, kbuf(j), tile, tok_bytes, false, i); };
     };
     auto pv = [&](int j) { e.template mfma_phase<true, false>(vbuf(j), 0); };
     auto softmax = [&](int j) { e.softmax(valid(tile_of(j))); };
@@ -133,15 +135,23 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
         lds_barrier();
     } else {
         if (n > 0) {
-            if (n > 1) F::all(smem, kbuf(1), tile_ptr(kbase, 1), tok_bytes, false, wave & 3, lane);
+            if (n > 1) fetch.all(smem, kbuf(1), tile_ptr(kbase, 1), tok_bytes, false);
             lds_barrier();
             e.template mfma_phase<false, true>(0, kbuf(0));                                    // M_0
             wait_global_loads();
             lds_barrier();
-            for (int j = 1; j < n; ++j) {
-                e.template softmax<F::BPW>(valid(tile_of(j - 1)), k_loads(j + 1, j + 1 < n)); // V_{j-1}
+            // the last tile has no K_{j+1} to fetch: peeled, so the loop body has no branch per load
+            for (int j = 1; j < n - 1; ++j) {
+                e.template softmax<F::BPW>(valid(tile_of(j - 1)), k_loads(j + 1));  // V_{j-1}
                 lds_barrier();
-                e.template mfma_phase<true, true>(vbuf(j - 1), kbuf(j));                       // M_j
+                e.template mfma_phase<true, true>(vbuf(j - 1), kbuf(j));            // M_j
+                wait_global_loads();
+                lds_barrier();
+            }
+            if (n > 1) {
+                softmax(n - 2);                  // V_{n-2}
+                lds_barrier();
+                e.template mfma_phase<true, true>(vbuf(n - 2), kbuf(n - 1));        // M_{n-1}
                 wait_global_loads();
                 lds_barrier();
             }

@@ -66,6 +66,14 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t voff, uint3
         : "v"(voff), "s"(base), "s"(lds)
         : "memory", "m0");
 }
+// A wave-uniform pointer pinned to scalar registers, so that address
+// arithmetic on it stays on the scalar unit.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+    const uint64_t b = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);

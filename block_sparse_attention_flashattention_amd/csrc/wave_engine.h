@@ -89,28 +89,43 @@ struct TileGeom {
 // is one direct-to-LDS 16-byte-per-lane load from a uniform row base plus a
 // 32-bit per-lane offset. `tile` points at row 0 of the tile for this head;
 // consecutive rows are tok_bytes apart.
+//
+// A lane's offset within its block depends on the block only through the
+// swizzle, which repeats every KP blocks for K and is the same for every
+// block for V; the KP + 1 offsets are computed once, so issuing a block costs
+// no vector ALU work (the row base and the LDS address are scalar).
 template <int BKV, int D, int WPF>
 struct TileFetch {
     using G = TileGeom<BKV, D>;
     static constexpr int BPW = G::TILE / 1024 / WPF;  // blocks per wave
     static_assert(BPW >= 1 && G::TILE % (1024 * WPF) == 0, "tile must split evenly over the waves");
+    // swizzle period in blocks: swz_k depends on row % 16 (NC=16) or row % 16 / 2 (NC=8)
+    static constexpr int KP = 16 / G::ROWS_PER_KB;
 
-    // block i (0 <= i < BPW) of wave gw's share
-    static __device__ __forceinline__ void block(char* smem, int dst, const char* tile, int tok_bytes, bool v_layout,
-                                                 int gw, int lane, int i) {
+    int gw;
+    uint32_t koff[KP];
+    uint32_t voff;
+
+    __device__ __forceinline__ TileFetch(int gw_, int lane, int tok_bytes) : gw(gw_) {
         const int rl = lane / G::NC, pos = lane % G::NC;
-        const int blk = gw * BPW + i;
-        const int row = blk * G::ROWS_PER_KB + rl;
-        const int c = pos ^ (v_layout ? swz_v<G::NC>(row) : swz_k<G::NC>(row));
-        const char* src = tile + (int64_t)(blk * G::ROWS_PER_KB) * tok_bytes;
-        const uint32_t off = (uint32_t)(rl * tok_bytes + c * 16);
-        lds_dma16(src, off, lds_addr(smem + dst + blk * 1024));
-    }
-    // wave gw's whole share
-    static __device__ __forceinline__ void all(char* smem, int dst, const char* tile, int tok_bytes, bool v_layout,
-                                               int gw, int lane) {
 #pragma unroll
-        for (int i = 0; i < BPW; ++i) block(smem, dst, tile, tok_bytes, v_layout, gw, lane, i);
+        for (int k = 0; k < KP; ++k) {
+            const int row = ((gw * BPW + k) % KP) * G::ROWS_PER_KB + rl;
+            koff[k] = (uint32_t)(rl * tok_bytes + ((pos ^ swz_k<G::NC>(row)) << 4));
+        }
+        voff = (uint32_t)(rl * tok_bytes + ((pos ^ swz_v<G::NC>(rl)) << 4));
+    }
+    // block i (0 <= i < BPW) of this wave's share
+    __device__ __forceinline__ void block(char* smem, int dst, const char* tile, int tok_bytes, bool v_layout,
+                                          int i) const {
+        const int blk = gw * BPW + i;
+        const char* src = tile + (int64_t)(blk * G::ROWS_PER_KB) * tok_bytes;
+        lds_dma16(src, v_layout ? voff : koff[i % KP], lds_addr(smem + dst + blk * 1024));
+    }
+    // this wave's whole share
+    __device__ __forceinline__ void all(char* smem, int dst, const char* tile, int tok_bytes, bool v_layout) const {
+#pragma unroll
+        for (int i = 0; i < BPW; ++i) block(smem, dst, tile, tok_bytes, v_layout, i);
     }
 };
 
@@ -181,6 +196,15 @@ struct WaveEngine {
         const uint16_t* qp = qrow + hi * 8;
 #pragma unroll
         for (int c = 0; c < DC; ++c) qreg[c] = *(const bf16x8*)(qp + c * 16);
+    }
+
+    // Makes the compiler wait for the Q loads here. Its wait counting does not
+    // see the direct-to-LDS loads issued through inline asm, so a Q register
+    // first used after some of them would get a wait that also covers those
+    // tile loads; consuming Q before the first tile load avoids that.
+    __device__ __forceinline__ void q_ready() const {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) asm volatile("" ::"v"(qreg[c]));
     }
 
     // MFMA phase: PV steps (O^T += V^T P^T over the V tile at LDS offset vb)

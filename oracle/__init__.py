@@ -7,7 +7,8 @@ calls anything here, and this package shares no code with it.
 * ``attn_rows`` / ``attn_full`` / ``probs_row`` wrap ``vsa_oracle.c``, a plain
   fp32 masked SDPA (FastVideo page, ``bench_vsa_blackwell.py``,
   ``ref_masked_sdpa_fp32``).
-* ``mask_to_csr`` / ``build_worklist`` live in ``frontend.py`` (numpy).
+* ``mask_to_csr`` / ``build_worklist`` / ``expand_valid`` live in
+  ``frontend.py`` (numpy).
 
 Parity of every function here is pinned by ``tests/test_oracle_pins.py`` and
 ``tests/test_frontend_oracle.py`` against brute force, library routines,
@@ -22,7 +23,7 @@ import subprocess
 
 import numpy as np
 
-from .frontend import build_worklist, mask_to_csr  # noqa: F401
+from .frontend import build_worklist, expand_valid, mask_to_csr  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "vsa_oracle.c")
@@ -58,10 +59,10 @@ def _load():
         p = ctypes.c_void_p
         i32 = ctypes.c_int
         i64 = ctypes.c_int64
-        lib.vsa_oracle_attn_rows.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
+        lib.vsa_oracle_attn_rows.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
                                              ctypes.c_float, p, i64, p, p, i32]
         lib.vsa_oracle_attn_rows.restype = i32
-        lib.vsa_oracle_probs_row.argtypes = [p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
+        lib.vsa_oracle_probs_row.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
                                              ctypes.c_float, i64, p]
         lib.vsa_oracle_probs_row.restype = i32
         _lib = lib
@@ -90,12 +91,22 @@ def _check(rc: int):
         raise ValueError(f"oracle: {_ERRORS.get(rc, rc)}")
 
 
-def attn_rows(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, rows=None, threads=0):
+def _valid_arr(kv_valid, S, block_kv):
+    if kv_valid is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(kv_valid), dtype=np.int32)
+    if a.shape != (S // block_kv,):
+        raise ValueError("kv_valid must hold one count per KV tile: [S/block_kv]")
+    return a
+
+
+def attn_rows(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, rows=None, threads=0, kv_valid=None):
     """O (fp32 [n, D]) and LSE (fp32 [n]) for flat rows (b*H + h)*S + i.
 
     q, k, v: bf16 [B, S, H, D] (torch tensors or uint16 bit arrays);
     kv_block_idx [B, H, NQ, ld] / kv_block_cnt [B, H, NQ] int32 block CSR.
-    ``rows=None`` computes every row in (b, h, i) order.
+    ``rows=None`` computes every row in (b, h, i) order. ``kv_valid``
+    [S/block_kv]: valid leading key tokens of each KV tile (None: all full).
     """
     qb, kb, vb = _bits(q), _bits(k), _bits(v)
     B, S, H, D = qb.shape
@@ -115,37 +126,50 @@ def attn_rows(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, row
         n = rows_arr.size
     o = np.empty((n, D), dtype=np.float32)
     lse = np.empty((n,), dtype=np.float32)
+    val = _valid_arr(kv_valid, S, block_kv)
     rc = _load().vsa_oracle_attn_rows(
-        _ptr(qb), _ptr(kb), _ptr(vb), _ptr(idx), _ptr(cnt), B, S, H, D, ld, block_q, block_kv,
+        _ptr(qb), _ptr(kb), _ptr(vb), _ptr(idx), _ptr(cnt), None if val is None else _ptr(val), B, S, H, D, ld,
+        block_q, block_kv,
         ctypes.c_float(scale), None if rows_arr is None else _ptr(rows_arr), n, _ptr(o), _ptr(lse),
         int(threads))
     _check(rc)
     return o, lse
 
 
-def attn_full(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, threads=0):
+def attn_full(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, threads=0, kv_valid=None):
     """O fp32 [B, S, H, D] and LSE fp32 [B, H, S] for every row."""
     qb = _bits(q)
     B, S, H, D = qb.shape
-    o, lse = attn_rows(qb, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, None, threads)
+    o, lse = attn_rows(qb, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, None, threads, kv_valid)
     o = o.reshape(B, H, S, D).transpose(0, 2, 1, 3).copy()
     return o, lse.reshape(B, H, S)
 
 
-def probs_row(q, k, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, flat_row):
+def probs_row(q, k, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, flat_row, kv_valid=None):
     """Softmax weights [S] of one query row over all key tokens (0 if masked)."""
     qb, kb = _bits(q), _bits(k)
     B, S, H, D = qb.shape
     idx = np.ascontiguousarray(kv_block_idx, dtype=np.int32)
     cnt = np.ascontiguousarray(kv_block_cnt, dtype=np.int32)
     p = np.empty((S,), dtype=np.float32)
-    rc = _load().vsa_oracle_probs_row(_ptr(qb), _ptr(kb), _ptr(idx), _ptr(cnt), B, S, H, D,
+    val = _valid_arr(kv_valid, S, block_kv)
+    rc = _load().vsa_oracle_probs_row(_ptr(qb), _ptr(kb), _ptr(idx), _ptr(cnt), None if val is None else _ptr(val),
+                                      B, S, H, D,
                                       idx.shape[3], block_q, block_kv, ctypes.c_float(scale),
                                       int(flat_row), _ptr(p))
     _check(rc)
     return p
 
 
-def selected_pairs(kv_block_cnt, block_q, block_kv) -> int:
-    """Number of selected (query token, key token) pairs of a block CSR."""
-    return int(np.asarray(kv_block_cnt, dtype=np.int64).sum()) * block_q * block_kv
+def selected_pairs(kv_block_cnt, block_q, block_kv, kv_block_idx=None, kv_valid=None) -> int:
+    """Number of selected (query token, key token) pairs of a block CSR; with
+    kv_valid, only the valid keys of each selected tile count."""
+    if kv_valid is None:
+        return int(np.asarray(kv_block_cnt, dtype=np.int64).sum()) * block_q * block_kv
+    idx = np.asarray(kv_block_idx)
+    cnt = np.asarray(kv_block_cnt)
+    val = np.asarray(kv_valid, dtype=np.int64)
+    total = 0
+    for pos in np.ndindex(cnt.shape):
+        total += int(val[idx[pos][:cnt[pos]]].sum())
+    return total * block_q

@@ -11,6 +11,12 @@ repeats every mask row 256/q_block times along Q and every column
 indices of the expanded mask (``arange(nkv).masked_select(mask)``) together
 with their count.
 
+``expand_valid``: per-tile valid key counts (partial tiles) at the physical
+KV tile size, from the logical blocks' valid token counts (the variable block
+sizes ``vbs`` of the FastVideo page's VSA wrapper): a logical block of LKV
+positions holding vbs valid tokens first, then padding, splits into LKV/PKV
+physical tiles holding clamp(vbs - r*PKV, 0, PKV) valid tokens each.
+
 ``build_worklist``: the order in which Q tiles are processed. Items
 (b, h, p) are encoded as their flat index into kv_block_cnt. Within each
 segment of ``segment`` consecutive items (one segment per batch and head when
@@ -70,3 +76,18 @@ def build_worklist(kv_block_cnt, ld, segment=None):
     for s0 in range(0, n, segment):
         out[s0:s0 + segment] = s0 + np.argsort(-c[s0:s0 + segment], kind="stable")
     return out
+
+
+def expand_valid(vbs, logical_kv, physical_kv):
+    """Valid key tokens per physical KV tile [NKV_l * LKV/PKV] from the valid
+    tokens per logical KV block vbs [NKV_l] (each in [0, LKV])."""
+    v = np.asarray(vbs, dtype=np.int64)
+    if logical_kv % physical_kv:
+        raise ValueError("physical tile size must divide the logical block size")
+    if np.any(v < 0) or np.any(v > logical_kv):
+        raise ValueError("valid counts must lie in [0, logical block size]")
+    e = logical_kv // physical_kv
+    out = np.empty((v.size, e), dtype=np.int32)
+    for r in range(e):
+        out[:, r] = np.clip(v - r * physical_kv, 0, physical_kv)
+    return out.reshape(-1)

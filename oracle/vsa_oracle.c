@@ -23,6 +23,14 @@
  * [B,H,NQ] int32. Entries may be in any order; they must be distinct and in
  * [0, S/block_kv).
  *
+ * Partial tiles (optional kv_valid [S/block_kv] int32, shared by all batches
+ * and heads): only the first kv_valid[t] key tokens of KV tile t exist, the
+ * rest of the tile is padding that no query attends to. This is the variable
+ * block size input `vbs` of the FastVideo page's VSA wrapper
+ * (block_sparse_attn_256_bshd(q, k, v, mask, vbs)), stated per physical tile;
+ * kv_valid = NULL means every tile is full. A query row whose selected tiles
+ * hold no valid key is an empty row (O = 0, LSE = -inf).
+ *
  * Evaluation order is fixed and independent of the tile shape: the selected
  * key tokens of a row are visited in ascending token order and every sum over
  * the head dimension runs d = 0..D-1. Hence two masks that select the same
@@ -53,16 +61,34 @@ static float bf16_to_f32(uint16_t b) {
     return f;
 }
 
-/* Mark the KV tiles selected by one CSR row; returns an error code. */
-static int mark_tiles(const int32_t* idx_row, int32_t n, int32_t ld, int32_t nkv, unsigned char* mark) {
+/*
+ * For one CSR row, allow[t] = number of leading key tokens of KV tile t the
+ * row may attend to: 0 for tiles the row does not select, kv_valid[t] (or
+ * the whole tile) for selected ones. Returns an error code.
+ */
+static int mark_tiles(const int32_t* idx_row, int32_t n, int32_t ld, int32_t nkv, const int32_t* kv_valid,
+                      int32_t block_kv, int32_t* allow) {
     if (n < 0 || n > ld) return ORACLE_ERR_CNT;
-    memset(mark, 0, (size_t)nkv);
+    for (int32_t t = 0; t < nkv; ++t) allow[t] = -1;
     for (int32_t e = 0; e < n; ++e) {
         int32_t t = idx_row[e];
         if (t < 0 || t >= nkv) return ORACLE_ERR_IDX_RANGE;
-        if (mark[t]) return ORACLE_ERR_IDX_DUP;
-        mark[t] = 1;
+        if (allow[t] >= 0) return ORACLE_ERR_IDX_DUP;
+        allow[t] = kv_valid ? kv_valid[t] : block_kv;
     }
+    for (int32_t t = 0; t < nkv; ++t)
+        if (allow[t] < 0) allow[t] = 0;
+    return ORACLE_OK;
+}
+
+/* May a query of this row attend to key token j? */
+static int allowed(const int32_t* allow, int block_kv, int j) { return (j % block_kv) < allow[j / block_kv]; }
+
+/* kv_valid entries must lie in [0, block_kv]. */
+static int check_valid(const int32_t* kv_valid, int nkv, int block_kv) {
+    if (!kv_valid) return ORACLE_OK;
+    for (int t = 0; t < nkv; ++t)
+        if (kv_valid[t] < 0 || kv_valid[t] > block_kv) return ORACLE_ERR_ARG;
     return ORACLE_OK;
 }
 
@@ -73,7 +99,7 @@ static int mark_tiles(const int32_t* idx_row, int32_t n, int32_t ld, int32_t nkv
  * exp(score - max). Returns the number of selected keys.
  */
 static int64_t row_weights(const uint16_t* q, const uint16_t* k, int S, int H, int D, int b, int h, int i,
-                           const unsigned char* mark, int nkv, int block_kv, float scale, float* qf, float* s,
+                           const int32_t* allow, int nkv, int block_kv, float scale, float* qf, float* s,
                            float* m_out, float* l_out) {
     const int64_t tok = (int64_t)H * D;
     const uint16_t* qrow = q + ((int64_t)b * S + i) * tok + (int64_t)h * D;
@@ -85,7 +111,7 @@ static int64_t row_weights(const uint16_t* q, const uint16_t* k, int S, int H, i
     for (int t = 0; t < nkv; ++t) {
         for (int jj = 0; jj < block_kv; ++jj) {
             int j = t * block_kv + jj;
-            if (!mark[t]) {
+            if (!allowed(allow, block_kv, j)) {
                 s[j] = -INFINITY;
                 continue;
             }
@@ -101,7 +127,7 @@ static int64_t row_weights(const uint16_t* q, const uint16_t* k, int S, int H, i
     float l = 0.0f;
     if (nsel > 0) {
         for (int j = 0; j < S; ++j) {
-            if (!mark[j / block_kv]) {
+            if (!allowed(allow, block_kv, j)) {
                 s[j] = 0.0f;
                 continue;
             }
@@ -109,7 +135,7 @@ static int64_t row_weights(const uint16_t* q, const uint16_t* k, int S, int H, i
             l += s[j];
         }
         for (int j = 0; j < S; ++j)
-            if (mark[j / block_kv]) s[j] = s[j] / l;
+            if (allowed(allow, block_kv, j)) s[j] = s[j] / l;
     } else {
         for (int j = 0; j < S; ++j) s[j] = 0.0f;
     }
@@ -122,6 +148,7 @@ static int64_t row_weights(const uint16_t* q, const uint16_t* k, int S, int H, i
  * Forward pass for a list of query rows.
  *   q, k, v : bf16 bit patterns, [B, S, H, D] contiguous
  *   kv_block_idx / kv_block_cnt : block CSR at tile shape block_q x block_kv
+ *   kv_valid : valid key tokens per KV tile [S/block_kv], or NULL (all full)
  *   rows    : flat row ids (b*H + h)*S + i, or NULL for all B*H*S rows in
  *             that order
  *   o       : [n_rows, D] fp32 output; lse : [n_rows] fp32 output
@@ -129,11 +156,13 @@ static int64_t row_weights(const uint16_t* q, const uint16_t* k, int S, int H, i
  * Returns 0, or a negative error code if any row's CSR entry is invalid.
  */
 int vsa_oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* kv_block_idx,
-                         const int32_t* kv_block_cnt, int B, int S, int H, int D, int ld, int block_q, int block_kv,
-                         float scale, const int64_t* rows, int64_t n_rows, float* o, float* lse, int n_threads) {
+                         const int32_t* kv_block_cnt, const int32_t* kv_valid, int B, int S, int H, int D, int ld,
+                         int block_q, int block_kv, float scale, const int64_t* rows, int64_t n_rows, float* o,
+                         float* lse, int n_threads) {
     if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || block_q <= 0 || block_kv <= 0 || ld < 0) return ORACLE_ERR_ARG;
     if (S % block_q || S % block_kv) return ORACLE_ERR_ARG;
     const int nq = S / block_q, nkv = S / block_kv;
+    if (check_valid(kv_valid, nkv, block_kv) != ORACLE_OK) return ORACLE_ERR_ARG;
     const int64_t total = (int64_t)B * H * S;
     if (rows == NULL) n_rows = total;
     int status = ORACLE_OK;
@@ -147,8 +176,8 @@ int vsa_oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v
     {
         float* s = (float*)malloc(sizeof(float) * (size_t)S);
         float* qf = (float*)malloc(sizeof(float) * (size_t)D);
-        unsigned char* mark = (unsigned char*)malloc((size_t)nkv);
-        if (!s || !qf || !mark) {
+        int32_t* allow = (int32_t*)malloc(sizeof(int32_t) * (size_t)nkv);
+        if (!s || !qf || !allow) {
 #pragma omp critical
             status = ORACLE_ERR_NOMEM;
         } else {
@@ -166,20 +195,20 @@ int vsa_oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v
                 int b = (int)(flat / ((int64_t)S * H));
                 int p = i / block_q;
                 int64_t crow = ((int64_t)b * H + h) * nq + p;
-                int rc = mark_tiles(kv_block_idx + crow * ld, kv_block_cnt[crow], ld, nkv, mark);
+                int rc = mark_tiles(kv_block_idx + crow * ld, kv_block_cnt[crow], ld, nkv, kv_valid, block_kv, allow);
                 if (rc != ORACLE_OK) {
 #pragma omp critical
                     status = rc;
                     continue;
                 }
                 float m, l;
-                int64_t nsel = row_weights(q, k, S, H, D, b, h, i, mark, nkv, block_kv, scale, qf, s, &m, &l);
+                int64_t nsel = row_weights(q, k, S, H, D, b, h, i, allow, nkv, block_kv, scale, qf, s, &m, &l);
                 /* out = softmax(scores) @ v, keys in ascending order */
                 for (int d = 0; d < D; ++d) orow[d] = 0.0f;
                 if (nsel > 0) {
                     const int64_t tok = (int64_t)H * D;
                     for (int j = 0; j < S; ++j) {
-                        if (!mark[j / block_kv]) continue;
+                        if (!allowed(allow, block_kv, j)) continue;
                         const uint16_t* vrow = v + ((int64_t)b * S + j) * tok + (int64_t)h * D;
                         float w = s[j];
                         for (int d = 0; d < D; ++d) orow[d] += w * bf16_to_f32(vrow[d]);
@@ -192,7 +221,7 @@ int vsa_oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v
         }
         free(s);
         free(qf);
-        free(mark);
+        free(allow);
     }
     return status;
 }
@@ -203,29 +232,30 @@ int vsa_oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v
  * invariants (rows sum to one, zero outside the mask).
  */
 int vsa_oracle_probs_row(const uint16_t* q, const uint16_t* k, const int32_t* kv_block_idx,
-                         const int32_t* kv_block_cnt, int B, int S, int H, int D, int ld, int block_q, int block_kv,
-                         float scale, int64_t flat_row, float* probs) {
+                         const int32_t* kv_block_cnt, const int32_t* kv_valid, int B, int S, int H, int D, int ld,
+                         int block_q, int block_kv, float scale, int64_t flat_row, float* probs) {
     if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || block_q <= 0 || block_kv <= 0 || ld < 0) return ORACLE_ERR_ARG;
     if (S % block_q || S % block_kv) return ORACLE_ERR_ARG;
     if (flat_row < 0 || flat_row >= (int64_t)B * H * S) return ORACLE_ERR_ARG;
     const int nq = S / block_q, nkv = S / block_kv;
+    if (check_valid(kv_valid, nkv, block_kv) != ORACLE_OK) return ORACLE_ERR_ARG;
     int i = (int)(flat_row % S);
     int h = (int)((flat_row / S) % H);
     int b = (int)(flat_row / ((int64_t)S * H));
     int64_t crow = ((int64_t)b * H + h) * nq + i / block_q;
-    unsigned char* mark = (unsigned char*)malloc((size_t)nkv);
+    int32_t* allow = (int32_t*)malloc(sizeof(int32_t) * (size_t)nkv);
     float* qf = (float*)malloc(sizeof(float) * (size_t)D);
-    if (!mark || !qf) {
-        free(mark);
+    if (!allow || !qf) {
+        free(allow);
         free(qf);
         return ORACLE_ERR_NOMEM;
     }
-    int rc = mark_tiles(kv_block_idx + crow * ld, kv_block_cnt[crow], ld, nkv, mark);
+    int rc = mark_tiles(kv_block_idx + crow * ld, kv_block_cnt[crow], ld, nkv, kv_valid, block_kv, allow);
     if (rc == ORACLE_OK) {
         float m, l;
-        row_weights(q, k, S, H, D, b, h, i, mark, nkv, block_kv, scale, qf, probs, &m, &l);
+        row_weights(q, k, S, H, D, b, h, i, allow, nkv, block_kv, scale, qf, probs, &m, &l);
     }
-    free(mark);
+    free(allow);
     free(qf);
     return rc;
 }

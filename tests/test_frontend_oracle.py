@@ -114,3 +114,21 @@ def test_count_mask_generator_invariants():
     assert abs(c.mean() - 51) < 1.0
     rows = np.arange(512)
     assert np.all(m[:, rows, rows] == 1)
+
+
+def test_expand_valid_matches_token_level_definition():
+    """Token r of logical block T exists iff r < vbs[T]; the physical tiles must
+    hold exactly those tokens as their valid prefixes."""
+    rng = np.random.default_rng(8)
+    for lkv, pkv in ((256, 128), (256, 64), (256, 256), (128, 32)):
+        vbs = rng.integers(0, lkv + 1, size=9)
+        vbs[0], vbs[1] = 0, lkv
+        val = frontend.expand_valid(vbs, lkv, pkv)
+        assert val.shape == (9 * lkv // pkv,) and val.dtype == np.int32
+        exists = np.concatenate([np.arange(lkv) < n for n in vbs])           # logical, per token
+        tiles = np.concatenate([np.arange(pkv) < n for n in val])            # physical prefixes
+        assert np.array_equal(exists, tiles)
+    with pytest.raises(ValueError):
+        frontend.expand_valid([257], 256, 64)
+    with pytest.raises(ValueError):
+        frontend.expand_valid([10], 256, 96)

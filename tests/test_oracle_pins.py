@@ -25,8 +25,9 @@ def _f64(x_bits):
     return (x_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def _token_mask(idx, cnt, S, block_q, block_kv):
-    """[B, H, S, S] bool: query i may see key j. Built by explicit loops."""
+def _token_mask(idx, cnt, S, block_q, block_kv, kv_valid=None):
+    """[B, H, S, S] bool: query i may see key j. Built by explicit loops; with
+    kv_valid only the first kv_valid[t] keys of tile t exist."""
     B, H, NQ, _ = idx.shape
     m = np.zeros((B, H, S, S), dtype=bool)
     for b in range(B):
@@ -34,15 +35,16 @@ def _token_mask(idx, cnt, S, block_q, block_kv):
             for p in range(NQ):
                 for e in range(int(cnt[b, h, p])):
                     t = int(idx[b, h, p, e])
-                    m[b, h, p * block_q:(p + 1) * block_q, t * block_kv:(t + 1) * block_kv] = True
+                    n = block_kv if kv_valid is None else int(kv_valid[t])
+                    m[b, h, p * block_q:(p + 1) * block_q, t * block_kv:t * block_kv + n] = True
     return m
 
 
-def _brute(q, k, v, idx, cnt, block_q, block_kv, scale):
+def _brute(q, k, v, idx, cnt, block_q, block_kv, scale, kv_valid=None):
     """float64 masked softmax attention; returns O [B,S,H,D], LSE [B,H,S]."""
     qf, kf, vf = (_f64(bf16_bits(t)).transpose(0, 2, 1, 3) for t in (q, k, v))  # [B,H,S,D]
     B, H, S, D = qf.shape
-    tm = _token_mask(idx, cnt, S, block_q, block_kv)
+    tm = _token_mask(idx, cnt, S, block_q, block_kv, kv_valid)
     s = np.einsum("bhid,bhjd->bhij", qf, kf) * scale
     s = np.where(tm, s, -np.inf)
     mx = s.max(-1, keepdims=True)
@@ -84,6 +86,85 @@ def test_matches_float64_brute_force(B, H, S, D, bq, bkv, cr):
     empty_rows = ~fin  # [B,H,S]
     o_bhsd = o.transpose(0, 2, 1, 3)
     assert np.all(o_bhsd[empty_rows] == 0.0)
+
+
+def _ragged(nkv, block_kv, seed, p_full=0.5):
+    """Valid key counts per tile: full, empty, or anywhere in between."""
+    rng = np.random.default_rng(seed)
+    val = rng.integers(0, block_kv + 1, size=nkv).astype(np.int32)
+    val[rng.random(nkv) < p_full] = block_kv
+    val[rng.random(nkv) < 0.1] = 0
+    return val
+
+
+@pytest.mark.parametrize("B,H,S,D,bq,bkv,cr", CASES)
+def test_partial_tiles_match_float64_brute_force(B, H, S, D, bq, bkv, cr):
+    q, k, v = qkv(B, S, H, D, seed=S + D + bq + 1)
+    nq, nkv = S // bq, S // bkv
+    idx, cnt = random_csr(B, H, nq, nkv, nkv, cr[0], min(cr[1], nkv), seed=7 * S + bkv + 1)
+    val = _ragged(nkv, bkv, seed=S + bkv)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = oracle.attn_full(q, k, v, idx, cnt, bq, bkv, scale, kv_valid=val)
+    o_ref, lse_ref = _brute(q, k, v, idx, cnt, bq, bkv, scale, kv_valid=val)
+    assert np.abs(o - o_ref).max() < 2e-5
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(fin, np.isfinite(lse))
+    assert np.abs(lse[fin] - lse_ref[fin]).max() < 2e-5 * max(1.0, np.abs(lse_ref[fin]).max())
+    assert np.all(o.transpose(0, 2, 1, 3)[~fin] == 0.0)
+    # all tiles full is the same as no validity input, bit for bit
+    full = np.full(nkv, bkv, np.int32)
+    o2, l2 = oracle.attn_full(q, k, v, idx, cnt, bq, bkv, scale, kv_valid=full)
+    o3, l3 = oracle.attn_full(q, k, v, idx, cnt, bq, bkv, scale)
+    assert np.array_equal(o2, o3) and np.array_equal(l2, l3)
+
+
+def test_partial_tiles_zero_keys_closed_form():
+    """K = 0 with partial tiles: LSE = ln(#valid selected keys), O = their V mean."""
+    B, H, S, D, bq, bkv = 1, 2, 256, 32, 64, 16
+    q, _, v = qkv(B, S, H, D, seed=43)
+    k = torch.zeros_like(q)
+    nkv = S // bkv
+    idx, cnt = random_csr(B, H, S // bq, nkv, nkv, 1, 9, seed=44)
+    val = _ragged(nkv, bkv, seed=45)
+    o, lse = oracle.attn_full(q, k, v, idx, cnt, bq, bkv, 0.2, kv_valid=val)
+    vf = _f64(bf16_bits(v))
+    for h in range(H):
+        for p in range(S // bq):
+            c = int(cnt[0, h, p])
+            tok = np.concatenate([np.arange(t * bkv, t * bkv + val[t]) for t in idx[0, h, p, :c]])
+            for i in range(p * bq, (p + 1) * bq, 13):
+                if tok.size == 0:
+                    assert lse[0, h, i] == -np.inf and np.all(o[0, i, h] == 0.0)
+                    continue
+                assert abs(lse[0, h, i] - math.log(tok.size)) < 1e-6 * math.log(tok.size) + 1e-7
+                assert np.abs(o[0, i, h] - vf[0, tok, h].mean(0)).max() < 1e-5
+
+
+def test_partial_tiles_are_bitwise_identical_across_tile_shapes():
+    """Ragged logical blocks expanded to finer tiles select the same key tokens."""
+    from workloads import anchor_topk_mask
+
+    B, H, S, D = 1, 2, 1024, 64
+    q, k, v = qkv(B, S, H, D, seed=33)
+    base = anchor_topk_mask(H, S // 256, S // 256, 2, seed=34)[None]
+    vbs = np.array([256, 200, 129, 64], dtype=np.int32)
+    results = []
+    for shape in ((256, 256), (256, 128), (128, 64), (64, 64)):
+        ld = S // shape[1]
+        idx, cnt, ovf = frontend.mask_to_csr(base, (256, 256), shape, ld)
+        val = frontend.expand_valid(vbs, 256, shape[1])
+        results.append(oracle.attn_full(q, k, v, idx, cnt, shape[0], shape[1], 0.125, kv_valid=val))
+    for o, l in results[1:]:
+        assert np.array_equal(o, results[0][0]) and np.array_equal(l, results[0][1])
+
+
+def test_invalid_valid_counts_are_rejected():
+    B, H, S, D, bq, bkv = 1, 1, 128, 16, 32, 32
+    q, k, v = qkv(B, S, H, D, seed=3)
+    idx, cnt = random_csr(B, H, S // bq, S // bkv, S // bkv, 1, 2, seed=4)
+    for bad in ([33, 32, 32, 32], [-1, 32, 32, 32]):
+        with pytest.raises(ValueError):
+            oracle.attn_full(q, k, v, idx, cnt, bq, bkv, 0.1, kv_valid=np.array(bad, np.int32))
 
 
 def test_dense_equals_torch_sdpa_float64():
@@ -226,11 +307,14 @@ MUTATIONS = {
     "scale_dropped": ("s[j] = acc * scale;", "s[j] = acc;"),
     "key_from_query_row": ("const uint16_t* krow = k + ((int64_t)b * S + j)",
                            "const uint16_t* krow = k + ((int64_t)b * S + i)"),
-    "value_tiles_use_block_q": ("if (!mark[j / block_kv]) continue;", "if (!mark[j / block_q]) continue;"),
-    "key_tile_offset": ("int j = t * block_kv + jj;", "int j = (t * block_kv + jj + block_kv) % S;"),
+    "value_tiles_use_block_q": ("if (!allowed(allow, block_kv, j)) continue;", "if (!allowed(allow, block_q, j)) continue;"),
+    "key_tile_offset": ("const uint16_t* krow = k + ((int64_t)b * S + j) * tok",
+                        "const uint16_t* krow = k + ((int64_t)b * S + (j + block_kv) % S) * tok"),
     "value_wrong_head": ("const uint16_t* vrow = v + ((int64_t)b * S + j) * tok + (int64_t)h * D;",
                          "const uint16_t* vrow = v + ((int64_t)b * S + j) * tok;"),
-    "no_normalisation": ("if (mark[j / block_kv]) s[j] = s[j] / l;", "if (mark[j / block_kv]) s[j] = s[j];"),
+    "no_normalisation": ("if (allowed(allow, block_kv, j)) s[j] = s[j] / l;", "if (allowed(allow, block_kv, j)) s[j] = s[j];"),
+    "valid_counts_ignored": ("allow[t] = kv_valid ? kv_valid[t] : block_kv;", "allow[t] = block_kv;"),
+    "valid_count_off_by_one": ("return (j % block_kv) < allow[j / block_kv];", "return (j % block_kv) <= allow[j / block_kv];"),
     "lse_without_max": ("lse[r] = m + logf(l);", "lse[r] = logf(l);"),
     "max_not_subtracted": ("s[j] = expf(s[j] - m);", "s[j] = expf(s[j]);"),
 }
@@ -261,9 +345,11 @@ def test_planted_mistake_is_caught(tmp_path, name, monkeypatch):
     q, k, v = qkv(B, S, H, D, seed=71)
     q = (q.float() * 3).to(torch.bfloat16)  # large scores so the max matters numerically
     idx, cnt = random_csr(B, H, S // bq, S // bkv, S // bkv, 1, 6, seed=72)
-    o, lse = oracle.attn_full(q, k, v, idx, cnt, bq, bkv, 0.3)
-    o_ref, lse_ref = _brute(q, k, v, idx, cnt, bq, bkv, 0.3)
-    with np.errstate(invalid="ignore"):
-        bad_o = not np.all(np.abs(o - o_ref) < 2e-5)
-        bad_l = not np.all(np.abs(lse - lse_ref) < 2e-5 * np.maximum(1.0, np.abs(lse_ref)))
-    assert bad_o or bad_l, f"mutation {name} went unnoticed"
+    caught = False
+    for val in (None, _ragged(S // bkv, bkv, seed=73)):  # full tiles, then partial tiles
+        o, lse = oracle.attn_full(q, k, v, idx, cnt, bq, bkv, 0.3, kv_valid=val)
+        o_ref, lse_ref = _brute(q, k, v, idx, cnt, bq, bkv, 0.3, kv_valid=val)
+        with np.errstate(invalid="ignore"):
+            caught |= not np.all(np.abs(o - o_ref) < 2e-5)
+            caught |= not np.all(np.abs(lse - lse_ref) < 2e-5 * np.maximum(1.0, np.abs(lse_ref)))
+    assert caught, f"mutation {name} went unnoticed"

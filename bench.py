@@ -242,13 +242,15 @@ def main():
     return 0
 
 
-def kernel_name(bq, bkv, d):
-    """Name of the forward kernel the library dispatches for this tile shape."""
+def kernel_name(bq, bkv, d, partial=False):
+    """Name of the forward kernel the library dispatches for this tile shape
+    (the last template argument: built for partial tiles)."""
+    p = "true" if partial else "false"
     if bq == 256:
-        return f"vsa_fwd_pp_kernel<{bkv},{d}>"
+        return f"vsa_fwd_pp_kernel<{bkv},{d},{p}>"
     if bq == 128:
-        return f"vsa_fwd_2s_kernel<{d}>"
-    return f"vsa_fwd_4s_kernel<{d}>"
+        return f"vsa_fwd_2s_kernel<{d},{p}>"
+    return f"vsa_fwd_4s_kernel<{d},{p}>"
 
 
 CSRC = os.path.join(ROOT, "block_sparse_attention_flashattention_amd", "csrc")

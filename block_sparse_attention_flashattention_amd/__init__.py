@@ -34,6 +34,7 @@ SYMBOLS = (
     "vsa_last_error",
     "vsa_mask_to_csr",
     "vsa_build_worklist",
+    "vsa_expand_valid",
     "vsa_attn_fwd",
     "vsa_attn_fwd_worklist",
     "vsa_release",
@@ -71,11 +72,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vsa_mask_to_csr.restype = i32
     lib.vsa_build_worklist.argtypes = [p, i32, i32, i32, p, p]
     lib.vsa_build_worklist.restype = i32
-    lib.vsa_attn_fwd.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p, p, p]
+    lib.vsa_attn_fwd.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p, p, p]
     lib.vsa_attn_fwd.restype = i32
-    lib.vsa_attn_fwd_worklist.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p, i32, p, p,
-                                          p]
+    lib.vsa_attn_fwd_worklist.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p, i32, p,
+                                          p, p]
     lib.vsa_attn_fwd_worklist.restype = i32
+    lib.vsa_expand_valid.argtypes = [p, i32, i32, i32, p, p]
+    lib.vsa_expand_valid.restype = i32
     lib.vsa_release.argtypes = []
     lib.vsa_release.restype = None
     _lib = lib
@@ -138,18 +141,29 @@ def _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse):
     return B, S, H, D, o, lse
 
 
+def _valid_ptr(kv_valid, S, block_kv, device):
+    if kv_valid is None:
+        return None
+    _dev(kv_valid, "kv_valid", torch.int32, 1)
+    if kv_valid.numel() != S // block_kv or kv_valid.device != device:
+        raise ValueError(f"kv_valid must be an int32 [{S // block_kv}] tensor on {device}")
+    return kv_valid.data_ptr()
+
+
 def vsa_attn_fwd(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale=None, o=None, lse=None,
-                 stream=None):
+                 stream=None, kv_valid=None):
     """Block-sparse attention forward; returns (o, lse).
 
     Builds the count-sorted work list internally, then runs the fused
-    kernel. ``scale`` defaults to 1/sqrt(D).
+    kernel. ``scale`` defaults to 1/sqrt(D). ``kv_valid`` (int32
+    [S/block_kv], optional): valid leading keys of each KV tile.
     """
     B, S, H, D, o, lse = _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     rc = load_library().vsa_attn_fwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(), B, S, H, D,
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(),
+        _valid_ptr(kv_valid, S, block_kv, q.device), B, S, H, D,
         kv_block_idx.shape[3], block_q, block_kv, float(scale), o.data_ptr(), lse.data_ptr(),
         _stream_ptr(stream, q.device))
     _check(rc)
@@ -157,14 +171,15 @@ def vsa_attn_fwd(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale=N
 
 
 def vsa_attn_fwd_worklist(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, work_list, scale=None, o=None,
-                          lse=None, stream=None):
+                          lse=None, stream=None, kv_valid=None):
     """The fused kernel alone over a caller-built work list; returns (o, lse)."""
     B, S, H, D, o, lse = _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse)
     _dev(work_list, "work_list", torch.int32, 1)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     rc = load_library().vsa_attn_fwd_worklist(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(), B, S, H, D,
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(),
+        _valid_ptr(kv_valid, S, block_kv, q.device), B, S, H, D,
         kv_block_idx.shape[3], block_q, block_kv, float(scale), work_list.data_ptr(), work_list.numel(),
         o.data_ptr(), lse.data_ptr(), _stream_ptr(stream, q.device))
     _check(rc)
@@ -226,6 +241,24 @@ def vsa_build_worklist(kv_block_cnt, max_cnt, work_list=None, segment=None, stre
                                            work_list.data_ptr(), _stream_ptr(stream, kv_block_cnt.device))
     _check(rc)
     return work_list
+
+
+def vsa_expand_valid(vbs, logical_block_kv, block_kv, kv_valid=None, stream=None):
+    """Valid keys per physical KV tile (int32 [nkv_logical * LKV/PKV]) from the
+    valid tokens per logical KV block ``vbs`` (int32 [nkv_logical] GPU tensor)."""
+    _dev(vbs, "vbs", torch.int32, 1)
+    if logical_block_kv % block_kv:
+        raise ValueError("block_kv must divide logical_block_kv")
+    n = vbs.numel() * (logical_block_kv // block_kv)
+    if kv_valid is None:
+        kv_valid = torch.empty((n,), dtype=torch.int32, device=vbs.device)
+    _dev(kv_valid, "kv_valid", torch.int32, 1)
+    if kv_valid.numel() != n:
+        raise ValueError(f"kv_valid must hold {n} entries")
+    rc = load_library().vsa_expand_valid(vbs.data_ptr(), vbs.numel(), logical_block_kv, block_kv,
+                                         kv_valid.data_ptr(), _stream_ptr(stream, vbs.device))
+    _check(rc)
+    return kv_valid
 
 
 def vsa_release() -> None:

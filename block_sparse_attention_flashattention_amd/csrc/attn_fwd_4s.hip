@@ -30,7 +30,7 @@ using namespace dev;
 
 constexpr int kIdxCap4s = 8192;  // CSR row entries staged in LDS (>= the largest idx_ld)
 
-template <int D>
+template <int D, bool PARTIAL>
 __global__ __launch_bounds__(512) void vsa_fwd_4s_kernel(FwdParams prm) {
     constexpr int BQ = 64;
     constexpr int SUB = 32;  // keys per sub-tile
@@ -84,16 +84,23 @@ __global__ __launch_bounds__(512) void vsa_fwd_4s_kernel(FwdParams prm) {
     e.load_q(prm.q + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D);
 
     int* lidx = (int*)(smem + NSTREAM * STREAM_LDS);
-    for (int i = tid; i < ldc; i += 512) lidx[i] = irow[i];
+    for (int i = tid; i < ldc; i += 512) lidx[i] = stage_entry<PARTIAL>(irow[i], nkv, block_kv, prm.kv_valid);
     e.q_ready();
 
-    auto tile_of = [&](int j) { return __builtin_amdgcn_readfirstlane(lidx[(first + j) / R]); };
+    // CSR tile of sub-tile j, and its valid keys within this sub-tile
+    auto tile_of = [&](int j) { return entry_tile<PARTIAL>(__builtin_amdgcn_readfirstlane(lidx[(first + j) / R])); };
     auto valid = [&](int t) { return t >= 0 && t < nkv; };
+    auto keys_of = [&](int j) {
+        if constexpr (!PARTIAL) return valid(tile_of(j)) ? SUB : 0;
+        const int nv = entry_keys<PARTIAL>(__builtin_amdgcn_readfirstlane(lidx[(first + j) / R]), block_kv) -
+                       ((first + j) % R) * SUB;
+        return nv < 0 ? 0 : (nv > SUB ? SUB : nv);
+    };
     const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
     const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
     using F = TileFetch<SUB, D, 2>;
     const int fw = rb;  // this wave's index among the waves fetching its stream's tiles
-    const F fetch(fw, lane, tok_bytes);
+    const F fetch(smem, fw, lane, tok_bytes);
     // sub-tile j of this stream in CSR tile t; out-of-range tiles load tile 0
     // and contribute nothing
     auto sub_ptr = [&](const char* base, int t, int j) {
@@ -111,17 +118,21 @@ __global__ __launch_bounds__(512) void vsa_fwd_4s_kernel(FwdParams prm) {
         const char* vt = tile_ptr(vbase, j);
         const int kd = kbuf(j + 1), vd = vbuf(j);
         return [=, &fetch](int i) {
-            if (i < F::BPW) fetch.block(smem, kd, kt, tok_bytes, false, i);
-            else fetch.block(smem, vd, vt, tok_bytes, true, i - F::BPW);
+            if (i < F::BPW) fetch.block(kd, kt, tok_bytes, false, i);
+            else fetch.block(vd, vt, tok_bytes, true, i - F::BPW);
         };
     };
     auto v_loads = [&](int j) {
         const char* vt = tile_ptr(vbase, j);
         const int vd = vbuf(j);
-        return [=, &fetch](int i) { fetch.block(smem, vd, vt, tok_bytes, true, i); };
+        return [=, &fetch](int i) { fetch.block(vd, vt, tok_bytes, true, i); };
     };
     auto pv = [&](int j) { e.template mfma_phase<true, false>(vbuf(j), 0); };
-    auto softmax = [&](int j) { e.softmax(valid(tile_of(j))); };
+    auto softmax = [&](int j) {
+        const int nv = keys_of(j);
+        if (PARTIAL && nv > 0 && nv < SUB) e.mask_keys(nv);
+        e.softmax(nv > 0);
+    };
 
     // Every wave passes the same number of barriers: a stream of length L in
     // group g uses 2L + 2 + g; shorter streams pad at the end.
@@ -136,7 +147,7 @@ __global__ __launch_bounds__(512) void vsa_fwd_4s_kernel(FwdParams prm) {
     // barrier then publishes both it and the staged row.
     if (ng > 0) {
         const int t0 = __builtin_amdgcn_readfirstlane(irow[first / R]);
-        fetch.all(smem, kbuf(0), sub_ptr(kbase, t0, 0), tok_bytes, false);
+        fetch.all(kbuf(0), sub_ptr(kbase, t0, 0), tok_bytes, false);
     }
     wait_global_loads();
     bar();
@@ -184,7 +195,8 @@ __global__ __launch_bounds__(512) void vsa_fwd_4s_kernel(FwdParams prm) {
 
 template <int D>
 hipError_t launch_4s(const FwdParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((vsa_fwd_4s_kernel<D>), dim3(p.n_work), dim3(512), 0, stream, p);
+    if (p.kv_valid) hipLaunchKernelGGL((vsa_fwd_4s_kernel<D, true>), dim3(p.n_work), dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((vsa_fwd_4s_kernel<D, false>), dim3(p.n_work), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 

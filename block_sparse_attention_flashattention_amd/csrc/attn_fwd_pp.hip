@@ -32,7 +32,7 @@ using namespace dev;
 
 constexpr int kIdxCap = 8192;  // CSR row entries staged in LDS (>= the largest idx_ld)
 
-template <int BKV, int D>
+template <int BKV, int D, bool PARTIAL>
 __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     using E = WaveEngine<BKV, D>;
     using G = TileGeom<BKV, D>;
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
     const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
     using F = TileFetch<BKV, D, 4>;  // a tile is fetched by the four waves of one group
-    const F fetch(wave & 3, lane, tok_bytes);
+    const F fetch(smem, wave & 3, lane, tok_bytes);
     // out-of-range entries load tile 0 and contribute nothing
     auto tile_at = [&](const char* base, int t) {
         return uniform_ptr(base + (int64_t)(valid(t) ? t : 0) * BKV * tok_bytes);
@@ -84,16 +84,18 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     // Stage this tile's CSR row in LDS: list entries are then read with
     // uniform LDS loads, which do not wait on outstanding global loads.
     int* lidx = (int*)(smem + LDS_TILES);
-    for (int i = tid; i < ldc; i += 512) lidx[i] = irow[i];
+    for (int i = tid; i < ldc; i += 512) lidx[i] = stage_entry<PARTIAL>(irow[i], nkv, BKV, prm.kv_valid);
     e.q_ready();
     // group 1 fetches K_0 (buffer 0 is free); an empty row fetches it too
-    if (grp == 1) fetch.all(smem, 0, tile_at(kbase, first_tile), tok_bytes, false);
+    if (grp == 1) fetch.all(0, tile_at(kbase, first_tile), tok_bytes, false);
     n = n < 0 ? 0 : (n > ldc ? ldc : n);
     wait_global_loads();
     lds_barrier();
 
-    // Tile index of list entry j (uniform).
-    auto tile_of = [&](int j) { return __builtin_amdgcn_readfirstlane(lidx[j]); };
+    // Tile index and valid key count of list entry j (uniform; -1 / 0 when
+    // the entry is out of range).
+    auto tile_of = [&](int j) { return entry_tile<PARTIAL>(__builtin_amdgcn_readfirstlane(lidx[j])); };
+    auto keys_of = [&](int j) { return entry_keys<PARTIAL>(__builtin_amdgcn_readfirstlane(lidx[j]), BKV); };
     auto tile_ptr = [&](const char* base, int j) { return tile_at(base, tile_of(j)); };
     // LDS byte offsets of the K and V buffers used for list entry j
     auto kbuf = [](int j) { return (j & 1) * G::TILE; };
@@ -102,14 +104,20 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     // the eight waves' loads do not queue up at the start of the phase.
     auto v_loads = [&](int j) {
         const char* tile = tile_ptr(vbase, j);
-        return [=, &fetch](int i) { fetch.block(smem, vbuf(j), tile, tok_bytes, true, i); };
+        return [=, &fetch](int i) { fetch.block(vbuf(j), tile, tok_bytes, true, i); };
     };
     auto k_loads = [&](int j) {
         const char* tile = tile_ptr(kbase, j);
-        return [=, &fetch](int i) { fetch.block(smem, kbuf(j), tile, tok_bytes, false, i); };
+        return [=, &fetch](int i) { fetch.block(kbuf(j), tile, tok_bytes, false, i); };
     };
     auto pv = [&](int j) { e.template mfma_phase<true, false>(vbuf(j), 0); };
-    auto softmax = [&](int j) { e.softmax(valid(tile_of(j))); };
+    // softmax of list entry j, masking a partial tile's missing keys first
+    auto softmax_of = [&](int j) {
+        const int nv = keys_of(j);
+        if (PARTIAL && nv > 0 && nv < BKV) e.mask_keys(nv);
+        return nv > 0;
+    };
+    auto softmax = [&](int j) { e.softmax(softmax_of(j)); };
 
     // Both groups pass 2(n+1) barriers after the prologue. Each group has its own loop so that
     // S (live from M_j to V_j) and P (live from V_j to M_{j+1}) never both
@@ -135,14 +143,14 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
         lds_barrier();
     } else {
         if (n > 0) {
-            if (n > 1) fetch.all(smem, kbuf(1), tile_ptr(kbase, 1), tok_bytes, false);
+            if (n > 1) fetch.all(kbuf(1), tile_ptr(kbase, 1), tok_bytes, false);
             lds_barrier();
             e.template mfma_phase<false, true>(0, kbuf(0));                                    // M_0
             wait_global_loads();
             lds_barrier();
             // the last tile has no K_{j+1} to fetch: peeled, so the loop body has no branch per load
             for (int j = 1; j < n - 1; ++j) {
-                e.template softmax<F::BPW>(valid(tile_of(j - 1)), k_loads(j + 1));  // V_{j-1}
+                e.template softmax<F::BPW>(softmax_of(j - 1), k_loads(j + 1));  // V_{j-1}
                 lds_barrier();
                 e.template mfma_phase<true, true>(vbuf(j - 1), kbuf(j));            // M_j
                 wait_global_loads();
@@ -171,7 +179,8 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
 
 template <int BKV, int D>
 hipError_t launch_pp(const FwdParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((vsa_fwd_pp_kernel<BKV, D>), dim3(p.n_work), dim3(512), 0, stream, p);
+    if (p.kv_valid) hipLaunchKernelGGL((vsa_fwd_pp_kernel<BKV, D, true>), dim3(p.n_work), dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((vsa_fwd_pp_kernel<BKV, D, false>), dim3(p.n_work), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -34,9 +34,9 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
     } while (0)
 
 // Validation shared by both forward entry points.
-int32_t check_fwd(const void* q, const void* k, const void* v, const int32_t* idx, const int32_t* cnt, int32_t batch,
-                  int32_t seqlen, int32_t heads, int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv,
-                  float scale, const void* o, const float* lse) {
+int32_t check_fwd(const void* q, const void* k, const void* v, const int32_t* idx, const int32_t* cnt,
+                  const int32_t* kv_valid, int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim,
+                  int32_t idx_ld, int32_t block_q, int32_t block_kv, float scale, const void* o, const float* lse) {
     VSA_REQUIRE(q && k && v && idx && cnt && o && lse, VSA_ERR_INVALID_ARG, "null tensor pointer");
     VSA_REQUIRE(batch >= 1 && seqlen >= 1 && heads >= 1 && head_dim >= 1, VSA_ERR_INVALID_ARG,
                 "batch, seqlen, heads and head_dim must be >= 1");
@@ -58,13 +58,16 @@ int32_t check_fwd(const void* q, const void* k, const void* v, const int32_t* id
     const int64_t n_items = (int64_t)batch * heads * (seqlen / block_q);
     VSA_REQUIRE(n_items <= INT32_MAX, VSA_ERR_INVALID_ARG, "batch*heads*seqlen/block_q exceeds int32");
     VSA_REQUIRE((int64_t)batch * seqlen <= INT32_MAX, VSA_ERR_INVALID_ARG, "batch*seqlen exceeds int32");
+    VSA_REQUIRE(seqlen / block_kv < vsa::kMaxTilesPartial, VSA_ERR_UNSUPPORTED,
+                "seqlen/block_kv must be below %d KV tiles", vsa::kMaxTilesPartial);
+    VSA_REQUIRE(aligned(kv_valid, 4), VSA_ERR_INVALID_ARG, "kv_valid must be 4-byte aligned");
     return VSA_OK;
 }
 
 vsa::FwdParams make_params(const void* q, const void* k, const void* v, const int32_t* idx, const int32_t* cnt,
-                           int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim, int32_t idx_ld,
-                           int32_t block_q, int32_t block_kv, float scale, const int32_t* work, int32_t n_work,
-                           void* o, float* lse) {
+                           const int32_t* kv_valid, int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim,
+                           int32_t idx_ld, int32_t block_q, int32_t block_kv, float scale, const int32_t* work,
+                           int32_t n_work, void* o, float* lse) {
     (void)head_dim;
     vsa::FwdParams p;
     p.q = (const uint16_t*)q;
@@ -73,6 +76,7 @@ vsa::FwdParams make_params(const void* q, const void* k, const void* v, const in
     p.idx = idx;
     p.cnt = cnt;
     p.work = work;
+    p.kv_valid = kv_valid;
     p.o = (uint16_t*)o;
     p.lse = lse;
     p.n_work = n_work;
@@ -121,7 +125,7 @@ int32_t worklist_buffer(size_t bytes, int32_t** out) {
 
 extern "C" {
 
-int32_t vsa_abi_version(void) { return 2; }
+int32_t vsa_abi_version(void) { return 3; }
 
 const char* vsa_status_string(int32_t status) {
     switch (status) {
@@ -182,30 +186,31 @@ int32_t vsa_build_worklist(const int32_t* kv_block_cnt, int32_t n_items, int32_t
 }
 
 int32_t vsa_attn_fwd_worklist(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
-                              const int32_t* kv_block_cnt, int32_t batch, int32_t seqlen, int32_t heads,
-                              int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv, float scale,
-                              const int32_t* work_list, int32_t n_work, void* o, float* lse, void* stream) {
+                              const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch, int32_t seqlen,
+                              int32_t heads, int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv,
+                              float scale, const int32_t* work_list, int32_t n_work, void* o, float* lse,
+                              void* stream) {
     g_last_error[0] = 0;
-    int32_t rc = check_fwd(q, k, v, kv_block_idx, kv_block_cnt, batch, seqlen, heads, head_dim, idx_ld, block_q,
-                           block_kv, scale, o, lse);
+    int32_t rc = check_fwd(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld,
+                           block_q, block_kv, scale, o, lse);
     if (rc != VSA_OK) return rc;
     VSA_REQUIRE(n_work >= 0, VSA_ERR_INVALID_ARG, "n_work must be >= 0");
     if (n_work == 0) return VSA_OK;
     VSA_REQUIRE(work_list && aligned(work_list, 4), VSA_ERR_INVALID_ARG, "work_list must be a 4-byte aligned pointer");
-    vsa::FwdParams p = make_params(q, k, v, kv_block_idx, kv_block_cnt, batch, seqlen, heads, head_dim, idx_ld,
-                                   block_q, block_kv, scale, work_list, n_work, o, lse);
+    vsa::FwdParams p = make_params(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim,
+                                   idx_ld, block_q, block_kv, scale, work_list, n_work, o, lse);
     hipError_t e = vsa::launch_fwd(block_q, block_kv, head_dim, p, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
     return VSA_OK;
 }
 
 int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
-                     const int32_t* kv_block_cnt, int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim,
-                     int32_t idx_ld, int32_t block_q, int32_t block_kv, float scale, void* o, float* lse,
-                     void* stream) {
+                     const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch, int32_t seqlen,
+                     int32_t heads, int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv, float scale,
+                     void* o, float* lse, void* stream) {
     g_last_error[0] = 0;
-    int32_t rc = check_fwd(q, k, v, kv_block_idx, kv_block_cnt, batch, seqlen, heads, head_dim, idx_ld, block_q,
-                           block_kv, scale, o, lse);
+    int32_t rc = check_fwd(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld,
+                           block_q, block_kv, scale, o, lse);
     if (rc != VSA_OK) return rc;
     VSA_REQUIRE(idx_ld <= vsa::kWorklistMaxCnt, VSA_ERR_UNSUPPORTED,
                 "idx_ld %d exceeds the work-list sort limit %d; use vsa_attn_fwd_worklist", idx_ld,
@@ -218,10 +223,27 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
     hipError_t e = vsa::launch_build_worklist(kv_block_cnt, n_items, seqlen / block_q, idx_ld, work,
                                               (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
-    vsa::FwdParams p = make_params(q, k, v, kv_block_idx, kv_block_cnt, batch, seqlen, heads, head_dim, idx_ld,
-                                   block_q, block_kv, scale, work, n_items, o, lse);
+    vsa::FwdParams p = make_params(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim,
+                                   idx_ld, block_q, block_kv, scale, work, n_items, o, lse);
     e = vsa::launch_fwd(block_q, block_kv, head_dim, p, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    return VSA_OK;
+}
+
+int32_t vsa_expand_valid(const int32_t* vbs, int32_t nkv_logical, int32_t logical_block_kv, int32_t block_kv,
+                         int32_t* kv_valid, void* stream) {
+    g_last_error[0] = 0;
+    VSA_REQUIRE(nkv_logical >= 0, VSA_ERR_INVALID_ARG, "nkv_logical must be >= 0");
+    VSA_REQUIRE(logical_block_kv >= 1 && block_kv >= 1 && logical_block_kv % block_kv == 0, VSA_ERR_INVALID_ARG,
+                "block_kv %d must divide logical_block_kv %d", block_kv, logical_block_kv);
+    const int64_t n = (int64_t)nkv_logical * (logical_block_kv / block_kv);
+    VSA_REQUIRE(n <= INT32_MAX, VSA_ERR_INVALID_ARG, "too many tiles");
+    if (n == 0) return VSA_OK;
+    VSA_REQUIRE(vbs && kv_valid, VSA_ERR_INVALID_ARG, "null pointer");
+    VSA_REQUIRE(aligned(vbs, 4) && aligned(kv_valid, 4), VSA_ERR_INVALID_ARG, "buffers must be 4-byte aligned");
+    hipError_t e = vsa::launch_expand_valid(vbs, nkv_logical, logical_block_kv / block_kv, block_kv, kv_valid,
+                                            (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "expand_valid launch");
     return VSA_OK;
 }
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "vsa_internal.h"
+
 namespace vsa {
 namespace dev {
 
@@ -74,6 +76,31 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
     return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
+// A CSR entry as staged in LDS: -1 for an index outside [0, nkv), else the
+// tile index with the number of invalid keys of the tile (block_kv minus its
+// clamped valid count; 0 without valid counts) in the bits above kTileBits.
+// Kernels built without partial tiles (PARTIAL = false) stage the raw index
+// and treat every in-range tile as full.
+template <bool PARTIAL>
+__device__ __forceinline__ int stage_entry(int t, int nkv, int block_kv, const int32_t* kv_valid) {
+    if (t < 0 || t >= nkv) return -1;
+    if constexpr (!PARTIAL) return t;
+    const int nv = kv_valid[t];
+    const int invalid = nv < 0 ? block_kv : (nv > block_kv ? 0 : block_kv - nv);
+    return t | (invalid << kTileBits);
+}
+template <bool PARTIAL>
+__device__ __forceinline__ int entry_tile(int e) {
+    if constexpr (!PARTIAL) return e;
+    return e < 0 ? -1 : (e & (kMaxTilesPartial - 1));
+}
+// valid keys of a staged entry's tile (0 for an out-of-range entry)
+template <bool PARTIAL>
+__device__ __forceinline__ int entry_keys(int e, int block_kv) {
+    if constexpr (!PARTIAL) return e < 0 ? 0 : block_kv;
+    return e < 0 ? 0 : block_kv - (e >> kTileBits);
+}
+
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);

@@ -144,6 +144,16 @@ __global__ __launch_bounds__(WAVES * 64) void worklist_kernel(const int32_t* __r
     }
 }
 
+// Valid keys per physical KV tile from valid tokens per logical KV block:
+// tile r of block T keeps clamp(vbs[T] - r*block_kv, 0, block_kv).
+__global__ void expand_valid_kernel(const int32_t* vbs, int n_out, int kv_ratio, int block_kv, int32_t* out) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n_out) return;
+    const int r = i % kv_ratio;
+    const int v = vbs[i / kv_ratio] - r * block_kv;
+    out[i] = v < 0 ? 0 : (v > block_kv ? block_kv : v);
+}
+
 }  // namespace
 
 hipError_t launch_mask_to_csr(const uint8_t* mask, int batch, int heads, int nq_logical, int nkv_logical,
@@ -167,6 +177,15 @@ hipError_t launch_build_worklist(const int32_t* cnt, int n_items, int segment, i
         hipLaunchKernelGGL((worklist_kernel<1, 8192, 13>), dim3(n_seg), dim3(64), 0, stream, cnt, segment, max_cnt,
                            work);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_expand_valid(const int32_t* vbs, int nkv_logical, int kv_ratio, int block_kv, int32_t* kv_valid,
+                               hipStream_t stream) {
+    const int n = nkv_logical * kv_ratio;
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(expand_valid_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, vbs, n, kv_ratio, block_kv,
+                       kv_valid);
     return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@ struct FwdParams {
     const int32_t* idx;      // [B, H, nq, ld]
     const int32_t* cnt;      // [B, H, nq]
     const int32_t* work;     // [n_work] flat (b*H + h)*nq + p; may be null = identity
+    const int32_t* kv_valid; // [nkv] valid leading keys per KV tile; null = all tiles full
     uint16_t* o;             // [B, S, H, D] bf16 bits
     float* lse;              // [B, H, S]
     int32_t n_work;
@@ -44,9 +45,16 @@ hipError_t launch_mask_to_csr(const uint8_t* mask, int batch, int heads, int nq_
                               int32_t* overflow, hipStream_t stream);
 hipError_t launch_build_worklist(const int32_t* cnt, int n_items, int segment, int max_cnt, int32_t* work,
                                  hipStream_t stream);
+hipError_t launch_expand_valid(const int32_t* vbs, int nkv_logical, int kv_ratio, int block_kv, int32_t* kv_valid,
+                               hipStream_t stream);
 
 constexpr int kWorklistMaxCnt = 8191;
 // Largest CSR row length the forward kernels accept (rows are staged in LDS).
 constexpr int kMaxIdxLd = 8191;
+// Staged CSR entries pack the tile index (low kTileBits bits) with the
+// number of invalid keys of a partial tile (the bits above), so a sequence
+// may hold fewer than 2^kTileBits KV tiles.
+constexpr int kTileBits = 22;
+constexpr int kMaxTilesPartial = 1 << kTileBits;
 
 }  // namespace vsa

@@ -103,10 +103,12 @@ struct TileFetch {
     static constexpr int KP = 16 / G::ROWS_PER_KB;
 
     int gw;
+    uint32_t lds0;  // LDS byte address of the tile buffers' base
     uint32_t koff[KP];
     uint32_t voff;
 
-    __device__ __forceinline__ TileFetch(int gw_, int lane, int tok_bytes) : gw(gw_) {
+    __device__ __forceinline__ TileFetch(const char* smem, int gw_, int lane, int tok_bytes)
+        : gw(gw_), lds0(lds_addr(smem)) {
         const int rl = lane / G::NC, pos = lane % G::NC;
 #pragma unroll
         for (int k = 0; k < KP; ++k) {
@@ -115,17 +117,17 @@ struct TileFetch {
         }
         voff = (uint32_t)(rl * tok_bytes + ((pos ^ swz_v<G::NC>(rl)) << 4));
     }
-    // block i (0 <= i < BPW) of this wave's share
-    __device__ __forceinline__ void block(char* smem, int dst, const char* tile, int tok_bytes, bool v_layout,
-                                          int i) const {
+    // block i (0 <= i < BPW) of this wave's share; dst is the tile buffer's
+    // byte offset from the base
+    __device__ __forceinline__ void block(int dst, const char* tile, int tok_bytes, bool v_layout, int i) const {
         const int blk = gw * BPW + i;
         const char* src = tile + (int64_t)(blk * G::ROWS_PER_KB) * tok_bytes;
-        lds_dma16(src, v_layout ? voff : koff[i % KP], lds_addr(smem + dst + blk * 1024));
+        lds_dma16(src, v_layout ? voff : koff[i % KP], lds0 + (uint32_t)(dst + blk * 1024));
     }
     // this wave's whole share
-    __device__ __forceinline__ void all(char* smem, int dst, const char* tile, int tok_bytes, bool v_layout) const {
+    __device__ __forceinline__ void all(int dst, const char* tile, int tok_bytes, bool v_layout) const {
 #pragma unroll
-        for (int i = 0; i < BPW; ++i) block(smem, dst, tile, tok_bytes, v_layout, i);
+        for (int i = 0; i < BPW; ++i) block(dst, tile, tok_bytes, v_layout, i);
     }
 };
 
@@ -271,10 +273,25 @@ struct WaveEngine {
         }
     }
 
+    // Partial tile: scores of keys at or past nv (0 < nv < BKV) become -inf,
+    // so those keys take no part in the softmax.
+    __device__ __forceinline__ void mask_keys(int nv) {
+        // key of register r in 32-key block nb: nb*32 + 8*(r/4) + 4*hi + r%4.
+        // Compared as (compile-time part) >= nv - 4*hi, so that no per-lane
+        // key table is formed (it would be hoisted out of the KV loop).
+        const int lim = nv - 4 * hi;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (nb * 32 + 8 * (r >> 2) + (r & 3) >= lim) sacc[nb][r] = -__builtin_inff();
+    }
+
     // Softmax of the scores in sacc into pk (bf16), with the lazy rescale of
-    // O and l. A tile whose list entry was out of range (ok == false)
-    // contributes nothing. hook(0..NH-1) is spread over the exponentials
-    // (and is called on skipped tiles too).
+    // O and l. A tile with no valid key (ok == false: a list entry out of
+    // range, or a partial tile with no valid key) contributes nothing.
+    // hook(0..NH-1) is spread over the exponentials (and is called on
+    // skipped tiles too).
     template <int NH = 0, typename Hook = NoHook>
     __device__ __forceinline__ void softmax(bool ok, Hook&& hook = Hook{}) {
         constexpr int CHUNKS = NB * 2;  // 8-score blocks per lane

@@ -42,6 +42,14 @@
  *    LSE = -inf (as the split-KV epilogue on page
  *    "BlackwellMultiHeadLatentAttentionForwardFP8", write_empty_output).
  *    Duplicate entries are counted twice.
+ *  - Partial tiles (optional): kv_valid [seqlen/block_kv] int32, shared by
+ *    every batch and head, gives the number of valid leading key tokens of
+ *    each KV tile; the rest of the tile is padding that no query attends to.
+ *    This is the per-block valid size `vbs` of the FastVideo page's VSA
+ *    wrapper (block_sparse_attn_256_bshd(q, k, v, mask, vbs)), per physical
+ *    tile (see vsa_expand_valid). NULL means every tile is full. Values are
+ *    clamped to [0, block_kv]; a query row left with no valid key gets O = 0
+ *    and LSE = -inf.
  */
 #ifndef VSA_ATTN_H
 #define VSA_ATTN_H
@@ -119,6 +127,21 @@ int32_t vsa_build_worklist(const int32_t* kv_block_cnt, int32_t n_items, int32_t
                            int32_t* work_list, void* stream);
 
 /*
+ * vsa_expand_valid -- valid key tokens per physical KV tile from valid tokens
+ * per logical KV block (the variable block sizes `vbs` of the FastVideo
+ * page's VSA wrapper): a logical block of logical_block_kv positions holding
+ * vbs[T] valid tokens first, then padding, splits into
+ * logical_block_kv/block_kv physical tiles, tile r keeping
+ * clamp(vbs[T] - r*block_kv, 0, block_kv) valid tokens.
+ *
+ *   vbs        [nkv_logical] int32, each in [0, logical_block_kv]
+ *   kv_valid   out [nkv_logical * logical_block_kv / block_kv] int32
+ *   block_kv must divide logical_block_kv.
+ */
+int32_t vsa_expand_valid(const int32_t* vbs, int32_t nkv_logical, int32_t logical_block_kv, int32_t block_kv,
+                         int32_t* kv_valid, void* stream);
+
+/*
  * vsa_attn_fwd -- fused block-sparse attention forward (O and LSE).
  *
  * Source: page 3, bench_vsa_blackwell.py, ref_masked_sdpa_fp32 (what is
@@ -129,16 +152,19 @@ int32_t vsa_build_worklist(const int32_t* kv_block_cnt, int32_t n_items, int32_t
  * nearest even, fp32 LSE in natural log.
  *
  *   block_q x block_kv in {64,128,256} x {64,128}; head_dim in {64, 128};
- *   seqlen divisible by both; 0 < scale < inf; 1 <= idx_ld <= 8191.
+ *   seqlen divisible by both; seqlen/block_kv < 2^22; 0 < scale < inf;
+ *   1 <= idx_ld <= 8191;
+ *   kv_valid: NULL or per-tile valid key counts (see the conventions above).
+ *   Kernels read the whole CSR row [0, idx_ld) of every listed query tile.
  *   Builds the work list (count-sorted within each batch and head, segment
  *   = seqlen/block_q) in a library-owned device buffer (grown on demand per
  *   device, released by vsa_release) and then runs the kernel in that
  *   order; see vsa_attn_fwd_worklist for the kernel alone.
  */
 int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
-                     const int32_t* kv_block_cnt, int32_t batch, int32_t seqlen, int32_t heads,
-                     int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv, float scale,
-                     void* o, float* lse, void* stream);
+                     const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch, int32_t seqlen,
+                     int32_t heads, int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv,
+                     float scale, void* o, float* lse, void* stream);
 
 /*
  * vsa_attn_fwd_worklist -- the attention kernel alone, over a caller-built
@@ -148,10 +174,10 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
  * written, once per listing. n_work >= 0.
  */
 int32_t vsa_attn_fwd_worklist(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
-                              const int32_t* kv_block_cnt, int32_t batch, int32_t seqlen, int32_t heads,
-                              int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv,
-                              float scale, const int32_t* work_list, int32_t n_work, void* o, float* lse,
-                              void* stream);
+                              const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch,
+                              int32_t seqlen, int32_t heads, int32_t head_dim, int32_t idx_ld, int32_t block_q,
+                              int32_t block_kv, float scale, const int32_t* work_list, int32_t n_work, void* o,
+                              float* lse, void* stream);
 
 /* Free the library-owned work-list buffers on every device. Not thread-safe
  * with concurrent vsa_attn_fwd calls. */

@@ -36,7 +36,7 @@ def test_header_declares_the_binding_symbols():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.vsa_abi_version() == 2
+    assert lib.vsa_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -52,11 +52,12 @@ A = 0x10000
 
 
 def _fwd(lib, **kw):
-    args = dict(q=A, k=A, v=A, idx=A, cnt=A, B=1, S=1024, H=2, D=128, ld=16, bq=128, bkv=64, scale=0.1, o=A, lse=A)
+    args = dict(q=A, k=A, v=A, idx=A, cnt=A, valid=None, B=1, S=1024, H=2, D=128, ld=16, bq=128, bkv=64, scale=0.1,
+                o=A, lse=A)
     args.update(kw)
-    return lib.vsa_attn_fwd(args["q"], args["k"], args["v"], args["idx"], args["cnt"], args["B"], args["S"],
-                            args["H"], args["D"], args["ld"], args["bq"], args["bkv"], args["scale"], args["o"],
-                            args["lse"], None)
+    return lib.vsa_attn_fwd(args["q"], args["k"], args["v"], args["idx"], args["cnt"], args["valid"], args["B"],
+                            args["S"], args["H"], args["D"], args["ld"], args["bq"], args["bkv"], args["scale"],
+                            args["o"], args["lse"], None)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -74,6 +75,8 @@ def _fwd(lib, **kw):
     (dict(q=A + 2), -1, "aligned"),
     (dict(lse=A + 2), -1, "aligned"),
     (dict(ld=9000), -2, "maximum"),
+    (dict(valid=A + 2), -1, "kv_valid"),
+    (dict(S=1 << 28, bq=256, H=1), -2, "KV tiles"),
 ])
 def test_attn_fwd_rejects_invalid_arguments(lib, kw, status, needle):
     assert _fwd(lib, **kw) == status
@@ -81,12 +84,15 @@ def test_attn_fwd_rejects_invalid_arguments(lib, kw, status, needle):
 
 
 def test_attn_fwd_worklist_rejects_bad_work_list(lib):
-    rc = lib.vsa_attn_fwd_worklist(A, A, A, A, A, 1, 1024, 2, 128, 16, 128, 64, 0.1, None, 5, A, A, None)
+    rc = lib.vsa_attn_fwd_worklist(A, A, A, A, A, None, 1, 1024, 2, 128, 16, 128, 64, 0.1, None, 5, A, A, None)
     assert rc == -1 and "work_list" in lib.vsa_last_error().decode()
-    rc = lib.vsa_attn_fwd_worklist(A, A, A, A, A, 1, 1024, 2, 128, 16, 128, 64, 0.1, A, -1, A, A, None)
+    rc = lib.vsa_attn_fwd_worklist(A, A, A, A, A, None, 1, 1024, 2, 128, 16, 128, 64, 0.1, A, -1, A, A, None)
     assert rc == -1
+    rc = lib.vsa_attn_fwd_worklist(A, A, A, A, A, A + 1, 1, 1024, 2, 128, 16, 128, 64, 0.1, A, 4, A, A, None)
+    assert rc == -1 and "kv_valid" in lib.vsa_last_error().decode()
     # n_work == 0 is a no-op that succeeds without touching the device
-    assert lib.vsa_attn_fwd_worklist(A, A, A, A, A, 1, 1024, 2, 128, 16, 128, 64, 0.1, None, 0, A, A, None) == 0
+    assert lib.vsa_attn_fwd_worklist(A, A, A, A, A, None, 1, 1024, 2, 128, 16, 128, 64, 0.1, None, 0, A, A,
+                                     None) == 0
 
 
 def test_mask_to_csr_rejects_invalid_arguments(lib):
@@ -109,6 +115,17 @@ def test_build_worklist_validation(lib):
     assert "segment" in lib.vsa_last_error().decode()
     assert lib.vsa_build_worklist(A, 10, 0, 10, A, None) == -1
     assert lib.vsa_build_worklist(None, 0, 1, 10, None, None) == 0  # empty list: nothing to do
+
+
+def test_expand_valid_validation(lib):
+    f = lib.vsa_expand_valid
+    assert f(A, 4, 256, 96, A, None) == -1  # block_kv must divide the logical block
+    assert "divide" in lib.vsa_last_error().decode()
+    assert f(None, 4, 256, 64, A, None) == -1
+    assert f(A, 4, 256, 64, None, None) == -1
+    assert f(A + 2, 4, 256, 64, A, None) == -1
+    assert f(A, -1, 256, 64, A, None) == -1
+    assert f(None, 0, 256, 64, None, None) == 0  # nothing to do
 
 
 def test_binding_refuses_cpu_tensors():

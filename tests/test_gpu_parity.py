@@ -164,8 +164,8 @@ def test_worklist_bit_exact(vsa, label, spec, ld, segment):
 
 # ------------------------------------------------------------ forward pass
 
-def _run_fwd(vsa, q, k, v, idx, cnt, bq, bkv, scale):
-    o, lse = vsa.vsa_attn_fwd(q, k, v, idx, cnt, bq, bkv, scale)
+def _run_fwd(vsa, q, k, v, idx, cnt, bq, bkv, scale, kv_valid=None):
+    o, lse = vsa.vsa_attn_fwd(q, k, v, idx, cnt, bq, bkv, scale, kv_valid=kv_valid)
     torch.cuda.synchronize()
     return o, lse
 
@@ -204,6 +204,43 @@ def test_every_tile_shape_all_rows(vsa, bq, bkv, D):
     rows = np.arange(B * H * S)
     check_rows(o, lse, rows, o_ref.transpose(0, 2, 1, 3).reshape(-1, D), lse_ref.reshape(-1), S, H,
                f"{bq}x{bkv} D={D}")
+
+
+@pytest.mark.parametrize("bq,bkv,D", SHAPES, ids=[f"{a}x{b}_d{c}" for a, b, c in SHAPES])
+def test_partial_tiles_every_tile_shape_all_rows(vsa, bq, bkv, D):
+    """Per-tile valid key counts (empty, partial, full tiles), including a row
+    whose selected tiles hold no valid key."""
+    B, H, S = 2, 2, 1024
+    say(f"forward partial tiles {bq}x{bkv} D={D}")
+    q, k, v = W.qkv(B, S, H, D, seed=bq + bkv + D + 5)
+    nq, nkv = S // bq, S // bkv
+    idx, cnt = W.random_csr(B, H, nq, nkv, nkv, 1, nkv, seed=bq * 7 + bkv + D + 5)
+    val = W.ragged_block_sizes(nkv, bkv, seed=bq + 3 * bkv + D, p_full=0.4)
+    val[:2] = 0
+    val[2] = 1
+    val[3] = bkv - 1
+    cnt[1, 0, nq - 1] = 2  # only tiles without valid keys: an empty row
+    idx[1, 0, nq - 1, :2] = [1, 0]
+    scale = 1.0 / math.sqrt(D)
+    o_ref, lse_ref = oracle.attn_full(q, k, v, idx, cnt, bq, bkv, scale, kv_valid=val)
+    assert np.all(np.isneginf(lse_ref[1, 0, (nq - 1) * bq:]))
+    o, lse = _run_fwd(vsa, dev(q), dev(k), dev(v), dev(idx), dev(cnt), bq, bkv, scale, kv_valid=dev(val))
+    check_rows(o, lse, np.arange(B * H * S), o_ref.transpose(0, 2, 1, 3).reshape(-1, D), lse_ref.reshape(-1), S, H,
+               f"partial {bq}x{bkv} D={D}")
+
+
+EXPAND_CASES = [(256, 128), (256, 64), (256, 256), (128, 32), (64, 64)]
+
+
+@pytest.mark.parametrize("lkv,pkv", EXPAND_CASES, ids=[f"{a}->{b}" for a, b in EXPAND_CASES])
+def test_expand_valid_bit_exact(vsa, lkv, pkv):
+    say(f"expand_valid {lkv}->{pkv}")
+    vbs = W.ragged_block_sizes(1000, lkv, seed=lkv + pkv)
+    vbs[:3] = [0, lkv, 1]
+    ref = ofront.expand_valid(vbs, lkv, pkv)
+    got = vsa.vsa_expand_valid(dev(vbs), lkv, pkv)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)
 
 
 def test_invalid_entries_are_skipped_and_counts_clamped(vsa):
@@ -270,18 +307,20 @@ def test_deterministic_and_stream_aware(vsa):
 
 # ------------------------------------------------ full-size workloads
 
-def _full_size(vsa, wl, shape, ld, label, tiles_per_head=2):
+def _full_size(vsa, wl, shape, ld, label, tiles_per_head=2, vbs=None):
     say(f"forward {label}: generating inputs")
     q, k, v = wl.qkv()
     mask = wl.logical_mask()
     qd, kd, vd = dev(q), dev(k), dev(v)
     idx, cnt = vsa.vsa_mask_to_csr(dev(mask), wl.logical_block, shape, ld)
+    val = None if vbs is None else vsa.vsa_expand_valid(dev(vbs), wl.logical_block[1], shape[1])
     say(f"forward {label}: kernel {shape[0]}x{shape[1]}")
-    o, lse = _run_fwd(vsa, qd, kd, vd, idx, cnt, shape[0], shape[1], wl.scale)
+    o, lse = _run_fwd(vsa, qd, kd, vd, idx, cnt, shape[0], shape[1], wl.scale, kv_valid=val)
     B, S, H, D = q.shape
     rows = sample_rows(B, H, S, shape[0], tiles_per_head, seed=shape[0] + shape[1])
     idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
-    o_ref, lse_ref = oracle.attn_rows(q, k, v, idx_h, cnt_h, shape[0], shape[1], wl.scale, rows)
+    val_h = None if vbs is None else ofront.expand_valid(vbs, wl.logical_block[1], shape[1])
+    o_ref, lse_ref = oracle.attn_rows(q, k, v, idx_h, cnt_h, shape[0], shape[1], wl.scale, rows, kv_valid=val_h)
     check_rows(o, lse, rows, o_ref, lse_ref, S, H, label)
     return o, lse
 
@@ -304,4 +343,19 @@ def test_vsa256_workload_sampled_and_cross_shape(vsa):
 
 def test_native64_workload_sampled(vsa):
     _full_size(vsa, W.NATIVE64, (64, 64), 92, "native64 64x64", tiles_per_head=3)
+    torch.cuda.empty_cache()
+
+
+def test_vsa256_ragged_blocks_sampled_and_cross_shape(vsa):
+    """VSA-256 with ragged logical KV blocks (valid tokens in [128, 256])."""
+    vbs = W.ragged_block_sizes(W.VSA256.seqlen // 256, 256, seed=2026, lo=128)
+    o0, l0 = _full_size(vsa, W.VSA256, (256, 128), 26, "vsa256 ragged 256x128", vbs=vbs)
+    for shape in ((128, 64), (64, 64)):
+        o1, l1 = _full_size(vsa, W.VSA256_FINE, shape, 52, f"vsa256 ragged {shape[0]}x{shape[1]}", vbs=vbs)
+        d = (o1.float() - o0.float()).abs()
+        lrel = ((l1 - l0).abs() / l0.abs().clamp_min(1.0)).max().item()
+        say(f"ragged cross-shape {shape}: max|dO|={d.max().item():.3e} mean|dO|={d.mean().item():.3e} "
+            f"LSE rel={lrel:.3e}")
+        assert d.max().item() <= O_MAX_ABS and d.mean().item() <= O_MEAN_ABS and lrel <= LSE_REL
+        del o1, l1
     torch.cuda.empty_cache()

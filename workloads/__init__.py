@@ -200,3 +200,13 @@ def random_csr(batch, heads, nq, nkv, ld, count_lo, count_hi, seed, shuffle=True
                     sel = np.sort(sel)
                 idx[b, h, p, :c] = sel
     return idx, cnt
+
+
+def ragged_block_sizes(n_blocks: int, block: int, seed: int, lo: int = 0, p_full: float = 0.3) -> np.ndarray:
+    """Valid token counts per KV block for partial-tile inputs: int32 [n_blocks],
+    each uniform in [lo, block], a fraction p_full of them exactly full. Video
+    latents whose tiles do not divide the frame give such ragged blocks."""
+    rng = np.random.default_rng(seed)
+    v = rng.integers(lo, block + 1, size=n_blocks).astype(np.int32)
+    v[rng.random(n_blocks) < p_full] = block
+    return v

@@ -6,9 +6,10 @@ calls anything here, and this package shares no code with it.
 
 * ``attn_rows`` / ``attn_full`` / ``probs_row`` wrap ``vsa_oracle.c``, a plain
   fp32 masked SDPA (FastVideo page, ``bench_vsa_blackwell.py``,
-  ``ref_masked_sdpa_fp32``).
-* ``mask_to_csr`` / ``build_worklist`` / ``expand_valid`` live in
-  ``frontend.py`` (numpy).
+  ``ref_masked_sdpa_fp32``); ``bwd_dq_rows`` / ``bwd_dkv_rows`` / ``bwd_full``
+  its gradients with respect to Q, K and V.
+* ``mask_to_csr`` / ``build_worklist`` / ``expand_valid`` / ``transpose_csr``
+  live in ``frontend.py`` (numpy).
 
 Parity of every function here is pinned by ``tests/test_oracle_pins.py`` and
 ``tests/test_frontend_oracle.py`` against brute force, library routines,
@@ -23,7 +24,7 @@ import subprocess
 
 import numpy as np
 
-from .frontend import build_worklist, expand_valid, mask_to_csr  # noqa: F401
+from .frontend import build_worklist, expand_valid, mask_to_csr, transpose_csr  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "vsa_oracle.c")
@@ -65,6 +66,12 @@ def _load():
         lib.vsa_oracle_probs_row.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
                                              ctypes.c_float, i64, p]
         lib.vsa_oracle_probs_row.restype = i32
+        lib.vsa_oracle_bwd_dq_rows.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
+                                               ctypes.c_float, p, i64, p, i32]
+        lib.vsa_oracle_bwd_dq_rows.restype = i32
+        lib.vsa_oracle_bwd_dkv_rows.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
+                                                ctypes.c_float, p, i64, p, p, i32]
+        lib.vsa_oracle_bwd_dkv_rows.restype = i32
         _lib = lib
     return _lib
 
@@ -143,6 +150,64 @@ def attn_full(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, thr
     o, lse = attn_rows(qb, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, None, threads, kv_valid)
     o = o.reshape(B, H, S, D).transpose(0, 2, 1, 3).copy()
     return o, lse.reshape(B, H, S)
+
+
+def _bwd_common(q, k, v, dout, kv_block_idx, kv_block_cnt, block_q, block_kv, kv_valid):
+    qb, kb, vb, db = _bits(q), _bits(k), _bits(v), _bits(dout)
+    B, S, H, D = qb.shape
+    for t in (kb, vb, db):
+        if t.shape != qb.shape:
+            raise ValueError("q, k, v, dout must share the shape [B, S, H, D]")
+    idx = np.ascontiguousarray(kv_block_idx, dtype=np.int32)
+    cnt = np.ascontiguousarray(kv_block_cnt, dtype=np.int32)
+    nq = S // block_q
+    if idx.ndim != 4 or idx.shape[:3] != (B, H, nq) or cnt.shape != (B, H, nq):
+        raise ValueError("CSR shapes must be idx [B,H,S/block_q,ld], cnt [B,H,S/block_q]")
+    val = _valid_arr(kv_valid, S, block_kv)
+    return qb, kb, vb, db, idx, cnt, val, (B, S, H, D)
+
+
+def bwd_dq_rows(q, k, v, dout, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, rows=None, threads=0,
+                kv_valid=None):
+    """dQ (fp32 [n, D]) for flat query rows (b*H + h)*S + i (None: all rows)."""
+    qb, kb, vb, db, idx, cnt, val, (B, S, H, D) = _bwd_common(q, k, v, dout, kv_block_idx, kv_block_cnt,
+                                                               block_q, block_kv, kv_valid)
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = B * H * S if rows_arr is None else rows_arr.size
+    dq = np.empty((n, D), dtype=np.float32)
+    rc = _load().vsa_oracle_bwd_dq_rows(
+        _ptr(qb), _ptr(kb), _ptr(vb), _ptr(db), _ptr(idx), _ptr(cnt), None if val is None else _ptr(val), B, S, H,
+        D, idx.shape[3], block_q, block_kv, ctypes.c_float(scale), None if rows_arr is None else _ptr(rows_arr), n,
+        _ptr(dq), int(threads))
+    _check(rc)
+    return dq
+
+
+def bwd_dkv_rows(q, k, v, dout, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, rows=None, threads=0,
+                 kv_valid=None):
+    """dK, dV (fp32 [n, D] each) for flat key rows (b*H + h)*S + j (None: all rows)."""
+    qb, kb, vb, db, idx, cnt, val, (B, S, H, D) = _bwd_common(q, k, v, dout, kv_block_idx, kv_block_cnt,
+                                                               block_q, block_kv, kv_valid)
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n = B * H * S if rows_arr is None else rows_arr.size
+    dk = np.empty((n, D), dtype=np.float32)
+    dv = np.empty((n, D), dtype=np.float32)
+    rc = _load().vsa_oracle_bwd_dkv_rows(
+        _ptr(qb), _ptr(kb), _ptr(vb), _ptr(db), _ptr(idx), _ptr(cnt), None if val is None else _ptr(val), B, S, H,
+        D, idx.shape[3], block_q, block_kv, ctypes.c_float(scale), None if rows_arr is None else _ptr(rows_arr), n,
+        _ptr(dk), _ptr(dv), int(threads))
+    _check(rc)
+    return dk, dv
+
+
+def bwd_full(q, k, v, dout, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, threads=0, kv_valid=None):
+    """dQ, dK, dV fp32 [B, S, H, D] for every row."""
+    B, S, H, D = _bits(q).shape
+    dq = bwd_dq_rows(q, k, v, dout, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, None, threads, kv_valid)
+    dk, dv = bwd_dkv_rows(q, k, v, dout, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, None, threads,
+                          kv_valid)
+    shape = lambda a: a.reshape(B, H, S, D).transpose(0, 2, 1, 3).copy()  # noqa: E731
+    return shape(dq), shape(dk), shape(dv)
 
 
 def probs_row(q, k, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, flat_row, kv_valid=None):

@@ -17,6 +17,11 @@ sizes ``vbs`` of the FastVideo page's VSA wrapper): a logical block of LKV
 positions holding vbs valid tokens first, then padding, splits into LKV/PKV
 physical tiles holding clamp(vbs - r*PKV, 0, PKV) valid tokens each.
 
+``transpose_csr``: the Q-direction lists the backward pass walks (page
+"block_sparsity.py" of the FastVideo page's FA4 files: the backward expects
+per-KV-tile lists of the Q tiles that select it, "transposed from forward"):
+for KV tile n, the ascending Q tile indices m whose forward row lists n.
+
 ``build_worklist``: the order in which Q tiles are processed. Items
 (b, h, p) are encoded as their flat index into kv_block_cnt. Within each
 segment of ``segment`` consecutive items (one segment per batch and head when
@@ -91,3 +96,34 @@ def expand_valid(vbs, logical_kv, physical_kv):
     for r in range(e):
         out[:, r] = np.clip(v - r * physical_kv, 0, physical_kv)
     return out.reshape(-1)
+
+
+def transpose_csr(kv_block_idx, kv_block_cnt, nkv, ld_q, fill=-1):
+    """Q-direction block CSR from a KV-direction one.
+
+    kv_block_idx [B, H, NQ, ld], kv_block_cnt [B, H, NQ] (entries [0, cnt) of
+    a row are distinct KV tiles in [0, nkv)). Returns (q_block_idx [B, H, nkv,
+    ld_q] int32, q_block_cnt [B, H, nkv] int32, overflow): row n lists, in
+    ascending order, the Q tiles m whose row holds n; slots past the count
+    hold ``fill``; a count above ld_q keeps the first ld_q entries and sets
+    overflow.
+    """
+    idx = np.asarray(kv_block_idx)
+    cnt = np.asarray(kv_block_cnt)
+    B, H, NQ, _ = idx.shape
+    q_idx = np.full((B, H, nkv, ld_q), fill, dtype=np.int32)
+    q_cnt = np.zeros((B, H, nkv), dtype=np.int32)
+    overflow = False
+    for b in range(B):
+        for h in range(H):
+            sel = np.zeros((nkv, NQ), dtype=bool)
+            for m in range(NQ):
+                for t in idx[b, h, m, :cnt[b, h, m]]:
+                    sel[t, m] = True
+            for n in range(nkv):
+                ms = np.nonzero(sel[n])[0].astype(np.int32)
+                q_cnt[b, h, n] = ms.size
+                k = min(ms.size, ld_q)
+                q_idx[b, h, n, :k] = ms[:k]
+                overflow |= ms.size > ld_q
+    return q_idx, q_cnt, bool(overflow)

@@ -259,3 +259,217 @@ int vsa_oracle_probs_row(const uint16_t* q, const uint16_t* k, const int32_t* kv
     free(qf);
     return rc;
 }
+
+
+/* ------------------------------------------------------------------------
+ * Backward pass (gradients of O with respect to Q, K and V), the standard
+ * softmax-attention derivative applied to the same masked fp32 scores as the
+ * forward (FastVideo page "[perf] Add fine-grained FA4 VSA kernels",
+ * benchmarks/bench_vsa_blackwell.py, ref_masked_sdpa_fp32: the gradient of
+ * that function; the page's block_sparsity.py, normalize_block_sparse_config_
+ * bwd, sets up the same computation over the transposed, Q-direction lists).
+ * With P the masked row softmax of scale * Q K^T, O = P V and dO given:
+ *     dV_j  = sum_i P_ij dO_i
+ *     dP_ij = dO_i . v_j,   D_i = dO_i . O_i = sum_j P_ij dP_ij
+ *     dS_ij = P_ij (dP_ij - D_i)
+ *     dQ_i  = scale * sum_j dS_ij k_j,   dK_j = scale * sum_i dS_ij q_i
+ * Everything is computed here from q, k, v, dO and the mask (O, P and D are
+ * recomputed in fp32, not taken from a forward run). Sums over keys run in
+ * ascending key order, sums over queries in ascending query order, and the
+ * head dimension d = 0..D-1, independent of the tile shape.
+ * ------------------------------------------------------------------------ */
+
+/* Query tile p's row may attend to key tile t?  Scans the CSR row. */
+static int row_selects(const int32_t* idx_row, int32_t n, int32_t t) {
+    for (int32_t e = 0; e < n; ++e)
+        if (idx_row[e] == t) return 1;
+    return 0;
+}
+
+/* P_i (in s, zero outside the mask), O_i (fp32) and D_i for one query row. */
+static int64_t row_prob_out(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout, int S,
+                            int H, int D, int b, int h, int i, const int32_t* allow, int nkv, int block_kv,
+                            float scale, float* qf, float* s, float* o, float* d_out) {
+    float m, l;
+    int64_t nsel = row_weights(q, k, S, H, D, b, h, i, allow, nkv, block_kv, scale, qf, s, &m, &l);
+    const int64_t tok = (int64_t)H * D;
+    for (int d = 0; d < D; ++d) o[d] = 0.0f;
+    if (nsel > 0) {
+        for (int j = 0; j < S; ++j) {
+            if (!allowed(allow, block_kv, j)) continue;
+            const uint16_t* vrow = v + ((int64_t)b * S + j) * tok + (int64_t)h * D;
+            for (int d = 0; d < D; ++d) o[d] += s[j] * bf16_to_f32(vrow[d]);
+        }
+    }
+    const uint16_t* drow = dout + ((int64_t)b * S + i) * tok + (int64_t)h * D;
+    float dd = 0.0f;
+    for (int d = 0; d < D; ++d) dd += bf16_to_f32(drow[d]) * o[d];
+    *d_out = dd;
+    return nsel;
+}
+
+/*
+ * dQ for a list of query rows (flat (b*H + h)*S + i, or NULL for all rows):
+ * dq [n_rows, D] fp32.
+ */
+int vsa_oracle_bwd_dq_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                           const int32_t* kv_block_idx, const int32_t* kv_block_cnt, const int32_t* kv_valid, int B,
+                           int S, int H, int D, int ld, int block_q, int block_kv, float scale, const int64_t* rows,
+                           int64_t n_rows, float* dq, int n_threads) {
+    if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || block_q <= 0 || block_kv <= 0 || ld < 0) return ORACLE_ERR_ARG;
+    if (S % block_q || S % block_kv) return ORACLE_ERR_ARG;
+    const int nq = S / block_q, nkv = S / block_kv;
+    if (check_valid(kv_valid, nkv, block_kv) != ORACLE_OK) return ORACLE_ERR_ARG;
+    const int64_t total = (int64_t)B * H * S;
+    if (rows == NULL) n_rows = total;
+    int status = ORACLE_OK;
+#ifdef _OPENMP
+    if (n_threads <= 0) n_threads = omp_get_max_threads();
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel num_threads(n_threads)
+    {
+        float* s = (float*)malloc(sizeof(float) * (size_t)S);
+        float* qf = (float*)malloc(sizeof(float) * (size_t)D);
+        float* o = (float*)malloc(sizeof(float) * (size_t)D);
+        float* dof = (float*)malloc(sizeof(float) * (size_t)D);
+        int32_t* allow = (int32_t*)malloc(sizeof(int32_t) * (size_t)nkv);
+        if (!s || !qf || !o || !dof || !allow) {
+#pragma omp critical
+            status = ORACLE_ERR_NOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 8)
+            for (int64_t r = 0; r < n_rows; ++r) {
+                int64_t flat = rows ? rows[r] : r;
+                float* dqrow = dq + r * D;
+                if (flat < 0 || flat >= total) {
+#pragma omp critical
+                    status = ORACLE_ERR_ARG;
+                    continue;
+                }
+                int i = (int)(flat % S);
+                int h = (int)((flat / S) % H);
+                int b = (int)(flat / ((int64_t)S * H));
+                int64_t crow = ((int64_t)b * H + h) * nq + i / block_q;
+                int rc = mark_tiles(kv_block_idx + crow * ld, kv_block_cnt[crow], ld, nkv, kv_valid, block_kv, allow);
+                if (rc != ORACLE_OK) {
+#pragma omp critical
+                    status = rc;
+                    continue;
+                }
+                float di;
+                row_prob_out(q, k, v, dout, S, H, D, b, h, i, allow, nkv, block_kv, scale, qf, s, o, &di);
+                const int64_t tok = (int64_t)H * D;
+                const uint16_t* drow = dout + ((int64_t)b * S + i) * tok + (int64_t)h * D;
+                for (int d = 0; d < D; ++d) dof[d] = bf16_to_f32(drow[d]);
+                for (int d = 0; d < D; ++d) dqrow[d] = 0.0f;
+                for (int j = 0; j < S; ++j) {
+                    if (!allowed(allow, block_kv, j)) continue;
+                    const uint16_t* vrow = v + ((int64_t)b * S + j) * tok + (int64_t)h * D;
+                    const uint16_t* krow = k + ((int64_t)b * S + j) * tok + (int64_t)h * D;
+                    float dp = 0.0f;
+                    for (int d = 0; d < D; ++d) dp += dof[d] * bf16_to_f32(vrow[d]);
+                    const float ds = s[j] * (dp - di);
+                    for (int d = 0; d < D; ++d) dqrow[d] += ds * bf16_to_f32(krow[d]);
+                }
+                for (int d = 0; d < D; ++d) dqrow[d] *= scale;
+            }
+        }
+        free(s);
+        free(qf);
+        free(o);
+        free(dof);
+        free(allow);
+    }
+    return status;
+}
+
+/*
+ * dK and dV for a list of key rows (flat (b*H + h)*S + j, or NULL for all):
+ * dk, dv [n_rows, D] fp32. For key j the sums run over the query rows i that
+ * may attend to it, in ascending order; each such row's softmax and D_i are
+ * recomputed.
+ */
+int vsa_oracle_bwd_dkv_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                            const int32_t* kv_block_idx, const int32_t* kv_block_cnt, const int32_t* kv_valid, int B,
+                            int S, int H, int D, int ld, int block_q, int block_kv, float scale, const int64_t* rows,
+                            int64_t n_rows, float* dk, float* dv, int n_threads) {
+    if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || block_q <= 0 || block_kv <= 0 || ld < 0) return ORACLE_ERR_ARG;
+    if (S % block_q || S % block_kv) return ORACLE_ERR_ARG;
+    const int nq = S / block_q, nkv = S / block_kv;
+    if (check_valid(kv_valid, nkv, block_kv) != ORACLE_OK) return ORACLE_ERR_ARG;
+    const int64_t total = (int64_t)B * H * S;
+    if (rows == NULL) n_rows = total;
+    int status = ORACLE_OK;
+#ifdef _OPENMP
+    if (n_threads <= 0) n_threads = omp_get_max_threads();
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel num_threads(n_threads)
+    {
+        float* s = (float*)malloc(sizeof(float) * (size_t)S);
+        float* qf = (float*)malloc(sizeof(float) * (size_t)D);
+        float* o = (float*)malloc(sizeof(float) * (size_t)D);
+        int32_t* allow = (int32_t*)malloc(sizeof(int32_t) * (size_t)nkv);
+        if (!s || !qf || !o || !allow) {
+#pragma omp critical
+            status = ORACLE_ERR_NOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t r = 0; r < n_rows; ++r) {
+                int64_t flat = rows ? rows[r] : r;
+                float* dkrow = dk + r * D;
+                float* dvrow = dv + r * D;
+                if (flat < 0 || flat >= total) {
+#pragma omp critical
+                    status = ORACLE_ERR_ARG;
+                    continue;
+                }
+                int j = (int)(flat % S);
+                int h = (int)((flat / S) % H);
+                int b = (int)(flat / ((int64_t)S * H));
+                const int64_t tok = (int64_t)H * D;
+                const uint16_t* vrow = v + ((int64_t)b * S + j) * tok + (int64_t)h * D;
+                for (int d = 0; d < D; ++d) dkrow[d] = 0.0f;
+                for (int d = 0; d < D; ++d) dvrow[d] = 0.0f;
+                for (int p = 0; p < nq; ++p) {
+                    int64_t crow = ((int64_t)b * H + h) * nq + p;
+                    int32_t n = kv_block_cnt[crow];
+                    if (n < 0 || n > ld) {
+#pragma omp critical
+                        status = ORACLE_ERR_CNT;
+                        break;
+                    }
+                    if (!row_selects(kv_block_idx + crow * ld, n, j / block_kv)) continue;
+                    int rc = mark_tiles(kv_block_idx + crow * ld, n, ld, nkv, kv_valid, block_kv, allow);
+                    if (rc != ORACLE_OK) {
+#pragma omp critical
+                        status = rc;
+                        break;
+                    }
+                    if (!allowed(allow, block_kv, j)) continue; /* padding key of a partial tile */
+                    for (int i = p * block_q; i < (p + 1) * block_q; ++i) {
+                        float di;
+                        row_prob_out(q, k, v, dout, S, H, D, b, h, i, allow, nkv, block_kv, scale, qf, s, o, &di);
+                        const uint16_t* drow = dout + ((int64_t)b * S + i) * tok + (int64_t)h * D;
+                        float dp = 0.0f;
+                        for (int d = 0; d < D; ++d) dp += bf16_to_f32(drow[d]) * bf16_to_f32(vrow[d]);
+                        const float pij = s[j];
+                        const float ds = pij * (dp - di);
+                        /* qf holds row i of Q (filled by row_weights) */
+                        for (int d = 0; d < D; ++d) dkrow[d] += ds * qf[d];
+                        for (int d = 0; d < D; ++d) dvrow[d] += pij * bf16_to_f32(drow[d]);
+                    }
+                }
+                for (int d = 0; d < D; ++d) dkrow[d] *= scale;
+            }
+        }
+        free(s);
+        free(qf);
+        free(o);
+        free(allow);
+    }
+    return status;
+}

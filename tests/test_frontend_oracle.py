@@ -132,3 +132,26 @@ def test_expand_valid_matches_token_level_definition():
         frontend.expand_valid([257], 256, 64)
     with pytest.raises(ValueError):
         frontend.expand_valid([10], 256, 96)
+
+
+def test_transpose_csr_lists_exactly_the_selecting_query_tiles():
+    from workloads import random_csr
+
+    for B, H, NQ, NKV, seed in ((2, 3, 12, 20, 1), (1, 2, 64, 32, 2)):
+        idx, cnt = random_csr(B, H, NQ, NKV, NKV, 0, NKV, seed=seed)
+        ld_q = NQ
+        q_idx, q_cnt, ovf = frontend.transpose_csr(idx, cnt, NKV, ld_q)
+        assert not ovf and q_idx.shape == (B, H, NKV, ld_q) and q_cnt.shape == (B, H, NKV)
+        fwd_pairs = {(b, h, m, int(t)) for b in range(B) for h in range(H) for m in range(NQ)
+                     for t in idx[b, h, m, :cnt[b, h, m]]}
+        bwd_pairs = {(b, h, int(m), n) for b in range(B) for h in range(H) for n in range(NKV)
+                     for m in q_idx[b, h, n, :q_cnt[b, h, n]]}
+        assert fwd_pairs == bwd_pairs
+        for pos in np.ndindex(q_cnt.shape):
+            row = q_idx[pos][:q_cnt[pos]]
+            assert np.all(np.diff(row) > 0) and np.all(q_idx[pos][q_cnt[pos]:] == -1)
+        assert q_cnt.sum() == cnt.sum()
+        # compact ld_q: truncation flags overflow
+        small = max(1, int(q_cnt.max()) - 1)
+        _, c2, ovf2 = frontend.transpose_csr(idx, cnt, NKV, small)
+        assert ovf2 and np.array_equal(c2, q_cnt)

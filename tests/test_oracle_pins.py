@@ -305,13 +305,14 @@ def test_invalid_csr_is_rejected(bad):
 
 MUTATIONS = {
     "scale_dropped": ("s[j] = acc * scale;", "s[j] = acc;"),
-    "key_from_query_row": ("const uint16_t* krow = k + ((int64_t)b * S + j)",
-                           "const uint16_t* krow = k + ((int64_t)b * S + i)"),
-    "value_tiles_use_block_q": ("if (!allowed(allow, block_kv, j)) continue;", "if (!allowed(allow, block_q, j)) continue;"),
-    "key_tile_offset": ("const uint16_t* krow = k + ((int64_t)b * S + j) * tok",
-                        "const uint16_t* krow = k + ((int64_t)b * S + (j + block_kv) % S) * tok"),
-    "value_wrong_head": ("const uint16_t* vrow = v + ((int64_t)b * S + j) * tok + (int64_t)h * D;",
-                         "const uint16_t* vrow = v + ((int64_t)b * S + j) * tok;"),
+    "key_from_query_row": ("const uint16_t* krow = k + ((int64_t)b * S + j) * tok + (int64_t)h * D;\n            float acc",
+                           "const uint16_t* krow = k + ((int64_t)b * S + i) * tok + (int64_t)h * D;\n            float acc"),
+    "value_tiles_use_block_q": ("if (!allowed(allow, block_kv, j)) continue;\n                        const uint16_t* vrow",
+                                "if (!allowed(allow, block_q, j)) continue;\n                        const uint16_t* vrow"),
+    "key_tile_offset": ("const uint16_t* krow = k + ((int64_t)b * S + j) * tok + (int64_t)h * D;\n            float acc",
+                        "const uint16_t* krow = k + ((int64_t)b * S + (j + block_kv) % S) * tok + (int64_t)h * D;\n            float acc"),
+    "value_wrong_head": ("const uint16_t* vrow = v + ((int64_t)b * S + j) * tok + (int64_t)h * D;\n                        float w",
+                         "const uint16_t* vrow = v + ((int64_t)b * S + j) * tok;\n                        float w"),
     "no_normalisation": ("if (allowed(allow, block_kv, j)) s[j] = s[j] / l;", "if (allowed(allow, block_kv, j)) s[j] = s[j];"),
     "valid_counts_ignored": ("allow[t] = kv_valid ? kv_valid[t] : block_kv;", "allow[t] = block_kv;"),
     "valid_count_off_by_one": ("return (j % block_kv) < allow[j / block_kv];", "return (j % block_kv) <= allow[j / block_kv];"),

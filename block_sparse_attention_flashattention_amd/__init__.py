@@ -35,8 +35,10 @@ SYMBOLS = (
     "vsa_mask_to_csr",
     "vsa_build_worklist",
     "vsa_expand_valid",
+    "vsa_csr_transpose",
     "vsa_attn_fwd",
     "vsa_attn_fwd_worklist",
+    "vsa_attn_bwd",
     "vsa_release",
 )
 
@@ -79,6 +81,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vsa_attn_fwd_worklist.restype = i32
     lib.vsa_expand_valid.argtypes = [p, i32, i32, i32, p, p]
     lib.vsa_expand_valid.restype = i32
+    lib.vsa_csr_transpose.argtypes = [p, p, i32, i32, i32, i32, i32, p, i32, p, p, p]
+    lib.vsa_csr_transpose.restype = i32
+    lib.vsa_attn_bwd.argtypes = [p, p, p, p, p, p, p, p, i32, p, p, i32, p, i32, i32, i32, i32, i32, i32, f32, p, p,
+                                 p, p]
+    lib.vsa_attn_bwd.restype = i32
     lib.vsa_release.argtypes = []
     lib.vsa_release.restype = None
     _lib = lib
@@ -259,6 +266,70 @@ def vsa_expand_valid(vbs, logical_block_kv, block_kv, kv_valid=None, stream=None
                                          kv_valid.data_ptr(), _stream_ptr(stream, vbs.device))
     _check(rc)
     return kv_valid
+
+
+def vsa_csr_transpose(kv_block_idx, kv_block_cnt, nkv, q_ld, q_block_idx=None, q_block_cnt=None, overflow=None,
+                      stream=None):
+    """Q-direction block CSR for the backward pass: (q_block_idx [B,H,nkv,q_ld],
+    q_block_cnt [B,H,nkv]), rows listing ascending query tiles."""
+    _dev(kv_block_idx, "kv_block_idx", torch.int32, 4)
+    _dev(kv_block_cnt, "kv_block_cnt", torch.int32, 3)
+    B, H, NQ, LD = kv_block_idx.shape
+    if tuple(kv_block_cnt.shape) != (B, H, NQ):
+        raise ValueError("kv_block_cnt must be [B, H, NQ] matching kv_block_idx")
+    dev = kv_block_idx.device
+    if q_block_idx is None:
+        q_block_idx = torch.full((B, H, nkv, q_ld), -1, dtype=torch.int32, device=dev)
+    if q_block_cnt is None:
+        q_block_cnt = torch.empty((B, H, nkv), dtype=torch.int32, device=dev)
+    _dev(q_block_idx, "q_block_idx", torch.int32, 4)
+    _dev(q_block_cnt, "q_block_cnt", torch.int32, 3)
+    if tuple(q_block_idx.shape) != (B, H, nkv, q_ld) or tuple(q_block_cnt.shape) != (B, H, nkv):
+        raise ValueError("output shapes must be [B,H,nkv,q_ld] and [B,H,nkv]")
+    ovf_ptr = None
+    if overflow is not None:
+        _dev(overflow, "overflow", torch.int32, 1)
+        ovf_ptr = overflow.data_ptr()
+    rc = load_library().vsa_csr_transpose(kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(), B, H, NQ, nkv, LD,
+                                          q_block_idx.data_ptr(), q_ld, q_block_cnt.data_ptr(), ovf_ptr,
+                                          _stream_ptr(stream, dev))
+    _check(rc)
+    return q_block_idx, q_block_cnt
+
+
+def vsa_attn_bwd(q, k, v, o, lse, dout, kv_block_idx, kv_block_cnt, q_block_idx, q_block_cnt, block_q, block_kv,
+                 scale=None, dq=None, dk=None, dv=None, stream=None, kv_valid=None):
+    """Backward pass of vsa_attn_fwd; returns (dq, dk, dv), bf16 [B, S, H, D].
+
+    ``o`` and ``lse`` are the forward's outputs; ``q_block_idx`` /
+    ``q_block_cnt`` the transposed CSR from ``vsa_csr_transpose``."""
+    B, S, H, D, o, lse = _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse)
+    _dev(dout, "dout", torch.bfloat16, 4)
+    if dout.shape != q.shape:
+        raise ValueError("dout must match q")
+    nkv = S // block_kv
+    _dev(q_block_idx, "q_block_idx", torch.int32, 4)
+    _dev(q_block_cnt, "q_block_cnt", torch.int32, 3)
+    if tuple(q_block_idx.shape[:3]) != (B, H, nkv) or tuple(q_block_cnt.shape) != (B, H, nkv):
+        raise ValueError(f"q_block_idx must be [B,H,{nkv},q_ld] and q_block_cnt [B,H,{nkv}]")
+    grads = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty_like(q)
+        _dev(t, name, torch.bfloat16, 4)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} must match q")
+        grads.append(t)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = load_library().vsa_attn_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+        kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(), kv_block_idx.shape[3], q_block_idx.data_ptr(),
+        q_block_cnt.data_ptr(), q_block_idx.shape[3], _valid_ptr(kv_valid, S, block_kv, q.device), B, S, H, D,
+        block_q, block_kv, float(scale), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
+        _stream_ptr(stream, q.device))
+    _check(rc)
+    return tuple(grads)
 
 
 def vsa_release() -> None:

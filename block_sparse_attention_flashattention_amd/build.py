@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvsa_attn.so")
-SOURCES = ["attn_fwd.hip", "attn_fwd_pp.hip", "attn_fwd_2s.hip", "attn_fwd_4s.hip", "frontend.hip", "capi.hip"]
+SOURCES = ["attn_fwd.hip", "attn_fwd_pp.hip", "attn_fwd_2s.hip", "attn_fwd_4s.hip", "attn_bwd.hip", "frontend.hip",
+           "capi.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

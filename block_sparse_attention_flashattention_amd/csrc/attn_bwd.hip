@@ -1,0 +1,513 @@
+// Block-sparse attention backward pass on gfx950: dQ, dK and dV.
+//
+// What is computed: the gradients of FastVideo page "[perf] Add fine-grained
+// FA4 VSA kernels", ref_masked_sdpa_fp32 (the masked softmax attention the
+// forward computes). With P the masked row softmax of scale * Q K^T
+// (recomputed from the forward's LSE), O the forward output and dO given:
+//     D_i  = dO_i . O_i
+//     dS   = P * (dO V^T - D)          (elementwise, per row i)
+//     dV   = P^T dO,   dK = scale * dS^T Q,   dQ = scale * dS K
+//
+// Schedule (no atomics, deterministic): dK and dV come from one workgroup per
+// KV tile that walks the query tiles selecting it (the Q-direction lists of
+// the page's FA4 block_sparsity.py backward) and accumulates in registers;
+// dQ comes from one workgroup per query tile that walks the forward list, as
+// the split-dQ form of the FlashAttention backward does. Both recompute P.
+//
+// Operand layouts follow the forward (wave_engine.h): 32x32x16 bf16 MFMA,
+// lane l / register r of a result holds row 8*(r/4) + 4*(l/32) + r%4 and
+// column l%32. A result used as a B operand keeps that row order in its k
+// slots, and the A operand that meets it is read with transposing LDS reads
+// whose rows follow the same order. Tiles read both by rows and transposed
+// (Q and dO for dK/dV, K for dQ) use the swz_d swizzle.
+#include "device_common.h"
+#include "vsa_internal.h"
+#include "wave_engine.h"
+
+namespace vsa {
+namespace {
+
+using namespace dev;
+
+constexpr int kIdxCapBwd = 8192;  // list entries staged in LDS
+
+// ---------------------------------------------------------------- preprocess
+// aux[0][(b*H + h)*S + i] = D_i = dO_i . O_i;  aux[1][...] = LSE_i * log2(e)
+// (+inf for an empty row, so that exp2(s - lse2) = 0).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+                                                       const float* __restrict__ lse, float* __restrict__ aux,
+                                                       int n_rows, int S, int H) {
+    constexpr int LPR = D / 8;     // lanes per token row (16 bytes each)
+    constexpr int RPW = 64 / LPR;  // rows per wave
+    const int lane = threadIdx.x & 63;
+    const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;  // (b*S + i)*H + h
+    float acc = 0.0f;
+    if (row < n_rows) {
+        const int64_t off = row * D + (lane % LPR) * 8;
+        const u32x4 a = *(const u32x4*)(o + off);
+        const u32x4 g = *(const u32x4*)(dout + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float a0 = __builtin_bit_cast(float, a[e] << 16), a1 = __builtin_bit_cast(float, a[e] & 0xffff0000u);
+            const float g0 = __builtin_bit_cast(float, g[e] << 16), g1 = __builtin_bit_cast(float, g[e] & 0xffff0000u);
+            acc = fmaf(a0, g0, acc);
+            acc = fmaf(a1, g1, acc);
+        }
+    }
+#pragma unroll
+    for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
+    if (row < n_rows && lane % LPR == 0) {
+        const int h = (int)(row % H);
+        const int64_t bi = row / H;  // b*S + i
+        const int64_t i = bi % S, b = bi / S;
+        const int64_t dst = (b * H + h) * S + i;
+        aux[dst] = acc;
+        const float l = lse[dst];
+        aux[(int64_t)n_rows + dst] = l == -__builtin_inff() ? __builtin_inff() : l * 1.4426950408889634f;
+    }
+}
+
+// Per-lane LDS offsets for the operand reads of one tile layout.
+template <int D>
+struct OperandOffsets {
+    static constexpr int ROW_BYTES = D * 2;
+    static constexpr int NC = D / 8;
+    static constexpr int DC = D / 16;
+    static constexpr int DB = D / 32;
+    int row[DC];   // 16-byte row read of row l%32, chunk 2c + hi (add 32*ROW_BYTES per 32-row block)
+    int trl[DB];   // transposing read, rows 4*hi + (0..3) of a 16-row group, d block db
+    int trh[DB];   // the same 8 rows further down
+    template <int LAYOUT>
+    __device__ __forceinline__ void init(int lane) {
+        const int l32 = lane & 31, hi = lane >> 5;
+        auto swz = [](int r) {
+            if constexpr (LAYOUT == kLayoutD) return swz_d<NC>(r);
+            else if constexpr (LAYOUT == kLayoutV) return swz_v<NC>(r);
+            else return swz_k<NC>(r);
+        };
+#pragma unroll
+        for (int c = 0; c < DC; ++c) row[c] = l32 * ROW_BYTES + (((2 * c + hi) ^ swz(l32)) << 4);
+        const int grp16 = lane >> 4, i = lane & 15;
+        const int r0 = (grp16 >> 1) * 4 + (i >> 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int d = db * 32 + (grp16 & 1) * 16 + 4 * (i & 3);
+            trl[db] = r0 * ROW_BYTES + (((d >> 3) ^ swz(r0)) << 4) + (d & 7) * 2;
+            trh[db] = (r0 + 8) * ROW_BYTES + (((d >> 3) ^ swz(r0 + 8)) << 4) + (d & 7) * 2;
+        }
+    }
+};
+
+// A operand of 16 k slots taken from rows g*16 + {4*hi + 0..3, 8 + 4*hi + 0..3}
+// of the tile at byte offset base, d block db (transposing reads).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const char* smem, int base, const OperandOffsets<D>& off, int db, int g) {
+    const char* p = smem + base + g * 16 * OperandOffsets<D>::ROW_BYTES;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + off.trl[db]));
+    const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + off.trh[db]));
+    return __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// B operand registers of 32 token rows: lane l holds row l%32, d = 16c + 8*hi + (0..7).
+template <int DC>
+__device__ __forceinline__ void load_rows(bf16x8 (&reg)[DC], const uint16_t* row_ptr, int hi) {
+    const uint16_t* p = row_ptr + hi * 8;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) reg[c] = *(const bf16x8*)(p + c * 16);
+}
+
+// Store a transposed accumulator (rows d, column = this lane's token row) as
+// bf16 times mul into the token row at dst (d = 0 of the row).
+template <int DB>
+__device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16 (&acc)[DB], float mul, int hi) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+            const int d0 = db * 32 + jg * 8 + hi * 4;
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[db][jg * 4 + 0] * mul, acc[db][jg * 4 + 1] * mul);
+            w[1] = pack_bf16x2(acc[db][jg * 4 + 2] * mul, acc[db][jg * 4 + 3] * mul);
+            *(u32x2*)(dst + d0) = w;
+        }
+    }
+}
+
+struct BwdParams {
+    const uint16_t *q, *k, *v, *dout;
+    const float* aux;         // [2][B*H*S]: D, then LSE*log2(e)
+    const int32_t* idx;       // forward CSR [B,H,nq,ld]
+    const int32_t* cnt;
+    const int32_t* qidx;      // Q-direction CSR [B,H,nkv,q_ld]
+    const int32_t* qcnt;
+    const int32_t* kv_valid;  // [nkv] or null
+    const int32_t* work_q;    // dQ work list (flat (b*H + h)*nq + p)
+    const int32_t* work_kv;   // dK/dV work list (flat (b*H + h)*nkv + n)
+    uint16_t *dq, *dk, *dv;
+    int32_t n_items_q, n_items_kv;
+    int32_t S, H, nq, nkv, ld, q_ld, block_q, block_kv;
+    int32_t n_rows;           // B*H*S
+    float scale, scale_log2;
+};
+
+// ----------------------------------------------------------------------- dQ
+// One workgroup per query tile of BQ rows, BQ/32 waves of 32 rows. The KV
+// list is walked in 64-key steps; per step K (swz_d: row reads for S^T = K
+// Q^T, transposing reads for dQ^T += K^T dS^T) and V (row reads for dP^T =
+// V dO^T) are fetched for the next step while this one is computed.
+template <int BQ, int D, bool PARTIAL>
+__global__ __launch_bounds__(BQ * 2) void vsa_bwd_dq_kernel(BwdParams prm) {
+    constexpr int NW = BQ / 32;
+    constexpr int SUB = 64;
+    using G = TileGeom<SUB, D>;
+    using F = TileFetch<SUB, D, NW>;
+    using OO = OperandOffsets<D>;
+    constexpr int DC = D / 16, DB = D / 32, NB = SUB / 32, KC = SUB / 16;
+    constexpr int STAGE = 2 * G::TILE;  // K, V
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + kIdxCapBwd * 4];
+
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wi = xcd_contiguous_block();
+    if (wi >= prm.n_items_q) return;
+    const int item = prm.work_q ? prm.work_q[wi] : wi;
+    if (item < 0 || item >= prm.n_items_q) return;
+    const int p = item % prm.nq, bh = item / prm.nq, h = bh % prm.H, b = bh / prm.H;
+    const int S = prm.S, nkv = prm.nkv, block_kv = prm.block_kv;
+    const int64_t tok_stride = (int64_t)prm.H * D;
+    const int tok_bytes = (int)(tok_stride * 2);
+    const int32_t* irow = prm.idx + (int64_t)item * prm.ld;
+    const int ldc = prm.ld < kIdxCapBwd ? prm.ld : kIdxCapBwd;
+    int n = prm.cnt[item];
+    n = n < 0 ? 0 : (n > ldc ? ldc : n);
+    const int R = block_kv / SUB;
+    const int steps = n * R;
+    const int q0 = p * BQ + wave * 32;
+    const int64_t qrow = ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D;
+
+    bf16x8 qreg[DC], doreg[DC];
+    load_rows<DC>(qreg, prm.q + qrow, hi);
+    load_rows<DC>(doreg, prm.dout + qrow, hi);
+    const int64_t arow = (int64_t)bh * S + q0 + l32;
+    const float dval = prm.aux[arow];
+    const float lse2 = prm.aux[(int64_t)prm.n_rows + arow];
+
+    int* lidx = (int*)(smem + 2 * STAGE);
+    for (int i = tid; i < ldc; i += BQ * 2) lidx[i] = stage_entry<PARTIAL>(irow[i], nkv, block_kv, prm.kv_valid);
+    // consume every loaded register before the first tile load (the compiler's
+    // wait counting does not see the inline-asm tile loads)
+#pragma unroll
+    for (int c = 0; c < DC; ++c) asm volatile("" ::"v"(qreg[c]), "v"(doreg[c]));
+    asm volatile("" ::"v"(dval), "v"(lse2));
+    wait_global_loads();
+    lds_barrier();
+
+    OO ko, vo;
+    ko.template init<kLayoutD>(lane);
+    vo.template init<kLayoutK>(lane);
+    const F fetch(smem, wave, lane, tok_bytes);
+    const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    auto entry = [&](int j) { return __builtin_amdgcn_readfirstlane(lidx[j / R]); };
+    auto step_ptr = [&](const char* base, int j) {
+        const int t = entry_tile<PARTIAL>(entry(j));
+        const int64_t row0 = (int64_t)(t >= 0 && t < nkv ? t : 0) * block_kv + (j % R) * SUB;
+        return uniform_ptr(base + row0 * tok_bytes);
+    };
+    auto fetch_step = [&](int j) {
+        const int st = (j & 1) * STAGE;
+        fetch.all(st, step_ptr(kbase, j), tok_bytes, kLayoutD);
+        fetch.all(st + G::TILE, step_ptr(vbase, j), tok_bytes, kLayoutK);
+    };
+
+    f32x16 dq[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+
+    if (steps > 0) fetch_step(0);
+    for (int j = 0; j < steps; ++j) {
+        wait_global_loads();
+        lds_barrier();  // step j's tiles are in LDS; step j-1's buffers are free
+        if (j + 1 < steps) fetch_step(j + 1);
+        const int e = entry(j);
+        const int t = entry_tile<PARTIAL>(e);
+        int nv = (t >= 0 && t < nkv) ? entry_keys<PARTIAL>(e, block_kv) - (j % R) * SUB : 0;
+        nv = nv < 0 ? 0 : (nv > SUB ? SUB : nv);
+        if (nv == 0) continue;  // uniform: every wave skips the same step
+        const int kb = (j & 1) * STAGE, vb = kb + G::TILE;
+        f32x16 s[NB], dp[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            s[nb] = f32x16{};
+            dp[nb] = f32x16{};
+#pragma unroll
+            for (int c = 0; c < DC; ++c) {
+                const bf16x8 ka = *(const bf16x8*)(smem + kb + ko.row[c] + nb * 32 * OO::ROW_BYTES);
+                s[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[c], s[nb], 0, 0, 0);
+                const bf16x8 va = *(const bf16x8*)(smem + vb + vo.row[c] + nb * 32 * OO::ROW_BYTES);
+                dp[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, doreg[c], dp[nb], 0, 0, 0);
+            }
+        }
+        // dS^T = P^T (dP^T - D), P^T = exp2(S^T * scale*log2e - LSE*log2e); keys at or past nv do not exist
+        bf16x8 pk[KC];
+#pragma unroll
+        for (int ch = 0; ch < KC; ++ch) {
+            const int nb = ch >> 1, half = ch & 1;
+            u32x4 w;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                float ds[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int r = half * 8 + 2 * e2 + u;
+                    const int key = nb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    const float pr = fast_exp2(fmaf(s[nb][r], prm.scale_log2, -lse2));
+                    ds[u] = (PARTIAL && key >= nv) ? 0.0f : pr * (dp[nb][r] - dval);
+                }
+                w[e2] = pack_bf16x2(ds[0], ds[1]);
+            }
+            pk[ch] = __builtin_bit_cast(bf16x8, w);
+        }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int g = 0; g < KC; ++g)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(smem, kb, ko, db, g), pk[g], dq[db], 0,
+                                                                 0, 0);
+    }
+    store_rows<DB>(prm.dq + qrow, dq, prm.scale, hi);
+}
+
+// -------------------------------------------------------------------- dK, dV
+// One workgroup per KV tile of BKV rows, BKV/32 waves of 32 key rows; K and V
+// rows stay in registers. The tile's Q-direction list is walked in 64-row
+// query steps: Q and dO (swz_d: row reads for S = Q K^T and dP = dO V^T,
+// transposing reads for dK^T += Q^T dS and dV^T += dO^T P) and the rows'
+// D and LSE are fetched for the next step while this one is computed.
+template <int BKV, int D, bool PARTIAL>
+__global__ __launch_bounds__(BKV * 2) void vsa_bwd_dkv_kernel(BwdParams prm) {
+    constexpr int NW = BKV / 32;
+    constexpr int QS = 64;  // query rows per step
+    using G = TileGeom<QS, D>;
+    using F = TileFetch<QS, D, NW>;
+    using OO = OperandOffsets<D>;
+    constexpr int DC = D / 16, DB = D / 32;
+    constexpr int STAGE = 2 * G::TILE + 2 * QS * 4;  // Q, dO, D[QS], lse2[QS]
+    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + kIdxCapBwd * 4];
+
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wi = xcd_contiguous_block();
+    if (wi >= prm.n_items_kv) return;
+    const int item = prm.work_kv ? prm.work_kv[wi] : wi;
+    if (item < 0 || item >= prm.n_items_kv) return;
+    const int nt = item % prm.nkv, bh = item / prm.nkv, h = bh % prm.H, b = bh / prm.H;
+    const int S = prm.S, nq = prm.nq, block_q = prm.block_q;
+    const int64_t tok_stride = (int64_t)prm.H * D;
+    const int tok_bytes = (int)(tok_stride * 2);
+    const int32_t* qrow_list = prm.qidx + (int64_t)item * prm.q_ld;
+    const int ldc = prm.q_ld < kIdxCapBwd ? prm.q_ld : kIdxCapBwd;
+    int n = prm.qcnt[item];
+    n = n < 0 ? 0 : (n > ldc ? ldc : n);
+    const int RQ = block_q / QS;
+    const int steps = n * RQ;
+    const int kv0 = nt * BKV + wave * 32;
+    const int64_t krow = ((int64_t)b * S + kv0 + l32) * tok_stride + (int64_t)h * D;
+    // valid keys of this wave's column (partial tiles)
+    int nv_tile = BKV;
+    if constexpr (PARTIAL) {
+        const int nvt = prm.kv_valid[nt];
+        nv_tile = nvt < 0 ? 0 : (nvt > BKV ? BKV : nvt);
+    }
+    const bool key_ok = wave * 32 + l32 < nv_tile;
+
+    bf16x8 kreg[DC], vreg[DC];
+    load_rows<DC>(kreg, prm.k + krow, hi);
+    load_rows<DC>(vreg, prm.v + krow, hi);
+
+    int* lq = (int*)(smem + 2 * STAGE);
+    for (int i = tid; i < ldc; i += BKV * 2) {
+        const int m = qrow_list[i];
+        lq[i] = (m >= 0 && m < nq) ? m : -1;
+    }
+#pragma unroll
+    for (int c = 0; c < DC; ++c) asm volatile("" ::"v"(kreg[c]), "v"(vreg[c]));
+    wait_global_loads();
+    lds_barrier();
+
+    OO qo;
+    qo.template init<kLayoutD>(lane);
+    const F fetch(smem, wave, lane, tok_bytes);
+    const char* qbase = (const char*)(prm.q + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    const char* dbase = (const char*)(prm.dout + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    const float* dvec = prm.aux + (int64_t)bh * S;
+    const float* lvec = prm.aux + (int64_t)prm.n_rows + (int64_t)bh * S;
+    auto entry = [&](int j) { return __builtin_amdgcn_readfirstlane(lq[j / RQ]); };
+    auto fetch_step = [&](int j) {
+        const int m = entry(j);
+        const int r0 = (m >= 0 ? m : 0) * block_q + (j % RQ) * QS;  // first query row of the step
+        const int st = (j & 1) * STAGE;
+        fetch.all(st, uniform_ptr(qbase + (int64_t)r0 * tok_bytes), tok_bytes, kLayoutD);
+        fetch.all(st + G::TILE, uniform_ptr(dbase + (int64_t)r0 * tok_bytes), tok_bytes, kLayoutD);
+        if (wave == 0 && lane < QS / 4) {
+            // D and lse2 of the step's rows: 256 bytes each, 16 bytes per lane
+            const uint32_t dst = fetch.lds0 + (uint32_t)(st + 2 * G::TILE);
+            lds_dma16(dvec + r0, (uint32_t)(lane * 16), dst);
+            lds_dma16(lvec + r0, (uint32_t)(lane * 16), dst + QS * 4);
+        }
+    };
+
+    f32x16 dk[DB], dv[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        dk[db] = f32x16{};
+        dv[db] = f32x16{};
+    }
+
+    if (steps > 0) fetch_step(0);
+    for (int j = 0; j < steps; ++j) {
+        wait_global_loads();
+        lds_barrier();
+        if (j + 1 < steps) fetch_step(j + 1);
+        if (entry(j) < 0) continue;  // uniform
+        const int qb = (j & 1) * STAGE, ob = qb + G::TILE, ab = qb + 2 * G::TILE;
+#pragma unroll
+        for (int qs = 0; qs < QS / 32; ++qs) {
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int c = 0; c < DC; ++c) {
+                const bf16x8 qa = *(const bf16x8*)(smem + qb + qo.row[c] + qs * 32 * OO::ROW_BYTES);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[c], s, 0, 0, 0);
+                const bf16x8 oa = *(const bf16x8*)(smem + ob + qo.row[c] + qs * 32 * OO::ROW_BYTES);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vreg[c], dp, 0, 0, 0);
+            }
+            // rows q = qs*32 + 8*(r/4) + 4*hi + r%4: their D and lse2, four at a time
+            bf16x8 pp[2], ps[2];
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                u32x4 wp, wsd;
+#pragma unroll
+                for (int k4 = 0; k4 < 2; ++k4) {
+                    const int qr = qs * 32 + 8 * (half * 2 + k4) + 4 * hi;
+                    const f32x4 dd = *(const f32x4*)(smem + ab + qr * 4);
+                    const f32x4 ll = *(const f32x4*)(smem + ab + QS * 4 + qr * 4);
+                    float pv[4], dsv[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int r = (half * 2 + k4) * 4 + u;
+                        const float pr = fast_exp2(fmaf(s[r], prm.scale_log2, -ll[u]));
+                        const bool off = PARTIAL && !key_ok;
+                        pv[u] = off ? 0.0f : pr;
+                        dsv[u] = off ? 0.0f : pr * (dp[r] - dd[u]);
+                    }
+                    wp[k4 * 2] = pack_bf16x2(pv[0], pv[1]);
+                    wp[k4 * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
+                    wsd[k4 * 2] = pack_bf16x2(dsv[0], dsv[1]);
+                    wsd[k4 * 2 + 1] = pack_bf16x2(dsv[2], dsv[3]);
+                }
+                pp[half] = __builtin_bit_cast(bf16x8, wp);
+                ps[half] = __builtin_bit_cast(bf16x8, wsd);
+            }
+            // dV^T += dO^T P, dK^T += Q^T dS over the 32 rows (two 16-row k chunks)
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(smem, ob, qo, db, qs * 2 + g), pp[g],
+                                                                     dv[db], 0, 0, 0);
+                    dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(smem, qb, qo, db, qs * 2 + g), ps[g],
+                                                                     dk[db], 0, 0, 0);
+                }
+        }
+    }
+    store_rows<DB>(prm.dk + krow, dk, prm.scale, hi);
+    store_rows<DB>(prm.dv + krow, dv, 1.0f, hi);
+}
+
+template <int D>
+hipError_t launch_prep(const uint16_t* o, const uint16_t* dout, const float* lse, float* aux, int n_rows, int S, int H,
+                       hipStream_t stream) {
+    constexpr int RPW = 64 / (D / 8);
+    const int rows_per_block = 4 * RPW;
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((n_rows + rows_per_block - 1) / rows_per_block), dim3(256), 0, stream,
+                       o, dout, lse, aux, n_rows, S, H);
+    return hipGetLastError();
+}
+
+template <int D, bool PARTIAL>
+hipError_t launch_dq_d(const BwdParams& p, hipStream_t stream) {
+    if (p.n_items_q <= 0) return hipSuccess;
+    switch (p.block_q) {
+        case 64: hipLaunchKernelGGL((vsa_bwd_dq_kernel<64, D, PARTIAL>), dim3(p.n_items_q), dim3(128), 0, stream, p); break;
+        case 128: hipLaunchKernelGGL((vsa_bwd_dq_kernel<128, D, PARTIAL>), dim3(p.n_items_q), dim3(256), 0, stream, p); break;
+        case 256: hipLaunchKernelGGL((vsa_bwd_dq_kernel<256, D, PARTIAL>), dim3(p.n_items_q), dim3(512), 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int D, bool PARTIAL>
+hipError_t launch_dkv_d(const BwdParams& p, hipStream_t stream) {
+    if (p.n_items_kv <= 0) return hipSuccess;
+    switch (p.block_kv) {
+        case 64: hipLaunchKernelGGL((vsa_bwd_dkv_kernel<64, D, PARTIAL>), dim3(p.n_items_kv), dim3(128), 0, stream, p); break;
+        case 128: hipLaunchKernelGGL((vsa_bwd_dkv_kernel<128, D, PARTIAL>), dim3(p.n_items_kv), dim3(256), 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_supported(int block_q, int block_kv, int head_dim) {
+    return (block_q == 64 || block_q == 128 || block_q == 256) && (block_kv == 64 || block_kv == 128) &&
+           (head_dim == 64 || head_dim == 128);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+    BwdParams p;
+    p.q = a.q;
+    p.k = a.k;
+    p.v = a.v;
+    p.dout = a.dout;
+    p.aux = a.aux;
+    p.idx = a.idx;
+    p.cnt = a.cnt;
+    p.qidx = a.qidx;
+    p.qcnt = a.qcnt;
+    p.kv_valid = a.kv_valid;
+    p.work_q = a.work_q;
+    p.work_kv = a.work_kv;
+    p.dq = a.dq;
+    p.dk = a.dk;
+    p.dv = a.dv;
+    p.S = a.S;
+    p.H = a.H;
+    p.nq = a.S / a.block_q;
+    p.nkv = a.S / a.block_kv;
+    p.ld = a.ld;
+    p.q_ld = a.q_ld;
+    p.block_q = a.block_q;
+    p.block_kv = a.block_kv;
+    p.n_rows = a.B * a.H * a.S;
+    p.n_items_q = a.B * a.H * p.nq;
+    p.n_items_kv = a.B * a.H * p.nkv;
+    p.scale = a.scale;
+    p.scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+    hipError_t e = a.D == 128 ? launch_prep<128>(a.o, a.dout, a.lse, a.aux, p.n_rows, a.S, a.H, stream)
+                              : launch_prep<64>(a.o, a.dout, a.lse, a.aux, p.n_rows, a.S, a.H, stream);
+    if (e != hipSuccess) return e;
+    const bool partial = a.kv_valid != nullptr;
+    if (a.D == 128) {
+        e = partial ? launch_dkv_d<128, true>(p, stream) : launch_dkv_d<128, false>(p, stream);
+        if (e != hipSuccess) return e;
+        return partial ? launch_dq_d<128, true>(p, stream) : launch_dq_d<128, false>(p, stream);
+    }
+    e = partial ? launch_dkv_d<64, true>(p, stream) : launch_dkv_d<64, false>(p, stream);
+    if (e != hipSuccess) return e;
+    return partial ? launch_dq_d<64, true>(p, stream) : launch_dq_d<64, false>(p, stream);
+}
+
+}  // namespace vsa

@@ -97,15 +97,16 @@ struct DeviceBuffer {
     size_t bytes = 0;
 };
 std::mutex g_buf_mutex;
-std::vector<DeviceBuffer> g_bufs;
+std::vector<DeviceBuffer> g_bufs;      // forward work list
+std::vector<DeviceBuffer> g_bwd_bufs;  // backward scratch (D, LSE*log2 e, two work lists)
 
-int32_t worklist_buffer(size_t bytes, int32_t** out) {
+int32_t device_buffer(std::vector<DeviceBuffer>& bufs, size_t bytes, void** out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lock(g_buf_mutex);
-    if ((int)g_bufs.size() <= dev) g_bufs.resize(dev + 1);
-    DeviceBuffer& b = g_bufs[dev];
+    if ((int)bufs.size() <= dev) bufs.resize(dev + 1);
+    DeviceBuffer& b = bufs[dev];
     if (b.bytes < bytes) {
         if (b.ptr) {
             e = hipFree(b.ptr);  // implicitly waits for work still using it
@@ -114,11 +115,18 @@ int32_t worklist_buffer(size_t bytes, int32_t** out) {
             if (e != hipSuccess) return hip_fail(e, "hipFree");
         }
         e = hipMalloc(&b.ptr, bytes);
-        if (e != hipSuccess) return hip_fail(e, "hipMalloc(work list)");
+        if (e != hipSuccess) return hip_fail(e, "hipMalloc(library buffer)");
         b.bytes = bytes;
     }
-    *out = (int32_t*)b.ptr;
+    *out = b.ptr;
     return VSA_OK;
+}
+
+int32_t worklist_buffer(size_t bytes, int32_t** out) {
+    void* p = nullptr;
+    int32_t rc = device_buffer(g_bufs, bytes, &p);
+    *out = (int32_t*)p;
+    return rc;
 }
 
 }  // namespace
@@ -230,6 +238,28 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
     return VSA_OK;
 }
 
+int32_t vsa_csr_transpose(const int32_t* kv_block_idx, const int32_t* kv_block_cnt, int32_t batch, int32_t heads,
+                          int32_t nq, int32_t nkv, int32_t idx_ld, int32_t* q_block_idx, int32_t q_ld,
+                          int32_t* q_block_cnt, int32_t* overflow, void* stream) {
+    g_last_error[0] = 0;
+    VSA_REQUIRE(kv_block_idx && kv_block_cnt && q_block_idx && q_block_cnt, VSA_ERR_INVALID_ARG, "null pointer");
+    VSA_REQUIRE(batch >= 1 && heads >= 1 && nq >= 1 && nkv >= 1, VSA_ERR_INVALID_ARG,
+                "batch, heads, nq and nkv must be >= 1");
+    VSA_REQUIRE(idx_ld >= 1 && q_ld >= 1, VSA_ERR_INVALID_ARG, "idx_ld and q_ld must be >= 1");
+    VSA_REQUIRE(nq <= 32 * vsa::kTransposeMaxWords, VSA_ERR_UNSUPPORTED, "nq %d exceeds %d", nq,
+                32 * vsa::kTransposeMaxWords);
+    VSA_REQUIRE((int64_t)batch * heads * nq * idx_ld <= INT32_MAX &&
+                    (int64_t)batch * heads * nkv * q_ld <= INT32_MAX && (int64_t)nq * idx_ld <= INT32_MAX,
+                VSA_ERR_INVALID_ARG, "problem too large");
+    VSA_REQUIRE(aligned(kv_block_idx, 4) && aligned(kv_block_cnt, 4) && aligned(q_block_idx, 4) &&
+                    aligned(q_block_cnt, 4) && aligned(overflow, 4),
+                VSA_ERR_INVALID_ARG, "index buffers must be 4-byte aligned");
+    hipError_t e = vsa::launch_csr_transpose(kv_block_idx, kv_block_cnt, batch * heads, nq, nkv, idx_ld, q_block_idx,
+                                             q_ld, q_block_cnt, overflow, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "csr_transpose launch");
+    return VSA_OK;
+}
+
 int32_t vsa_expand_valid(const int32_t* vbs, int32_t nkv_logical, int32_t logical_block_kv, int32_t block_kv,
                          int32_t* kv_valid, void* stream) {
     g_last_error[0] = 0;
@@ -247,12 +277,81 @@ int32_t vsa_expand_valid(const int32_t* vbs, int32_t nkv_logical, int32_t logica
     return VSA_OK;
 }
 
+int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     const int32_t* kv_block_idx, const int32_t* kv_block_cnt, int32_t idx_ld,
+                     const int32_t* q_block_idx, const int32_t* q_block_cnt, int32_t q_ld, const int32_t* kv_valid,
+                     int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim, int32_t block_q,
+                     int32_t block_kv, float scale, void* dq, void* dk, void* dv, void* stream) {
+    g_last_error[0] = 0;
+    int32_t rc = check_fwd(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld,
+                           block_q, block_kv, scale, o, lse);
+    if (rc != VSA_OK) return rc;
+    VSA_REQUIRE(dout && dq && dk && dv && q_block_idx && q_block_cnt, VSA_ERR_INVALID_ARG, "null pointer");
+    VSA_REQUIRE(aligned(dout, 16) && aligned(dq, 16) && aligned(dk, 16) && aligned(dv, 16), VSA_ERR_INVALID_ARG,
+                "dout, dq, dk, dv must be 16-byte aligned");
+    VSA_REQUIRE(aligned(q_block_idx, 4) && aligned(q_block_cnt, 4), VSA_ERR_INVALID_ARG,
+                "q_block_idx, q_block_cnt must be 4-byte aligned");
+    VSA_REQUIRE(q_ld >= 1 && q_ld <= vsa::kWorklistMaxCnt, VSA_ERR_UNSUPPORTED, "q_ld must be in [1, %d]",
+                vsa::kWorklistMaxCnt);
+    VSA_REQUIRE(idx_ld <= vsa::kWorklistMaxCnt, VSA_ERR_UNSUPPORTED, "idx_ld %d exceeds %d", idx_ld,
+                vsa::kWorklistMaxCnt);
+    VSA_REQUIRE(vsa::bwd_supported(block_q, block_kv, head_dim), VSA_ERR_UNSUPPORTED,
+                "no backward kernel for block_q=%d block_kv=%d head_dim=%d", block_q, block_kv, head_dim);
+    const int64_t rows = (int64_t)batch * heads * seqlen;
+    const int32_t nq = seqlen / block_q, nkv = seqlen / block_kv;
+    const int32_t items_q = batch * heads * nq, items_kv = batch * heads * nkv;
+    void* buf = nullptr;
+    rc = device_buffer(g_bwd_bufs, (size_t)rows * 2 * sizeof(float) + ((size_t)items_q + items_kv) * sizeof(int32_t),
+                       &buf);
+    if (rc != VSA_OK) return rc;
+    float* aux = (float*)buf;
+    int32_t* work_q = (int32_t*)(aux + rows * 2);
+    int32_t* work_kv = work_q + items_q;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = vsa::launch_build_worklist(kv_block_cnt, items_q, nq, idx_ld, work_q, st);
+    if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
+    e = vsa::launch_build_worklist(q_block_cnt, items_kv, nkv, q_ld, work_kv, st);
+    if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
+    vsa::BwdArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.o = (const uint16_t*)o;
+    a.dout = (const uint16_t*)dout;
+    a.lse = lse;
+    a.aux = aux;
+    a.idx = kv_block_idx;
+    a.cnt = kv_block_cnt;
+    a.qidx = q_block_idx;
+    a.qcnt = q_block_cnt;
+    a.kv_valid = kv_valid;
+    a.work_q = work_q;
+    a.work_kv = work_kv;
+    a.dq = (uint16_t*)dq;
+    a.dk = (uint16_t*)dk;
+    a.dv = (uint16_t*)dv;
+    a.B = batch;
+    a.S = seqlen;
+    a.H = heads;
+    a.D = head_dim;
+    a.ld = idx_ld;
+    a.q_ld = q_ld;
+    a.block_q = block_q;
+    a.block_kv = block_kv;
+    a.scale = scale;
+    e = vsa::launch_bwd(a, st);
+    if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
+    return VSA_OK;
+}
+
 void vsa_release(void) {
     std::lock_guard<std::mutex> lock(g_buf_mutex);
-    for (auto& b : g_bufs) {
-        if (b.ptr) (void)hipFree(b.ptr);
-        b.ptr = nullptr;
-        b.bytes = 0;
+    for (auto* v : {&g_bufs, &g_bwd_bufs}) {
+        for (auto& b : *v) {
+            if (b.ptr) (void)hipFree(b.ptr);
+            b.ptr = nullptr;
+            b.bytes = 0;
+        }
     }
 }
 

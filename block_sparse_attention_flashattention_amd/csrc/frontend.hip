@@ -144,6 +144,61 @@ __global__ __launch_bounds__(WAVES * 64) void worklist_kernel(const int32_t* __r
     }
 }
 
+// Q-direction lists for the backward pass (the per-KV-tile lists of the query
+// tiles that select the tile, "transposed from forward" in the FastVideo
+// page's FA4 block_sparsity.py). One workgroup per (batch, head): the
+// selection is marked in an LDS bitmap [KV tile][Q tile], a chunk of KV tiles
+// at a time, then one wave per KV tile lists the set bits in ascending order
+// with ballot + prefix popcount.
+constexpr int kTransposeLdsWords = 16384;  // 64 KB bitmap per chunk
+
+__global__ __launch_bounds__(1024) void csr_transpose_kernel(const int32_t* __restrict__ idx,
+                                                             const int32_t* __restrict__ cnt, int nq, int nkv, int ld,
+                                                             int32_t* __restrict__ q_idx, int q_ld,
+                                                             int32_t* __restrict__ q_cnt,
+                                                             int32_t* __restrict__ overflow) {
+    __shared__ uint32_t bits[kTransposeLdsWords];
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wpr = (nq + 31) / 32;                 // bitmap words per KV tile
+    const int chunk = kTransposeLdsWords / wpr;     // KV tiles per pass (>= 1: host checks wpr)
+    const int32_t* crow = idx + (int64_t)bh * nq * ld;
+    const int32_t* ccnt = cnt + (int64_t)bh * nq;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int n0 = 0; n0 < nkv; n0 += chunk) {
+        const int n1 = min(nkv, n0 + chunk);
+        for (int w = tid; w < (n1 - n0) * wpr; w += 1024) bits[w] = 0u;
+        __syncthreads();
+        for (int e = tid; e < nq * ld; e += 1024) {
+            const int m = e / ld, slot = e % ld;
+            int c = ccnt[m];
+            c = c < 0 ? 0 : (c > ld ? ld : c);
+            if (slot >= c) continue;
+            const int t = crow[e];
+            if (t >= n0 && t < n1) atomicOr(&bits[(t - n0) * wpr + (m >> 5)], 1u << (m & 31));
+        }
+        __syncthreads();
+        for (int n = n0 + wave; n < n1; n += 16) {
+            const uint32_t* row = bits + (n - n0) * wpr;
+            int32_t* orow = q_idx + ((int64_t)bh * nkv + n) * q_ld;
+            int running = 0;
+            for (int base = 0; base < nq; base += 64) {
+                const int m = base + lane;
+                const bool sel = m < nq && ((row[m >> 5] >> (m & 31)) & 1u);
+                const uint64_t bal = __ballot(sel);
+                const int pos = running + __popcll(bal & below);
+                if (sel && pos < q_ld) orow[pos] = m;
+                running += __popcll(bal);
+            }
+            if (lane == 0) {
+                q_cnt[(int64_t)bh * nkv + n] = running;
+                if (running > q_ld && overflow) *overflow = 1;
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // Valid keys per physical KV tile from valid tokens per logical KV block:
 // tile r of block T keeps clamp(vbs[T] - r*block_kv, 0, block_kv).
 __global__ void expand_valid_kernel(const int32_t* vbs, int n_out, int kv_ratio, int block_kv, int32_t* out) {
@@ -177,6 +232,14 @@ hipError_t launch_build_worklist(const int32_t* cnt, int n_items, int segment, i
         hipLaunchKernelGGL((worklist_kernel<1, 8192, 13>), dim3(n_seg), dim3(64), 0, stream, cnt, segment, max_cnt,
                            work);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_csr_transpose(const int32_t* idx, const int32_t* cnt, int batch_heads, int nq, int nkv, int ld,
+                                int32_t* q_idx, int q_ld, int32_t* q_cnt, int32_t* overflow, hipStream_t stream) {
+    if (batch_heads <= 0 || nkv <= 0) return hipSuccess;
+    hipLaunchKernelGGL(csr_transpose_kernel, dim3(batch_heads), dim3(1024), 0, stream, idx, cnt, nq, nkv, ld, q_idx,
+                       q_ld, q_cnt, overflow);
     return hipGetLastError();
 }
 

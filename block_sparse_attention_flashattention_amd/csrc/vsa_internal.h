@@ -39,12 +39,33 @@ hipError_t launch_fwd_4s(int block_kv, int head_dim, const FwdParams& p, hipStre
 // Whether launch_fwd has a kernel for this configuration.
 bool fwd_supported(int block_q, int block_kv, int head_dim);
 
+// Arguments of the backward pass (attn_bwd.hip). aux: [2 * B*H*S] fp32
+// scratch (D, LSE*log2 e); work lists as for the forward.
+struct BwdArgs {
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float* lse;
+    float* aux;
+    const int32_t *idx, *cnt;    // forward CSR
+    const int32_t *qidx, *qcnt;  // Q-direction CSR
+    const int32_t* kv_valid;
+    const int32_t *work_q, *work_kv;
+    uint16_t *dq, *dk, *dv;
+    int32_t B, S, H, D, ld, q_ld, block_q, block_kv;
+    float scale;
+};
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+bool bwd_supported(int block_q, int block_kv, int head_dim);
+
 // Front-end launches (frontend.hip).
 hipError_t launch_mask_to_csr(const uint8_t* mask, int batch, int heads, int nq_logical, int nkv_logical,
                               int q_ratio, int kv_ratio, int nq_physical, int32_t* idx, int ld, int32_t* cnt,
                               int32_t* overflow, hipStream_t stream);
 hipError_t launch_build_worklist(const int32_t* cnt, int n_items, int segment, int max_cnt, int32_t* work,
                                  hipStream_t stream);
+// Q-direction CSR for the backward pass; nq must be <= 32 * kTransposeMaxWords.
+hipError_t launch_csr_transpose(const int32_t* idx, const int32_t* cnt, int batch_heads, int nq, int nkv, int ld,
+                                int32_t* q_idx, int q_ld, int32_t* q_cnt, int32_t* overflow, hipStream_t stream);
+constexpr int kTransposeMaxWords = 16384;
 hipError_t launch_expand_valid(const int32_t* vbs, int nkv_logical, int kv_ratio, int block_kv, int32_t* kv_valid,
                                hipStream_t stream);
 

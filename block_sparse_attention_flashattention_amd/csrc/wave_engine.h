@@ -44,6 +44,20 @@ __device__ __forceinline__ int swz_v(int row) {
     else return ((row >> 1) & 1) << 2;
 }
 
+// Swizzle for tiles read both ways (16-byte row reads of 16 consecutive rows
+// and transposing reads of 8 rows x 4 chunks), as the backward pass reads Q,
+// dO and K: conflict-free for both, since it is injective on 16 consecutive
+// rows (same-parity rows for NC = 8) and sends the rows of a transposing read
+// to distinct 4-chunk groups.
+template <int NC>
+__device__ __forceinline__ int swz_d(int row) {
+    if constexpr (NC == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+// LDS tile layouts: K (row reads), V (transposing reads), D (both).
+enum TileLayout : int { kLayoutK = 0, kLayoutV = 1, kLayoutD = 2 };
+
 // Scheduling pins for MFMA steps [S0, S1) of one MFMA phase of NS steps:
 // per step its MFMA followed by the LDS reads of the step RING ahead; with
 // PRE, first the reads of the first RING steps (the ring fill). The pins of
@@ -105,6 +119,7 @@ struct TileFetch {
     int gw;
     uint32_t lds0;  // LDS byte address of the tile buffers' base
     uint32_t koff[KP];
+    uint32_t doff[KP];
     uint32_t voff;
 
     __device__ __forceinline__ TileFetch(const char* smem, int gw_, int lane, int tok_bytes)
@@ -114,20 +129,22 @@ struct TileFetch {
         for (int k = 0; k < KP; ++k) {
             const int row = ((gw * BPW + k) % KP) * G::ROWS_PER_KB + rl;
             koff[k] = (uint32_t)(rl * tok_bytes + ((pos ^ swz_k<G::NC>(row)) << 4));
+            doff[k] = (uint32_t)(rl * tok_bytes + ((pos ^ swz_d<G::NC>(row)) << 4));
         }
         voff = (uint32_t)(rl * tok_bytes + ((pos ^ swz_v<G::NC>(rl)) << 4));
     }
     // block i (0 <= i < BPW) of this wave's share; dst is the tile buffer's
-    // byte offset from the base
-    __device__ __forceinline__ void block(int dst, const char* tile, int tok_bytes, bool v_layout, int i) const {
+    // byte offset from the base; layout is a TileLayout
+    __device__ __forceinline__ void block(int dst, const char* tile, int tok_bytes, int layout, int i) const {
         const int blk = gw * BPW + i;
         const char* src = tile + (int64_t)(blk * G::ROWS_PER_KB) * tok_bytes;
-        lds_dma16(src, v_layout ? voff : koff[i % KP], lds0 + (uint32_t)(dst + blk * 1024));
+        const uint32_t off = layout == kLayoutV ? voff : (layout == kLayoutD ? doff[i % KP] : koff[i % KP]);
+        lds_dma16(src, off, lds0 + (uint32_t)(dst + blk * 1024));
     }
     // this wave's whole share
-    __device__ __forceinline__ void all(int dst, const char* tile, int tok_bytes, bool v_layout) const {
+    __device__ __forceinline__ void all(int dst, const char* tile, int tok_bytes, int layout) const {
 #pragma unroll
-        for (int i = 0; i < BPW; ++i) block(dst, tile, tok_bytes, v_layout, i);
+        for (int i = 0; i < BPW; ++i) block(dst, tile, tok_bytes, layout, i);
     }
 };
 

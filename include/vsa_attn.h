@@ -127,6 +127,25 @@ int32_t vsa_build_worklist(const int32_t* kv_block_cnt, int32_t n_items, int32_t
                            int32_t* work_list, void* stream);
 
 /*
+ * vsa_csr_transpose -- Q-direction lists for the backward pass: for every KV
+ * tile, the query tiles that select it (FastVideo page, FA4 block_sparsity.py,
+ * normalize_block_sparse_config_bwd: the backward walks per-KV-tile lists of
+ * query tiles, "transposed from forward").
+ *
+ *   kv_block_idx / kv_block_cnt  forward CSR [batch, heads, nq, idx_ld] /
+ *                  [batch, heads, nq] (row m uses entries [0, min(cnt, idx_ld))).
+ *   q_block_idx    out [batch, heads, nkv, q_ld]: ascending query tile indices;
+ *                  slots past the count are not written.
+ *   q_block_cnt    out [batch, heads, nkv]: the true count (even if > q_ld).
+ *   overflow       optional out (device int32, may be NULL): set to 1 if a
+ *                  count exceeds q_ld; never cleared by this call.
+ *   Forward entries outside [0, nkv) are ignored. nq <= 524288.
+ */
+int32_t vsa_csr_transpose(const int32_t* kv_block_idx, const int32_t* kv_block_cnt, int32_t batch, int32_t heads,
+                          int32_t nq, int32_t nkv, int32_t idx_ld, int32_t* q_block_idx, int32_t q_ld,
+                          int32_t* q_block_cnt, int32_t* overflow, void* stream);
+
+/*
  * vsa_expand_valid -- valid key tokens per physical KV tile from valid tokens
  * per logical KV block (the variable block sizes `vbs` of the FastVideo
  * page's VSA wrapper): a logical block of logical_block_kv positions holding
@@ -178,6 +197,37 @@ int32_t vsa_attn_fwd_worklist(const void* q, const void* k, const void* v, const
                               int32_t seqlen, int32_t heads, int32_t head_dim, int32_t idx_ld, int32_t block_q,
                               int32_t block_kv, float scale, const int32_t* work_list, int32_t n_work, void* o,
                               float* lse, void* stream);
+
+/*
+ * vsa_attn_bwd -- backward pass: dQ, dK and dV of vsa_attn_fwd.
+ *
+ * Source: the gradient of page 3's ref_masked_sdpa_fp32 (the function the
+ * forward computes); the backward walks, per KV tile, the query tiles that
+ * select it (FA4 block_sparsity.py, normalize_block_sparse_config_bwd). With
+ * P recomputed from the forward's LSE, D_i = dO_i . O_i, dS = P (dO V^T - D):
+ * dV = P^T dO, dK = scale dS^T Q, dQ = scale dS K. Deterministic: dK and dV
+ * of a KV tile accumulate in one workgroup over its query tiles in list
+ * order, dQ of a query tile in one workgroup over its KV tiles in list order;
+ * no atomics. bf16 in and out, fp32 accumulation.
+ *
+ *   q, k, v, o, dout, dq, dk, dv   [batch, seqlen, heads, head_dim] bf16
+ *                  (o: the forward output; dq, dk, dv written, every row)
+ *   lse            [batch, heads, seqlen] fp32 from the forward
+ *   kv_block_idx / kv_block_cnt / idx_ld   the forward CSR
+ *   q_block_idx / q_block_cnt / q_ld       its transpose (vsa_csr_transpose)
+ *   kv_valid       as for the forward (NULL: full tiles); padding keys get
+ *                  dK = dV = 0
+ *   Same shape limits as vsa_attn_fwd; q_ld, idx_ld <= 8191. Uses a
+ *   library-owned device buffer of 8*batch*heads*seqlen bytes plus the work
+ *   lists (grown on demand per device, released by vsa_release); calls that
+ *   share a device must not overlap in time on different streams. Padding
+ *   tokens of partial tiles must hold finite values.
+ */
+int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     const int32_t* kv_block_idx, const int32_t* kv_block_cnt, int32_t idx_ld,
+                     const int32_t* q_block_idx, const int32_t* q_block_cnt, int32_t q_ld, const int32_t* kv_valid,
+                     int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim, int32_t block_q,
+                     int32_t block_kv, float scale, void* dq, void* dk, void* dv, void* stream);
 
 /* Free the library-owned work-list buffers on every device. Not thread-safe
  * with concurrent vsa_attn_fwd calls. */

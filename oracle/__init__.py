@@ -72,6 +72,9 @@ def _load():
         lib.vsa_oracle_bwd_dkv_rows.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
                                                 ctypes.c_float, p, i64, p, p, i32]
         lib.vsa_oracle_bwd_dkv_rows.restype = i32
+        lib.vsa_oracle_bwd_full.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32,
+                                            ctypes.c_float, p, p, p, i32]
+        lib.vsa_oracle_bwd_full.restype = i32
         _lib = lib
     return _lib
 
@@ -201,13 +204,17 @@ def bwd_dkv_rows(q, k, v, dout, kv_block_idx, kv_block_cnt, block_q, block_kv, s
 
 
 def bwd_full(q, k, v, dout, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, threads=0, kv_valid=None):
-    """dQ, dK, dV fp32 [B, S, H, D] for every row."""
-    B, S, H, D = _bits(q).shape
-    dq = bwd_dq_rows(q, k, v, dout, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, None, threads, kv_valid)
-    dk, dv = bwd_dkv_rows(q, k, v, dout, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, None, threads,
-                          kv_valid)
-    shape = lambda a: a.reshape(B, H, S, D).transpose(0, 2, 1, 3).copy()  # noqa: E731
-    return shape(dq), shape(dk), shape(dv)
+    """dQ, dK, dV fp32 [B, S, H, D] for every row (one pass per head)."""
+    qb, kb, vb, db, idx, cnt, val, (B, S, H, D) = _bwd_common(q, k, v, dout, kv_block_idx, kv_block_cnt,
+                                                               block_q, block_kv, kv_valid)
+    dq = np.empty((B, S, H, D), dtype=np.float32)
+    dk = np.empty_like(dq)
+    dv = np.empty_like(dq)
+    rc = _load().vsa_oracle_bwd_full(
+        _ptr(qb), _ptr(kb), _ptr(vb), _ptr(db), _ptr(idx), _ptr(cnt), None if val is None else _ptr(val), B, S, H,
+        D, idx.shape[3], block_q, block_kv, ctypes.c_float(scale), _ptr(dq), _ptr(dk), _ptr(dv), int(threads))
+    _check(rc)
+    return dq, dk, dv
 
 
 def probs_row(q, k, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, flat_row, kv_valid=None):

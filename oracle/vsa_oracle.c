@@ -473,3 +473,89 @@ int vsa_oracle_bwd_dkv_rows(const uint16_t* q, const uint16_t* k, const uint16_t
     }
     return status;
 }
+
+
+/*
+ * All three gradients for every row: one head at a time (OpenMP over heads),
+ * query rows in ascending order; each row's dS row is added into the dK and
+ * dV rows of the keys it sees, so every dK/dV sum runs over queries in
+ * ascending order, the same order as vsa_oracle_bwd_dkv_rows (whose results
+ * this reproduces bit for bit, only faster). dq, dk, dv: [B, S, H, D] fp32.
+ */
+int vsa_oracle_bwd_full(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                        const int32_t* kv_block_idx, const int32_t* kv_block_cnt, const int32_t* kv_valid, int B, int S,
+                        int H, int D, int ld, int block_q, int block_kv, float scale, float* dq, float* dk, float* dv,
+                        int n_threads) {
+    if (B <= 0 || S <= 0 || H <= 0 || D <= 0 || block_q <= 0 || block_kv <= 0 || ld < 0) return ORACLE_ERR_ARG;
+    if (S % block_q || S % block_kv) return ORACLE_ERR_ARG;
+    const int nq = S / block_q, nkv = S / block_kv;
+    if (check_valid(kv_valid, nkv, block_kv) != ORACLE_OK) return ORACLE_ERR_ARG;
+    int status = ORACLE_OK;
+#ifdef _OPENMP
+    if (n_threads <= 0) n_threads = omp_get_max_threads();
+#else
+    (void)n_threads;
+#endif
+#pragma omp parallel num_threads(n_threads)
+    {
+        float* s = (float*)malloc(sizeof(float) * (size_t)S);
+        float* qf = (float*)malloc(sizeof(float) * (size_t)D);
+        float* o = (float*)malloc(sizeof(float) * (size_t)D);
+        float* dof = (float*)malloc(sizeof(float) * (size_t)D);
+        int32_t* allow = (int32_t*)malloc(sizeof(int32_t) * (size_t)nkv);
+        if (!s || !qf || !o || !dof || !allow) {
+#pragma omp critical
+            status = ORACLE_ERR_NOMEM;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int bh = 0; bh < B * H; ++bh) {
+                const int b = bh / H, h = bh % H;
+                const int64_t tok = (int64_t)H * D;
+                for (int j = 0; j < S; ++j)
+                    for (int d = 0; d < D; ++d) {
+                        dk[((int64_t)b * S + j) * tok + (int64_t)h * D + d] = 0.0f;
+                        dv[((int64_t)b * S + j) * tok + (int64_t)h * D + d] = 0.0f;
+                    }
+                for (int i = 0; i < S; ++i) {
+                    int64_t crow = ((int64_t)b * H + h) * nq + i / block_q;
+                    float* dqrow = dq + ((int64_t)b * S + i) * tok + (int64_t)h * D;
+                    int rc = mark_tiles(kv_block_idx + crow * ld, kv_block_cnt[crow], ld, nkv, kv_valid, block_kv,
+                                        allow);
+                    if (rc != ORACLE_OK) {
+#pragma omp critical
+                        status = rc;
+                        break;
+                    }
+                    float di;
+                    row_prob_out(q, k, v, dout, S, H, D, b, h, i, allow, nkv, block_kv, scale, qf, s, o, &di);
+                    const uint16_t* drow = dout + ((int64_t)b * S + i) * tok + (int64_t)h * D;
+                    for (int d = 0; d < D; ++d) dof[d] = bf16_to_f32(drow[d]);
+                    for (int d = 0; d < D; ++d) dqrow[d] = 0.0f;
+                    for (int j = 0; j < S; ++j) {
+                        if (!allowed(allow, block_kv, j)) continue;
+                        const uint16_t* vrow = v + ((int64_t)b * S + j) * tok + (int64_t)h * D;
+                        const uint16_t* krow = k + ((int64_t)b * S + j) * tok + (int64_t)h * D;
+                        float* dkrow = dk + ((int64_t)b * S + j) * tok + (int64_t)h * D;
+                        float* dvrow = dv + ((int64_t)b * S + j) * tok + (int64_t)h * D;
+                        float dp = 0.0f;
+                        for (int d = 0; d < D; ++d) dp += dof[d] * bf16_to_f32(vrow[d]);
+                        const float pij = s[j];
+                        const float ds = pij * (dp - di);
+                        for (int d = 0; d < D; ++d) dqrow[d] += ds * bf16_to_f32(krow[d]);
+                        for (int d = 0; d < D; ++d) dkrow[d] += ds * qf[d];
+                        for (int d = 0; d < D; ++d) dvrow[d] += pij * dof[d];
+                    }
+                    for (int d = 0; d < D; ++d) dqrow[d] *= scale;
+                }
+                for (int j = 0; j < S; ++j)
+                    for (int d = 0; d < D; ++d) dk[((int64_t)b * S + j) * tok + (int64_t)h * D + d] *= scale;
+            }
+        }
+        free(s);
+        free(qf);
+        free(o);
+        free(dof);
+        free(allow);
+    }
+    return status;
+}

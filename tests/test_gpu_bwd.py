@@ -1,0 +1,188 @@
+"""GPU parity of the backward pass (dQ, dK, dV) and the Q-direction CSR
+against the CPU oracle, through the C ABI.
+
+The oracle recomputes the forward from q, k, v and the mask; the GPU
+backward uses the GPU forward's O and LSE, as a caller would. Tolerances
+(bf16 gradients compared after conversion to fp32, against fp32 oracle
+gradients): max |d| <= 2e-2 * max(1, max |ref|) and mean |d| <= 2e-3 *
+max(1, mean |ref|) per tensor -- the forward's bounds scaled to the
+gradient's magnitude: bf16 rounding of the output (2^-9 relative) and of P
+and dS inside the MFMA products (2^-9 relative per term, averaging over the
+sums) keep the error well inside them. Integer outputs are bit-exact.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import frontend as ofront
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+G_MAX = 2e-2
+G_MEAN = 2e-3
+
+
+def say(msg):
+    line = f"[gpu-bwd] {msg}"
+    print(line, flush=True)
+    path = os.environ.get("VSA_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(line + "\n")
+
+
+@pytest.fixture(scope="module")
+def vsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_flashattention_amd as m
+
+    m.load_library()
+    return m
+
+
+def dev(x):
+    if isinstance(x, np.ndarray):
+        x = torch.from_numpy(np.ascontiguousarray(x))
+    return x.contiguous().to("cuda")
+
+
+def check(name, got, ref, label):
+    d = np.abs(got - ref)
+    mx, mean = float(d.max()), float(d.mean())
+    rmax, rmean = float(np.abs(ref).max()), float(np.abs(ref).mean())
+    say(f"{label} {name}: max|d|={mx:.3e} (ref max {rmax:.3e}) mean|d|={mean:.3e} (ref mean {rmean:.3e})")
+    assert np.isfinite(got).all(), f"{label} {name}: non-finite"
+    assert mx <= G_MAX * max(1.0, rmax), f"{label} {name}: max |d| {mx}"
+    assert mean <= G_MEAN * max(1.0, rmean), f"{label} {name}: mean |d| {mean}"
+
+
+TRANSPOSE_CASES = [
+    ("random", None),
+    ("vsa256 256x128", (W.VSA256, (256, 128), 26)),
+    ("native64", (W.NATIVE64, (64, 64), 92)),
+]
+
+
+@pytest.mark.parametrize("label,spec", TRANSPOSE_CASES, ids=[c[0] for c in TRANSPOSE_CASES])
+def test_csr_transpose_bit_exact(vsa, label, spec):
+    say(f"csr_transpose {label}")
+    if spec is None:
+        B, H, NQ, NKV = 2, 3, 40, 24
+        idx, cnt = W.random_csr(B, H, NQ, NKV, NKV, 0, NKV, seed=17)
+        cnt[0, 0, 0] = 0
+        idx[1, 2, 3, 0] = -4  # out-of-range entry: ignored
+        idx[1, 2, 3, 1] = NKV + 3
+    else:
+        wl, shape, ld = spec
+        idx, cnt, _ = ofront.mask_to_csr(wl.logical_mask(), wl.logical_block, shape, ld)
+        NQ, NKV = idx.shape[2], wl.seqlen // shape[1]
+    clean_idx = idx.copy()
+    # the oracle takes valid rows only: drop out-of-range entries (the kernel ignores them)
+    clean_cnt = cnt.copy()
+    for pos in np.ndindex(cnt.shape):
+        ent = [t for t in idx[pos][:cnt[pos]] if 0 <= t < NKV]
+        clean_idx[pos][:len(ent)] = ent
+        clean_cnt[pos] = len(ent)
+    q_ld = NQ
+    ref_idx, ref_cnt, ref_ovf = ofront.transpose_csr(clean_idx, clean_cnt, NKV, q_ld)
+    ovf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    q_idx, q_cnt = vsa.vsa_csr_transpose(dev(idx), dev(cnt), NKV, q_ld, overflow=ovf)
+    torch.cuda.synchronize()
+    assert np.array_equal(q_cnt.cpu().numpy(), ref_cnt)
+    valid = np.arange(q_ld)[None, None, None, :] < ref_cnt[..., None]
+    assert np.array_equal(np.where(valid, q_idx.cpu().numpy(), -1), np.where(valid, ref_idx, -1))
+    assert bool(ovf.item()) == ref_ovf
+    # compact row length: counts stay true, overflow is flagged
+    small = max(1, int(ref_cnt.max()) - 1)
+    ovf.zero_()
+    _, c2 = vsa.vsa_csr_transpose(dev(idx), dev(cnt), NKV, small, overflow=ovf)
+    torch.cuda.synchronize()
+    assert np.array_equal(c2.cpu().numpy(), ref_cnt) and ovf.item() == 1
+
+
+def _run_bwd(vsa, q, k, v, do, idx, cnt, bq, bkv, scale, kv_valid=None):
+    B, S, H, D = q.shape
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    idxd, cntd = dev(idx), dev(cnt)
+    vd_valid = None if kv_valid is None else dev(kv_valid)
+    o, lse = vsa.vsa_attn_fwd(qd, kd, vd, idxd, cntd, bq, bkv, scale, kv_valid=vd_valid)
+    nkv = S // bkv
+    q_idx, q_cnt = vsa.vsa_csr_transpose(idxd, cntd, nkv, S // bq)
+    dq, dk, dv = vsa.vsa_attn_bwd(qd, kd, vd, o, lse, dod, idxd, cntd, q_idx, q_cnt, bq, bkv, scale,
+                                  kv_valid=vd_valid)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+BWD_SHAPES = [(bq, bkv, d) for bq in (64, 128, 256) for bkv in (64, 128) for d in (64, 128)]
+
+
+@pytest.mark.parametrize("bq,bkv,D", BWD_SHAPES, ids=[f"{a}x{b}_d{c}" for a, b, c in BWD_SHAPES])
+@pytest.mark.parametrize("partial", [False, True], ids=["full", "partial"])
+def test_backward_every_tile_shape_all_rows(vsa, bq, bkv, D, partial):
+    B, H, S = 1, 2, 768
+    label = f"{bq}x{bkv} D={D} {'partial' if partial else 'full'}"
+    say(f"backward {label}")
+    q, k, v = W.qkv(B, S, H, D, seed=bq + bkv + D + 100)
+    do = W.qkv(B, S, H, D, seed=bq + bkv + D + 101)[0]
+    nq, nkv = S // bq, S // bkv
+    idx, cnt = W.random_csr(B, H, nq, nkv, nkv, 0, nkv, seed=bq * 3 + bkv + D)
+    cnt[0, 0, 0] = 0  # an empty query tile
+    val = None
+    if partial:
+        val = W.ragged_block_sizes(nkv, bkv, seed=bq + bkv + D, p_full=0.4)
+        val[0] = 0
+    scale = 1.0 / math.sqrt(D)
+    dq, dk, dv = _run_bwd(vsa, q, k, v, do, idx, cnt, bq, bkv, scale, val)
+    rq, rk, rv = oracle.bwd_full(q, k, v, do, idx, cnt, bq, bkv, scale, kv_valid=val)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check(name, got.float().cpu().numpy(), ref, label)
+
+
+def test_backward_is_deterministic(vsa):
+    B, H, S, D, bq, bkv = 1, 2, 1024, 128, 128, 64
+    say("backward determinism")
+    q, k, v = W.qkv(B, S, H, D, seed=7)
+    do = W.qkv(B, S, H, D, seed=8)[0]
+    idx, cnt = W.random_csr(B, H, S // bq, S // bkv, S // bkv, 1, 12, seed=9)
+    a = _run_bwd(vsa, q, k, v, do, idx, cnt, bq, bkv, 0.09)
+    b = _run_bwd(vsa, q, k, v, do, idx, cnt, bq, bkv, 0.09)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_vsa256_sampled_rows(vsa):
+    """Full-size VSA-256 (B1 H24 S32768 D128) at 256x128: sampled dQ rows and
+    sampled dK/dV rows against the oracle."""
+    wl = W.VSA256
+    say("backward vsa256 256x128: inputs")
+    q, k, v = wl.qkv()
+    do = W.qkv(wl.batch, wl.seqlen, wl.heads, wl.head_dim, seed=4242)[0]
+    idx, cnt, _ = ofront.mask_to_csr(wl.logical_mask(), wl.logical_block, (256, 128), 26)
+    say("backward vsa256 256x128: kernels")
+    dq, dk, dv = _run_bwd(vsa, q, k, v, do, idx, cnt, 256, 128, wl.scale)
+    B, S, H, D = q.shape
+    rng = np.random.default_rng(5)
+    heads = [0, 11, 23]
+    qrows = np.array([h * S + r for h in heads for r in rng.integers(0, S, size=24)], dtype=np.int64)
+    krows = np.array([h * S + r for h in heads for r in rng.integers(0, S, size=3)], dtype=np.int64)
+    say("backward vsa256: oracle dQ rows")
+    rq = oracle.bwd_dq_rows(q, k, v, do, idx, cnt, 256, 128, wl.scale, qrows)
+    say("backward vsa256: oracle dK/dV rows")
+    rk, rv = oracle.bwd_dkv_rows(q, k, v, do, idx, cnt, 256, 128, wl.scale, krows)
+
+    def pick(t, rows):
+        h, i = rows // S, rows % S
+        return t.float().cpu().numpy()[0, i, h]
+
+    check("dQ", pick(dq, qrows), rq, "vsa256 sampled")
+    check("dK", pick(dk, krows), rk, "vsa256 sampled")
+    check("dV", pick(dv, krows), rv, "vsa256 sampled")
+    torch.cuda.empty_cache()

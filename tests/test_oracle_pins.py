@@ -307,8 +307,8 @@ MUTATIONS = {
     "scale_dropped": ("s[j] = acc * scale;", "s[j] = acc;"),
     "key_from_query_row": ("const uint16_t* krow = k + ((int64_t)b * S + j) * tok + (int64_t)h * D;\n            float acc",
                            "const uint16_t* krow = k + ((int64_t)b * S + i) * tok + (int64_t)h * D;\n            float acc"),
-    "value_tiles_use_block_q": ("if (!allowed(allow, block_kv, j)) continue;\n                        const uint16_t* vrow",
-                                "if (!allowed(allow, block_q, j)) continue;\n                        const uint16_t* vrow"),
+    "value_tiles_use_block_q": ("if (!allowed(allow, block_kv, j)) continue;\n                        const uint16_t* vrow = v + ((int64_t)b * S + j) * tok + (int64_t)h * D;\n                        float w",
+                                "if (!allowed(allow, block_q, j)) continue;\n                        const uint16_t* vrow = v + ((int64_t)b * S + j) * tok + (int64_t)h * D;\n                        float w"),
     "key_tile_offset": ("const uint16_t* krow = k + ((int64_t)b * S + j) * tok + (int64_t)h * D;\n            float acc",
                         "const uint16_t* krow = k + ((int64_t)b * S + (j + block_kv) % S) * tok + (int64_t)h * D;\n            float acc"),
     "value_wrong_head": ("const uint16_t* vrow = v + ((int64_t)b * S + j) * tok + (int64_t)h * D;\n                        float w",

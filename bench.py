@@ -53,6 +53,8 @@ def parse_args():
                     help="seconds of extra steps during which amd-smi samples the gfx clock (0: skip)")
     ap.add_argument("--flush-steps", type=int, default=10,
                     help="kernel launches timed after writing a buffer larger than the last-level cache")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the backward leg (dQ, dK, dV of the same workload; reported beside the headline)")
     ap.add_argument("--traffic-from-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                                   "COPY_WRITE_DIR"), default=None,
                     help="write the traffic JSON from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE output directories "
@@ -186,12 +188,14 @@ def main():
         del junk
 
     clock = sample_clock(step, args.clock_seconds) if args.clock_seconds > 0 else None
+    backward = None if args.no_backward else time_backward(vsa, q, k, v, o, lse, idx, cnt, bq, bkv, scale, D, pairs,
+                                                           args.steps, stream)
 
     # Algorithmic HBM bytes of one kernel launch: Q, K, V read once, O and
     # LSE written once, CSR indices and counts read once.
     alg_bytes = (3 * B * S * H * D + B * S * H * D) * 2 + B * H * S * 4 + (B * H * nq) * (ld + 2) * 4
     kname = kernel_name(bq, bkv, D)
-    traffic = read_traffic(args.traffic or default_traffic_path(kname, wl.name, bq, bkv))
+    traffic = read_traffic(args.traffic or default_traffic_path(kname, wl.name, bq, bkv), kname)
 
     result = {
         "metric": METRIC,
@@ -223,6 +227,7 @@ def main():
         "kernel_ms_post_flush": None if kernel_ms_flush is None else round(kernel_ms_flush, 4),
         "kernel_tflops_post_flush": None if kernel_ms_flush is None else round(flops / (kernel_ms_flush * 1e-3) / 1e12, 2),
         "clock": clock,
+        "backward": backward,
         "roofline": {
             "bound": "mfma",
             "achieved": round(kernel_tflops, 2),
@@ -242,6 +247,40 @@ def main():
     return 0
 
 
+def time_backward(vsa, q, k, v, o, lse, idx, cnt, bq, bkv, scale, D, pairs, steps, stream):
+    """Backward leg: the Q-direction CSR plus dQ, dK, dV of this workload,
+    timed like the forward (HIP events on the launch stream). Throughput uses
+    the usual 10*D flops per selected pair (QK^T, dO V^T, P^T dO, dS K,
+    dS^T Q); the kernels recompute QK^T and dO V^T once more (14*D executed)."""
+    import torch
+
+    B, S, H, _ = q.shape
+    nkv = S // bkv
+    g = torch.Generator(device="cpu").manual_seed(4242)
+    dout = torch.randn(q.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to(q.device)
+    q_idx = torch.empty((B, H, nkv, S // bq), dtype=torch.int32, device=q.device)
+    q_cnt = torch.empty((B, H, nkv), dtype=torch.int32, device=q.device)
+    grads = [torch.empty_like(q) for _ in range(3)]
+
+    def run():
+        vsa.vsa_csr_transpose(idx, cnt, nkv, S // bq, q_idx, q_cnt, stream=stream)
+        vsa.vsa_attn_bwd(q, k, v, o, lse, dout, idx, cnt, q_idx, q_cnt, bq, bkv, scale, *grads, stream=stream)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tflops = 10.0 * D * pairs / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "tflops": round(tflops, 2), "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+            "flops_per_pair": f"10*D={10 * D}", "scope": "vsa_csr_transpose + vsa_attn_bwd (prep, dK/dV, dQ)"}
+
+
 def kernel_name(bq, bkv, d, partial=False):
     """Name of the forward kernel the library dispatches for this tile shape
     (the last template argument: built for partial tiles)."""
@@ -256,15 +295,17 @@ def kernel_name(bq, bkv, d, partial=False):
 CSRC = os.path.join(ROOT, "block_sparse_attention_flashattention_amd", "csrc")
 
 
-def kernel_source_hash():
-    """sha256 over the HIP sources the library is built from."""
+def kernel_source_hash(kname):
+    """sha256 over the sources a forward kernel is compiled from: its own
+    file, the dispatcher and the headers they include."""
     import hashlib
+    own = {"vsa_fwd_pp_kernel": "attn_fwd_pp.hip", "vsa_fwd_2s_kernel": "attn_fwd_2s.hip",
+           "vsa_fwd_4s_kernel": "attn_fwd_4s.hip"}[kname.split("<")[0]]
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in sorted([own, "attn_fwd.hip", "wave_engine.h", "device_common.h", "vsa_internal.h"]):
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -273,14 +314,14 @@ def default_traffic_path(kname, workload, bq, bkv):
     return os.path.join(ROOT, "profiles", f"traffic_{stem}_{bq}x{bkv}_{workload}.json")
 
 
-def read_traffic(path):
+def read_traffic(path, kname):
     """HBM bytes per launch from a traffic JSON, or None if it is missing or
     was measured on other kernel sources."""
     if not path or not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_hash") != kernel_source_hash():
+    if t.get("source_hash") != kernel_source_hash(kname):
         return None
     return t.get("bytes_per_launch")
 
@@ -316,7 +357,7 @@ def write_traffic(args):
         "bytes_per_launch": round(fetch + write),
         "fetch_bytes": round(fetch), "write_bytes": round(write),
         "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
-        "source_hash": kernel_source_hash(),
+        "source_hash": kernel_source_hash(kname),
     }
     path = args.traffic or default_traffic_path(kname, wl.name, bq, bkv)
     with open(path, "w") as f:

@@ -373,16 +373,25 @@ __global__ __launch_bounds__(BKV * 2) void vsa_bwd_dkv_kernel(BwdParams prm) {
         if (j + 1 < steps) fetch_step(j + 1);
         if (entry(j) < 0) continue;  // uniform
         const int qb = (j & 1) * STAGE, ob = qb + G::TILE, ab = qb + 2 * G::TILE;
+        // S = Q K^T and dP = dO V^T for both 32-row halves first, so that one
+        // half's exp/dS work can overlap the other half's MFMAs
+        f32x16 s[QS / 32], dp[QS / 32];
 #pragma unroll
         for (int qs = 0; qs < QS / 32; ++qs) {
-            f32x16 s = f32x16{}, dp = f32x16{};
+            s[qs] = f32x16{};
+            dp[qs] = f32x16{};
+        }
 #pragma unroll
-            for (int c = 0; c < DC; ++c) {
+        for (int c = 0; c < DC; ++c)
+#pragma unroll
+            for (int qs = 0; qs < QS / 32; ++qs) {
                 const bf16x8 qa = *(const bf16x8*)(smem + qb + qo.row[c] + qs * 32 * OO::ROW_BYTES);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[c], s, 0, 0, 0);
+                s[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[c], s[qs], 0, 0, 0);
                 const bf16x8 oa = *(const bf16x8*)(smem + ob + qo.row[c] + qs * 32 * OO::ROW_BYTES);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vreg[c], dp, 0, 0, 0);
+                dp[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vreg[c], dp[qs], 0, 0, 0);
             }
+#pragma unroll
+        for (int qs = 0; qs < QS / 32; ++qs) {
             // rows q = qs*32 + 8*(r/4) + 4*hi + r%4: their D and lse2, four at a time
             bf16x8 pp[2], ps[2];
 #pragma unroll
@@ -397,10 +406,10 @@ __global__ __launch_bounds__(BKV * 2) void vsa_bwd_dkv_kernel(BwdParams prm) {
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int r = (half * 2 + k4) * 4 + u;
-                        const float pr = fast_exp2(fmaf(s[r], prm.scale_log2, -ll[u]));
+                        const float pr = fast_exp2(fmaf(s[qs][r], prm.scale_log2, -ll[u]));
                         const bool off = PARTIAL && !key_ok;
                         pv[u] = off ? 0.0f : pr;
-                        dsv[u] = off ? 0.0f : pr * (dp[r] - dd[u]);
+                        dsv[u] = off ? 0.0f : pr * (dp[qs][r] - dd[u]);
                     }
                     wp[k4 * 2] = pack_bf16x2(pv[0], pv[1]);
                     wp[k4 * 2 + 1] = pack_bf16x2(pv[2], pv[3]);

@@ -136,3 +136,40 @@ def test_binding_refuses_cpu_tensors():
     cnt = torch.zeros(1, 1, 2, dtype=torch.int32)
     with pytest.raises(ValueError, match="GPU"):
         vsa.vsa_attn_fwd(q, q, q, idx, cnt, 64, 64)
+
+
+def test_csr_transpose_validation(lib):
+    f = lib.vsa_csr_transpose
+    # kv_block_idx, kv_block_cnt, B, H, nq, nkv, idx_ld, q_block_idx, q_ld, q_block_cnt, overflow, stream
+    assert f(None, A, 1, 1, 4, 4, 4, A, 4, A, None, None) == -1
+    assert f(A, A, 0, 1, 4, 4, 4, A, 4, A, None, None) == -1
+    assert f(A, A, 1, 1, 4, 4, 0, A, 4, A, None, None) == -1
+    assert f(A, A, 1, 1, 4, 4, 4, A, 0, A, None, None) == -1
+    assert f(A, A, 1, 1, 1 << 20, 4, 4, A, 4, A, None, None) == -2  # nq above the bitmap limit
+    assert f(A, A, 1, 1, 4, 4, 4, A + 2, 4, A, None, None) == -1
+
+
+def _bwd(lib, **kw):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, do=A, idx=A, cnt=A, ld=16, qidx=A, qcnt=A, qld=16, valid=None, B=1, S=1024,
+             H=2, D=128, bq=128, bkv=64, scale=0.1, dq=A, dk=A, dv=A)
+    a.update(kw)
+    return lib.vsa_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["idx"], a["cnt"], a["ld"], a["qidx"],
+                            a["qcnt"], a["qld"], a["valid"], a["B"], a["S"], a["H"], a["D"], a["bq"], a["bkv"],
+                            a["scale"], a["dq"], a["dk"], a["dv"], None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(do=None), -1, "null"),
+    (dict(dq=None), -1, "null"),
+    (dict(qidx=None), -1, "null"),
+    (dict(o=None), -1, "null"),
+    (dict(dk=A + 4), -1, "aligned"),
+    (dict(qld=0), -2, "q_ld"),
+    (dict(qld=9000), -2, "q_ld"),
+    (dict(S=1000), -1, "divisible"),
+    (dict(D=96), -2, "head_dim"),
+    (dict(valid=A + 2), -1, "kv_valid"),
+])
+def test_attn_bwd_rejects_invalid_arguments(lib, kw, status, needle):
+    assert _bwd(lib, **kw) == status
+    assert needle in lib.vsa_last_error().decode()

@@ -53,6 +53,9 @@ def parse_args():
                     help="seconds of extra steps during which amd-smi samples the gfx clock (0: skip)")
     ap.add_argument("--flush-steps", type=int, default=10,
                     help="kernel launches timed after writing a buffer larger than the last-level cache")
+    ap.add_argument("--ragged", type=int, default=None, metavar="SEED",
+                    help="partial KV tiles: ragged valid-token counts per logical KV block drawn with this seed "
+                         "(the masked kernels run; throughput counts valid pairs only)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward leg (dQ, dK, dV of the same workload; reported beside the headline)")
     ap.add_argument("--traffic-from-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -118,19 +121,25 @@ def main():
     lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
     scale = wl.scale
     stream = torch.cuda.current_stream(dev)
+    vbs = kv_valid = None
+    if args.ragged is not None:
+        vbs = torch.from_numpy(W.ragged_block_sizes(S // lkv, lkv, seed=args.ragged)).to(dev)
+        kv_valid = torch.empty((S // bkv,), dtype=torch.int32, device=dev)
 
     def step(ev0=None, ev1=None):
         vsa.vsa_mask_to_csr(mask, (lq, lkv), (bq, bkv), ld, idx, cnt, stream=stream)
         vsa.vsa_build_worklist(cnt, ld, work, segment=nq, stream=stream)
+        if vbs is not None:
+            vsa.vsa_expand_valid(vbs, lkv, bkv, kv_valid, stream=stream)
         if ev0 is not None:
             ev0.record(stream)
-        vsa.vsa_attn_fwd_worklist(q, k, v, idx, cnt, bq, bkv, work, scale, o, lse, stream=stream)
+        vsa.vsa_attn_fwd_worklist(q, k, v, idx, cnt, bq, bkv, work, scale, o, lse, stream=stream, kv_valid=kv_valid)
         if ev1 is not None:
             ev1.record(stream)
 
     step()
     torch.cuda.synchronize()
-    pairs = int(cnt.to(torch.int64).sum().item()) * bq * bkv
+    pairs = selected_pairs(idx, cnt, bq, bkv, kv_valid)
     flops = 4.0 * D * pairs
     t_pre = time.perf_counter() + args.prewarm_seconds
     while time.perf_counter() < t_pre:
@@ -157,7 +166,9 @@ def main():
     # work list (what a caller without a cached work list pays).
     def wrapper():
         vsa.vsa_mask_to_csr(mask, (lq, lkv), (bq, bkv), ld, idx, cnt, stream=stream)
-        vsa.vsa_attn_fwd(q, k, v, idx, cnt, bq, bkv, scale, o, lse, stream=stream)
+        if vbs is not None:
+            vsa.vsa_expand_valid(vbs, lkv, bkv, kv_valid, stream=stream)
+        vsa.vsa_attn_fwd(q, k, v, idx, cnt, bq, bkv, scale, o, lse, stream=stream, kv_valid=kv_valid)
 
     for _ in range(2):
         wrapper()
@@ -180,7 +191,8 @@ def main():
             junk.fill_(i & 0xFF)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            vsa.vsa_attn_fwd_worklist(q, k, v, idx, cnt, bq, bkv, work, scale, o, lse, stream=stream)
+            vsa.vsa_attn_fwd_worklist(q, k, v, idx, cnt, bq, bkv, work, scale, o, lse, stream=stream,
+                                      kv_valid=kv_valid)
             e1.record(stream)
             fl_events.append((e0, e1))
         torch.cuda.synchronize()
@@ -189,12 +201,12 @@ def main():
 
     clock = sample_clock(step, args.clock_seconds) if args.clock_seconds > 0 else None
     backward = None if args.no_backward else time_backward(vsa, q, k, v, o, lse, idx, cnt, bq, bkv, scale, D, pairs,
-                                                           args.steps, stream)
+                                                           args.steps, stream, kv_valid)
 
     # Algorithmic HBM bytes of one kernel launch: Q, K, V read once, O and
     # LSE written once, CSR indices and counts read once.
     alg_bytes = (3 * B * S * H * D + B * S * H * D) * 2 + B * H * S * 4 + (B * H * nq) * (ld + 2) * 4
-    kname = kernel_name(bq, bkv, D)
+    kname = kernel_name(bq, bkv, D, partial=kv_valid is not None)
     traffic = read_traffic(args.traffic or default_traffic_path(kname, wl.name, bq, bkv), kname)
 
     result = {
@@ -217,6 +229,8 @@ def main():
             "selected_pairs": pairs,
             "density": round(pairs / (B * H * S * S), 5),
             "parallelism": "single_gpu",
+            "partial_tiles": None if vbs is None else {
+                "vbs_seed": args.ragged, "valid_token_fraction": round(float(vbs.float().mean().item()) / lkv, 4)},
         },
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "kernel_ms": round(kernel_ms, 4),
@@ -241,13 +255,26 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, q_cpu, k_cpu, v_cpu, idx, cnt, bq, bkv, ld, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, q_cpu, k_cpu, v_cpu, idx, cnt, bq, bkv, ld, args.cpu_seconds,
+                                              None if kv_valid is None else kv_valid.cpu().numpy())
 
     print(json.dumps(result), flush=True)
     return 0
 
 
-def time_backward(vsa, q, k, v, o, lse, idx, cnt, bq, bkv, scale, D, pairs, steps, stream):
+def selected_pairs(idx, cnt, bq, bkv, kv_valid=None):
+    """Selected (query, key) token pairs of a block CSR: block_q times the
+    valid keys of every listed KV tile (block_kv each without partial tiles)."""
+    import torch
+    if kv_valid is None:
+        return int(cnt.to(torch.int64).sum().item()) * bq * bkv
+    ld = idx.shape[-1]
+    listed = torch.arange(ld, device=idx.device) < cnt[..., None]
+    keys = kv_valid.to(torch.int64)[idx.to(torch.int64).clamp(0, kv_valid.numel() - 1)]
+    return int((keys * listed).sum().item()) * bq
+
+
+def time_backward(vsa, q, k, v, o, lse, idx, cnt, bq, bkv, scale, D, pairs, steps, stream, kv_valid=None):
     """Backward leg: the Q-direction CSR plus dQ, dK, dV of this workload,
     timed like the forward (HIP events on the launch stream). Throughput uses
     the usual 10*D flops per selected pair (QK^T, dO V^T, P^T dO, dS K,
@@ -264,7 +291,8 @@ def time_backward(vsa, q, k, v, o, lse, idx, cnt, bq, bkv, scale, D, pairs, step
 
     def run():
         vsa.vsa_csr_transpose(idx, cnt, nkv, S // bq, q_idx, q_cnt, stream=stream)
-        vsa.vsa_attn_bwd(q, k, v, o, lse, dout, idx, cnt, q_idx, q_cnt, bq, bkv, scale, *grads, stream=stream)
+        vsa.vsa_attn_bwd(q, k, v, o, lse, dout, idx, cnt, q_idx, q_cnt, bq, bkv, scale, *grads, stream=stream,
+                         kv_valid=kv_valid)
 
     for _ in range(3):
         run()
@@ -310,7 +338,7 @@ def kernel_source_hash(kname):
 
 
 def default_traffic_path(kname, workload, bq, bkv):
-    stem = kname.split("<")[0]
+    stem = kname.split("<")[0] + ("_partial" if kname.endswith("true>") else "")
     return os.path.join(ROOT, "profiles", f"traffic_{stem}_{bq}x{bkv}_{workload}.json")
 
 
@@ -344,7 +372,7 @@ def write_traffic(args):
     import workloads as W
     wl = W.WORKLOADS[args.workload]
     bq, bkv = (int(x) for x in args.tile.lower().split("x")) if args.tile else wl.physical[0]
-    kname = kernel_name(bq, bkv, wl.head_dim)
+    kname = kernel_name(bq, bkv, wl.head_dim, partial=args.ragged is not None)
     stem = kname.split("<")[0]
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_from_counters
     copy_bytes = 1 << 30
@@ -408,7 +436,7 @@ def sample_clock(step, seconds):
             "source": "amd-smi metric --clock, sampled while steps ran back to back"}
 
 
-def cpu_baseline(wl, q, k, v, idx, cnt, bq, bkv, ld, seconds):
+def cpu_baseline(wl, q, k, v, idx, cnt, bq, bkv, ld, seconds, kv_valid=None):
     """Time the CPU oracle on a bounded sample of query rows of this workload."""
     import oracle
 
@@ -430,9 +458,13 @@ def cpu_baseline(wl, q, k, v, idx, cnt, bq, bkv, ld, seconds):
     def run(n_tiles):
         rows, items = rows_for(n_tiles)
         t0 = time.perf_counter()
-        oracle.attn_rows(q, k, v, idx_h, cnt_h, bq, bkv, wl.scale, rows, threads)
+        oracle.attn_rows(q, k, v, idx_h, cnt_h, bq, bkv, wl.scale, rows, threads, kv_valid=kv_valid)
         dt = time.perf_counter() - t0
-        flops = 4.0 * D * float(cnt_h.reshape(-1)[items].sum()) * bq * bkv
+        if kv_valid is None:
+            flops = 4.0 * D * float(cnt_h.reshape(-1)[items].sum()) * bq * bkv
+        else:
+            flat_idx, flat_cnt = idx_h.reshape(-1, idx_h.shape[-1]), cnt_h.reshape(-1)
+            flops = 4.0 * D * bq * float(sum(kv_valid[flat_idx[i, :flat_cnt[i]]].sum() for i in items))
         return dt, flops, rows.size
 
     dt, fl, _ = run(max(1, threads // 4))

@@ -22,6 +22,15 @@ physical tiles holding clamp(vbs - r*PKV, 0, PKV) valid tokens each.
 per-KV-tile lists of the Q tiles that select it, "transposed from forward"):
 for KV tile n, the ascending Q tile indices m whose forward row lists n.
 
+``pair_q_tiles``: the pairing of adjacent 64-row query tiles onto 128-row
+tiles (FastVideo page, README of the fine-grained VSA kernels and the
+benchmark notes: at the Q256 API boundary the Q64 children of a logical row
+have identical KV lists and are "safely paired" onto the physical Q128/KV64
+schedule; arbitrary Q64 lists keep the native Q64 kernel). Query tiles 2p and
+2p+1 pair when their counts are equal and their stored lists are equal entry
+by entry, in order; the paired row p holds row 2p's list. The pairing is used
+only when every pair of the CSR pairs.
+
 ``build_worklist``: the order in which Q tiles are processed. Items
 (b, h, p) are encoded as their flat index into kv_block_cnt. Within each
 segment of ``segment`` consecutive items (one segment per batch and head when
@@ -127,3 +136,33 @@ def transpose_csr(kv_block_idx, kv_block_cnt, nkv, ld_q, fill=-1):
                 q_idx[b, h, n, :k] = ms[:k]
                 overflow |= ms.size > ld_q
     return q_idx, q_cnt, bool(overflow)
+
+
+def pair_q_tiles(kv_block_idx, kv_block_cnt, fill=-1):
+    """Pair query tiles (2p, 2p+1) of a block CSR onto tiles twice as tall.
+
+    kv_block_idx [B, H, NQ, ld], kv_block_cnt [B, H, NQ], NQ even. Returns
+    (idx [B, H, NQ/2, ld] int32, cnt [B, H, NQ/2] int32, unpaired): row p
+    holds the count of row 2p and its first min(count, ld) entries (slots past
+    them hold ``fill``); ``unpaired`` counts the pairs whose two rows differ
+    in count or in any of those entries.
+    """
+    idx = np.asarray(kv_block_idx)
+    cnt = np.asarray(kv_block_cnt)
+    B, H, NQ, ld = idx.shape
+    if NQ % 2:
+        raise ValueError("the number of query tiles must be even")
+    out_idx = np.full((B, H, NQ // 2, ld), fill, dtype=np.int32)
+    out_cnt = np.zeros((B, H, NQ // 2), dtype=np.int32)
+    unpaired = 0
+    for b in range(B):
+        for h in range(H):
+            for p in range(NQ // 2):
+                c0, c1 = int(cnt[b, h, 2 * p]), int(cnt[b, h, 2 * p + 1])
+                n = max(0, min(c0, ld))
+                top = idx[b, h, 2 * p, :n]
+                out_idx[b, h, p, :n] = top
+                out_cnt[b, h, p] = c0
+                same = c0 == c1 and np.array_equal(top, idx[b, h, 2 * p + 1, :n])
+                unpaired += 0 if same else 1
+    return out_idx, out_cnt, unpaired

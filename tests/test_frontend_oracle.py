@@ -155,3 +155,47 @@ def test_transpose_csr_lists_exactly_the_selecting_query_tiles():
         small = max(1, int(q_cnt.max()) - 1)
         _, c2, ovf2 = frontend.transpose_csr(idx, cnt, NKV, small)
         assert ovf2 and np.array_equal(c2, q_cnt)
+
+
+@pytest.mark.parametrize("lblock,pkv", [((256, 256), 64), ((128, 64), 64), ((256, 256), 128)])
+def test_pairing_of_exact_expanded_q64_rows_gives_the_q128_csr(lblock, pkv):
+    """Exact expansion of a logical mask with LQ >= 128 gives Q64 rows whose
+    pairs always agree; the paired CSR is then the expansion at Q128 itself,
+    and it selects the same token pairs as the Q64 CSR."""
+    S = 1024
+    nql, nkvl = S // lblock[0], S // lblock[1]
+    mask = anchor_topk_mask(3, nql, nkvl, max(1, nkvl // 3), seed=17)[None]
+    ld = nkvl * (lblock[1] // pkv)
+    idx64, cnt64, _ = frontend.mask_to_csr(mask, lblock, (64, pkv), ld)
+    idx128, cnt128, _ = frontend.mask_to_csr(mask, lblock, (128, pkv), ld)
+    pidx, pcnt, unpaired = frontend.pair_q_tiles(idx64, cnt64)
+    assert unpaired == 0
+    assert np.array_equal(pidx, idx128) and np.array_equal(pcnt, cnt128)
+    assert np.array_equal(_selected_by_csr(pidx, pcnt, (128, pkv), S), _selected_by_csr(idx64, cnt64, (64, pkv), S))
+
+
+def test_pairing_counts_each_kind_of_differing_pair():
+    """Starting from a fully paired CSR, each planted difference (one entry
+    changed, two entries swapped, a count changed, a difference only past the
+    stored prefix) is counted exactly when it changes the stored list."""
+    mask = anchor_topk_mask(2, 4, 16, 5, seed=3)[None]
+    idx, cnt, _ = frontend.mask_to_csr(mask, (256, 64), (64, 64), 16)
+    assert frontend.pair_q_tiles(idx, cnt)[2] == 0
+    idx, cnt = idx.copy(), cnt.copy()
+    assert np.all(cnt == 5)
+    idx[0, 0, 1, 0] = min(set(range(16)) - set(idx[0, 0, 0, :5].tolist()))  # another tile
+    idx[0, 1, 3, [0, 1]] = idx[0, 1, 3, [1, 0]]   # same set, another order: not paired
+    cnt[0, 1, 5] -= 1                              # shorter list
+    idx[0, 0, 7, 10] = 3                           # past the count: ignored
+    _, _, unpaired = frontend.pair_q_tiles(idx, cnt)
+    assert unpaired == 3
+    pidx, pcnt, _ = frontend.pair_q_tiles(idx, cnt)
+    assert pcnt[0, 1, 2] == cnt[0, 1, 4] and np.array_equal(pidx[0, 1, 1, :5], idx[0, 1, 2, :5])
+
+
+def test_pairing_of_natively_sampled_q64_rows_is_refused():
+    mask = anchor_count_mask(2, 32, 32, 3, 12, seed=5)[None]
+    idx, cnt, _ = frontend.mask_to_csr(mask, (64, 64), (64, 64), 32)
+    assert frontend.pair_q_tiles(idx, cnt)[2] > 0
+    with pytest.raises(ValueError):
+        frontend.pair_q_tiles(idx[:, :, :3], cnt[:, :, :3])

@@ -56,6 +56,10 @@ def parse_args():
     ap.add_argument("--ragged", type=int, default=None, metavar="SEED",
                     help="partial KV tiles: ragged valid-token counts per logical KV block drawn with this seed "
                          "(the masked kernels run; throughput counts valid pairs only)")
+    ap.add_argument("--paired", action="store_true",
+                    help="64-row tiles through vsa_attn_fwd_paired: adjacent query tiles with identical lists run as "
+                         "128-row tiles (decided on the device; the timed scope then includes the pairing and both "
+                         "work lists)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward leg (dQ, dK, dV of the same workload; reported beside the headline)")
     ap.add_argument("--traffic-from-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -126,20 +130,35 @@ def main():
         vbs = torch.from_numpy(W.ragged_block_sizes(S // lkv, lkv, seed=args.ragged)).to(dev)
         kv_valid = torch.empty((S // bkv,), dtype=torch.int32, device=dev)
 
+    if args.paired and bq != 64:
+        print("--paired needs 64-row query tiles", file=sys.stderr)
+        return 2
+
+    def attention():
+        if args.paired:
+            vsa.vsa_attn_fwd_paired(q, k, v, idx, cnt, bkv, scale, o, lse, stream=stream, kv_valid=kv_valid)
+        else:
+            vsa.vsa_attn_fwd_worklist(q, k, v, idx, cnt, bq, bkv, work, scale, o, lse, stream=stream,
+                                      kv_valid=kv_valid)
+
     def step(ev0=None, ev1=None):
         vsa.vsa_mask_to_csr(mask, (lq, lkv), (bq, bkv), ld, idx, cnt, stream=stream)
-        vsa.vsa_build_worklist(cnt, ld, work, segment=nq, stream=stream)
+        if not args.paired:
+            vsa.vsa_build_worklist(cnt, ld, work, segment=nq, stream=stream)
         if vbs is not None:
             vsa.vsa_expand_valid(vbs, lkv, bkv, kv_valid, stream=stream)
         if ev0 is not None:
             ev0.record(stream)
-        vsa.vsa_attn_fwd_worklist(q, k, v, idx, cnt, bq, bkv, work, scale, o, lse, stream=stream, kv_valid=kv_valid)
+        attention()
         if ev1 is not None:
             ev1.record(stream)
 
     step()
     torch.cuda.synchronize()
     pairs = selected_pairs(idx, cnt, bq, bkv, kv_valid)
+    run_bq = bq
+    if args.paired:  # which schedule the device will choose (read once, outside the timed region)
+        run_bq = 128 if int(vsa.vsa_pair_q_tiles(idx, cnt)[2].item()) == 0 else 64
     flops = 4.0 * D * pairs
     t_pre = time.perf_counter() + args.prewarm_seconds
     while time.perf_counter() < t_pre:
@@ -168,7 +187,10 @@ def main():
         vsa.vsa_mask_to_csr(mask, (lq, lkv), (bq, bkv), ld, idx, cnt, stream=stream)
         if vbs is not None:
             vsa.vsa_expand_valid(vbs, lkv, bkv, kv_valid, stream=stream)
-        vsa.vsa_attn_fwd(q, k, v, idx, cnt, bq, bkv, scale, o, lse, stream=stream, kv_valid=kv_valid)
+        if args.paired:
+            attention()
+        else:
+            vsa.vsa_attn_fwd(q, k, v, idx, cnt, bq, bkv, scale, o, lse, stream=stream, kv_valid=kv_valid)
 
     for _ in range(2):
         wrapper()
@@ -191,8 +213,7 @@ def main():
             junk.fill_(i & 0xFF)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            vsa.vsa_attn_fwd_worklist(q, k, v, idx, cnt, bq, bkv, work, scale, o, lse, stream=stream,
-                                      kv_valid=kv_valid)
+            attention()
             e1.record(stream)
             fl_events.append((e0, e1))
         torch.cuda.synchronize()
@@ -206,8 +227,8 @@ def main():
     # Algorithmic HBM bytes of one kernel launch: Q, K, V read once, O and
     # LSE written once, CSR indices and counts read once.
     alg_bytes = (3 * B * S * H * D + B * S * H * D) * 2 + B * H * S * 4 + (B * H * nq) * (ld + 2) * 4
-    kname = kernel_name(bq, bkv, D, partial=kv_valid is not None)
-    traffic = read_traffic(args.traffic or default_traffic_path(kname, wl.name, bq, bkv), kname)
+    kname = kernel_name(run_bq, bkv, D, partial=kv_valid is not None)
+    traffic = read_traffic(args.traffic or default_traffic_path(kname, wl.name, run_bq, bkv), kname)
 
     result = {
         "metric": METRIC,
@@ -226,6 +247,7 @@ def main():
             "workload": wl.name,
             "batch": B, "heads": H, "seq_len": S, "head_dim": D,
             "logical_block": f"{lq}x{lkv}", "tile": f"{bq}x{bkv}",
+            "paired_onto": f"{run_bq}x{bkv}" if args.paired else None,
             "selected_pairs": pairs,
             "density": round(pairs / (B * H * S * S), 5),
             "parallelism": "single_gpu",

@@ -36,7 +36,9 @@ SYMBOLS = (
     "vsa_build_worklist",
     "vsa_expand_valid",
     "vsa_csr_transpose",
+    "vsa_pair_q_tiles",
     "vsa_attn_fwd",
+    "vsa_attn_fwd_paired",
     "vsa_attn_fwd_worklist",
     "vsa_attn_bwd",
     "vsa_release",
@@ -83,6 +85,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vsa_expand_valid.restype = i32
     lib.vsa_csr_transpose.argtypes = [p, p, i32, i32, i32, i32, i32, p, i32, p, p, p]
     lib.vsa_csr_transpose.restype = i32
+    lib.vsa_pair_q_tiles.argtypes = [p, p, i32, i32, i32, i32, p, p, p, p]
+    lib.vsa_pair_q_tiles.restype = i32
+    lib.vsa_attn_fwd_paired.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, p]
+    lib.vsa_attn_fwd_paired.restype = i32
     lib.vsa_attn_bwd.argtypes = [p, p, p, p, p, p, p, p, i32, p, p, i32, p, i32, i32, i32, i32, i32, i32, f32, p, p,
                                  p, p]
     lib.vsa_attn_bwd.restype = i32
@@ -175,6 +181,49 @@ def vsa_attn_fwd(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale=N
         _stream_ptr(stream, q.device))
     _check(rc)
     return o, lse
+
+
+def vsa_attn_fwd_paired(q, k, v, kv_block_idx, kv_block_cnt, block_kv, scale=None, o=None, lse=None, stream=None,
+                        kv_valid=None):
+    """Forward over a 64-row query tile CSR that runs adjacent tiles as one
+    128-row tile when every pair has identical lists (decided on the device);
+    returns (o, lse), the same as vsa_attn_fwd with block_q=64 up to rounding order."""
+    B, S, H, D, o, lse = _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, 64, block_kv, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = load_library().vsa_attn_fwd_paired(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(),
+        _valid_ptr(kv_valid, S, block_kv, q.device), B, S, H, D,
+        kv_block_idx.shape[3], block_kv, float(scale), o.data_ptr(), lse.data_ptr(), _stream_ptr(stream, q.device))
+    _check(rc)
+    return o, lse
+
+
+def vsa_pair_q_tiles(kv_block_idx, kv_block_cnt, paired_idx=None, paired_cnt=None, unpaired=None, stream=None):
+    """Pair query tiles (2p, 2p+1): returns (paired_idx [B,H,NQ/2,ld],
+    paired_cnt [B,H,NQ/2], unpaired [1]) as GPU tensors; no host sync."""
+    _dev(kv_block_idx, "kv_block_idx", torch.int32, 4)
+    _dev(kv_block_cnt, "kv_block_cnt", torch.int32, 3)
+    B, H, NQ, LD = kv_block_idx.shape
+    if tuple(kv_block_cnt.shape) != (B, H, NQ):
+        raise ValueError("kv_block_cnt must be [B, H, NQ]")
+    dev = kv_block_idx.device
+    if paired_idx is None:
+        paired_idx = torch.full((B, H, NQ // 2, LD), -1, dtype=torch.int32, device=dev)
+    if paired_cnt is None:
+        paired_cnt = torch.empty((B, H, NQ // 2), dtype=torch.int32, device=dev)
+    if unpaired is None:
+        unpaired = torch.empty((1,), dtype=torch.int32, device=dev)
+    _dev(paired_idx, "paired_idx", torch.int32, 4)
+    _dev(paired_cnt, "paired_cnt", torch.int32, 3)
+    _dev(unpaired, "unpaired", torch.int32, 1)
+    if tuple(paired_idx.shape) != (B, H, NQ // 2, LD) or tuple(paired_cnt.shape) != (B, H, NQ // 2):
+        raise ValueError("paired_idx / paired_cnt must be [B, H, NQ/2, ld] / [B, H, NQ/2]")
+    rc = load_library().vsa_pair_q_tiles(kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(), B, H, NQ, LD,
+                                         paired_idx.data_ptr(), paired_cnt.data_ptr(), unpaired.data_ptr(),
+                                         _stream_ptr(stream, dev))
+    _check(rc)
+    return paired_idx, paired_cnt, unpaired
 
 
 def vsa_attn_fwd_worklist(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, work_list, scale=None, o=None,

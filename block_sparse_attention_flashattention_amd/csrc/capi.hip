@@ -99,6 +99,7 @@ struct DeviceBuffer {
 std::mutex g_buf_mutex;
 std::vector<DeviceBuffer> g_bufs;      // forward work list
 std::vector<DeviceBuffer> g_bwd_bufs;  // backward scratch (D, LSE*log2 e, two work lists)
+std::vector<DeviceBuffer> g_pair_bufs; // paired forward: counter, paired CSR, two work lists
 
 int32_t device_buffer(std::vector<DeviceBuffer>& bufs, size_t bytes, void** out) {
     int dev = 0;
@@ -133,7 +134,7 @@ int32_t worklist_buffer(size_t bytes, int32_t** out) {
 
 extern "C" {
 
-int32_t vsa_abi_version(void) { return 3; }
+int32_t vsa_abi_version(void) { return 4; }
 
 const char* vsa_status_string(int32_t status) {
     switch (status) {
@@ -235,6 +236,70 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
                                    idx_ld, block_q, block_kv, scale, work, n_items, o, lse);
     e = vsa::launch_fwd(block_q, block_kv, head_dim, p, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    return VSA_OK;
+}
+
+int32_t vsa_pair_q_tiles(const int32_t* kv_block_idx, const int32_t* kv_block_cnt, int32_t batch, int32_t heads,
+                         int32_t nq, int32_t idx_ld, int32_t* paired_idx, int32_t* paired_cnt, int32_t* unpaired,
+                         void* stream) {
+    g_last_error[0] = 0;
+    VSA_REQUIRE(kv_block_idx && kv_block_cnt && paired_idx && paired_cnt && unpaired, VSA_ERR_INVALID_ARG,
+                "null pointer");
+    VSA_REQUIRE(batch >= 1 && heads >= 1 && nq >= 2 && nq % 2 == 0, VSA_ERR_INVALID_ARG,
+                "batch and heads must be >= 1 and nq a positive even number (got nq=%d)", nq);
+    VSA_REQUIRE(idx_ld >= 1, VSA_ERR_INVALID_ARG, "idx_ld must be >= 1");
+    VSA_REQUIRE((int64_t)batch * heads * nq * idx_ld <= INT32_MAX, VSA_ERR_INVALID_ARG, "problem too large");
+    VSA_REQUIRE(aligned(kv_block_idx, 4) && aligned(kv_block_cnt, 4) && aligned(paired_idx, 4) &&
+                    aligned(paired_cnt, 4) && aligned(unpaired, 4),
+                VSA_ERR_INVALID_ARG, "index buffers must be 4-byte aligned");
+    hipError_t e = vsa::launch_pair_q_tiles(kv_block_idx, kv_block_cnt, batch * heads * (nq / 2), idx_ld, paired_idx,
+                                            paired_cnt, unpaired, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "pair_q_tiles launch");
+    return VSA_OK;
+}
+
+int32_t vsa_attn_fwd_paired(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
+                            const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch, int32_t seqlen,
+                            int32_t heads, int32_t head_dim, int32_t idx_ld, int32_t block_kv, float scale, void* o,
+                            float* lse, void* stream) {
+    g_last_error[0] = 0;
+    int32_t rc = check_fwd(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld, 64,
+                           block_kv, scale, o, lse);
+    if (rc != VSA_OK) return rc;
+    VSA_REQUIRE(idx_ld <= vsa::kWorklistMaxCnt, VSA_ERR_UNSUPPORTED, "idx_ld %d exceeds the work-list sort limit %d",
+                idx_ld, vsa::kWorklistMaxCnt);
+    if (seqlen % 128 != 0 || !vsa::fwd_supported(128, block_kv, head_dim))  // nothing to pair
+        return vsa_attn_fwd(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld, 64,
+                            block_kv, scale, o, lse, stream);
+    const int nq = seqlen / 64;
+    const int64_t n_items = (int64_t)batch * heads * nq, n_pairs = n_items / 2;
+    // [unpaired, pad to 256 B][paired cnt][work 128][work 64][paired idx]
+    const size_t words = 64 + (size_t)n_pairs * 2 + (size_t)n_items + (size_t)n_pairs * idx_ld;
+    void* buf = nullptr;
+    rc = device_buffer(g_pair_bufs, words * sizeof(int32_t), &buf);
+    if (rc != VSA_OK) return rc;
+    int32_t* unpaired = (int32_t*)buf;
+    int32_t* pcnt = unpaired + 64;
+    int32_t* work128 = pcnt + n_pairs;
+    int32_t* work64 = work128 + n_pairs;
+    int32_t* pidx = work64 + n_items;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = vsa::launch_pair_q_tiles(kv_block_idx, kv_block_cnt, (int)n_pairs, idx_ld, pidx, pcnt, unpaired, st);
+    if (e != hipSuccess) return hip_fail(e, "pair_q_tiles launch");
+    // Exactly one of the two schedules gets a non-empty work list: the
+    // 128-row one if every pair agrees, else the native 64-row one.
+    e = vsa::launch_build_worklist(pcnt, (int)n_pairs, nq / 2, idx_ld, work128, st, unpaired, true);
+    if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
+    e = vsa::launch_build_worklist(kv_block_cnt, (int)n_items, nq, idx_ld, work64, st, unpaired, false);
+    if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
+    vsa::FwdParams p128 = make_params(q, k, v, pidx, pcnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld, 128,
+                                      block_kv, scale, work128, (int32_t)n_pairs, o, lse);
+    e = vsa::launch_fwd(128, block_kv, head_dim, p128, st);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch (128-row tiles)");
+    vsa::FwdParams p64 = make_params(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim,
+                                     idx_ld, 64, block_kv, scale, work64, (int32_t)n_items, o, lse);
+    e = vsa::launch_fwd(64, block_kv, head_dim, p64, st);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch (64-row tiles)");
     return VSA_OK;
 }
 
@@ -346,7 +411,7 @@ int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 void vsa_release(void) {
     std::lock_guard<std::mutex> lock(g_buf_mutex);
-    for (auto* v : {&g_bufs, &g_bwd_bufs}) {
+    for (auto* v : {&g_bufs, &g_bwd_bufs, &g_pair_bufs}) {
         for (auto& b : *v) {
             if (b.ptr) (void)hipFree(b.ptr);
             b.ptr = nullptr;

@@ -66,9 +66,14 @@ __device__ __forceinline__ uint64_t same_key_lanes(int key, bool active) {
 // segment; per-wave histograms give each wave its own output offsets, and
 // within a wave the rank among equal keys comes from ballots, so the result
 // is deterministic and equal keys keep ascending item order.
+//
+// With a gate, the list is built only if (*gate == 0) == run_if_zero;
+// otherwise every entry is -1, which the attention kernels skip. This lets
+// the device choose between two schedules without a host round trip.
 template <int WAVES, int BINS, int KEY_BITS>
 __global__ __launch_bounds__(WAVES * 64) void worklist_kernel(const int32_t* __restrict__ cnt_all, int seg,
-                                                             int max_cnt, int32_t* __restrict__ work_all) {
+                                                             int max_cnt, int32_t* __restrict__ work_all,
+                                                             const int32_t* __restrict__ gate, int run_if_zero) {
     const int32_t* cnt = cnt_all + (int64_t)blockIdx.x * seg;
     int32_t* work = work_all + (int64_t)blockIdx.x * seg;
     const int first_item = blockIdx.x * seg;
@@ -77,6 +82,10 @@ __global__ __launch_bounds__(WAVES * 64) void worklist_kernel(const int32_t* __r
     __shared__ int wave_total[WAVES];
     constexpr int NT = WAVES * 64;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (gate != nullptr && ((*gate == 0) != (run_if_zero != 0))) {
+        for (int i = tid; i < n; i += NT) work[i] = -1;
+        return;
+    }
     const int nbins = max_cnt + 1;
     for (int i = tid; i < WAVES * BINS; i += NT) (&hist[0][0])[i] = 0;
     __syncthreads();
@@ -199,6 +208,42 @@ __global__ __launch_bounds__(1024) void csr_transpose_kernel(const int32_t* __re
     }
 }
 
+// Pairing of query tiles (2p, 2p+1) onto tiles twice as tall (FastVideo page:
+// the Q64 children of one Q256 row share their KV list and run on the
+// Q128/KV64 schedule). One wave per pair: row p of the output takes row 2p's
+// count and stored entries; a pair whose counts or stored entries differ adds
+// one to *unpaired (zeroed by zero_kernel before this launch).
+__global__ __launch_bounds__(256) void pair_q_tiles_kernel(const int32_t* __restrict__ idx,
+                                                           const int32_t* __restrict__ cnt, int n_pairs, int ld,
+                                                           int32_t* __restrict__ out_idx,
+                                                           int32_t* __restrict__ out_cnt,
+                                                           int32_t* __restrict__ unpaired) {
+    const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (pair >= n_pairs) return;
+    const int c0 = cnt[2 * (int64_t)pair], c1 = cnt[2 * (int64_t)pair + 1];
+    const int n = c0 < 0 ? 0 : (c0 > ld ? ld : c0);
+    const int32_t* r0 = idx + 2 * (int64_t)pair * ld;
+    const int32_t* r1 = r0 + ld;
+    int32_t* o = out_idx + (int64_t)pair * ld;
+    bool differ = false;
+    for (int base = 0; base < n; base += 64) {
+        const int j = base + lane;
+        if (j < n) {
+            const int32_t t = r0[j];
+            o[j] = t;
+            differ |= t != r1[j];
+        }
+    }
+    differ = __ballot(differ) != 0ull || c0 != c1;
+    if (lane == 0) {
+        out_cnt[pair] = c0;
+        if (differ) atomicAdd(unpaired, 1);
+    }
+}
+
+__global__ void zero_kernel(int32_t* p) { *p = 0; }
+
 // Valid keys per physical KV tile from valid tokens per logical KV block:
 // tile r of block T keeps clamp(vbs[T] - r*block_kv, 0, block_kv).
 __global__ void expand_valid_kernel(const int32_t* vbs, int n_out, int kv_ratio, int block_kv, int32_t* out) {
@@ -222,16 +267,26 @@ hipError_t launch_mask_to_csr(const uint8_t* mask, int batch, int heads, int nq_
 }
 
 hipError_t launch_build_worklist(const int32_t* cnt, int n_items, int segment, int max_cnt, int32_t* work,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, const int32_t* gate, bool run_if_zero) {
     if (n_items <= 0) return hipSuccess;
     const int n_seg = n_items / segment;
     if (max_cnt < 2048) {
         hipLaunchKernelGGL((worklist_kernel<4, 2048, 11>), dim3(n_seg), dim3(256), 0, stream, cnt, segment, max_cnt,
-                           work);
+                           work, gate, (int)run_if_zero);
     } else {
         hipLaunchKernelGGL((worklist_kernel<1, 8192, 13>), dim3(n_seg), dim3(64), 0, stream, cnt, segment, max_cnt,
-                           work);
+                           work, gate, (int)run_if_zero);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_pair_q_tiles(const int32_t* idx, const int32_t* cnt, int n_pairs, int ld, int32_t* out_idx,
+                               int32_t* out_cnt, int32_t* unpaired, hipStream_t stream) {
+    hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(1), 0, stream, unpaired);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || n_pairs <= 0) return e;
+    hipLaunchKernelGGL(pair_q_tiles_kernel, dim3((n_pairs + 3) / 4), dim3(256), 0, stream, idx, cnt, n_pairs, ld,
+                       out_idx, out_cnt, unpaired);
     return hipGetLastError();
 }
 

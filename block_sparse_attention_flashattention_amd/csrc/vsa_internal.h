@@ -60,8 +60,14 @@ bool bwd_supported(int block_q, int block_kv, int head_dim);
 hipError_t launch_mask_to_csr(const uint8_t* mask, int batch, int heads, int nq_logical, int nkv_logical,
                               int q_ratio, int kv_ratio, int nq_physical, int32_t* idx, int ld, int32_t* cnt,
                               int32_t* overflow, hipStream_t stream);
+// With a gate, the list is built only if (*gate == 0) == run_if_zero, and
+// is all -1 (skipped by the kernels) otherwise.
 hipError_t launch_build_worklist(const int32_t* cnt, int n_items, int segment, int max_cnt, int32_t* work,
-                                 hipStream_t stream);
+                                 hipStream_t stream, const int32_t* gate = nullptr, bool run_if_zero = true);
+// Query tiles (2p, 2p+1) -> tile p of twice the height; *unpaired = number of
+// pairs whose lists differ (zeroed by the launch itself, in stream order).
+hipError_t launch_pair_q_tiles(const int32_t* idx, const int32_t* cnt, int n_pairs, int ld, int32_t* out_idx,
+                               int32_t* out_cnt, int32_t* unpaired, hipStream_t stream);
 // Q-direction CSR for the backward pass; nq must be <= 32 * kTransposeMaxWords.
 hipError_t launch_csr_transpose(const int32_t* idx, const int32_t* cnt, int batch_heads, int nq, int nkv, int ld,
                                 int32_t* q_idx, int q_ld, int32_t* q_cnt, int32_t* overflow, hipStream_t stream);

@@ -1,5 +1,5 @@
 /*
- * vsa_attn.h -- block-sparse attention forward for AMD Instinct MI355X (gfx950).
+ * vsa_attn.h -- block-sparse attention (forward and backward) for AMD Instinct MI355X (gfx950).
  *
  * C ABI of libvsa_attn.so. Every entry point takes plain pointers and sizes;
  * no framework types cross this boundary.
@@ -23,7 +23,7 @@
  *      kv_block_idx    [batch, heads, seqlen/block_q, idx_ld]  int32
  *      kv_block_cnt    [batch, heads, seqlen/block_q]          int32
  *    This is the per-query-tile list form of FA4's block-sparse tensors
- *    (page 3, block_sparsity.py, BlockSparseTensorsTorch full_block_cnt /
+ *    (FastVideo page, fa4 block_sparsity.py, BlockSparseTensorsTorch full_block_cnt /
  *    full_block_idx, including the "compact" last dimension idx_ld that
  *    only needs to hold the largest count).
  *  - Pointers named in a signature are DEVICE pointers unless stated. The
@@ -79,7 +79,7 @@ const char* vsa_last_error(void);
 /*
  * vsa_mask_to_csr -- mask front-end, step 1: exact expansion + block CSR.
  *
- * Source: page 3, bench_vsa_blackwell.py, expand_exact256_mask (repeat every
+ * Source: FastVideo page, bench_vsa_blackwell.py, expand_exact256_mask (repeat every
  * logical row block_q-fold and column block_kv-fold, which keeps the
  * selected token pairs) and arm_fa4 (per physical Q tile, the ascending
  * indices of its selected physical KV tiles, and their count).
@@ -163,7 +163,7 @@ int32_t vsa_expand_valid(const int32_t* vbs, int32_t nkv_logical, int32_t logica
 /*
  * vsa_attn_fwd -- fused block-sparse attention forward (O and LSE).
  *
- * Source: page 3, bench_vsa_blackwell.py, ref_masked_sdpa_fp32 (what is
+ * Source: FastVideo page, bench_vsa_blackwell.py, ref_masked_sdpa_fp32 (what is
  * computed) and arm_fa4 / the _flash_attn_fwd call (the tile-list input and
  * outputs). Online softmax in base 2 with scale*log2(e) folded into one
  * multiply (page "BlackwellMultiHeadLatentAttentionForwardFP8", softmax
@@ -199,9 +199,53 @@ int32_t vsa_attn_fwd_worklist(const void* q, const void* k, const void* v, const
                               float* lse, void* stream);
 
 /*
+ * vsa_pair_q_tiles -- pair query tiles (2p, 2p+1) onto tiles twice as tall.
+ *
+ * Source: FastVideo page, README of the fine-grained VSA kernels and the
+ * notes of bench_vsa_blackwell.py: at the Q256 API boundary the Q64 children
+ * of one logical row have identical KV lists and are paired onto the
+ * physical Q128/KV64 schedule; distinct Q64 lists keep the native kernel.
+ *
+ *   kv_block_idx / kv_block_cnt   CSR of nq query tiles (nq even, >= 2)
+ *   paired_idx     out [batch, heads, nq/2, idx_ld]: row p holds the first
+ *                  min(count, idx_ld) entries of row 2p (slots past them
+ *                  are not written)
+ *   paired_cnt     out [batch, heads, nq/2]: the count of row 2p
+ *   unpaired       out, one device int32: the number of pairs whose counts
+ *                  or stored entries (compared in order) differ; written in
+ *                  stream order, no host synchronisation.
+ * The paired CSR selects the same token pairs as the input iff *unpaired
+ * is 0.
+ */
+int32_t vsa_pair_q_tiles(const int32_t* kv_block_idx, const int32_t* kv_block_cnt, int32_t batch, int32_t heads,
+                         int32_t nq, int32_t idx_ld, int32_t* paired_idx, int32_t* paired_cnt, int32_t* unpaired,
+                         void* stream);
+
+/*
+ * vsa_attn_fwd_paired -- vsa_attn_fwd for a 64-row query tile CSR that runs
+ * adjacent tiles as 128-row tiles when every pair has identical lists.
+ *
+ * Same arguments as vsa_attn_fwd with block_q = 64. The pairing
+ * (vsa_pair_q_tiles) and the choice are made on the device: the 128-row
+ * kernel runs over the paired CSR if every pair agrees, otherwise the
+ * native 64-row kernel runs over the input; the other launch finds an empty
+ * work list. Either way O and LSE are those of the input CSR (the 128-row
+ * kernel splits each list over two streams instead of four, so the
+ * rounding order differs). If seqlen is not a multiple of 128 this is
+ * vsa_attn_fwd. Uses a library-owned device buffer of about
+ * 4*(batch*heads*seqlen/64)*(idx_ld/2 + 2) bytes (grown on demand per
+ * device, released by vsa_release); calls on one device must not overlap
+ * in time on different streams.
+ */
+int32_t vsa_attn_fwd_paired(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
+                            const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch, int32_t seqlen,
+                            int32_t heads, int32_t head_dim, int32_t idx_ld, int32_t block_kv, float scale, void* o,
+                            float* lse, void* stream);
+
+/*
  * vsa_attn_bwd -- backward pass: dQ, dK and dV of vsa_attn_fwd.
  *
- * Source: the gradient of page 3's ref_masked_sdpa_fp32 (the function the
+ * Source: the gradient of the FastVideo page's ref_masked_sdpa_fp32 (the function the
  * forward computes); the backward walks, per KV tile, the query tiles that
  * select it (FA4 block_sparsity.py, normalize_block_sparse_config_bwd). With
  * P recomputed from the forward's LSE, D_i = dO_i . O_i, dS = P (dO V^T - D):

@@ -18,7 +18,7 @@
  * with no selected key gives O = 0 and LSE = -inf).
  *
  * Block mask input is the per-Q-tile list form used by FA4's block-sparse
- * interface (page 3, block_sparsity.py, BlockSparseTensorsTorch full_block_*):
+ * interface (FastVideo page, fa4 block_sparsity.py, BlockSparseTensorsTorch full_block_*):
  * kv_block_idx [B,H,NQ,ld] int32 (row p uses entries [0, cnt)), kv_block_cnt
  * [B,H,NQ] int32. Entries may be in any order; they must be distinct and in
  * [0, S/block_kv).

@@ -36,7 +36,7 @@ def test_header_declares_the_binding_symbols():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.vsa_abi_version() == 3
+    assert lib.vsa_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -173,3 +173,25 @@ def _bwd(lib, **kw):
 def test_attn_bwd_rejects_invalid_arguments(lib, kw, status, needle):
     assert _bwd(lib, **kw) == status
     assert needle in lib.vsa_last_error().decode()
+
+
+def test_pair_q_tiles_validation(lib):
+    f = lib.vsa_pair_q_tiles
+    # kv_block_idx, kv_block_cnt, B, H, nq, idx_ld, paired_idx, paired_cnt, unpaired, stream
+    assert f(None, A, 1, 1, 4, 4, A, A, A, None) == -1
+    assert f(A, A, 1, 1, 4, 4, A, A, None, None) == -1
+    assert f(A, A, 1, 1, 5, 4, A, A, A, None) == -1  # odd tile count
+    assert "even" in lib.vsa_last_error().decode()
+    assert f(A, A, 1, 1, 0, 4, A, A, A, None) == -1
+    assert f(A, A, 1, 1, 4, 0, A, A, A, None) == -1
+    assert f(A, A, 1, 1, 4, 4, A, A, A + 2, None) == -1
+
+
+def test_attn_fwd_paired_validation(lib):
+    f = lib.vsa_attn_fwd_paired
+    # q, k, v, idx, cnt, kv_valid, B, S, H, D, ld, block_kv, scale, o, lse, stream
+    assert f(A, A, A, A, A, None, 1, 1024, 2, 128, 16, 64, 0.1, None, A, None) == -1
+    assert f(A, A, A, A, A, None, 1, 1000, 2, 128, 16, 64, 0.1, A, A, None) == -1  # not a multiple of 64
+    assert f(A, A, A, A, A, None, 1, 1024, 2, 96, 16, 64, 0.1, A, A, None) == -2
+    assert f(A, A, A, A, A, None, 1, 1024, 2, 128, 16, 256, 0.1, A, A, None) == -2
+    assert f(A, A, A, A, A, None, 1, 1024, 2, 128, 9000, 64, 0.1, A, A, None) in (-1, -2)

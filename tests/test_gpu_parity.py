@@ -359,3 +359,125 @@ def test_vsa256_ragged_blocks_sampled_and_cross_shape(vsa):
         assert d.max().item() <= O_MAX_ABS and d.mean().item() <= O_MEAN_ABS and lrel <= LSE_REL
         del o1, l1
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------- Q64 pairing onto Q128 tiles
+
+def _exact_expanded_q64(B, H, S, lblock, bkv, keep, seed):
+    mask = np.stack([W.anchor_topk_mask(H, S // lblock[0], S // lblock[1], keep, seed=seed + b) for b in range(B)])
+    ld = keep * (lblock[1] // bkv)
+    idx, cnt, _ = ofront.mask_to_csr(mask, lblock, (64, bkv), ld)
+    return idx, cnt
+
+
+PAIR_CASES = [
+    ("vsa256 exact 64x64", W.VSA256, (64, 64), 52),
+    ("native64", W.NATIVE64, (64, 64), 92),
+]
+
+
+@pytest.mark.parametrize("label,wl,shape,ld", PAIR_CASES, ids=[c[0] for c in PAIR_CASES])
+def test_pair_q_tiles_bit_exact(vsa, label, wl, shape, ld):
+    say(f"pair_q_tiles {label}")
+    idx_ref, cnt_ref, _ = ofront.mask_to_csr(wl.logical_mask(), wl.logical_block, shape, ld)
+    pidx_ref, pcnt_ref, unp_ref = ofront.pair_q_tiles(idx_ref, cnt_ref)
+    pidx, pcnt, unp = vsa.vsa_pair_q_tiles(dev(idx_ref), dev(cnt_ref))
+    torch.cuda.synchronize()
+    assert int(unp.item()) == unp_ref
+    assert np.array_equal(pcnt.cpu().numpy(), pcnt_ref)
+    valid = np.arange(ld)[None, None, None, :] < np.minimum(pcnt_ref, ld)[..., None]
+    assert np.array_equal(np.where(valid, pidx.cpu().numpy(), -1), np.where(valid, pidx_ref, -1))
+    say(f"pair_q_tiles {label}: unpaired={unp_ref}")
+
+
+def test_pair_q_tiles_planted_differences(vsa):
+    """Pairs that differ in one entry, in order only, in count, or only past
+    the stored prefix (ignored); counts above ld and negative counts."""
+    say("pair_q_tiles planted differences")
+    idx, cnt = _exact_expanded_q64(2, 3, 4096, (256, 256), 64, 5, seed=41)
+    ld = idx.shape[-1]
+    idx, cnt = idx.copy(), cnt.copy()
+    idx[0, 0, 1, 0] = min(set(range(64)) - set(idx[0, 0, 0, :10].tolist()))
+    idx[0, 1, 3, [0, 1]] = idx[0, 1, 3, [1, 0]]
+    cnt[1, 2, 5] -= 1
+    cnt[1, 0, 8] = cnt[1, 0, 9] = ld + 7          # both clamp to ld: the stored entries agree
+    cnt[1, 1, 10] = cnt[1, 1, 11] = -3            # both empty
+    pidx_ref, pcnt_ref, unp_ref = ofront.pair_q_tiles(idx, cnt)
+    assert unp_ref == 3
+    pidx, pcnt, unp = vsa.vsa_pair_q_tiles(dev(idx), dev(cnt))
+    torch.cuda.synchronize()
+    assert int(unp.item()) == unp_ref
+    assert np.array_equal(pcnt.cpu().numpy(), pcnt_ref)
+    valid = np.arange(ld)[None, None, None, :] < np.clip(pcnt_ref, 0, ld)[..., None]
+    assert np.array_equal(np.where(valid, pidx.cpu().numpy(), -1), np.where(valid, pidx_ref, -1))
+
+
+PAIRED_FWD = [(bkv, D, partial) for bkv in (64, 128) for D in (64, 128) for partial in (False, True)]
+
+
+@pytest.mark.parametrize("bkv,D,partial", PAIRED_FWD, ids=[f"kv{a}_d{b}{'_partial' if c else ''}" for a, b, c in
+                                                          PAIRED_FWD])
+def test_paired_forward_all_rows(vsa, bkv, D, partial):
+    """Exact-expanded Q64 lists run as 128-row tiles (bitwise the 128-row
+    result), distinct lists as 64-row tiles (bitwise the 64-row result);
+    both against the oracle on every row."""
+    B, H, S = 2, 2, 2048
+    q, k, v = W.qkv(B, S, H, D, seed=bkv + D + 71)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    scale = 1.0 / math.sqrt(D)
+    val = None
+    if partial:
+        val = W.ragged_block_sizes(S // bkv, bkv, seed=bkv + D, p_full=0.4)
+        val[:2] = [0, 1]
+    vald = None if val is None else dev(val)
+    pairable = _exact_expanded_q64(B, H, S, (256, 256), bkv, 3, seed=D + bkv)
+    distinct = W.random_csr(B, H, S // 64, S // bkv, S // bkv, 0, S // bkv // 2, seed=D + bkv + 1)
+    for label, (idx, cnt) in (("pairable", pairable), ("distinct", distinct)):
+        idx = np.ascontiguousarray(idx[..., :max(1, int(cnt.max()))])
+        say(f"paired forward {label} kv{bkv} D={D} partial={partial}")
+        pidx, pcnt, unp = ofront.pair_q_tiles(idx, cnt)
+        assert (unp == 0) == (label == "pairable")
+        o, lse = vsa.vsa_attn_fwd_paired(qd, kd, vd, dev(idx), dev(cnt), bkv, scale, kv_valid=vald)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.attn_full(q, k, v, idx, cnt, 64, bkv, scale, kv_valid=val)
+        check_rows(o, lse, np.arange(B * H * S), o_ref.transpose(0, 2, 1, 3).reshape(-1, D), lse_ref.reshape(-1),
+                   S, H, f"paired {label} kv{bkv} D={D}")
+        if label == "pairable":
+            o2, l2 = _run_fwd(vsa, qd, kd, vd, dev(pidx), dev(pcnt), 128, bkv, scale, kv_valid=vald)
+        else:
+            o2, l2 = _run_fwd(vsa, qd, kd, vd, dev(idx), dev(cnt), 64, bkv, scale, kv_valid=vald)
+        assert torch.equal(o, o2) and torch.equal(lse, l2), f"{label}: not the expected schedule's result"
+
+
+def test_paired_forward_odd_tile_count_runs_native(vsa):
+    B, H, S, D, bkv = 1, 2, 960, 64, 64
+    say("paired forward with an odd number of 64-row tiles")
+    q, k, v = W.qkv(B, S, H, D, seed=8)
+    idx, cnt = W.random_csr(B, H, S // 64, S // bkv, S // bkv, 0, 6, seed=9)
+    o, lse = vsa.vsa_attn_fwd_paired(dev(q), dev(k), dev(v), dev(idx), dev(cnt), bkv, 0.125)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_full(q, k, v, idx, cnt, 64, bkv, 0.125)
+    check_rows(o, lse, np.arange(B * H * S), o_ref.transpose(0, 2, 1, 3).reshape(-1, D), lse_ref.reshape(-1), S, H,
+               "paired odd nq")
+
+
+def test_vsa256_paired_64x64_sampled(vsa):
+    """The VSA-256 mask requested at 64x64 runs as 128x64 tiles: sampled rows
+    against the oracle and bitwise equal to the 128x64 kernel's result."""
+    wl = W.VSA256_FINE
+    say("paired forward vsa256 64x64: generating inputs")
+    q, k, v = wl.qkv()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    mask = dev(wl.logical_mask())
+    idx, cnt = vsa.vsa_mask_to_csr(mask, wl.logical_block, (64, 64), 52)
+    o, lse = vsa.vsa_attn_fwd_paired(qd, kd, vd, idx, cnt, 64, wl.scale)
+    torch.cuda.synchronize()
+    B, S, H, D = q.shape
+    rows = sample_rows(B, H, S, 64, 2, seed=64)
+    o_ref, lse_ref = oracle.attn_rows(q, k, v, idx.cpu().numpy(), cnt.cpu().numpy(), 64, 64, wl.scale, rows)
+    check_rows(o, lse, rows, o_ref, lse_ref, S, H, "vsa256 paired 64x64")
+    idx2, cnt2 = vsa.vsa_mask_to_csr(mask, wl.logical_block, (128, 64), 52)
+    o2, l2 = _run_fwd(vsa, qd, kd, vd, idx2, cnt2, 128, 64, wl.scale)
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+    del o, lse, o2, l2
+    torch.cuda.empty_cache()

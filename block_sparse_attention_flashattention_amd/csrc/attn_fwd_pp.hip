@@ -48,7 +48,12 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
 
     const int wi = xcd_contiguous_block();
     if (wi >= prm.n_work) return;
-    const int item = prm.work ? prm.work[wi] : wi;
+    // With split lists, workgroup wi serves part wi % splits of work entry
+    // wi / splits and takes the list entries part, part + splits, ...
+    const int SP = prm.splits;
+    const int slot = SP == 1 ? wi : wi / SP;
+    const int part = wi - slot * SP;
+    const int item = prm.work ? prm.work[slot] : slot;
     if (item < 0 || item >= prm.n_items) return;
 
     const int p = item % prm.nq;
@@ -61,9 +66,12 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     // The count, the CSR row, Q and the first K tile are all fetched at once
     // (none of these loads waits for another; the row is read up to its
     // allocated length ld, so it does not need the count first).
-    const int32_t* irow = prm.idx + (int64_t)item * prm.ld;
-    const int ldc = prm.ld < kIdxCap ? prm.ld : kIdxCap;
-    const int first_tile = __builtin_amdgcn_readfirstlane(irow[0]);
+    const int32_t* irow = prm.idx + (int64_t)item * prm.ld + part;
+    const int ldp = prm.ld > part ? (prm.ld - part + SP - 1) / SP : 0;  // this part's slots of the row
+    const int ldc = ldp < kIdxCap ? ldp : kIdxCap;
+    // (a part with no slot reads a valid address and ignores the value)
+    const int first_raw = __builtin_amdgcn_readfirstlane(*(ldp > 0 ? irow : prm.idx));
+    const int first_tile = ldp > 0 ? first_raw : -1;
     int n = prm.cnt[item];
     const int nkv = prm.nkv;
     const int q0 = p * BQ + wave * 32;
@@ -84,11 +92,13 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     // Stage this tile's CSR row in LDS: list entries are then read with
     // uniform LDS loads, which do not wait on outstanding global loads.
     int* lidx = (int*)(smem + LDS_TILES);
-    for (int i = tid; i < ldc; i += 512) lidx[i] = stage_entry<PARTIAL>(irow[i], nkv, BKV, prm.kv_valid);
+    for (int i = tid; i < ldc; i += 512) lidx[i] = stage_entry<PARTIAL>(irow[(int64_t)i * SP], nkv, BKV, prm.kv_valid);
     e.q_ready();
     // group 1 fetches K_0 (buffer 0 is free); an empty row fetches it too
     if (grp == 1) fetch.all(0, tile_at(kbase, first_tile), tok_bytes, false);
-    n = n < 0 ? 0 : (n > ldc ? ldc : n);
+    n = n < 0 ? 0 : (n > prm.ld ? prm.ld : n);
+    n = n > part ? (n - part + SP - 1) / SP : 0;  // this part's entries
+    n = n > ldc ? ldc : n;
     wait_global_loads();
     lds_barrier();
 
@@ -173,6 +183,27 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
         }
     }
 
+    if (SP > 1) {
+        // Split list: publish this part's rows; the last part of the item to
+        // arrive merges all parts in part order (so the result does not
+        // depend on which one that is) and writes O and LSE. Nothing waits.
+        constexpr int64_t WORDS = (int64_t)E::STATE_WORDS * 64;
+        e.export_state(prm.ws_partial + ((int64_t)wi * 8 + wave) * WORDS);
+        __threadfence();
+        lds_barrier();
+        int* flag = (int*)smem;  // the tile buffers are free now
+        if (tid == 0) {
+            const int last = atomicAdd(prm.ws_counter + item, 1) == SP - 1;
+            if (last) prm.ws_counter[item] = 0;  // ready for the next launch
+            *flag = last;
+        }
+        lds_barrier();
+        if (__builtin_amdgcn_readfirstlane(*flag) == 0) return;
+        __threadfence();
+        const float* parts = prm.ws_partial + ((int64_t)slot * SP * 8 + wave) * WORDS;
+        e.import_state(parts);
+        for (int q = 1; q < SP; ++q) e.merge_state(parts + (int64_t)q * 8 * WORDS);
+    }
     e.store(prm.o + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D,
             prm.lse + ((int64_t)b * prm.H + h) * S + q0 + l32);
 }

@@ -88,6 +88,9 @@ vsa::FwdParams make_params(const void* q, const void* k, const void* v, const in
     p.block_kv = block_kv;
     p.n_items = batch * heads * p.nq;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    p.splits = 1;
+    p.ws_counter = nullptr;
+    p.ws_partial = nullptr;
     return p;
 }
 
@@ -100,6 +103,8 @@ std::mutex g_buf_mutex;
 std::vector<DeviceBuffer> g_bufs;      // forward work list
 std::vector<DeviceBuffer> g_bwd_bufs;  // backward scratch (D, LSE*log2 e, two work lists)
 std::vector<DeviceBuffer> g_pair_bufs; // paired forward: counter, paired CSR, two work lists
+std::vector<DeviceBuffer> g_split_bufs; // split lists: per-item counters, then partial row states
+std::vector<int> g_cu_count;            // compute units per device
 
 int32_t device_buffer(std::vector<DeviceBuffer>& bufs, size_t bytes, void** out) {
     int dev = 0;
@@ -120,6 +125,41 @@ int32_t device_buffer(std::vector<DeviceBuffer>& bufs, size_t bytes, void** out)
         b.bytes = bytes;
     }
     *out = b.ptr;
+    return VSA_OK;
+}
+
+// Compute units of the current device (cached).
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(g_buf_mutex);
+    if ((int)g_cu_count.size() <= dev) g_cu_count.resize(dev + 1, 0);
+    if (g_cu_count[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) g_cu_count[dev] = n;
+    }
+    return g_cu_count[dev];
+}
+
+// Workspace of the split-list forward: counter_bytes of per-item counters
+// (zeroed whenever the buffer is (re)allocated; the kernel returns each to 0)
+// followed by the partial row states.
+int32_t split_buffer(size_t counter_bytes, size_t bytes, hipStream_t stream, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    bool fresh = false;
+    {
+        std::lock_guard<std::mutex> lock(g_buf_mutex);
+        if ((int)g_split_bufs.size() <= dev) g_split_bufs.resize(dev + 1);
+        fresh = g_split_bufs[dev].bytes < bytes;
+    }
+    int32_t rc = device_buffer(g_split_bufs, bytes, out);
+    if (rc != VSA_OK) return rc;
+    if (fresh) {
+        e = hipMemsetAsync(*out, 0, counter_bytes, stream);
+        if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(split counters)");
+    }
     return VSA_OK;
 }
 
@@ -234,6 +274,23 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
     if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
     vsa::FwdParams p = make_params(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim,
                                    idx_ld, block_q, block_kv, scale, work, n_items, o, lse);
+    // Too few 256-row work items to occupy every compute unit: split each
+    // list over 2 or 4 workgroups (partial states merged by the last one).
+    if (block_q == 256) {
+        const int cus = cu_count();
+        while (p.splits < 4 && (int64_t)n_items * p.splits * 2 <= cus) p.splits *= 2;
+    }
+    if (p.splits > 1) {
+        const size_t counters = ((size_t)n_items * sizeof(int32_t) + 255) / 256 * 256;
+        const size_t state_words = (size_t)(head_dim / 32 * 16 + 2) * 64;  // per wave
+        const size_t bytes = counters + (size_t)n_items * p.splits * 8 * state_words * sizeof(float);
+        void* ws = nullptr;
+        rc = split_buffer(counters, bytes, (hipStream_t)stream, &ws);
+        if (rc != VSA_OK) return rc;
+        p.ws_counter = (int32_t*)ws;
+        p.ws_partial = (float*)((char*)ws + counters);
+        p.n_work = n_items * p.splits;
+    }
     e = vsa::launch_fwd(block_q, block_kv, head_dim, p, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
     return VSA_OK;
@@ -411,7 +468,7 @@ int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 void vsa_release(void) {
     std::lock_guard<std::mutex> lock(g_buf_mutex);
-    for (auto* v : {&g_bufs, &g_bwd_bufs, &g_pair_bufs}) {
+    for (auto* v : {&g_bufs, &g_bwd_bufs, &g_pair_bufs, &g_split_bufs}) {
         for (auto& b : *v) {
             if (b.ptr) (void)hipFree(b.ptr);
             b.ptr = nullptr;

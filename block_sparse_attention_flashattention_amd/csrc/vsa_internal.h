@@ -23,6 +23,13 @@ struct FwdParams {
     int32_t S, H, nq, nkv, ld;
     int32_t block_kv;        // tokens per KV tile of the CSR
     float scale_log2;        // softmax scale * log2(e)
+    // Split lists (256-row tiles only): work entry w is served by workgroups
+    // w*splits .. w*splits + splits-1, part q taking list entries q, q+splits, ...;
+    // partial states go to ws_partial, the last part to finish merges them
+    // (ws_counter: one int per item, zero between launches).
+    int32_t splits;
+    int32_t* ws_counter;
+    float* ws_partial;
 };
 
 // Launch the forward kernel for one (block_q, block_kv, head_dim); returns

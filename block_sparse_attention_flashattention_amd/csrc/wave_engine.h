@@ -364,6 +364,15 @@ struct WaveEngine {
         words[(DB * 16) * 64 + lane] = m_run;
         words[(DB * 16 + 1) * 64 + lane] = l_run;
     }
+    // Replace this wave's state by an exported one.
+    __device__ __forceinline__ void import_state(const float* words) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] = words[(db * 16 + r) * 64 + lane];
+        m_run = words[(DB * 16) * 64 + lane];
+        l_run = words[(DB * 16 + 1) * 64 + lane];
+    }
     // Merge another wave's partial state (exported above) into this one:
     // both sums are rescaled to the larger of the two (stale) maxima.
     __device__ __forceinline__ void merge_state(const float* words) {

@@ -179,6 +179,13 @@ int32_t vsa_expand_valid(const int32_t* vbs, int32_t nkv_logical, int32_t logica
  *   = seqlen/block_q) in a library-owned device buffer (grown on demand per
  *   device, released by vsa_release) and then runs the kernel in that
  *   order; see vsa_attn_fwd_worklist for the kernel alone.
+ *   With block_q = 256 and fewer than half as many query tiles as the GPU
+ *   has compute units, each tile's list is split over 2 or 4 workgroups
+ *   whose partial rows are merged with the log-sum-exp rule (page
+ *   "BlackwellMultiHeadLatentAttentionForwardFP8", split-KV reduction):
+ *   the last workgroup of a tile to finish merges all parts in part order,
+ *   so results stay deterministic. This uses another library-owned buffer
+ *   of about 17 KB per 32 rows and part.
  */
 int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
                      const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch, int32_t seqlen,

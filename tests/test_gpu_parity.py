@@ -341,6 +341,43 @@ def test_vsa256_workload_sampled_and_cross_shape(vsa):
     torch.cuda.empty_cache()
 
 
+def test_dense_workload_split_lists_sampled(vsa):
+    """Dense S=4k on 256-row tiles: 128 query tiles for 256 compute units, so
+    each list is split over two workgroups and the partial rows merged."""
+    o0, l0 = _full_size(vsa, W.DENSE, (256, 128), 32, "dense 256x128 (split lists)")
+    o1, l1 = _full_size(vsa, W.DENSE, (128, 128), 32, "dense 128x128")
+    d = (o1.float() - o0.float()).abs()
+    lrel = ((l1 - l0).abs() / l0.abs().clamp_min(1.0)).max().item()
+    say(f"dense split vs 128x128: max|dO|={d.max().item():.3e} mean|dO|={d.mean().item():.3e} LSE rel={lrel:.3e}")
+    assert d.max().item() <= O_MAX_ABS and d.mean().item() <= O_MEAN_ABS and lrel <= LSE_REL
+
+
+def test_split_lists_deterministic_and_equal_to_unsplit(vsa):
+    """256-row tiles with few work items run split lists (vsa_attn_fwd);
+    two runs agree bitwise, and the unsplit kernel (vsa_attn_fwd_worklist)
+    agrees within the tolerance; lists shorter than the number of parts
+    leave some parts empty."""
+    B, H, S, D, bq, bkv = 1, 2, 2048, 128, 256, 128
+    say("split lists: determinism and unsplit agreement")
+    q, k, v = (dev(t) for t in W.qkv(B, S, H, D, seed=77))
+    nq, nkv = S // bq, S // bkv
+    idx, cnt = W.random_csr(B, H, nq, nkv, nkv, 0, nkv, seed=78)
+    cnt[0, 0, :4] = [0, 1, 2, 3]
+    idx, cnt = dev(idx), dev(cnt)
+    o1, l1 = _run_fwd(vsa, q, k, v, idx, cnt, bq, bkv, 0.09)
+    o2, l2 = _run_fwd(vsa, q, k, v, idx, cnt, bq, bkv, 0.09)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    work = torch.arange(B * H * nq, dtype=torch.int32, device="cuda")
+    o3, l3 = vsa.vsa_attn_fwd_worklist(q, k, v, idx, cnt, bq, bkv, work, 0.09)
+    torch.cuda.synchronize()
+    d = (o1.float() - o3.float()).abs()
+    fin = torch.isfinite(l3)
+    assert torch.equal(fin, torch.isfinite(l1))
+    lrel = ((l1[fin] - l3[fin]).abs() / l3[fin].abs().clamp_min(1.0)).max().item()
+    say(f"split vs unsplit: max|dO|={d.max().item():.3e} LSE rel={lrel:.3e}")
+    assert d.max().item() <= O_MAX_ABS and lrel <= LSE_REL
+
+
 def test_native64_workload_sampled(vsa):
     _full_size(vsa, W.NATIVE64, (64, 64), 92, "native64 64x64", tiles_per_head=3)
     torch.cuda.empty_cache()

@@ -165,7 +165,7 @@ class Workload:
 # own tiles and on finer tiles, native Q64/KV64 with skewed counts).
 TINY = Workload("tiny_64x64_b1h2s1024d64", 1, 2, 1024, 64, (64, 64), ((64, 64),),
                 "topk", keep=8, keep_fraction=0.5)
-DENSE = Workload("dense_b1h8s4096d128", 1, 8, 4096, 128, (128, 128), ((128, 128),),
+DENSE = Workload("dense_b1h8s4096d128", 1, 8, 4096, 128, (256, 256), ((128, 128), (256, 128)),
                  "dense", keep_fraction=1.0)
 VSA256 = Workload("vsa256_b1h24s32768d128_keep13", 1, 24, 32768, 128, (256, 256),
                   ((256, 128),), "topk", keep=13, keep_fraction=0.1)

@@ -282,14 +282,17 @@ __global__ __launch_bounds__(BQ * 2) void vsa_bwd_dq_kernel(BwdParams prm) {
 
 // -------------------------------------------------------------------- dK, dV
 // One workgroup per KV tile of BKV rows, BKV/32 waves of 32 key rows; K and V
-// rows stay in registers. The tile's Q-direction list is walked in 64-row
+// rows stay in registers. The tile's Q-direction list is walked in 32-row
 // query steps: Q and dO (swz_d: row reads for S = Q K^T and dP = dO V^T,
 // transposing reads for dK^T += Q^T dS and dV^T += dO^T P) and the rows'
 // D and LSE are fetched for the next step while this one is computed.
+// 32-row steps keep a 128-key workgroup within 256 registers per wave, so two
+// workgroups share a compute unit and each SIMD has a second wave whose MFMAs
+// can run while this one computes exponentials.
 template <int BKV, int D, bool PARTIAL>
-__global__ __launch_bounds__(BKV * 2) void vsa_bwd_dkv_kernel(BwdParams prm) {
+__global__ __launch_bounds__(BKV * 2, BKV == 128 ? 2 : 1) void vsa_bwd_dkv_kernel(BwdParams prm) {
     constexpr int NW = BKV / 32;
-    constexpr int QS = 64;  // query rows per step
+    constexpr int QS = 32;  // query rows per step
     using G = TileGeom<QS, D>;
     using F = TileFetch<QS, D, NW>;
     using OO = OperandOffsets<D>;
@@ -373,8 +376,8 @@ __global__ __launch_bounds__(BKV * 2) void vsa_bwd_dkv_kernel(BwdParams prm) {
         if (j + 1 < steps) fetch_step(j + 1);
         if (entry(j) < 0) continue;  // uniform
         const int qb = (j & 1) * STAGE, ob = qb + G::TILE, ab = qb + 2 * G::TILE;
-        // S = Q K^T and dP = dO V^T for both 32-row halves first, so that one
-        // half's exp/dS work can overlap the other half's MFMAs
+        // S = Q K^T and dP = dO V^T for every 32-row block of the step first,
+        // then per block the exp/dS work and the dV, dK products
         f32x16 s[QS / 32], dp[QS / 32];
 #pragma unroll
         for (int qs = 0; qs < QS / 32; ++qs) {

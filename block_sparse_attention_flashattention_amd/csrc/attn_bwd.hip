@@ -20,6 +20,10 @@
 // slots, and the A operand that meets it is read with transposing LDS reads
 // whose rows follow the same order. Tiles read both by rows and transposed
 // (Q and dO for dK/dV, K for dQ) use the swz_d swizzle.
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "device_common.h"
 #include "vsa_internal.h"
 #include "wave_engine.h"
@@ -29,7 +33,19 @@ namespace {
 
 using namespace dev;
 
-constexpr int kIdxCapBwd = 8192;  // list entries staged in LDS
+constexpr int kIdxCapBwd = 8192;  // list entries staged in LDS (at most)
+
+// Keys per dQ step: 32 for 64-row tiles, so that four of those two-wave
+// workgroups fit a compute unit's LDS; 64 otherwise.
+template <int BQ>
+constexpr int dq_sub() { return BQ == 64 ? 32 : 64; }
+// LDS of the two kernels: two stages of streamed tiles, then the staged list
+// (its length is known at launch only, so the LDS is sized then).
+template <int BQ, int D>
+constexpr int dq_stage_bytes() { return 2 * dq_sub<BQ>() * D * 2; }
+constexpr int kDkvQs = 32;  // query rows per dK/dV step
+template <int D>
+constexpr int dkv_stage_bytes() { return 2 * kDkvQs * D * 2 + 2 * kDkvQs * 4; }
 
 // ---------------------------------------------------------------- preprocess
 // aux[0][(b*H + h)*S + i] = D_i = dO_i . O_i;  aux[1][...] = LSE_i * log2(e)
@@ -153,19 +169,23 @@ struct BwdParams {
 
 // ----------------------------------------------------------------------- dQ
 // One workgroup per query tile of BQ rows, BQ/32 waves of 32 rows. The KV
-// list is walked in 64-key steps; per step K (swz_d: row reads for S^T = K
-// Q^T, transposing reads for dQ^T += K^T dS^T) and V (row reads for dP^T =
-// V dO^T) are fetched for the next step while this one is computed.
+// list is walked in 64-key steps (32 for 64-row tiles); per step K (swz_d:
+// row reads for S^T = K Q^T, transposing reads for dQ^T += K^T dS^T) and V
+// (row reads for dP^T = V dO^T) are fetched for the next step while this one
+// is computed. Every variant stays within 256 registers per wave, so each
+// SIMD runs two waves (of one workgroup at 256 rows, of two or four smaller
+// ones otherwise).
 template <int BQ, int D, bool PARTIAL>
-__global__ __launch_bounds__(BQ * 2) void vsa_bwd_dq_kernel(BwdParams prm) {
+__global__ __launch_bounds__(BQ * 2, 2) void vsa_bwd_dq_kernel(BwdParams prm) {
     constexpr int NW = BQ / 32;
-    constexpr int SUB = 64;
+    constexpr int SUB = dq_sub<BQ>();
     using G = TileGeom<SUB, D>;
     using F = TileFetch<SUB, D, NW>;
     using OO = OperandOffsets<D>;
     constexpr int DC = D / 16, DB = D / 32, NB = SUB / 32, KC = SUB / 16;
     constexpr int STAGE = 2 * G::TILE;  // K, V
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + kIdxCapBwd * 4];
+    static_assert(STAGE == dq_stage_bytes<BQ, D>(), "launch sizes the LDS from dq_stage_bytes");
+    extern __shared__ __attribute__((aligned(1024))) char smem[];  // 2 stages, then the list
 
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -290,15 +310,16 @@ __global__ __launch_bounds__(BQ * 2) void vsa_bwd_dq_kernel(BwdParams prm) {
 // workgroups share a compute unit and each SIMD has a second wave whose MFMAs
 // can run while this one computes exponentials.
 template <int BKV, int D, bool PARTIAL>
-__global__ __launch_bounds__(BKV * 2, BKV == 128 ? 2 : 1) void vsa_bwd_dkv_kernel(BwdParams prm) {
+__global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) {
     constexpr int NW = BKV / 32;
-    constexpr int QS = 32;  // query rows per step
+    constexpr int QS = kDkvQs;  // query rows per step
     using G = TileGeom<QS, D>;
     using F = TileFetch<QS, D, NW>;
     using OO = OperandOffsets<D>;
     constexpr int DC = D / 16, DB = D / 32;
     constexpr int STAGE = 2 * G::TILE + 2 * QS * 4;  // Q, dO, D[QS], lse2[QS]
-    __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE + kIdxCapBwd * 4];
+    static_assert(STAGE == dkv_stage_bytes<D>(), "launch sizes the LDS from dkv_stage_bytes");
+    extern __shared__ __attribute__((aligned(1024))) char smem[];  // 2 stages, then the list
 
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -448,27 +469,56 @@ hipError_t launch_prep(const uint16_t* o, const uint16_t* dout, const float* lse
     return hipGetLastError();
 }
 
+// Launch with `lds` bytes of dynamic LDS (allowing more than the default
+// limit once per kernel when needed).
+hipError_t allow_lds(const void* kernel, int lds) {
+    static std::mutex mutex;
+    static std::vector<std::pair<const void*, int>> raised;  // kernel, bytes allowed
+    std::lock_guard<std::mutex> lock(mutex);
+    for (auto& r : raised)
+        if (r.first == kernel && r.second >= lds) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess) raised.emplace_back(kernel, lds);
+    return e;
+}
+
+template <typename K>
+hipError_t launch_dyn(K kernel, int grid, int threads, int lds, const BwdParams& p, hipStream_t stream) {
+    if (lds > 65536) {
+        const hipError_t e = allow_lds(reinterpret_cast<const void*>(kernel), lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), lds, stream, p);
+    return hipGetLastError();
+}
+
 template <int D, bool PARTIAL>
 hipError_t launch_dq_d(const BwdParams& p, hipStream_t stream) {
     if (p.n_items_q <= 0) return hipSuccess;
+    const int list = 4 * (p.ld < kIdxCapBwd ? p.ld : kIdxCapBwd);
     switch (p.block_q) {
-        case 64: hipLaunchKernelGGL((vsa_bwd_dq_kernel<64, D, PARTIAL>), dim3(p.n_items_q), dim3(128), 0, stream, p); break;
-        case 128: hipLaunchKernelGGL((vsa_bwd_dq_kernel<128, D, PARTIAL>), dim3(p.n_items_q), dim3(256), 0, stream, p); break;
-        case 256: hipLaunchKernelGGL((vsa_bwd_dq_kernel<256, D, PARTIAL>), dim3(p.n_items_q), dim3(512), 0, stream, p); break;
+        case 64:
+            return launch_dyn(vsa_bwd_dq_kernel<64, D, PARTIAL>, p.n_items_q, 128, 2 * dq_stage_bytes<64, D>() + list, p,
+                              stream);
+        case 128:
+            return launch_dyn(vsa_bwd_dq_kernel<128, D, PARTIAL>, p.n_items_q, 256, 2 * dq_stage_bytes<128, D>() + list,
+                              p, stream);
+        case 256:
+            return launch_dyn(vsa_bwd_dq_kernel<256, D, PARTIAL>, p.n_items_q, 512, 2 * dq_stage_bytes<256, D>() + list,
+                              p, stream);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 template <int D, bool PARTIAL>
 hipError_t launch_dkv_d(const BwdParams& p, hipStream_t stream) {
     if (p.n_items_kv <= 0) return hipSuccess;
+    const int lds = 2 * dkv_stage_bytes<D>() + 4 * (p.q_ld < kIdxCapBwd ? p.q_ld : kIdxCapBwd);
     switch (p.block_kv) {
-        case 64: hipLaunchKernelGGL((vsa_bwd_dkv_kernel<64, D, PARTIAL>), dim3(p.n_items_kv), dim3(128), 0, stream, p); break;
-        case 128: hipLaunchKernelGGL((vsa_bwd_dkv_kernel<128, D, PARTIAL>), dim3(p.n_items_kv), dim3(256), 0, stream, p); break;
+        case 64: return launch_dyn(vsa_bwd_dkv_kernel<64, D, PARTIAL>, p.n_items_kv, 128, lds, p, stream);
+        case 128: return launch_dyn(vsa_bwd_dkv_kernel<128, D, PARTIAL>, p.n_items_kv, 256, lds, p, stream);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace

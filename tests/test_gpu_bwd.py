@@ -158,31 +158,39 @@ def test_backward_is_deterministic(vsa):
         assert torch.equal(x, y)
 
 
-def test_backward_vsa256_sampled_rows(vsa):
-    """Full-size VSA-256 (B1 H24 S32768 D128) at 256x128: sampled dQ rows and
-    sampled dK/dV rows against the oracle."""
-    wl = W.VSA256
-    say("backward vsa256 256x128: inputs")
+FULL_SIZE = [
+    ("vsa256 256x128", W.VSA256, (256, 128), 26),
+    ("vsa256 64x64", W.VSA256_FINE, (64, 64), 52),
+    ("native64 64x64", W.NATIVE64, (64, 64), 92),
+]
+
+
+@pytest.mark.parametrize("label,wl,tile,ld", FULL_SIZE, ids=[c[0] for c in FULL_SIZE])
+def test_backward_full_size_sampled_rows(vsa, label, wl, tile, ld):
+    """Full-size workloads (B1 H24 S32768 D128): sampled dQ rows and sampled
+    dK/dV rows against the oracle."""
+    say(f"backward {label}: inputs")
     q, k, v = wl.qkv()
     do = W.qkv(wl.batch, wl.seqlen, wl.heads, wl.head_dim, seed=4242)[0]
-    idx, cnt, _ = ofront.mask_to_csr(wl.logical_mask(), wl.logical_block, (256, 128), 26)
-    say("backward vsa256 256x128: kernels")
-    dq, dk, dv = _run_bwd(vsa, q, k, v, do, idx, cnt, 256, 128, wl.scale)
+    idx, cnt, _ = ofront.mask_to_csr(wl.logical_mask(), wl.logical_block, tile, ld)
+    say(f"backward {label}: kernels")
+    dq, dk, dv = _run_bwd(vsa, q, k, v, do, idx, cnt, tile[0], tile[1], wl.scale)
     B, S, H, D = q.shape
     rng = np.random.default_rng(5)
     heads = [0, 11, 23]
     qrows = np.array([h * S + r for h in heads for r in rng.integers(0, S, size=24)], dtype=np.int64)
     krows = np.array([h * S + r for h in heads for r in rng.integers(0, S, size=3)], dtype=np.int64)
-    say("backward vsa256: oracle dQ rows")
-    rq = oracle.bwd_dq_rows(q, k, v, do, idx, cnt, 256, 128, wl.scale, qrows)
-    say("backward vsa256: oracle dK/dV rows")
-    rk, rv = oracle.bwd_dkv_rows(q, k, v, do, idx, cnt, 256, 128, wl.scale, krows)
+    say(f"backward {label}: oracle dQ rows")
+    rq = oracle.bwd_dq_rows(q, k, v, do, idx, cnt, tile[0], tile[1], wl.scale, qrows)
+    say(f"backward {label}: oracle dK/dV rows")
+    rk, rv = oracle.bwd_dkv_rows(q, k, v, do, idx, cnt, tile[0], tile[1], wl.scale, krows)
 
     def pick(t, rows):
         h, i = rows // S, rows % S
         return t.float().cpu().numpy()[0, i, h]
 
-    check("dQ", pick(dq, qrows), rq, "vsa256 sampled")
-    check("dK", pick(dk, krows), rk, "vsa256 sampled")
-    check("dV", pick(dv, krows), rv, "vsa256 sampled")
+    check("dQ", pick(dq, qrows), rq, f"{label} sampled")
+    check("dK", pick(dk, krows), rk, f"{label} sampled")
+    check("dV", pick(dv, krows), rv, f"{label} sampled")
+    del dq, dk, dv
     torch.cuda.empty_cache()

@@ -20,10 +20,6 @@
 // slots, and the A operand that meets it is read with transposing LDS reads
 // whose rows follow the same order. Tiles read both by rows and transposed
 // (Q and dO for dK/dV, K for dQ) use the swz_d swizzle.
-#include <mutex>
-#include <utility>
-#include <vector>
-
 #include "device_common.h"
 #include "vsa_internal.h"
 #include "wave_engine.h"
@@ -471,21 +467,10 @@ hipError_t launch_prep(const uint16_t* o, const uint16_t* dout, const float* lse
 
 // Launch with `lds` bytes of dynamic LDS (allowing more than the default
 // limit once per kernel when needed).
-hipError_t allow_lds(const void* kernel, int lds) {
-    static std::mutex mutex;
-    static std::vector<std::pair<const void*, int>> raised;  // kernel, bytes allowed
-    std::lock_guard<std::mutex> lock(mutex);
-    for (auto& r : raised)
-        if (r.first == kernel && r.second >= lds) return hipSuccess;
-    const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e == hipSuccess) raised.emplace_back(kernel, lds);
-    return e;
-}
-
 template <typename K>
 hipError_t launch_dyn(K kernel, int grid, int threads, int lds, const BwdParams& p, hipStream_t stream) {
     if (lds > 65536) {
-        const hipError_t e = allow_lds(reinterpret_cast<const void*>(kernel), lds);
+        const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(kernel), lds);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), lds, stream, p);

@@ -104,7 +104,6 @@ std::vector<DeviceBuffer> g_bufs;      // forward work list
 std::vector<DeviceBuffer> g_bwd_bufs;  // backward scratch (D, LSE*log2 e, two work lists)
 std::vector<DeviceBuffer> g_pair_bufs; // paired forward: counter, paired CSR, two work lists
 std::vector<DeviceBuffer> g_split_bufs; // split lists: per-item counters, then partial row states
-std::vector<int> g_cu_count;            // compute units per device
 
 int32_t device_buffer(std::vector<DeviceBuffer>& bufs, size_t bytes, void** out) {
     int dev = 0;
@@ -126,19 +125,6 @@ int32_t device_buffer(std::vector<DeviceBuffer>& bufs, size_t bytes, void** out)
     }
     *out = b.ptr;
     return VSA_OK;
-}
-
-// Compute units of the current device (cached).
-int cu_count() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    std::lock_guard<std::mutex> lock(g_buf_mutex);
-    if ((int)g_cu_count.size() <= dev) g_cu_count.resize(dev + 1, 0);
-    if (g_cu_count[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) g_cu_count[dev] = n;
-    }
-    return g_cu_count[dev];
 }
 
 // Workspace of the split-list forward: counter_bytes of per-item counters
@@ -277,7 +263,7 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
     // Too few 256-row work items to occupy every compute unit: split each
     // list over 2 or 4 workgroups (partial states merged by the last one).
     if (block_q == 256) {
-        const int cus = cu_count();
+        const int cus = vsa::device_cu_count();
         while (p.splits < 4 && (int64_t)n_items * p.splits * 2 <= cus) p.splits *= 2;
     }
     if (p.splits > 1) {

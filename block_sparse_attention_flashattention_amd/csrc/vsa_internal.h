@@ -5,6 +5,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <utility>
+#include <vector>
+
 namespace vsa {
 
 // Arguments of the fused forward kernel. All pointers are device pointers.
@@ -42,6 +46,41 @@ hipError_t launch_fwd_pp(int block_kv, int head_dim, const FwdParams& p, hipStre
 hipError_t launch_fwd_2s(int block_kv, int head_dim, const FwdParams& p, hipStream_t stream);
 // 64-row query tiles: the four-KV-stream ping-pong kernel (attn_fwd_4s.hip).
 hipError_t launch_fwd_4s(int block_kv, int head_dim, const FwdParams& p, hipStream_t stream);
+
+// 64- and 128-row query tiles with independent waves (attn_fwd_iw.hip).
+hipError_t launch_fwd_iw(int block_q, int head_dim, const FwdParams& p, hipStream_t stream);
+
+// Let `kernel` be launched with `bytes` of dynamic LDS (above the default
+// limit); remembered per kernel. Host only.
+inline hipError_t allow_dynamic_lds(const void* kernel, int bytes) {
+    static std::mutex mutex;
+    static std::vector<std::pair<const void*, int>> allowed;
+    std::lock_guard<std::mutex> lock(mutex);
+    for (auto& a : allowed)
+        if (a.first == kernel && a.second >= bytes) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) allowed.emplace_back(kernel, bytes);
+    return e;
+}
+
+// Compute units of the current device (cached per device; 0 if unknown). Host only.
+inline int device_cu_count() {
+    static std::mutex mutex;
+    static std::vector<int> counts;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mutex);
+    if ((int)counts.size() <= dev) counts.resize(dev + 1, 0);
+    if (counts[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) counts[dev] = n;
+    }
+    return counts[dev];
+}
+
+// Work items per compute unit from which 64- and 128-row tiles run the
+// independent-wave kernel rather than the eight-wave multi-stream ones.
+constexpr int kIwItemsPerCu = 8;
 
 // Whether launch_fwd has a kernel for this configuration.
 bool fwd_supported(int block_q, int block_kv, int head_dim);

@@ -229,6 +229,35 @@ def test_partial_tiles_every_tile_shape_all_rows(vsa, bq, bkv, D):
                f"partial {bq}x{bkv} D={D}")
 
 
+MANY_ITEMS = [(64, 64, 64), (64, 128, 128), (128, 64, 64), (128, 128, 128)]
+
+
+@pytest.mark.parametrize("bq,bkv,D", MANY_ITEMS, ids=[f"{a}x{b}_d{c}" for a, b, c in MANY_ITEMS])
+@pytest.mark.parametrize("partial", [False, True], ids=["full", "partial"])
+def test_many_work_items_all_rows(vsa, bq, bkv, D, partial):
+    """At least eight 64- or 128-row work items per compute unit: these run the
+    independent-wave kernel (the small cases above run the multi-stream ones).
+    Empty rows, short and long lists, partial tiles; every row."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    S = 2048
+    B, H = 2, max(1, -(-8 * cus * bq // (2 * S)))
+    nq, nkv = S // bq, S // bkv
+    assert B * H * nq >= 8 * cus
+    say(f"forward many items {bq}x{bkv} D={D} partial={partial}: B={B} H={H}")
+    q, k, v = W.qkv(B, S, H, D, seed=bq + bkv + D + partial)
+    idx, cnt = W.random_csr(B, H, nq, nkv, nkv // 4, 0, nkv // 4, seed=bq * 3 + bkv + D)
+    val = None
+    if partial:
+        val = W.ragged_block_sizes(nkv, bkv, seed=bq + bkv, p_full=0.4)
+        val[:2] = [0, 1]
+    scale = 1.0 / math.sqrt(D)
+    o_ref, lse_ref = oracle.attn_full(q, k, v, idx, cnt, bq, bkv, scale, kv_valid=val)
+    o, lse = _run_fwd(vsa, dev(q), dev(k), dev(v), dev(idx), dev(cnt), bq, bkv, scale,
+                      kv_valid=None if val is None else dev(val))
+    check_rows(o, lse, np.arange(B * H * S), o_ref.transpose(0, 2, 1, 3).reshape(-1, D), lse_ref.reshape(-1), S, H,
+               f"many items {bq}x{bkv} D={D} partial={partial}")
+
+
 EXPAND_CASES = [(256, 128), (256, 64), (256, 256), (128, 32), (64, 64)]
 
 

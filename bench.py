@@ -227,7 +227,7 @@ def main():
     # Algorithmic HBM bytes of one kernel launch: Q, K, V read once, O and
     # LSE written once, CSR indices and counts read once.
     alg_bytes = (3 * B * S * H * D + B * S * H * D) * 2 + B * H * S * 4 + (B * H * nq) * (ld + 2) * 4
-    kname = kernel_name(run_bq, bkv, D, partial=kv_valid is not None)
+    kname = kernel_name(run_bq, bkv, D, partial=kv_valid is not None, n_items=B * H * (S // run_bq))
     traffic = read_traffic(args.traffic or default_traffic_path(kname, wl.name, run_bq, bkv), kname)
 
     result = {
@@ -331,12 +331,29 @@ def time_backward(vsa, q, k, v, o, lse, idx, cnt, bq, bkv, scale, D, pairs, step
             "flops_per_pair": f"10*D={10 * D}", "scope": "vsa_csr_transpose + vsa_attn_bwd (prep, dK/dV, dQ)"}
 
 
-def kernel_name(bq, bkv, d, partial=False):
+IW_ITEMS_PER_CU = 8  # the library's switch to the independent-wave kernel
+
+
+def compute_units():
+    """Compute units of GPU 0 (MI355X's 256 when no GPU is visible)."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.get_device_properties(0).multi_processor_count
+    except Exception:
+        pass
+    return 256
+
+
+def kernel_name(bq, bkv, d, partial=False, n_items=None):
     """Name of the forward kernel the library dispatches for this tile shape
-    (the last template argument: built for partial tiles)."""
+    and number of work items (the last template argument: built for partial
+    tiles)."""
     p = "true" if partial else "false"
     if bq == 256:
         return f"vsa_fwd_pp_kernel<{bkv},{d},{p}>"
+    if n_items is not None and n_items >= IW_ITEMS_PER_CU * compute_units():
+        return f"vsa_fwd_iw_kernel<{bq},{d},{p}>"
     if bq == 128:
         return f"vsa_fwd_2s_kernel<{d},{p}>"
     return f"vsa_fwd_4s_kernel<{d},{p}>"
@@ -350,7 +367,7 @@ def kernel_source_hash(kname):
     file, the dispatcher and the headers they include."""
     import hashlib
     own = {"vsa_fwd_pp_kernel": "attn_fwd_pp.hip", "vsa_fwd_2s_kernel": "attn_fwd_2s.hip",
-           "vsa_fwd_4s_kernel": "attn_fwd_4s.hip"}[kname.split("<")[0]]
+           "vsa_fwd_4s_kernel": "attn_fwd_4s.hip", "vsa_fwd_iw_kernel": "attn_fwd_iw.hip"}[kname.split("<")[0]]
     h = hashlib.sha256()
     for name in sorted([own, "attn_fwd.hip", "wave_engine.h", "device_common.h", "vsa_internal.h"]):
         h.update(name.encode())
@@ -394,7 +411,9 @@ def write_traffic(args):
     import workloads as W
     wl = W.WORKLOADS[args.workload]
     bq, bkv = (int(x) for x in args.tile.lower().split("x")) if args.tile else wl.physical[0]
-    kname = kernel_name(bq, bkv, wl.head_dim, partial=args.ragged is not None)
+    run_bq = 128 if args.paired else bq
+    kname = kernel_name(run_bq, bkv, wl.head_dim, partial=args.ragged is not None,
+                        n_items=wl.batch * wl.heads * (wl.seqlen // run_bq))
     stem = kname.split("<")[0]
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_from_counters
     copy_bytes = 1 << 30
@@ -409,7 +428,7 @@ def write_traffic(args):
         "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
         "source_hash": kernel_source_hash(kname),
     }
-    path = args.traffic or default_traffic_path(kname, wl.name, bq, bkv)
+    path = args.traffic or default_traffic_path(kname, wl.name, run_bq, bkv)
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")

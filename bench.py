@@ -60,6 +60,10 @@ def parse_args():
                     help="64-row tiles through vsa_attn_fwd_paired: adjacent query tiles with identical lists run as "
                          "128-row tiles (decided on the device; the timed scope then includes the pairing and both "
                          "work lists)")
+    ap.add_argument("--scope", choices=("kernel", "entry"), default="kernel",
+                    help="kernel: the attention kernel over the work list built in the step (vsa_build_worklist + "
+                         "vsa_attn_fwd_worklist, the kernel alone is timed); entry: vsa_attn_fwd, which builds its own "
+                         "work list and splits lists when there are few work items (all of it is timed)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward leg (dQ, dK, dV of the same workload; reported beside the headline)")
     ap.add_argument("--traffic-from-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -137,13 +141,15 @@ def main():
     def attention():
         if args.paired:
             vsa.vsa_attn_fwd_paired(q, k, v, idx, cnt, bkv, scale, o, lse, stream=stream, kv_valid=kv_valid)
+        elif args.scope == "entry":
+            vsa.vsa_attn_fwd(q, k, v, idx, cnt, bq, bkv, scale, o, lse, stream=stream, kv_valid=kv_valid)
         else:
             vsa.vsa_attn_fwd_worklist(q, k, v, idx, cnt, bq, bkv, work, scale, o, lse, stream=stream,
                                       kv_valid=kv_valid)
 
     def step(ev0=None, ev1=None):
         vsa.vsa_mask_to_csr(mask, (lq, lkv), (bq, bkv), ld, idx, cnt, stream=stream)
-        if not args.paired:
+        if not args.paired and args.scope == "kernel":
             vsa.vsa_build_worklist(cnt, ld, work, segment=nq, stream=stream)
         if vbs is not None:
             vsa.vsa_expand_valid(vbs, lkv, bkv, kv_valid, stream=stream)
@@ -227,7 +233,8 @@ def main():
     # Algorithmic HBM bytes of one kernel launch: Q, K, V read once, O and
     # LSE written once, CSR indices and counts read once.
     alg_bytes = (3 * B * S * H * D + B * S * H * D) * 2 + B * H * S * 4 + (B * H * nq) * (ld + 2) * 4
-    kname = kernel_name(run_bq, bkv, D, partial=kv_valid is not None, n_items=B * H * (S // run_bq))
+    kname = kernel_name(run_bq, bkv, D, partial=kv_valid is not None, n_items=B * H * (S // run_bq),
+                        entry=args.scope == "entry")
     traffic = read_traffic(args.traffic or default_traffic_path(kname, wl.name, run_bq, bkv), kname)
 
     result = {
@@ -248,6 +255,8 @@ def main():
             "batch": B, "heads": H, "seq_len": S, "head_dim": D,
             "logical_block": f"{lq}x{lkv}", "tile": f"{bq}x{bkv}",
             "paired_onto": f"{run_bq}x{bkv}" if args.paired else None,
+            "timed_scope": "vsa_attn_fwd_paired" if args.paired else (
+                "vsa_attn_fwd" if args.scope == "entry" else "vsa_attn_fwd_worklist"),
             "selected_pairs": pairs,
             "density": round(pairs / (B * H * S * S), 5),
             "parallelism": "single_gpu",
@@ -345,14 +354,16 @@ def compute_units():
     return 256
 
 
-def kernel_name(bq, bkv, d, partial=False, n_items=None):
+def kernel_name(bq, bkv, d, partial=False, n_items=None, entry=False):
     """Name of the forward kernel the library dispatches for this tile shape
     and number of work items (the last template argument: built for partial
-    tiles)."""
+    tiles); entry: through vsa_attn_fwd, which splits the lists of few 64-row
+    items over the independent-wave kernel."""
     p = "true" if partial else "false"
     if bq == 256:
         return f"vsa_fwd_pp_kernel<{bkv},{d},{p}>"
-    if n_items is not None and n_items >= IW_ITEMS_PER_CU * compute_units():
+    many = n_items is not None and n_items >= IW_ITEMS_PER_CU * compute_units()
+    if many or (entry and bq == 64):
         return f"vsa_fwd_iw_kernel<{bq},{d},{p}>"
     if bq == 128:
         return f"vsa_fwd_2s_kernel<{d},{p}>"
@@ -413,7 +424,7 @@ def write_traffic(args):
     bq, bkv = (int(x) for x in args.tile.lower().split("x")) if args.tile else wl.physical[0]
     run_bq = 128 if args.paired else bq
     kname = kernel_name(run_bq, bkv, wl.head_dim, partial=args.ragged is not None,
-                        n_items=wl.batch * wl.heads * (wl.seqlen // run_bq))
+                        n_items=wl.batch * wl.heads * (wl.seqlen // run_bq), entry=args.scope == "entry")
     stem = kname.split("<")[0]
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_from_counters
     copy_bytes = 1 << 30

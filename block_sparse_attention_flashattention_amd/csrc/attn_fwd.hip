@@ -24,7 +24,8 @@ hipError_t launch_fwd(int block_q, int block_kv, int head_dim, const FwdParams& 
     if (block_q == 256) return launch_fwd_pp(block_kv, head_dim, p, stream);
     // Many work items: independent waves, several workgroups per compute unit.
     // Few: all eight waves of a workgroup on one tile, over two or four streams.
-    if ((int64_t)p.n_work >= (int64_t)kIwItemsPerCu * device_cu_count()) return launch_fwd_iw(block_q, head_dim, p, stream);
+    if (p.splits > 1 || (int64_t)p.n_work >= (int64_t)kIwItemsPerCu * device_cu_count())
+        return launch_fwd_iw(block_q, head_dim, p, stream);
     if (block_q == 128) return launch_fwd_2s(block_kv, head_dim, p, stream);
     return launch_fwd_4s(block_kv, head_dim, p, stream);
 }

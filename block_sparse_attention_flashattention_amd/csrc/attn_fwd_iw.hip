@@ -50,7 +50,12 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_fwd_iw_kernel(FwdParams prm) {
 
     const int wi = xcd_contiguous_block();
     if (wi >= prm.n_work) return;
-    const int item = prm.work ? prm.work[wi] : wi;
+    // With split lists, workgroup wi serves part wi % splits of work entry
+    // wi / splits and takes the list entries part, part + splits, ...
+    const int SP = prm.splits;
+    const int slot = SP == 1 ? wi : wi / SP;
+    const int part = wi - slot * SP;
+    const int item = prm.work ? prm.work[slot] : slot;
     if (item < 0 || item >= prm.n_items) return;
 
     const int p = item % prm.nq;
@@ -61,9 +66,12 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_fwd_iw_kernel(FwdParams prm) {
     const int64_t tok_stride = (int64_t)prm.H * D;
     const int tok_bytes = (int)(tok_stride * 2);
     // the count, the CSR row, Q and the first K sub-tile are fetched at once
-    const int32_t* irow = prm.idx + (int64_t)item * prm.ld;
-    const int ldc = prm.ld < kIdxCapIw ? prm.ld : kIdxCapIw;
-    const int first_tile = __builtin_amdgcn_readfirstlane(irow[0]);
+    const int32_t* irow = prm.idx + (int64_t)item * prm.ld + part;
+    const int ldp = prm.ld > part ? (prm.ld - part + SP - 1) / SP : 0;  // this part's slots of the row
+    const int ldc = ldp < kIdxCapIw ? ldp : kIdxCapIw;
+    // (a part with no slot reads a valid address and ignores the value)
+    const int first_raw = __builtin_amdgcn_readfirstlane(*(ldp > 0 ? irow : prm.idx));
+    const int first_tile = ldp > 0 ? first_raw : -1;
     int n = prm.cnt[item];
     const int nkv = prm.nkv;
     const int block_kv = prm.block_kv;
@@ -83,10 +91,13 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_fwd_iw_kernel(FwdParams prm) {
     e.load_q(prm.q + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D);
 
     int* lidx = (int*)(smem + 4 * G::TILE);
-    for (int i = tid; i < ldc; i += BQ * 2) lidx[i] = stage_entry<PARTIAL>(irow[i], nkv, block_kv, prm.kv_valid);
+    for (int i = tid; i < ldc; i += BQ * 2)
+        lidx[i] = stage_entry<PARTIAL>(irow[(int64_t)i * SP], nkv, block_kv, prm.kv_valid);
     e.q_ready();
     fetch.all(0, sub_ptr(kbase, first_tile, 0), tok_bytes, kLayoutK);
-    n = n < 0 ? 0 : (n > ldc ? ldc : n);
+    n = n < 0 ? 0 : (n > prm.ld ? prm.ld : n);
+    n = n > part ? (n - part + SP - 1) / SP : 0;  // this part's entries
+    n = n > ldc ? ldc : n;
     const int N = n * R;
     wait_global_loads();
     lds_barrier();
@@ -137,6 +148,30 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_fwd_iw_kernel(FwdParams prm) {
             lds_barrier();
         }
         e.template mfma_phase<true, false>(vbuf(N - 1), 0);  // O += V_{N-1} P_{N-1}
+    }
+    if (SP > 1) {
+        // Split list: every part publishes its rows (device-scope stores,
+        // then a wait for them), and the last part of the item to arrive
+        // merges all parts in part order, so the result does not depend on
+        // which one that is, and writes O and LSE. Nothing waits on another
+        // workgroup, and no fence invalidates the caches that the other
+        // workgroups are reading K and V through.
+        constexpr int64_t WORDS = (int64_t)E::STATE_WORDS * 64;
+        e.template export_state<true>(prm.ws_partial + ((int64_t)wi * NW + wave) * WORDS);
+        wait_global_loads();  // the stores have reached the coherence point
+        lds_barrier();
+        int* flag = (int*)smem;  // the tile buffers are free now
+        if (tid == 0) {
+            const int last = __hip_atomic_fetch_add(prm.ws_counter + item, 1, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT) == SP - 1;
+            if (last) __hip_atomic_store(prm.ws_counter + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *flag = last;
+        }
+        lds_barrier();
+        if (__builtin_amdgcn_readfirstlane(*flag) == 0) return;
+        const float* parts = prm.ws_partial + ((int64_t)slot * SP * NW + wave) * WORDS;
+        e.template import_state<true>(parts);
+        for (int q = 1; q < SP; ++q) e.template merge_state<true>(parts + (int64_t)q * NW * WORDS);
     }
     e.store(prm.o + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D,
             prm.lse + ((int64_t)b * prm.H + h) * S + q0 + l32);

@@ -184,25 +184,28 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     }
 
     if (SP > 1) {
-        // Split list: publish this part's rows; the last part of the item to
-        // arrive merges all parts in part order (so the result does not
-        // depend on which one that is) and writes O and LSE. Nothing waits.
+        // Split list: every part publishes its rows (device-scope stores,
+        // then a wait for them), and the last part of the item to arrive
+        // merges all parts in part order, so the result does not depend on
+        // which one that is, and writes O and LSE. Nothing waits on another
+        // workgroup, and no fence invalidates the caches that the other
+        // workgroups are reading K and V through.
         constexpr int64_t WORDS = (int64_t)E::STATE_WORDS * 64;
-        e.export_state(prm.ws_partial + ((int64_t)wi * 8 + wave) * WORDS);
-        __threadfence();
+        e.template export_state<true>(prm.ws_partial + ((int64_t)wi * 8 + wave) * WORDS);
+        wait_global_loads();  // the stores have reached the coherence point
         lds_barrier();
         int* flag = (int*)smem;  // the tile buffers are free now
         if (tid == 0) {
-            const int last = atomicAdd(prm.ws_counter + item, 1) == SP - 1;
-            if (last) prm.ws_counter[item] = 0;  // ready for the next launch
+            const int last = __hip_atomic_fetch_add(prm.ws_counter + item, 1, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT) == SP - 1;
+            if (last) __hip_atomic_store(prm.ws_counter + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             *flag = last;
         }
         lds_barrier();
         if (__builtin_amdgcn_readfirstlane(*flag) == 0) return;
-        __threadfence();
         const float* parts = prm.ws_partial + ((int64_t)slot * SP * 8 + wave) * WORDS;
-        e.import_state(parts);
-        for (int q = 1; q < SP; ++q) e.merge_state(parts + (int64_t)q * 8 * WORDS);
+        e.template import_state<true>(parts);
+        for (int q = 1; q < SP; ++q) e.template merge_state<true>(parts + (int64_t)q * 8 * WORDS);
     }
     e.store(prm.o + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D,
             prm.lse + ((int64_t)b * prm.H + h) * S + q0 + l32);

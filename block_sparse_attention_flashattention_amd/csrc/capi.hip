@@ -260,16 +260,21 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
     if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
     vsa::FwdParams p = make_params(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim,
                                    idx_ld, block_q, block_kv, scale, work, n_items, o, lse);
-    // Too few 256-row work items to occupy every compute unit: split each
-    // list over 2 or 4 workgroups (partial states merged by the last one).
+    // Too few work items to occupy every compute unit: split each list over
+    // 2 or 4 workgroups (partial states merged by the last one). 256-row
+    // tiles run one workgroup per compute unit; 64-row tiles go to the
+    // independent-wave kernel, four per compute unit. (128-row tiles with few
+    // items measured faster on the two-stream kernel unsplit.)
+    const int cus = vsa::device_cu_count();
     if (block_q == 256) {
-        const int cus = vsa::device_cu_count();
         while (p.splits < 4 && (int64_t)n_items * p.splits * 2 <= cus) p.splits *= 2;
+    } else if (block_q == 64 && (int64_t)n_items < (int64_t)vsa::kIwItemsPerCu * cus) {
+        while (p.splits < 4 && (int64_t)n_items * p.splits < 4LL * cus) p.splits *= 2;
     }
     if (p.splits > 1) {
         const size_t counters = ((size_t)n_items * sizeof(int32_t) + 255) / 256 * 256;
         const size_t state_words = (size_t)(head_dim / 32 * 16 + 2) * 64;  // per wave
-        const size_t bytes = counters + (size_t)n_items * p.splits * 8 * state_words * sizeof(float);
+        const size_t bytes = counters + (size_t)n_items * p.splits * (block_q / 32) * state_words * sizeof(float);
         void* ws = nullptr;
         rc = split_buffer(counters, bytes, (hipStream_t)stream, &ws);
         if (rc != VSA_OK) return rc;

@@ -356,35 +356,52 @@ struct WaveEngine {
 
     // Partial-row exchange between two waves that own the same rows (same
     // lane -> row/column mapping): words[e * 64 + lane], e < STATE_WORDS.
+    // DEV: between workgroups through global memory, with device-scope
+    // stores and loads (written through to and read from the device's
+    // coherence point), so that no cache-wide fence is needed; the writer
+    // waits for its stores before it signals.
+    template <bool DEV>
+    static __device__ __forceinline__ void put(float* p, float v) {
+        if constexpr (DEV) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else *p = v;
+    }
+    template <bool DEV>
+    static __device__ __forceinline__ float get(const float* p) {
+        if constexpr (DEV) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else return *p;
+    }
+    template <bool DEV = false>
     __device__ __forceinline__ void export_state(float* words) const {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) words[(db * 16 + r) * 64 + lane] = oacc[db][r];
-        words[(DB * 16) * 64 + lane] = m_run;
-        words[(DB * 16 + 1) * 64 + lane] = l_run;
+            for (int r = 0; r < 16; ++r) put<DEV>(&words[(db * 16 + r) * 64 + lane], oacc[db][r]);
+        put<DEV>(&words[(DB * 16) * 64 + lane], m_run);
+        put<DEV>(&words[(DB * 16 + 1) * 64 + lane], l_run);
     }
     // Replace this wave's state by an exported one.
+    template <bool DEV = false>
     __device__ __forceinline__ void import_state(const float* words) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] = words[(db * 16 + r) * 64 + lane];
-        m_run = words[(DB * 16) * 64 + lane];
-        l_run = words[(DB * 16 + 1) * 64 + lane];
+            for (int r = 0; r < 16; ++r) oacc[db][r] = get<DEV>(&words[(db * 16 + r) * 64 + lane]);
+        m_run = get<DEV>(&words[(DB * 16) * 64 + lane]);
+        l_run = get<DEV>(&words[(DB * 16 + 1) * 64 + lane]);
     }
     // Merge another wave's partial state (exported above) into this one:
     // both sums are rescaled to the larger of the two (stale) maxima.
+    template <bool DEV = false>
     __device__ __forceinline__ void merge_state(const float* words) {
-        const float m1 = words[(DB * 16) * 64 + lane];
-        const float l1 = words[(DB * 16 + 1) * 64 + lane];
+        const float m1 = get<DEV>(&words[(DB * 16) * 64 + lane]);
+        const float l1 = get<DEV>(&words[(DB * 16 + 1) * 64 + lane]);
         const float m = fmaxf(m_run, m1);
         const float a0 = m == -__builtin_inff() ? 0.0f : fast_exp2(m_run - m);
         const float a1 = m == -__builtin_inff() ? 0.0f : fast_exp2(m1 - m);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + words[(db * 16 + r) * 64 + lane] * a1;
+            for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + get<DEV>(&words[(db * 16 + r) * 64 + lane]) * a1;
         l_run = l_run * a0 + l1 * a1;
         m_run = m;
     }

@@ -180,7 +180,8 @@ int32_t vsa_expand_valid(const int32_t* vbs, int32_t nkv_logical, int32_t logica
  *   device, released by vsa_release) and then runs the kernel in that
  *   order; see vsa_attn_fwd_worklist for the kernel alone.
  *   With block_q = 256 and fewer than half as many query tiles as the GPU
- *   has compute units, each tile's list is split over 2 or 4 workgroups
+ *   has compute units, or block_q = 64 and fewer than 8 query tiles per
+ *   compute unit, each tile's list is split over 2 or 4 workgroups
  *   whose partial rows are merged with the log-sum-exp rule (page
  *   "BlackwellMultiHeadLatentAttentionForwardFP8", split-KV reduction):
  *   the last workgroup of a tile to finish merges all parts in part order,

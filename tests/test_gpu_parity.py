@@ -381,12 +381,13 @@ def test_dense_workload_split_lists_sampled(vsa):
     assert d.max().item() <= O_MAX_ABS and d.mean().item() <= O_MEAN_ABS and lrel <= LSE_REL
 
 
-def test_split_lists_deterministic_and_equal_to_unsplit(vsa):
-    """256-row tiles with few work items run split lists (vsa_attn_fwd);
-    two runs agree bitwise, and the unsplit kernel (vsa_attn_fwd_worklist)
-    agrees within the tolerance; lists shorter than the number of parts
-    leave some parts empty."""
-    B, H, S, D, bq, bkv = 1, 2, 2048, 128, 256, 128
+@pytest.mark.parametrize("bq,bkv", [(256, 128), (64, 64)])
+def test_split_lists_deterministic_and_equal_to_unsplit(vsa, bq, bkv):
+    """256- and 64-row tiles with few work items run split lists
+    (vsa_attn_fwd); two runs agree bitwise, and the unsplit kernel
+    (vsa_attn_fwd_worklist) agrees within the tolerance; lists shorter than
+    the number of parts leave some parts empty."""
+    B, H, S, D = 1, 2, 2048, 128
     say("split lists: determinism and unsplit agreement")
     q, k, v = (dev(t) for t in W.qkv(B, S, H, D, seed=77))
     nq, nkv = S // bq, S // bkv
@@ -508,10 +509,12 @@ def test_paired_forward_all_rows(vsa, bkv, D, partial):
         o_ref, lse_ref = oracle.attn_full(q, k, v, idx, cnt, 64, bkv, scale, kv_valid=val)
         check_rows(o, lse, np.arange(B * H * S), o_ref.transpose(0, 2, 1, 3).reshape(-1, D), lse_ref.reshape(-1),
                    S, H, f"paired {label} kv{bkv} D={D}")
-        if label == "pairable":
-            o2, l2 = _run_fwd(vsa, qd, kd, vd, dev(pidx), dev(pcnt), 128, bkv, scale, kv_valid=vald)
-        else:
-            o2, l2 = _run_fwd(vsa, qd, kd, vd, dev(idx), dev(cnt), 64, bkv, scale, kv_valid=vald)
+        # the schedule it must have run: the unsplit kernel over the paired
+        # (128-row) or the input (64-row) lists, as the work-list entry runs it
+        ridx, rcnt, rbq = (pidx, pcnt, 128) if label == "pairable" else (idx, cnt, 64)
+        work = torch.arange(rcnt.size, dtype=torch.int32, device="cuda")
+        o2, l2 = vsa.vsa_attn_fwd_worklist(qd, kd, vd, dev(ridx), dev(rcnt), rbq, bkv, work, scale, kv_valid=vald)
+        torch.cuda.synchronize()
         assert torch.equal(o, o2) and torch.equal(lse, l2), f"{label}: not the expected schedule's result"
 
 

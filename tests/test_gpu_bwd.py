@@ -194,3 +194,40 @@ def test_backward_full_size_sampled_rows(vsa, label, wl, tile, ld):
     check("dV", pick(dv, krows), rv, f"{label} sampled")
     del dq, dk, dv
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("bq,bkv", [(256, 128), (128, 64), (64, 64)])
+def test_maximum_list_stride_and_empty_head(vsa, bq, bkv):
+    """idx_ld = q_ld = 8191 (the largest accepted; the kernels stage whole
+    rows, and the backward then needs more than 64 KB of LDS), with every row
+    of head 1 empty: forward and backward against the oracle on all rows."""
+    B, H, S, D = 1, 2, 1024, 64
+    say(f"maximum list stride {bq}x{bkv}")
+    q, k, v = W.qkv(B, S, H, D, seed=bq + bkv + 3)
+    do = W.qkv(B, S, H, D, seed=bq + bkv + 4)[0]
+    nq, nkv = S // bq, S // bkv
+    idx_c, cnt = W.random_csr(B, H, nq, nkv, nkv, 1, nkv, seed=bq + bkv + 5)
+    cnt[0, 1, :] = 0
+    LD = 8191
+    idx = np.full((B, H, nq, LD), -1, dtype=np.int32)
+    idx[..., :nkv] = idx_c
+    scale = 1.0 / math.sqrt(D)
+    o_ref, lse_ref = oracle.attn_full(q, k, v, idx_c, cnt, bq, bkv, scale)
+    qd, kd, vd, dod = dev(q), dev(k), dev(v), dev(do)
+    idxd, cntd = dev(idx), dev(cnt)
+    o, lse = vsa.vsa_attn_fwd(qd, kd, vd, idxd, cntd, bq, bkv, scale)
+    torch.cuda.synchronize()
+    og, lg = o.float().cpu().numpy(), lse.cpu().numpy()
+    assert np.all(og[0, :, 1] == 0.0) and np.all(np.isneginf(lg[0, 1]))
+    d = np.abs(og - o_ref)  # both [B, S, H, D]
+    assert d.max() <= 2e-2 and d.mean() <= 2e-3
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(fin, np.isfinite(lg))
+    assert (np.abs(lg[fin] - lse_ref[fin]) / np.maximum(1.0, np.abs(lse_ref[fin]))).max() <= 1e-3
+    q_idx, q_cnt = vsa.vsa_csr_transpose(idxd, cntd, nkv, LD)
+    dq, dk, dv = vsa.vsa_attn_bwd(qd, kd, vd, o, lse, dod, idxd, cntd, q_idx, q_cnt, bq, bkv, scale)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.bwd_full(q, k, v, do, idx_c, cnt, bq, bkv, scale)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check(name, got.float().cpu().numpy(), ref, f"max stride {bq}x{bkv}")
+        assert np.all(got.float().cpu().numpy()[0, :, 1] == 0.0)

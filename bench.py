@@ -529,7 +529,21 @@ def cpu_baseline(wl, q, k, v, idx, cnt, bq, bkv, ld, seconds, kv_valid=None):
         "kind": "oracle",
         "sample": f"{n_tiles} of {B * H * nq} query tiles ({n_rows} rows, {fl:.3e} sparse-aware flops) "
                   f"in {dt:.1f} s",
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
     }
+
+
+def cpu_model():
+    """Model name of the host CPU (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

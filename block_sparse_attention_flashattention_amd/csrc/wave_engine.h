@@ -160,7 +160,9 @@ struct WaveEngine {
     static constexpr int NB = BKV / 32;  // 32-key blocks of S^T
     static constexpr int DB = D / 32;    // 32-wide d blocks of O^T
     static constexpr int KC = BKV / 16;  // PV k-steps
-    static constexpr int RING = 4;       // operand prefetch distance (MFMA steps)
+    // operand prefetch distance (MFMA steps): deeper for 32-key sub-tiles,
+    // whose MFMA phases are short enough for the fill to show
+    static constexpr int RING = BKV <= 32 ? 6 : 4;
     // fp32 words per lane exchanged when two waves merge their partial rows
     static constexpr int STATE_WORDS = DB * 16 + 2;
 

@@ -366,7 +366,7 @@ def kernel_name(bq, bkv, d, partial=False, n_items=None, entry=False):
     if many or (entry and bq == 64):
         return f"vsa_fwd_iw_kernel<{bq},{d},{p}>"
     if bq == 128:
-        return f"vsa_fwd_2s_kernel<{d},{p}>"
+        return f"vsa_fwd_2t_kernel<{d},{p}>" if bkv == 128 else f"vsa_fwd_2s_kernel<{d},{p}>"
     return f"vsa_fwd_4s_kernel<{d},{p}>"
 
 
@@ -378,7 +378,8 @@ def kernel_source_hash(kname):
     file, the dispatcher and the headers they include."""
     import hashlib
     own = {"vsa_fwd_pp_kernel": "attn_fwd_pp.hip", "vsa_fwd_2s_kernel": "attn_fwd_2s.hip",
-           "vsa_fwd_4s_kernel": "attn_fwd_4s.hip", "vsa_fwd_iw_kernel": "attn_fwd_iw.hip"}[kname.split("<")[0]]
+           "vsa_fwd_4s_kernel": "attn_fwd_4s.hip", "vsa_fwd_iw_kernel": "attn_fwd_iw.hip",
+           "vsa_fwd_2t_kernel": "attn_fwd_2t.hip"}[kname.split("<")[0]]
     h = hashlib.sha256()
     for name in sorted([own, "attn_fwd.hip", "wave_engine.h", "device_common.h", "vsa_internal.h"]):
         h.update(name.encode())

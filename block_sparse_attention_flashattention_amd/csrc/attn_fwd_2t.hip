@@ -1,0 +1,209 @@
+// Fused block-sparse attention forward for 128-row query tiles over 128-key
+// KV tiles, for launches with few work items (dense attention at S = 4k):
+// two KV streams of whole tiles, each stream single-buffered, each group
+// fetching the other group's next tiles.
+//
+// What is computed: FastVideo page "[perf] Add fine-grained FA4 VSA kernels",
+// ref_masked_sdpa_fp32 (per-wave arithmetic in wave_engine.h). The two-stream
+// split of a query tile's list with an FP32 merge follows that page's fork
+// notes; the merge is the split-KV combination of page
+// "BlackwellMultiHeadLatentAttentionForwardFP8" (reduction_kernel).
+//
+// Schedule. Wave w and wave w+4 own the same 32 rows; group 0 (waves 0-3)
+// takes the first half of the list, group 1 the second. Both groups
+// alternate MFMA phases (M_j: O += V_{j-1} P_{j-1}, S_j = K_j Q^T, 64 MFMAs
+// per wave as in the 256-row kernel) and softmax phases, group 1 one phase
+// behind, with a workgroup barrier after every phase ("window"):
+//
+//     window:   0      1      2      3     ...
+//     group 0:  M_0    V_0    M_1    V_1   ...
+//     group 1:  -      M_0    V_0    M_1   ...
+//
+// Each group holds one K and one V tile in LDS (4 tiles = 128 KB at D = 128).
+// After group g's M_j both of its buffers are free; during the next window,
+// the waves of the other group, which are then in an MFMA phase, fetch g's
+// K_{j+1} and V_j with direct-to-LDS loads spread over that phase and wait
+// for them before the window's barrier. Tile loads thus never enter a
+// softmax phase, and each has one window to land (the K/V of a dense head are
+// L2-resident). At the end group 1 hands its partial rows to group 0 through
+// LDS, which merges and writes O and LSE.
+#include "device_common.h"
+#include "vsa_internal.h"
+#include "wave_engine.h"
+
+namespace vsa {
+namespace {
+
+using namespace dev;
+
+constexpr int kIdxCap2t = 8192;  // CSR row entries staged in LDS (>= the largest idx_ld)
+
+template <int D, bool PARTIAL>
+__global__ __launch_bounds__(512) void vsa_fwd_2t_kernel(FwdParams prm) {
+    constexpr int BQ = 128;
+    constexpr int BKV = 128;
+    using E = WaveEngine<BKV, D>;
+    using G = TileGeom<BKV, D>;
+    using F = TileFetch<BKV, D, 4>;  // a tile is fetched by the four waves of the other group
+    constexpr int GROUP_LDS = 2 * G::TILE;  // K, V of one group
+    static_assert(4 * E::STATE_WORDS * 64 * 4 <= 2 * GROUP_LDS, "merge exchange must fit in the tile buffers");
+    __shared__ __attribute__((aligned(1024))) char smem[2 * GROUP_LDS + kIdxCap2t * 4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;
+    const int l32 = lane & 31;
+
+    const int wi = xcd_contiguous_block();
+    if (wi >= prm.n_work) return;
+    const int item = prm.work ? prm.work[wi] : wi;
+    if (item < 0 || item >= prm.n_items) return;
+
+    const int p = item % prm.nq;
+    const int bh = item / prm.nq;
+    const int h = bh % prm.H;
+    const int b = bh / prm.H;
+    const int S = prm.S;
+    const int64_t tok_stride = (int64_t)prm.H * D;
+    const int tok_bytes = (int)(tok_stride * 2);
+    const int32_t* irow = prm.idx + (int64_t)item * prm.ld;
+    const int ldc = prm.ld < kIdxCap2t ? prm.ld : kIdxCap2t;
+    int n = prm.cnt[item];
+    n = n < 0 ? 0 : (n > ldc ? ldc : n);
+    const int nkv = prm.nkv;
+    const int q0 = p * BQ + (wave & 3) * 32;
+    // group 0: entries [0, N0), group 1: [N0, n)
+    const int N0 = (n + 1) / 2, N1 = n - N0;
+    const int ng = grp ? N1 : N0;
+
+    E e;
+    e.init(smem, lane, prm.scale_log2);
+    e.load_q(prm.q + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D);
+
+    int* lidx = (int*)(smem + 2 * GROUP_LDS);
+    for (int i = tid; i < ldc; i += 512) lidx[i] = stage_entry<PARTIAL>(irow[i], nkv, BKV, prm.kv_valid);
+    e.q_ready();
+
+    auto valid = [&](int t) { return t >= 0 && t < nkv; };
+    const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    const F fetch(smem, wave & 3, lane, tok_bytes);
+    auto tile_at = [&](const char* base, int t) {
+        return uniform_ptr(base + (int64_t)(valid(t) ? t : 0) * BKV * tok_bytes);
+    };
+    // buffers of group g
+    auto kbuf = [](int g) { return g * GROUP_LDS; };
+    auto vbuf = [](int g) { return g * GROUP_LDS + G::TILE; };
+    // list entry of tile j of group g, and its valid keys
+    auto entry = [&](int g, int j) { return __builtin_amdgcn_readfirstlane(lidx[(g ? N0 : 0) + j]); };
+    auto tile_of = [&](int g, int j) { return entry_tile<PARTIAL>(entry(g, j)); };
+    auto keys_of = [&](int g, int j) { return entry_keys<PARTIAL>(entry(g, j), BKV); };
+
+    // group 0's K_0 (entry 0), fetched by group 0 itself before the first window
+    if (grp == 0 && N0 > 0) fetch.all(kbuf(0), tile_at(kbase, __builtin_amdgcn_readfirstlane(irow[0])), tok_bytes, kLayoutK);
+    wait_global_loads();
+    lds_barrier();
+
+    // Loads issued by this group's M_j for the other group o = 1 - grp:
+    // group 0's M_j fetches group 1's K_j and V_{j-1}; group 1's M_j fetches
+    // group 0's K_{j+1} and V_j. Hooks 0..BPW-1: K, BPW..2*BPW-1: V.
+    const int o = 1 - grp;
+    const int no = grp ? N0 : N1;
+    auto other_loads = [&](int j) {
+        const int kj = grp ? j + 1 : j, vj = grp ? j : j - 1;
+        const bool dk = kj < no, dv = vj >= 0 && vj < no;
+        const char* kt = dk ? tile_at(kbase, tile_of(o, kj)) : nullptr;
+        const char* vt = dv ? tile_at(vbase, tile_of(o, vj)) : nullptr;
+        const int kd = kbuf(o), vd = vbuf(o);
+        return [=, &fetch](int i) {
+            if (i < F::BPW) {
+                if (dk) fetch.block(kd, kt, tok_bytes, kLayoutK, i);
+            } else {
+                if (dv) fetch.block(vd, vt, tok_bytes, kLayoutV, i - F::BPW);
+            }
+        };
+    };
+    auto softmax = [&](int j) __attribute__((always_inline)) {
+        const int nv = keys_of(grp, j);
+        if (PARTIAL && nv > 0 && nv < BKV) e.mask_keys(nv);
+        e.softmax(nv > 0);
+    };
+
+    // Group g runs M_j in window 2j + g and V_j (or nothing) in window
+    // 2j + 1 + g, for j = 0 .. m_last: its own M phases run to M_ng (the PV of
+    // its last tile), and beyond that only the other group's last loads.
+    // Each group's loop body is M_j then V_j, so that S (live from M_j to
+    // V_j) and P (from V_j to M_{j+1}) never both cross the back-edge; every
+    // wave passes the same number of barriers (the shorter side pads).
+    const int m_last0 = N0;                         // group 0: M_0 .. M_{N0}
+    const int m_last1 = N1 > N0 - 1 ? N1 : N0 - 1;  // group 1: M_0 .. M_{max(N1, N0-1)}
+    const int m_last = grp ? m_last1 : m_last0;
+    const int b0 = n > 0 ? 2 * m_last0 + 2 : 0, b1 = n > 0 ? 2 * m_last1 + 3 : 0;
+    const int total = b0 > b1 ? b0 : b1;
+    int nbar = 0;
+    auto bar = [&]() {
+        lds_barrier();
+        ++nbar;
+    };
+    if (n > 0) {
+        if (grp == 1) bar();
+        int j = 0;
+        if (ng > 0) {
+            e.template mfma_phase<false, true, 2 * F::BPW>(0, kbuf(grp), other_loads(0));  // M_0
+            wait_global_loads();
+            bar();
+            softmax(0);  // V_0
+            bar();
+            for (j = 1; j < ng; ++j) {
+                e.template mfma_phase<true, true, 2 * F::BPW>(vbuf(grp), kbuf(grp), other_loads(j));  // M_j
+                wait_global_loads();
+                bar();
+                softmax(j);  // V_j
+                bar();
+            }
+            e.template mfma_phase<true, false, 2 * F::BPW>(vbuf(grp), 0, other_loads(j));  // M_ng
+            wait_global_loads();
+            bar();
+            bar();
+            ++j;
+        }
+        for (; j <= m_last; ++j) {  // only the other group's loads
+            const auto hooks = other_loads(j);
+#pragma unroll
+            for (int i = 0; i < 2 * F::BPW; ++i) hooks(i);
+            wait_global_loads();
+            bar();
+            bar();
+        }
+    }
+    while (nbar < total) bar();
+
+    // merge the two streams' partial rows; the tile buffers are free now
+    float* xch = (float*)smem + (wave & 3) * E::STATE_WORDS * 64;
+    if (grp == 1) e.export_state(xch);
+    lds_barrier();
+    if (grp == 0) {
+        e.merge_state(xch);
+        e.store(prm.o + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D,
+                prm.lse + ((int64_t)b * prm.H + h) * S + q0 + l32);
+    }
+}
+
+template <int D>
+hipError_t launch_2t(const FwdParams& p, hipStream_t stream) {
+    if (p.kv_valid) hipLaunchKernelGGL((vsa_fwd_2t_kernel<D, true>), dim3(p.n_work), dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((vsa_fwd_2t_kernel<D, false>), dim3(p.n_work), dim3(512), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_2t(int head_dim, const FwdParams& p, hipStream_t stream) {
+    if (p.n_work <= 0) return hipSuccess;
+    if (head_dim == 128) return launch_2t<128>(p, stream);
+    if (head_dim == 64) return launch_2t<64>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace vsa

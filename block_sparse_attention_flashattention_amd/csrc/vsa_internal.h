@@ -47,6 +47,8 @@ hipError_t launch_fwd_2s(int block_kv, int head_dim, const FwdParams& p, hipStre
 // 64-row query tiles: the four-KV-stream ping-pong kernel (attn_fwd_4s.hip).
 hipError_t launch_fwd_4s(int block_kv, int head_dim, const FwdParams& p, hipStream_t stream);
 
+// 128-row query tiles over 128-key tiles, whole-tile streams (attn_fwd_2t.hip).
+hipError_t launch_fwd_2t(int head_dim, const FwdParams& p, hipStream_t stream);
 // 64- and 128-row query tiles with independent waves (attn_fwd_iw.hip).
 hipError_t launch_fwd_iw(int block_q, int head_dim, const FwdParams& p, hipStream_t stream);
 

@@ -1,7 +1,6 @@
 // Fused block-sparse attention forward for 128-row query tiles over 128-key
 // KV tiles, for launches with few work items (dense attention at S = 4k):
-// two KV streams of whole tiles, each stream single-buffered, each group
-// fetching the other group's next tiles.
+// two KV streams of whole tiles, each stream single-buffered.
 //
 // What is computed: FastVideo page "[perf] Add fine-grained FA4 VSA kernels",
 // ref_masked_sdpa_fp32 (per-wave arithmetic in wave_engine.h). The two-stream
@@ -20,13 +19,14 @@
 //     group 1:  -      M_0    V_0    M_1   ...
 //
 // Each group holds one K and one V tile in LDS (4 tiles = 128 KB at D = 128).
-// After group g's M_j both of its buffers are free; during the next window,
-// the waves of the other group, which are then in an MFMA phase, fetch g's
-// K_{j+1} and V_j with direct-to-LDS loads spread over that phase and wait
-// for them before the window's barrier. Tile loads thus never enter a
-// softmax phase, and each has one window to land (the K/V of a dense head are
-// L2-resident). At the end group 1 hands its partial rows to group 0 through
-// LDS, which merges and writes O and LSE.
+// After group g's M_j both of its buffers are free for one window. All tile
+// loads are issued by group 0, whose waves are the older ones on their SIMDs:
+// group 1's K_j and V_{j-1} during group 0's M_j, group 0's own K_{j+1} and
+// V_j during its softmax V_j (which is shorter than group 1's M_j running
+// beside it). The loads are direct-to-LDS, spread over the phase, and waited
+// for before the window's barrier, so each has one window to land (the K/V
+// of a dense head are L2-resident). At the end group 1 hands its partial
+// rows to group 0 through LDS, which merges and writes O and LSE.
 #include "device_common.h"
 #include "vsa_internal.h"
 #include "wave_engine.h"
@@ -75,7 +75,6 @@ __global__ __launch_bounds__(512) void vsa_fwd_2t_kernel(FwdParams prm) {
     const int q0 = p * BQ + (wave & 3) * 32;
     // group 0: entries [0, N0), group 1: [N0, n)
     const int N0 = (n + 1) / 2, N1 = n - N0;
-    const int ng = grp ? N1 : N0;
 
     E e;
     e.init(smem, lane, prm.scale_log2);
@@ -105,17 +104,18 @@ __global__ __launch_bounds__(512) void vsa_fwd_2t_kernel(FwdParams prm) {
     wait_global_loads();
     lds_barrier();
 
-    // Loads issued by this group's M_j for the other group o = 1 - grp:
-    // group 0's M_j fetches group 1's K_j and V_{j-1}; group 1's M_j fetches
-    // group 0's K_{j+1} and V_j. Hooks 0..BPW-1: K, BPW..2*BPW-1: V.
-    const int o = 1 - grp;
-    const int no = grp ? N0 : N1;
-    auto other_loads = [&](int j) {
-        const int kj = grp ? j + 1 : j, vj = grp ? j : j - 1;
-        const bool dk = kj < no, dv = vj >= 0 && vj < no;
-        const char* kt = dk ? tile_at(kbase, tile_of(o, kj)) : nullptr;
-        const char* vt = dv ? tile_at(vbase, tile_of(o, vj)) : nullptr;
-        const int kd = kbuf(o), vd = vbuf(o);
+    // Every tile load is issued by group 0 (waves 0-3, the older waves on
+    // each SIMD): during its M_j it fetches group 1's K_j and V_{j-1}, and
+    // during its softmax V_j its own K_{j+1} and V_j. Loads issued by the
+    // younger wave of a SIMD while the older one runs its softmax were
+    // measured to stretch that MFMA phase by a third; the older wave's
+    // softmax has the slack for them. Hooks 0..BPW-1: K, BPW..2*BPW-1: V.
+    auto loads = [&](int g, int kj, int vj) {
+        const int ng_ = g ? N1 : N0;
+        const bool dk = kj < ng_, dv = vj >= 0 && vj < ng_;
+        const char* kt = dk ? tile_at(kbase, tile_of(g, kj)) : nullptr;
+        const char* vt = dv ? tile_at(vbase, tile_of(g, vj)) : nullptr;
+        const int kd = kbuf(g), vd = vbuf(g);
         return [=, &fetch](int i) {
             if (i < F::BPW) {
                 if (dk) fetch.block(kd, kt, tok_bytes, kLayoutK, i);
@@ -124,22 +124,22 @@ __global__ __launch_bounds__(512) void vsa_fwd_2t_kernel(FwdParams prm) {
             }
         };
     };
-    auto softmax = [&](int j) __attribute__((always_inline)) {
+    auto issue = [](const auto& hooks) {
+#pragma unroll
+        for (int i = 0; i < 2 * F::BPW; ++i) hooks(i);
+    };
+    auto softmax_ok = [&](int j) __attribute__((always_inline)) {
         const int nv = keys_of(grp, j);
         if (PARTIAL && nv > 0 && nv < BKV) e.mask_keys(nv);
-        e.softmax(nv > 0);
+        return nv > 0;
     };
 
-    // Group g runs M_j in window 2j + g and V_j (or nothing) in window
-    // 2j + 1 + g, for j = 0 .. m_last: its own M phases run to M_ng (the PV of
-    // its last tile), and beyond that only the other group's last loads.
-    // Each group's loop body is M_j then V_j, so that S (live from M_j to
-    // V_j) and P (from V_j to M_{j+1}) never both cross the back-edge; every
-    // wave passes the same number of barriers (the shorter side pads).
-    const int m_last0 = N0;                         // group 0: M_0 .. M_{N0}
-    const int m_last1 = N1 > N0 - 1 ? N1 : N0 - 1;  // group 1: M_0 .. M_{max(N1, N0-1)}
-    const int m_last = grp ? m_last1 : m_last0;
-    const int b0 = n > 0 ? 2 * m_last0 + 2 : 0, b1 = n > 0 ? 2 * m_last1 + 3 : 0;
+    // Group g runs M_j in window 2j + g and its softmax V_j in window
+    // 2j + 1 + g, for j = 0 .. ng (M_ng is the PV of its last tile). Each
+    // group's loop body is M_j then V_j, so that S (live from M_j to V_j) and
+    // P (from V_j to M_{j+1}) never both cross the back-edge; every wave
+    // passes the same number of barriers (the shorter side pads).
+    const int b0 = n > 0 ? 2 * N0 + 2 : 0, b1 = n > 0 ? 2 * N1 + 3 : 0;
     const int total = b0 > b1 ? b0 : b1;
     int nbar = 0;
     auto bar = [&]() {
@@ -147,34 +147,47 @@ __global__ __launch_bounds__(512) void vsa_fwd_2t_kernel(FwdParams prm) {
         ++nbar;
     };
     if (n > 0) {
-        if (grp == 1) bar();
-        int j = 0;
-        if (ng > 0) {
-            e.template mfma_phase<false, true, 2 * F::BPW>(0, kbuf(grp), other_loads(0));  // M_0
+        if (grp == 0) {
+            // N0 >= 1 and N0 >= N1
+            e.template mfma_phase<false, true, 2 * F::BPW>(0, kbuf(0), loads(1, 0, -1));  // M_0
             wait_global_loads();
             bar();
-            softmax(0);  // V_0
+            issue(loads(0, 1, 0));
+            e.softmax(softmax_ok(0));  // V_0
+            wait_global_loads();
             bar();
-            for (j = 1; j < ng; ++j) {
-                e.template mfma_phase<true, true, 2 * F::BPW>(vbuf(grp), kbuf(grp), other_loads(j));  // M_j
+            int j = 1;
+            for (; j < N0; ++j) {
+                e.template mfma_phase<true, true, 2 * F::BPW>(vbuf(0), kbuf(0), loads(1, j, j - 1));  // M_j
                 wait_global_loads();
                 bar();
-                softmax(j);  // V_j
+                issue(loads(0, j + 1, j));
+                e.softmax(softmax_ok(j));  // V_j
+                wait_global_loads();
                 bar();
             }
-            e.template mfma_phase<true, false, 2 * F::BPW>(vbuf(grp), 0, other_loads(j));  // M_ng
+            e.template mfma_phase<true, false, 2 * F::BPW>(vbuf(0), 0, loads(1, j, j - 1));  // M_N0
             wait_global_loads();
             bar();
             bar();
-            ++j;
-        }
-        for (; j <= m_last; ++j) {  // only the other group's loads
-            const auto hooks = other_loads(j);
-#pragma unroll
-            for (int i = 0; i < 2 * F::BPW; ++i) hooks(i);
-            wait_global_loads();
+        } else {
             bar();
-            bar();
+            if (N1 > 0) {
+                e.template mfma_phase<false, true>(0, kbuf(1));  // M_0
+                bar();
+                e.softmax(softmax_ok(0));  // V_0
+                bar();
+                int j = 1;
+                for (; j < N1; ++j) {
+                    e.template mfma_phase<true, true>(vbuf(1), kbuf(1));  // M_j
+                    bar();
+                    e.softmax(softmax_ok(j));  // V_j
+                    bar();
+                }
+                e.template mfma_phase<true, false>(vbuf(1), 0);  // M_N1
+                bar();
+                bar();
+            }
         }
     }
     while (nbar < total) bar();

@@ -257,6 +257,9 @@ struct WaveEngine {
                 return *(const bf16x8*)(smem + kb + koff[c] + nb * 32 * G::ROW_BYTES);
             }
         };
+        // Raised issue priority for the phase: where another wave on the
+        // SIMD runs its softmax, this wave's MFMAs and operand reads go first.
+        __builtin_amdgcn_s_setprio(1);
         if constexpr (QK) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) sacc[nb] = f32x16{};
@@ -290,6 +293,7 @@ struct WaveEngine {
                 ((hook(H), steps.template operator()<H * NS / NH, (H + 1) * NS / NH, false>()), ...);
             }(std::make_integer_sequence<int, NH>{});
         }
+        __builtin_amdgcn_s_setprio(0);
     }
 
     // Partial tile: scores of keys at or past nv (0 < nv < BKV) become -inf,

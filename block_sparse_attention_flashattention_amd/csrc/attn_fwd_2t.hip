@@ -19,14 +19,12 @@
 //     group 1:  -      M_0    V_0    M_1   ...
 //
 // Each group holds one K and one V tile in LDS (4 tiles = 128 KB at D = 128).
-// After group g's M_j both of its buffers are free for one window. All tile
-// loads are issued by group 0, whose waves are the older ones on their SIMDs:
-// group 1's K_j and V_{j-1} during group 0's M_j, group 0's own K_{j+1} and
-// V_j during its softmax V_j (which is shorter than group 1's M_j running
-// beside it). The loads are direct-to-LDS, spread over the phase, and waited
-// for before the window's barrier, so each has one window to land (the K/V
-// of a dense head are L2-resident). At the end group 1 hands its partial
-// rows to group 0 through LDS, which merges and writes O and LSE.
+// After group g's M_j both of its buffers are free for one window, in which
+// its K_{j+1} and V_j are fetched with direct-to-LDS loads and waited for
+// before the window's barrier (the K/V of a dense head are L2-resident).
+// Which waves issue which loads is set by measurement (see the note at the
+// loads below). At the end group 1 hands its partial rows to group 0
+// through LDS, which merges and writes O and LSE.
 #include "device_common.h"
 #include "vsa_internal.h"
 #include "wave_engine.h"
@@ -75,6 +73,7 @@ __global__ __launch_bounds__(512) void vsa_fwd_2t_kernel(FwdParams prm) {
     const int q0 = p * BQ + (wave & 3) * 32;
     // group 0: entries [0, N0), group 1: [N0, n)
     const int N0 = (n + 1) / 2, N1 = n - N0;
+    const int ng = grp ? N1 : N0;
 
     E e;
     e.init(smem, lane, prm.scale_log2);
@@ -99,34 +98,37 @@ __global__ __launch_bounds__(512) void vsa_fwd_2t_kernel(FwdParams prm) {
     auto tile_of = [&](int g, int j) { return entry_tile<PARTIAL>(entry(g, j)); };
     auto keys_of = [&](int g, int j) { return entry_keys<PARTIAL>(entry(g, j), BKV); };
 
-    // group 0's K_0 (entry 0), fetched by group 0 itself before the first window
-    if (grp == 0 && N0 > 0) fetch.all(kbuf(0), tile_at(kbase, __builtin_amdgcn_readfirstlane(irow[0])), tok_bytes, kLayoutK);
+    // K_0 of each group, fetched by that group before the first window; its
+    // tile index is read from the CSR row in global memory, since the staged
+    // copy is not visible to every wave before the barrier
+    if (ng > 0)
+        fetch.all(kbuf(grp), tile_at(kbase, __builtin_amdgcn_readfirstlane(irow[grp ? N0 : 0])), tok_bytes, kLayoutK);
     wait_global_loads();
     lds_barrier();
 
-    // Every tile load is issued by group 0 (waves 0-3, the older waves on
-    // each SIMD): during its M_j it fetches group 1's K_j and V_{j-1}, and
-    // during its softmax V_j its own K_{j+1} and V_j. Loads issued by the
-    // younger wave of a SIMD while the older one runs its softmax were
-    // measured to stretch that MFMA phase by a third; the older wave's
-    // softmax has the slack for them. Hooks 0..BPW-1: K, BPW..2*BPW-1: V.
-    auto loads = [&](int g, int kj, int vj) {
-        const int ng_ = g ? N1 : N0;
-        const bool dk = kj < ng_, dv = vj >= 0 && vj < ng_;
+    // Where the tile loads go. Group 0 (waves 0-3, the older wave on each
+    // SIMD) fetches its own K_{j+1} and V_j during its softmax V_j, and group
+    // 1's V_{j-1} during its M_j, spread over the MFMA steps; group 1 fetches
+    // its own K_{j+1} during its softmax V_j. Loads issued by the younger
+    // wave of a SIMD while the older one runs its softmax were measured to
+    // stretch that MFMA phase by a third, so group 1 issues none in its
+    // MFMA phases; each group's softmax runs beside a longer MFMA phase and
+    // has the slack for its loads.
+    auto k_loads = [&](int g, int kj) {  // BPW hooks: K_kj of group g, if it exists
+        const bool dk = kj < (g ? N1 : N0);
         const char* kt = dk ? tile_at(kbase, tile_of(g, kj)) : nullptr;
+        const int kd = kbuf(g);
+        return [=, &fetch](int i) { if (dk) fetch.block(kd, kt, tok_bytes, kLayoutK, i); };
+    };
+    auto v_loads = [&](int g, int vj) {  // BPW hooks: V_vj of group g, if it exists
+        const bool dv = vj >= 0 && vj < (g ? N1 : N0);
         const char* vt = dv ? tile_at(vbase, tile_of(g, vj)) : nullptr;
-        const int kd = kbuf(g), vd = vbuf(g);
-        return [=, &fetch](int i) {
-            if (i < F::BPW) {
-                if (dk) fetch.block(kd, kt, tok_bytes, kLayoutK, i);
-            } else {
-                if (dv) fetch.block(vd, vt, tok_bytes, kLayoutV, i - F::BPW);
-            }
-        };
+        const int vd = vbuf(g);
+        return [=, &fetch](int i) { if (dv) fetch.block(vd, vt, tok_bytes, kLayoutV, i); };
     };
     auto issue = [](const auto& hooks) {
 #pragma unroll
-        for (int i = 0; i < 2 * F::BPW; ++i) hooks(i);
+        for (int i = 0; i < F::BPW; ++i) hooks(i);
     };
     auto softmax_ok = [&](int j) __attribute__((always_inline)) {
         const int nv = keys_of(grp, j);
@@ -149,24 +151,25 @@ __global__ __launch_bounds__(512) void vsa_fwd_2t_kernel(FwdParams prm) {
     if (n > 0) {
         if (grp == 0) {
             // N0 >= 1 and N0 >= N1
-            e.template mfma_phase<false, true, 2 * F::BPW>(0, kbuf(0), loads(1, 0, -1));  // M_0
-            wait_global_loads();
+            e.template mfma_phase<false, true>(0, kbuf(0));  // M_0
             bar();
-            issue(loads(0, 1, 0));
+            issue(k_loads(0, 1));
+            issue(v_loads(0, 0));
             e.softmax(softmax_ok(0));  // V_0
             wait_global_loads();
             bar();
             int j = 1;
             for (; j < N0; ++j) {
-                e.template mfma_phase<true, true, 2 * F::BPW>(vbuf(0), kbuf(0), loads(1, j, j - 1));  // M_j
+                e.template mfma_phase<true, true, F::BPW>(vbuf(0), kbuf(0), v_loads(1, j - 1));  // M_j
                 wait_global_loads();
                 bar();
-                issue(loads(0, j + 1, j));
+                issue(k_loads(0, j + 1));
+                issue(v_loads(0, j));
                 e.softmax(softmax_ok(j));  // V_j
                 wait_global_loads();
                 bar();
             }
-            e.template mfma_phase<true, false, 2 * F::BPW>(vbuf(0), 0, loads(1, j, j - 1));  // M_N0
+            e.template mfma_phase<true, false, F::BPW>(vbuf(0), 0, v_loads(1, j - 1));  // M_N0
             wait_global_loads();
             bar();
             bar();
@@ -175,13 +178,17 @@ __global__ __launch_bounds__(512) void vsa_fwd_2t_kernel(FwdParams prm) {
             if (N1 > 0) {
                 e.template mfma_phase<false, true>(0, kbuf(1));  // M_0
                 bar();
+                issue(k_loads(1, 1));
                 e.softmax(softmax_ok(0));  // V_0
+                wait_global_loads();
                 bar();
                 int j = 1;
                 for (; j < N1; ++j) {
                     e.template mfma_phase<true, true>(vbuf(1), kbuf(1));  // M_j
                     bar();
+                    issue(k_loads(1, j + 1));
                     e.softmax(softmax_ok(j));  // V_j
+                    wait_global_loads();
                     bar();
                 }
                 e.template mfma_phase<true, false>(vbuf(1), 0);  // M_N1

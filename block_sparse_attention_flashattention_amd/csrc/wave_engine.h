@@ -343,9 +343,11 @@ struct WaveEngine {
 #pragma unroll
         for (int ch = 0; ch < CHUNKS; ++ch) {
             // hooks h with floor(h * CHUNKS / NH) == ch run before chunk ch
+            if constexpr (NH > 0) {
 #pragma unroll
-            for (int h = 0; h < NH; ++h)
-                if (h * CHUNKS / NH == ch) hook(h);
+                for (int h = 0; h < NH; ++h)
+                    if (h * CHUNKS / NH == ch) hook(h);
+            }
             const int nb = ch >> 1, half = ch & 1;
             u32x4 w;
 #pragma unroll

@@ -252,6 +252,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_bwd_dq_kernel(BwdParams prm) {
         nv = nv < 0 ? 0 : (nv > SUB ? SUB : nv);
         if (nv == 0) continue;  // uniform: every wave skips the same step
         const int kb = (j & 1) * STAGE, vb = kb + G::TILE;
+        // MFMA blocks at raised issue priority, the exp / dS work at normal
+        // priority: the other workgroup's wave on the SIMD fills the gaps
+        __builtin_amdgcn_s_setprio(1);
         f32x16 s[NB], dp[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -265,6 +268,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_bwd_dq_kernel(BwdParams prm) {
                 dp[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, doreg[c], dp[nb], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         // dS^T = P^T (dP^T - D), P^T = exp2(S^T * scale*log2e - LSE*log2e); keys at or past nv do not exist
         bf16x8 pk[KC];
 #pragma unroll
@@ -286,12 +290,14 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_bwd_dq_kernel(BwdParams prm) {
             pk[ch] = __builtin_bit_cast(bf16x8, w);
         }
         // dQ^T += K^T dS^T
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int g = 0; g < KC; ++g)
 #pragma unroll
             for (int db = 0; db < DB; ++db)
                 dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(smem, kb, ko, db, g), pk[g], dq[db], 0,
                                                                  0, 0);
+        __builtin_amdgcn_s_setprio(0);
     }
     store_rows<DB>(prm.dq + qrow, dq, prm.scale, hi);
 }
@@ -396,6 +402,7 @@ __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) 
         // S = Q K^T and dP = dO V^T for every 32-row block of the step first,
         // then per block the exp/dS work and the dV, dK products
         f32x16 s[QS / 32], dp[QS / 32];
+        __builtin_amdgcn_s_setprio(1);  // MFMA blocks at raised issue priority, as in the dQ kernel
 #pragma unroll
         for (int qs = 0; qs < QS / 32; ++qs) {
             s[qs] = f32x16{};
@@ -410,6 +417,7 @@ __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) 
                 const bf16x8 oa = *(const bf16x8*)(smem + ob + qo.row[c] + qs * 32 * OO::ROW_BYTES);
                 dp[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vreg[c], dp[qs], 0, 0, 0);
             }
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int qs = 0; qs < QS / 32; ++qs) {
             // rows q = qs*32 + 8*(r/4) + 4*hi + r%4: their D and lse2, four at a time
@@ -440,6 +448,7 @@ __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) 
                 ps[half] = __builtin_bit_cast(bf16x8, wsd);
             }
             // dV^T += dO^T P, dK^T += Q^T dS over the 32 rows (two 16-row k chunks)
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -449,6 +458,7 @@ __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) 
                     dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand<D>(smem, qb, qo, db, qs * 2 + g), ps[g],
                                                                      dk[db], 0, 0, 0);
                 }
+            __builtin_amdgcn_s_setprio(0);
         }
     }
     store_rows<DB>(prm.dk + krow, dk, prm.scale, hi);

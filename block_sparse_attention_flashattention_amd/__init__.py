@@ -42,6 +42,7 @@ SYMBOLS = (
     "vsa_attn_fwd_worklist",
     "vsa_attn_bwd",
     "vsa_release",
+    "vsa_set_max_splits",
 )
 
 
@@ -94,6 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vsa_attn_bwd.restype = i32
     lib.vsa_release.argtypes = []
     lib.vsa_release.restype = None
+    lib.vsa_set_max_splits.argtypes = [i32]
+    lib.vsa_set_max_splits.restype = i32
     _lib = lib
     return lib
 
@@ -383,3 +386,9 @@ def vsa_attn_bwd(q, k, v, o, lse, dout, kv_block_idx, kv_block_cnt, q_block_idx,
 
 def vsa_release() -> None:
     load_library().vsa_release()
+
+
+def vsa_set_max_splits(max_splits: int) -> int:
+    """Most parts (1, 2 or 4) a work item's list may be split into when a
+    launch has too few items; returns the previous value."""
+    return int(load_library().vsa_set_max_splits(int(max_splits)))

@@ -146,6 +146,48 @@ __device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16 (&acc)[DB
     }
 }
 
+// Split lists: every part of a work item publishes its accumulators (NA
+// 16-float blocks per lane) with device-scope stores, waits for them, then
+// bumps the item's counter; the last part to arrive returns true with the sum
+// of all parts, taken in part order so that the result does not depend on
+// which part that is, and resets the counter. The others return false. mine:
+// this wave's slot; parts: part 0's slot for this wave, part q at q * stride.
+// smem is free LDS (the tile stages, after the last step).
+template <int NA>
+__device__ __forceinline__ bool merge_parts(f32x16 (&acc)[NA], float* mine, const float* parts, int64_t stride,
+                                            int SP, int32_t* counter, char* smem, int tid) {
+    const int lane = tid & 63;
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            __hip_atomic_store(&mine[(a * 16 + r) * 64 + lane], acc[a][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_global_loads();  // the stores have reached the coherence point
+    lds_barrier();
+    int* flag = (int*)smem;
+    if (tid == 0) {
+        const int last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == SP - 1;
+        if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = last;
+    }
+    lds_barrier();
+    if (__builtin_amdgcn_readfirstlane(*flag) == 0) return false;
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[a][r] = __hip_atomic_load(&parts[(a * 16 + r) * 64 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int q = 1; q < SP; ++q) {
+#pragma unroll
+        for (int a = 0; a < NA; ++a)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                acc[a][r] += __hip_atomic_load(&parts[q * stride + (a * 16 + r) * 64 + lane], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return true;
+}
+
 struct BwdParams {
     const uint16_t *q, *k, *v, *dout;
     const float* aux;         // [2][B*H*S]: D, then LSE*log2(e)
@@ -158,6 +200,11 @@ struct BwdParams {
     const int32_t* work_kv;   // dK/dV work list (flat (b*H + h)*nkv + n)
     uint16_t *dq, *dk, *dv;
     int32_t n_items_q, n_items_kv;
+    // split lists (1 = off): workgroup wi serves part wi % splits of work
+    // entry wi / splits; per-item counters and partial accumulators
+    int32_t splits_q, splits_kv;
+    int32_t *ws_counter_q, *ws_counter_kv;
+    float *ws_q, *ws_kv;
     int32_t S, H, nq, nkv, ld, q_ld, block_q, block_kv;
     int32_t n_rows;           // B*H*S
     float scale, scale_log2;
@@ -171,7 +218,7 @@ struct BwdParams {
 // is computed. Every variant stays within 256 registers per wave, so each
 // SIMD runs two waves (of one workgroup at 256 rows, of two or four smaller
 // ones otherwise).
-template <int BQ, int D, bool PARTIAL>
+template <int BQ, int D, bool PARTIAL, bool SPLIT>
 __global__ __launch_bounds__(BQ * 2, 2) void vsa_bwd_dq_kernel(BwdParams prm) {
     constexpr int NW = BQ / 32;
     constexpr int SUB = dq_sub<BQ>();
@@ -186,17 +233,23 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_bwd_dq_kernel(BwdParams prm) {
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wi = xcd_contiguous_block();
-    if (wi >= prm.n_items_q) return;
-    const int item = prm.work_q ? prm.work_q[wi] : wi;
+    const int SP = SPLIT ? prm.splits_q : 1;  // built apart so the unsplit loop keeps its registers
+    if (wi >= prm.n_items_q * SP) return;
+    const int slot = SP == 1 ? wi : wi / SP;
+    const int part = wi - slot * SP;  // takes list entries part, part + SP, ...
+    const int item = prm.work_q ? prm.work_q[slot] : slot;
     if (item < 0 || item >= prm.n_items_q) return;
     const int p = item % prm.nq, bh = item / prm.nq, h = bh % prm.H, b = bh / prm.H;
     const int S = prm.S, nkv = prm.nkv, block_kv = prm.block_kv;
     const int64_t tok_stride = (int64_t)prm.H * D;
     const int tok_bytes = (int)(tok_stride * 2);
-    const int32_t* irow = prm.idx + (int64_t)item * prm.ld;
-    const int ldc = prm.ld < kIdxCapBwd ? prm.ld : kIdxCapBwd;
+    const int32_t* irow = prm.idx + (int64_t)item * prm.ld + part;
+    const int ldp = prm.ld > part ? (prm.ld - part + SP - 1) / SP : 0;  // this part's slots of the row
+    const int ldc = ldp < kIdxCapBwd ? ldp : kIdxCapBwd;
     int n = prm.cnt[item];
-    n = n < 0 ? 0 : (n > ldc ? ldc : n);
+    n = n < 0 ? 0 : (n > prm.ld ? prm.ld : n);
+    n = n > part ? (n - part + SP - 1) / SP : 0;  // this part's entries
+    n = n > ldc ? ldc : n;
     const int R = block_kv / SUB;
     const int steps = n * R;
     const int q0 = p * BQ + wave * 32;
@@ -210,7 +263,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_bwd_dq_kernel(BwdParams prm) {
     const float lse2 = prm.aux[(int64_t)prm.n_rows + arow];
 
     int* lidx = (int*)(smem + 2 * STAGE);
-    for (int i = tid; i < ldc; i += BQ * 2) lidx[i] = stage_entry<PARTIAL>(irow[i], nkv, block_kv, prm.kv_valid);
+    for (int i = tid; i < ldc; i += BQ * 2)
+        lidx[i] = stage_entry<PARTIAL>(irow[(int64_t)i * SP], nkv, block_kv, prm.kv_valid);
     // consume every loaded register before the first tile load (the compiler's
     // wait counting does not see the inline-asm tile loads)
 #pragma unroll
@@ -299,6 +353,12 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_bwd_dq_kernel(BwdParams prm) {
                                                                  0, 0);
         __builtin_amdgcn_s_setprio(0);
     }
+    if (SPLIT) {
+        float* mine = prm.ws_q + ((int64_t)wi * NW + wave) * (DB * 16 * 64);
+        const float* parts = prm.ws_q + ((int64_t)slot * SP * NW + wave) * (DB * 16 * 64);
+        if (!merge_parts<DB>(dq, mine, parts, (int64_t)NW * DB * 16 * 64, SP, prm.ws_counter_q + item, smem, tid))
+            return;
+    }
     store_rows<DB>(prm.dq + qrow, dq, prm.scale, hi);
 }
 
@@ -311,7 +371,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_bwd_dq_kernel(BwdParams prm) {
 // 32-row steps keep a 128-key workgroup within 256 registers per wave, so two
 // workgroups share a compute unit and each SIMD has a second wave whose MFMAs
 // can run while this one computes exponentials.
-template <int BKV, int D, bool PARTIAL>
+template <int BKV, int D, bool PARTIAL, bool SPLIT>
 __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) {
     constexpr int NW = BKV / 32;
     constexpr int QS = kDkvQs;  // query rows per step
@@ -326,17 +386,23 @@ __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) 
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wi = xcd_contiguous_block();
-    if (wi >= prm.n_items_kv) return;
-    const int item = prm.work_kv ? prm.work_kv[wi] : wi;
+    const int SP = SPLIT ? prm.splits_kv : 1;  // built apart so the unsplit loop keeps its registers
+    if (wi >= prm.n_items_kv * SP) return;
+    const int slot = SP == 1 ? wi : wi / SP;
+    const int part = wi - slot * SP;  // takes list entries part, part + SP, ...
+    const int item = prm.work_kv ? prm.work_kv[slot] : slot;
     if (item < 0 || item >= prm.n_items_kv) return;
     const int nt = item % prm.nkv, bh = item / prm.nkv, h = bh % prm.H, b = bh / prm.H;
     const int S = prm.S, nq = prm.nq, block_q = prm.block_q;
     const int64_t tok_stride = (int64_t)prm.H * D;
     const int tok_bytes = (int)(tok_stride * 2);
-    const int32_t* qrow_list = prm.qidx + (int64_t)item * prm.q_ld;
-    const int ldc = prm.q_ld < kIdxCapBwd ? prm.q_ld : kIdxCapBwd;
+    const int32_t* qrow_list = prm.qidx + (int64_t)item * prm.q_ld + part;
+    const int ldp = prm.q_ld > part ? (prm.q_ld - part + SP - 1) / SP : 0;  // this part's slots of the row
+    const int ldc = ldp < kIdxCapBwd ? ldp : kIdxCapBwd;
     int n = prm.qcnt[item];
-    n = n < 0 ? 0 : (n > ldc ? ldc : n);
+    n = n < 0 ? 0 : (n > prm.q_ld ? prm.q_ld : n);
+    n = n > part ? (n - part + SP - 1) / SP : 0;  // this part's entries
+    n = n > ldc ? ldc : n;
     const int RQ = block_q / QS;
     const int steps = n * RQ;
     const int kv0 = nt * BKV + wave * 32;
@@ -355,7 +421,7 @@ __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) 
 
     int* lq = (int*)(smem + 2 * STAGE);
     for (int i = tid; i < ldc; i += BKV * 2) {
-        const int m = qrow_list[i];
+        const int m = qrow_list[(int64_t)i * SP];
         lq[i] = (m >= 0 && m < nq) ? m : -1;
     }
 #pragma unroll
@@ -461,6 +527,23 @@ __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) 
             __builtin_amdgcn_s_setprio(0);
         }
     }
+    if (SPLIT) {
+        constexpr int64_t W = 2 * DB * 16 * 64;  // dK, then dV
+        f32x16 acc[2 * DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            acc[db] = dk[db];
+            acc[DB + db] = dv[db];
+        }
+        float* mine = prm.ws_kv + ((int64_t)wi * NW + wave) * W;
+        const float* parts = prm.ws_kv + ((int64_t)slot * SP * NW + wave) * W;
+        if (!merge_parts<2 * DB>(acc, mine, parts, (int64_t)NW * W, SP, prm.ws_counter_kv + item, smem, tid)) return;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            dk[db] = acc[db];
+            dv[db] = acc[DB + db];
+        }
+    }
     store_rows<DB>(prm.dk + krow, dk, prm.scale, hi);
     store_rows<DB>(prm.dv + krow, dv, 1.0f, hi);
 }
@@ -487,20 +570,37 @@ hipError_t launch_dyn(K kernel, int grid, int threads, int lds, const BwdParams&
     return hipGetLastError();
 }
 
+template <int D, bool PARTIAL, bool SPLIT>
+hipError_t launch_dq_s(const BwdParams& p, hipStream_t stream) {
+    const int list = 4 * (p.ld < kIdxCapBwd ? p.ld : kIdxCapBwd);
+    const int grid = p.n_items_q * p.splits_q;
+    switch (p.block_q) {
+        case 64:
+            return launch_dyn(vsa_bwd_dq_kernel<64, D, PARTIAL, SPLIT>, grid, 128, 2 * dq_stage_bytes<64, D>() + list, p,
+                              stream);
+        case 128:
+            return launch_dyn(vsa_bwd_dq_kernel<128, D, PARTIAL, SPLIT>, grid, 256,
+                              2 * dq_stage_bytes<128, D>() + list, p, stream);
+        case 256:
+            return launch_dyn(vsa_bwd_dq_kernel<256, D, PARTIAL, SPLIT>, grid, 512,
+                              2 * dq_stage_bytes<256, D>() + list, p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int D, bool PARTIAL>
 hipError_t launch_dq_d(const BwdParams& p, hipStream_t stream) {
     if (p.n_items_q <= 0) return hipSuccess;
-    const int list = 4 * (p.ld < kIdxCapBwd ? p.ld : kIdxCapBwd);
-    switch (p.block_q) {
-        case 64:
-            return launch_dyn(vsa_bwd_dq_kernel<64, D, PARTIAL>, p.n_items_q, 128, 2 * dq_stage_bytes<64, D>() + list, p,
-                              stream);
-        case 128:
-            return launch_dyn(vsa_bwd_dq_kernel<128, D, PARTIAL>, p.n_items_q, 256, 2 * dq_stage_bytes<128, D>() + list,
-                              p, stream);
-        case 256:
-            return launch_dyn(vsa_bwd_dq_kernel<256, D, PARTIAL>, p.n_items_q, 512, 2 * dq_stage_bytes<256, D>() + list,
-                              p, stream);
+    return p.splits_q > 1 ? launch_dq_s<D, PARTIAL, true>(p, stream) : launch_dq_s<D, PARTIAL, false>(p, stream);
+}
+
+template <int D, bool PARTIAL, bool SPLIT>
+hipError_t launch_dkv_s(const BwdParams& p, hipStream_t stream) {
+    const int lds = 2 * dkv_stage_bytes<D>() + 4 * (p.q_ld < kIdxCapBwd ? p.q_ld : kIdxCapBwd);
+    const int grid = p.n_items_kv * p.splits_kv;
+    switch (p.block_kv) {
+        case 64: return launch_dyn(vsa_bwd_dkv_kernel<64, D, PARTIAL, SPLIT>, grid, 128, lds, p, stream);
+        case 128: return launch_dyn(vsa_bwd_dkv_kernel<128, D, PARTIAL, SPLIT>, grid, 256, lds, p, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -508,12 +608,7 @@ hipError_t launch_dq_d(const BwdParams& p, hipStream_t stream) {
 template <int D, bool PARTIAL>
 hipError_t launch_dkv_d(const BwdParams& p, hipStream_t stream) {
     if (p.n_items_kv <= 0) return hipSuccess;
-    const int lds = 2 * dkv_stage_bytes<D>() + 4 * (p.q_ld < kIdxCapBwd ? p.q_ld : kIdxCapBwd);
-    switch (p.block_kv) {
-        case 64: return launch_dyn(vsa_bwd_dkv_kernel<64, D, PARTIAL>, p.n_items_kv, 128, lds, p, stream);
-        case 128: return launch_dyn(vsa_bwd_dkv_kernel<128, D, PARTIAL>, p.n_items_kv, 256, lds, p, stream);
-        default: return hipErrorInvalidValue;
-    }
+    return p.splits_kv > 1 ? launch_dkv_s<D, PARTIAL, true>(p, stream) : launch_dkv_s<D, PARTIAL, false>(p, stream);
 }
 
 }  // namespace
@@ -553,6 +648,12 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.n_items_kv = a.B * a.H * p.nkv;
     p.scale = a.scale;
     p.scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+    p.splits_q = a.splits_q > 1 ? a.splits_q : 1;
+    p.splits_kv = a.splits_kv > 1 ? a.splits_kv : 1;
+    p.ws_counter_q = a.ws_counter_q;
+    p.ws_counter_kv = a.ws_counter_kv;
+    p.ws_q = a.ws_q;
+    p.ws_kv = a.ws_kv;
     hipError_t e = a.D == 128 ? launch_prep<128>(a.o, a.dout, a.lse, a.aux, p.n_rows, a.S, a.H, stream)
                               : launch_prep<64>(a.o, a.dout, a.lse, a.aux, p.n_rows, a.S, a.H, stream);
     if (e != hipSuccess) return e;

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -98,12 +99,12 @@ vsa::FwdParams make_params(const void* q, const void* k, const void* v, const in
 struct DeviceBuffer {
     void* ptr = nullptr;
     size_t bytes = 0;
+    size_t zeroed = 0;  // split workspaces: leading bytes known to hold zero counters
 };
 std::mutex g_buf_mutex;
 std::vector<DeviceBuffer> g_bufs;      // forward work list
 std::vector<DeviceBuffer> g_bwd_bufs;  // backward scratch (D, LSE*log2 e, two work lists)
 std::vector<DeviceBuffer> g_pair_bufs; // paired forward: counter, paired CSR, two work lists
-std::vector<DeviceBuffer> g_split_bufs; // split lists: per-item counters, then partial row states
 
 int32_t device_buffer(std::vector<DeviceBuffer>& bufs, size_t bytes, void** out) {
     int dev = 0;
@@ -122,30 +123,34 @@ int32_t device_buffer(std::vector<DeviceBuffer>& bufs, size_t bytes, void** out)
         e = hipMalloc(&b.ptr, bytes);
         if (e != hipSuccess) return hip_fail(e, "hipMalloc(library buffer)");
         b.bytes = bytes;
+        b.zeroed = 0;
     }
     *out = b.ptr;
     return VSA_OK;
 }
 
-// Workspace of the split-list forward: counter_bytes of per-item counters
-// (zeroed whenever the buffer is (re)allocated; the kernel returns each to 0)
-// followed by the partial row states.
-int32_t split_buffer(size_t counter_bytes, size_t bytes, hipStream_t stream, void** out) {
+// Workspace of a split-list launch: counter_bytes of per-item counters
+// followed by the partial states. The kernels return every counter they use
+// to 0, but the bytes past the previous call's counters held partial states,
+// so the counters are cleared whenever they reach beyond the bytes known to
+// be zero (a new buffer holds none).
+std::atomic<int32_t> g_max_splits{4};        // vsa_set_max_splits
+std::vector<DeviceBuffer> g_split_bufs;      // forward
+std::vector<DeviceBuffer> g_bwd_split_bufs;  // backward
+int32_t split_buffer(std::vector<DeviceBuffer>& bufs, size_t counter_bytes, size_t bytes, hipStream_t stream,
+                     void** out) {
+    int32_t rc = device_buffer(bufs, bytes, out);
+    if (rc != VSA_OK) return rc;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    bool fresh = false;
-    {
-        std::lock_guard<std::mutex> lock(g_buf_mutex);
-        if ((int)g_split_bufs.size() <= dev) g_split_bufs.resize(dev + 1);
-        fresh = g_split_bufs[dev].bytes < bytes;
-    }
-    int32_t rc = device_buffer(g_split_bufs, bytes, out);
-    if (rc != VSA_OK) return rc;
-    if (fresh) {
+    std::lock_guard<std::mutex> lock(g_buf_mutex);
+    DeviceBuffer& b = bufs[dev];
+    if (b.zeroed < counter_bytes) {
         e = hipMemsetAsync(*out, 0, counter_bytes, stream);
         if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(split counters)");
     }
+    b.zeroed = counter_bytes;  // past them the partial states are written
     return VSA_OK;
 }
 
@@ -160,7 +165,12 @@ int32_t worklist_buffer(size_t bytes, int32_t** out) {
 
 extern "C" {
 
-int32_t vsa_abi_version(void) { return 4; }
+int32_t vsa_abi_version(void) { return 5; }
+
+int32_t vsa_set_max_splits(int32_t max_splits) {
+    const int32_t m = max_splits >= 4 ? 4 : (max_splits >= 2 ? 2 : 1);
+    return g_max_splits.exchange(m);
+}
 
 const char* vsa_status_string(int32_t status) {
     switch (status) {
@@ -266,17 +276,18 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
     // independent-wave kernel, four per compute unit. (128-row tiles with few
     // items measured faster on the two-stream kernel unsplit.)
     const int cus = vsa::device_cu_count();
+    const int max_splits = g_max_splits.load();
     if (block_q == 256) {
-        while (p.splits < 4 && (int64_t)n_items * p.splits * 2 <= cus) p.splits *= 2;
+        while (p.splits < max_splits && (int64_t)n_items * p.splits * 2 <= cus) p.splits *= 2;
     } else if (block_q == 64 && (int64_t)n_items < (int64_t)vsa::kIwItemsPerCu * cus) {
-        while (p.splits < 4 && (int64_t)n_items * p.splits < 4LL * cus) p.splits *= 2;
+        while (p.splits < max_splits && (int64_t)n_items * p.splits < 4LL * cus) p.splits *= 2;
     }
     if (p.splits > 1) {
         const size_t counters = ((size_t)n_items * sizeof(int32_t) + 255) / 256 * 256;
         const size_t state_words = (size_t)(head_dim / 32 * 16 + 2) * 64;  // per wave
         const size_t bytes = counters + (size_t)n_items * p.splits * (block_q / 32) * state_words * sizeof(float);
         void* ws = nullptr;
-        rc = split_buffer(counters, bytes, (hipStream_t)stream, &ws);
+        rc = split_buffer(g_split_bufs, counters, bytes, (hipStream_t)stream, &ws);
         if (rc != VSA_OK) return rc;
         p.ws_counter = (int32_t*)ws;
         p.ws_partial = (float*)((char*)ws + counters);
@@ -452,6 +463,29 @@ int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o,
     a.block_q = block_q;
     a.block_kv = block_kv;
     a.scale = scale;
+    // Fewer work items than two waves per SIMD: split each list over 2 or 4
+    // workgroups whose fp32 accumulators the last one sums (deterministic).
+    const int64_t waves = 8LL * vsa::device_cu_count();
+    const int max_splits = g_max_splits.load();
+    while (a.splits_q < max_splits && (int64_t)items_q * a.splits_q * (block_q / 32) < waves) a.splits_q *= 2;
+    while (a.splits_kv < max_splits && (int64_t)items_kv * a.splits_kv * (block_kv / 32) < waves) a.splits_kv *= 2;
+    if (a.splits_q > 1 || a.splits_kv > 1) {
+        const size_t cq = ((size_t)items_q * sizeof(int32_t) + 255) / 256 * 256;
+        const size_t ckv = ((size_t)items_kv * sizeof(int32_t) + 255) / 256 * 256;
+        const size_t wq = a.splits_q > 1 ? (size_t)items_q * a.splits_q * (block_q / 32) *
+                                               vsa::bwd_split_words_q(head_dim) * sizeof(float)
+                                         : 0;
+        const size_t wkv = a.splits_kv > 1 ? (size_t)items_kv * a.splits_kv * (block_kv / 32) *
+                                                 vsa::bwd_split_words_kv(head_dim) * sizeof(float)
+                                           : 0;
+        void* ws = nullptr;
+        rc = split_buffer(g_bwd_split_bufs, cq + ckv, cq + ckv + wq + wkv, st, &ws);
+        if (rc != VSA_OK) return rc;
+        a.ws_counter_q = (int32_t*)ws;
+        a.ws_counter_kv = (int32_t*)((char*)ws + cq);
+        a.ws_q = (float*)((char*)ws + cq + ckv);
+        a.ws_kv = (float*)((char*)ws + cq + ckv + wq);
+    }
     e = vsa::launch_bwd(a, st);
     if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
     return VSA_OK;
@@ -459,7 +493,7 @@ int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 void vsa_release(void) {
     std::lock_guard<std::mutex> lock(g_buf_mutex);
-    for (auto* v : {&g_bufs, &g_bwd_bufs, &g_pair_bufs, &g_split_bufs}) {
+    for (auto* v : {&g_bufs, &g_bwd_bufs, &g_pair_bufs, &g_split_bufs, &g_bwd_split_bufs}) {
         for (auto& b : *v) {
             if (b.ptr) (void)hipFree(b.ptr);
             b.ptr = nullptr;

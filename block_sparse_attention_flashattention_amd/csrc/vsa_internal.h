@@ -100,7 +100,14 @@ struct BwdArgs {
     uint16_t *dq, *dk, *dv;
     int32_t B, S, H, D, ld, q_ld, block_q, block_kv;
     float scale;
+    // split lists (1 = off) and their workspaces (counters zero on entry)
+    int32_t splits_q = 1, splits_kv = 1;
+    int32_t *ws_counter_q = nullptr, *ws_counter_kv = nullptr;
+    float *ws_q = nullptr, *ws_kv = nullptr;
 };
+// Accumulator floats per wave that a split backward part publishes.
+inline int bwd_split_words_q(int head_dim) { return head_dim / 32 * 16 * 64; }
+inline int bwd_split_words_kv(int head_dim) { return 2 * head_dim / 32 * 16 * 64; }
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 bool bwd_supported(int block_q, int block_kv, int head_dim);
 

@@ -260,7 +260,11 @@ int32_t vsa_attn_fwd_paired(const void* q, const void* k, const void* v, const i
  * dV = P^T dO, dK = scale dS^T Q, dQ = scale dS K. Deterministic: dK and dV
  * of a KV tile accumulate in one workgroup over its query tiles in list
  * order, dQ of a query tile in one workgroup over its KV tiles in list order;
- * no atomics. bf16 in and out, fp32 accumulation.
+ * no floating-point atomics. bf16 in and out, fp32 accumulation. When the
+ * query tiles (or KV tiles) number fewer than two waves per SIMD of the GPU,
+ * each list is split over 2 or 4 workgroups (at most vsa_set_max_splits):
+ * each publishes its fp32 partial sums, and the last to finish adds all
+ * parts in part order, so results stay deterministic on a given GPU.
  *
  *   q, k, v, o, dout, dq, dk, dv   [batch, seqlen, heads, head_dim] bf16
  *                  (o: the forward output; dq, dk, dv written, every row)
@@ -271,7 +275,9 @@ int32_t vsa_attn_fwd_paired(const void* q, const void* k, const void* v, const i
  *                  dK = dV = 0
  *   Same shape limits as vsa_attn_fwd; q_ld, idx_ld <= 8191. Uses a
  *   library-owned device buffer of 8*batch*heads*seqlen bytes plus the work
- *   lists (grown on demand per device, released by vsa_release); calls that
+ *   lists, and with split lists another of 4*head_dim bytes per token row and
+ *   part for dQ and twice that for dK and dV (both grown on demand per
+ *   device, released by vsa_release); calls that
  *   share a device must not overlap in time on different streams. Padding
  *   tokens of partial tiles must hold finite values.
  */
@@ -284,6 +290,18 @@ int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o,
 /* Free the library-owned work-list buffers on every device. Not thread-safe
  * with concurrent vsa_attn_fwd calls. */
 void vsa_release(void);
+
+/*
+ * vsa_set_max_splits -- the most parts (1, 2 or 4; other values are rounded
+ * down to one of those, values below 2 give 1) into which vsa_attn_fwd and
+ * vsa_attn_bwd may split a work item's list when a launch has too few work
+ * items to fill the GPU. The default is 4. Whether a launch splits depends
+ * on the GPU's compute unit count, and a split changes the fp32 summation
+ * order, so 1 gives results that are bit-identical across GPU models (at
+ * some speed when items are few). Process-wide; takes effect for calls that
+ * start after it returns. Returns the previous value.
+ */
+int32_t vsa_set_max_splits(int32_t max_splits);
 
 #ifdef __cplusplus
 }

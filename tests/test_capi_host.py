@@ -36,7 +36,19 @@ def test_header_declares_the_binding_symbols():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.vsa_abi_version() == 4
+    assert lib.vsa_abi_version() == 5
+
+
+def test_set_max_splits_rounds_and_returns_previous(lib):
+    prev = lib.vsa_set_max_splits(3)
+    try:
+        assert prev in (1, 2, 4)
+        assert lib.vsa_set_max_splits(0) == 2  # 3 was rounded down to 2
+        assert lib.vsa_set_max_splits(100) == 1
+        assert lib.vsa_set_max_splits(-5) == 4
+        assert lib.vsa_set_max_splits(2) == 1
+    finally:
+        lib.vsa_set_max_splits(prev)
 
 
 def test_status_strings(lib):

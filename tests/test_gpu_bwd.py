@@ -124,11 +124,21 @@ def _run_bwd(vsa, q, k, v, do, idx, cnt, bq, bkv, scale, kv_valid=None):
 BWD_SHAPES = [(bq, bkv, d) for bq in (64, 128, 256) for bkv in (64, 128) for d in (64, 128)]
 
 
+@pytest.fixture
+def max_splits(vsa, request):
+    """Cap on split lists for the test (restored afterwards)."""
+    prev = vsa.vsa_set_max_splits(request.param)
+    yield request.param
+    vsa.vsa_set_max_splits(prev)
+
+
 @pytest.mark.parametrize("bq,bkv,D", BWD_SHAPES, ids=[f"{a}x{b}_d{c}" for a, b, c in BWD_SHAPES])
 @pytest.mark.parametrize("partial", [False, True], ids=["full", "partial"])
-def test_backward_every_tile_shape_all_rows(vsa, bq, bkv, D, partial):
+@pytest.mark.parametrize("max_splits", [4, 1], ids=["split", "unsplit"], indirect=True)
+def test_backward_every_tile_shape_all_rows(vsa, bq, bkv, D, partial, max_splits):
+    """At this size every list is split (four parts) unless max_splits is 1."""
     B, H, S = 1, 2, 768
-    label = f"{bq}x{bkv} D={D} {'partial' if partial else 'full'}"
+    label = f"{bq}x{bkv} D={D} {'partial' if partial else 'full'} max_splits={max_splits}"
     say(f"backward {label}")
     q, k, v = W.qkv(B, S, H, D, seed=bq + bkv + D + 100)
     do = W.qkv(B, S, H, D, seed=bq + bkv + D + 101)[0]
@@ -146,9 +156,12 @@ def test_backward_every_tile_shape_all_rows(vsa, bq, bkv, D, partial):
         check(name, got.float().cpu().numpy(), ref, label)
 
 
-def test_backward_is_deterministic(vsa):
+@pytest.mark.parametrize("max_splits", [4, 1], ids=["split", "unsplit"], indirect=True)
+def test_backward_is_deterministic(vsa, max_splits):
+    """Two runs agree bit for bit, with split lists (the last part to finish
+    sums all parts in part order) and without."""
     B, H, S, D, bq, bkv = 1, 2, 1024, 128, 128, 64
-    say("backward determinism")
+    say(f"backward determinism max_splits={max_splits}")
     q, k, v = W.qkv(B, S, H, D, seed=7)
     do = W.qkv(B, S, H, D, seed=8)[0]
     idx, cnt = W.random_csr(B, H, S // bq, S // bkv, S // bkv, 1, 12, seed=9)
@@ -156,6 +169,32 @@ def test_backward_is_deterministic(vsa):
     b = _run_bwd(vsa, q, k, v, do, idx, cnt, bq, bkv, 0.09)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_dense_backward_split_lists_sampled(vsa):
+    """Dense S=4k at 128x128 (256 query and 256 KV tiles: split in two on a
+    256-CU GPU): sampled dQ and dK/dV rows against the oracle."""
+    wl = W.DENSE
+    say("dense backward 128x128: inputs")
+    q, k, v = wl.qkv()
+    do = W.qkv(wl.batch, wl.seqlen, wl.heads, wl.head_dim, seed=4243)[0]
+    idx, cnt, _ = ofront.mask_to_csr(wl.logical_mask(), wl.logical_block, (128, 128), 32)
+    dq, dk, dv = _run_bwd(vsa, q, k, v, do, idx, cnt, 128, 128, wl.scale)
+    B, S, H, D = q.shape
+    rng = np.random.default_rng(6)
+    qrows = np.array([h * S + r for h in range(H) for r in rng.integers(0, S, size=8)], dtype=np.int64)
+    krows = np.array([h * S + r for h in range(H) for r in rng.integers(0, S, size=4)], dtype=np.int64)
+    say("dense backward 128x128: oracle rows")
+    rq = oracle.bwd_dq_rows(q, k, v, do, idx, cnt, 128, 128, wl.scale, qrows)
+    rk, rv = oracle.bwd_dkv_rows(q, k, v, do, idx, cnt, 128, 128, wl.scale, krows)
+
+    def pick(t, rows):
+        h, i = rows // S, rows % S
+        return t.float().cpu().numpy()[0, i, h]
+
+    check("dQ", pick(dq, qrows), rq, "dense split sampled")
+    check("dK", pick(dk, krows), rk, "dense split sampled")
+    check("dV", pick(dv, krows), rv, "dense split sampled")
 
 
 FULL_SIZE = [

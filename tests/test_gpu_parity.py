@@ -408,6 +408,28 @@ def test_split_lists_deterministic_and_equal_to_unsplit(vsa, bq, bkv):
     assert d.max().item() <= O_MAX_ABS and lrel <= LSE_REL
 
 
+def test_split_workspace_reuse_with_more_items(vsa):
+    """A split launch with few items and large partial states, then one with
+    more items whose counters reach into the first one's state bytes while
+    its whole workspace still fits the buffer: the counters must read zero,
+    so every row of the second launch is written and matches the oracle."""
+    say("split workspace reuse")
+    vsa.vsa_release()
+    B, S, H, D = 1, 32768, 1, 128  # 128 items of 256 rows: split in two
+    q, k, v = (dev(t) for t in W.qkv(B, S, H, D, seed=91))
+    idx, cnt = W.random_csr(B, H, S // 256, S // 128, 2, 2, 2, seed=92)
+    _run_fwd(vsa, q, k, v, dev(idx), dev(cnt), 256, 128, 0.09)
+    B, S, H, D = 1, 16384, 2, 64  # 512 items of 64 rows: split in two
+    q, k, v = W.qkv(B, S, H, D, seed=93)
+    idx, cnt = W.random_csr(B, H, S // 64, S // 64, 3, 0, 3, seed=94)
+    o_ref, lse_ref = oracle.attn_full(q, k, v, idx, cnt, 64, 64, 0.125)
+    for rep in range(2):
+        o, lse = _run_fwd(vsa, dev(q), dev(k), dev(v), dev(idx), dev(cnt), 64, 64, 0.125)
+        rows = np.arange(B * H * S)
+        check_rows(o, lse, rows, o_ref.transpose(0, 2, 1, 3).reshape(-1, D), lse_ref.reshape(-1), S, H,
+                   f"split reuse call {rep}")
+
+
 def test_native64_workload_sampled(vsa):
     _full_size(vsa, W.NATIVE64, (64, 64), 92, "native64 64x64", tiles_per_head=3)
     torch.cuda.empty_cache()

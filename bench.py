@@ -406,11 +406,15 @@ def read_traffic(path, kname):
 
 
 def _counter_mean(d, counter, kernel_prefix):
+    """Mean of one counter over the dispatches whose kernel name contains
+    `kernel_prefix` (spaces ignored, so a full template name such as
+    vsa_fwd_iw_kernel<128,128,false> selects one instantiation)."""
     import csv
     vals = []
+    want = kernel_prefix.replace(" ", "")
     with open(os.path.join(d, "run_counter_collection.csv")) as f:
         for r in csv.DictReader(f):
-            if r["Counter_Name"] == counter and kernel_prefix in r["Kernel_Name"]:
+            if r["Counter_Name"] == counter and want in r["Kernel_Name"].replace(" ", ""):
                 vals.append(float(r["Counter_Value"]))
     if not vals:
         raise SystemExit(f"no {counter} rows for {kernel_prefix!r} in {d}")
@@ -426,13 +430,12 @@ def write_traffic(args):
     run_bq = 128 if args.paired else bq
     kname = kernel_name(run_bq, bkv, wl.head_dim, partial=args.ragged is not None,
                         n_items=wl.batch * wl.heads * (wl.seqlen // run_bq), entry=args.scope == "entry")
-    stem = kname.split("<")[0]
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_from_counters
     copy_bytes = 1 << 30
     fetch_scale = copy_bytes / (1024.0 * _counter_mean(cfetch_dir, "FETCH_SIZE", "copy"))
     write_scale = copy_bytes / (1024.0 * _counter_mean(cwrite_dir, "WRITE_SIZE", "copy"))
-    fetch = _counter_mean(fetch_dir, "FETCH_SIZE", stem) * 1024.0 * fetch_scale
-    write = _counter_mean(write_dir, "WRITE_SIZE", stem) * 1024.0 * write_scale
+    fetch = _counter_mean(fetch_dir, "FETCH_SIZE", kname) * 1024.0 * fetch_scale
+    write = _counter_mean(write_dir, "WRITE_SIZE", kname) * 1024.0 * write_scale
     out = {
         "kernel": kname, "workload": wl.name, "tile": f"{bq}x{bkv}",
         "bytes_per_launch": round(fetch + write),

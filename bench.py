@@ -60,6 +60,10 @@ def parse_args():
                     help="64-row tiles through vsa_attn_fwd_paired: adjacent query tiles with identical lists run as "
                          "128-row tiles (decided on the device; the timed scope then includes the pairing and both "
                          "work lists)")
+    ap.add_argument("--coalesce", action="store_true",
+                    help="64- or 128-row tiles through vsa_attn_fwd_coalesced: adjacent query tiles with identical "
+                         "lists run as one tile, level by level up to 256 rows (decided on the device; the timed "
+                         "scope then includes the pairing, the gates and all work lists)")
     ap.add_argument("--scope", choices=("kernel", "entry"), default="kernel",
                     help="kernel: the attention kernel over the work list built in the step (vsa_build_worklist + "
                          "vsa_attn_fwd_worklist, the kernel alone is timed); entry: vsa_attn_fwd, which builds its own "
@@ -137,10 +141,15 @@ def main():
     if args.paired and bq != 64:
         print("--paired needs 64-row query tiles", file=sys.stderr)
         return 2
+    if args.coalesce and (bq not in (64, 128) or args.paired):
+        print("--coalesce needs 64- or 128-row query tiles and excludes --paired", file=sys.stderr)
+        return 2
 
     def attention():
         if args.paired:
             vsa.vsa_attn_fwd_paired(q, k, v, idx, cnt, bkv, scale, o, lse, stream=stream, kv_valid=kv_valid)
+        elif args.coalesce:
+            vsa.vsa_attn_fwd_coalesced(q, k, v, idx, cnt, bq, bkv, scale, o, lse, stream=stream, kv_valid=kv_valid)
         elif args.scope == "entry":
             vsa.vsa_attn_fwd(q, k, v, idx, cnt, bq, bkv, scale, o, lse, stream=stream, kv_valid=kv_valid)
         else:
@@ -149,7 +158,7 @@ def main():
 
     def step(ev0=None, ev1=None):
         vsa.vsa_mask_to_csr(mask, (lq, lkv), (bq, bkv), ld, idx, cnt, stream=stream)
-        if not args.paired and args.scope == "kernel":
+        if not (args.paired or args.coalesce) and args.scope == "kernel":
             vsa.vsa_build_worklist(cnt, ld, work, segment=nq, stream=stream)
         if vbs is not None:
             vsa.vsa_expand_valid(vbs, lkv, bkv, kv_valid, stream=stream)
@@ -165,6 +174,14 @@ def main():
     run_bq = bq
     if args.paired:  # which schedule the device will choose (read once, outside the timed region)
         run_bq = 128 if int(vsa.vsa_pair_q_tiles(idx, cnt)[2].item()) == 0 else 64
+    if args.coalesce:  # the same, level by level up to 256 rows
+        ri, rc = idx, cnt
+        while run_bq < 256 and S % 256 == 0:
+            pi, pc, un = vsa.vsa_pair_q_tiles(ri, rc)
+            if int(un.item()) != 0:
+                break
+            ri, rc, run_bq = pi, pc, run_bq * 2
+        del ri, rc
     flops = 4.0 * D * pairs
     t_pre = time.perf_counter() + args.prewarm_seconds
     while time.perf_counter() < t_pre:
@@ -193,7 +210,7 @@ def main():
         vsa.vsa_mask_to_csr(mask, (lq, lkv), (bq, bkv), ld, idx, cnt, stream=stream)
         if vbs is not None:
             vsa.vsa_expand_valid(vbs, lkv, bkv, kv_valid, stream=stream)
-        if args.paired:
+        if args.paired or args.coalesce:
             attention()
         else:
             vsa.vsa_attn_fwd(q, k, v, idx, cnt, bq, bkv, scale, o, lse, stream=stream, kv_valid=kv_valid)
@@ -254,8 +271,8 @@ def main():
             "workload": wl.name,
             "batch": B, "heads": H, "seq_len": S, "head_dim": D,
             "logical_block": f"{lq}x{lkv}", "tile": f"{bq}x{bkv}",
-            "paired_onto": f"{run_bq}x{bkv}" if args.paired else None,
-            "timed_scope": "vsa_attn_fwd_paired" if args.paired else (
+            "paired_onto": f"{run_bq}x{bkv}" if (args.paired or args.coalesce) else None,
+            "timed_scope": "vsa_attn_fwd_paired" if args.paired else "vsa_attn_fwd_coalesced" if args.coalesce else (
                 "vsa_attn_fwd" if args.scope == "entry" else "vsa_attn_fwd_worklist"),
             "selected_pairs": pairs,
             "density": round(pairs / (B * H * S * S), 5),
@@ -427,7 +444,8 @@ def write_traffic(args):
     import workloads as W
     wl = W.WORKLOADS[args.workload]
     bq, bkv = (int(x) for x in args.tile.lower().split("x")) if args.tile else wl.physical[0]
-    run_bq = 128 if args.paired else bq
+    # (the schedule an exact-expanded mask runs on)
+    run_bq = 128 if args.paired else (256 if args.coalesce else bq)
     kname = kernel_name(run_bq, bkv, wl.head_dim, partial=args.ragged is not None,
                         n_items=wl.batch * wl.heads * (wl.seqlen // run_bq), entry=args.scope == "entry")
     fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_from_counters

@@ -39,6 +39,7 @@ SYMBOLS = (
     "vsa_pair_q_tiles",
     "vsa_attn_fwd",
     "vsa_attn_fwd_paired",
+    "vsa_attn_fwd_coalesced",
     "vsa_attn_fwd_worklist",
     "vsa_attn_bwd",
     "vsa_release",
@@ -90,6 +91,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vsa_pair_q_tiles.restype = i32
     lib.vsa_attn_fwd_paired.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, f32, p, p, p]
     lib.vsa_attn_fwd_paired.restype = i32
+    lib.vsa_attn_fwd_coalesced.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p, p, p]
+    lib.vsa_attn_fwd_coalesced.restype = i32
     lib.vsa_attn_bwd.argtypes = [p, p, p, p, p, p, p, p, i32, p, p, i32, p, i32, i32, i32, i32, i32, i32, f32, p, p,
                                  p, p]
     lib.vsa_attn_bwd.restype = i32
@@ -198,6 +201,23 @@ def vsa_attn_fwd_paired(q, k, v, kv_block_idx, kv_block_cnt, block_kv, scale=Non
         q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(),
         _valid_ptr(kv_valid, S, block_kv, q.device), B, S, H, D,
         kv_block_idx.shape[3], block_kv, float(scale), o.data_ptr(), lse.data_ptr(), _stream_ptr(stream, q.device))
+    _check(rc)
+    return o, lse
+
+
+def vsa_attn_fwd_coalesced(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale=None, o=None, lse=None,
+                           stream=None, kv_valid=None):
+    """Forward over a 64- or 128-row query tile CSR that runs adjacent tiles
+    with identical lists as one tile, level by level up to 256 rows (decided
+    on the device); returns (o, lse), those of vsa_attn_fwd up to rounding order."""
+    B, S, H, D, o, lse = _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = load_library().vsa_attn_fwd_coalesced(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(),
+        _valid_ptr(kv_valid, S, block_kv, q.device), B, S, H, D,
+        kv_block_idx.shape[3], block_q, block_kv, float(scale), o.data_ptr(), lse.data_ptr(),
+        _stream_ptr(stream, q.device))
     _check(rc)
     return o, lse
 

@@ -105,6 +105,7 @@ std::mutex g_buf_mutex;
 std::vector<DeviceBuffer> g_bufs;      // forward work list
 std::vector<DeviceBuffer> g_bwd_bufs;  // backward scratch (D, LSE*log2 e, two work lists)
 std::vector<DeviceBuffer> g_pair_bufs; // paired forward: counter, paired CSR, two work lists
+std::vector<DeviceBuffer> g_coal_bufs; // coalesced forward: counters, gates, paired CSRs, three work lists
 
 int32_t device_buffer(std::vector<DeviceBuffer>& bufs, size_t bytes, void** out) {
     int dev = 0;
@@ -165,7 +166,7 @@ int32_t worklist_buffer(size_t bytes, int32_t** out) {
 
 extern "C" {
 
-int32_t vsa_abi_version(void) { return 5; }
+int32_t vsa_abi_version(void) { return 6; }
 
 int32_t vsa_set_max_splits(int32_t max_splits) {
     const int32_t m = max_splits >= 4 ? 4 : (max_splits >= 2 ? 2 : 1);
@@ -362,6 +363,96 @@ int32_t vsa_attn_fwd_paired(const void* q, const void* k, const void* v, const i
     return VSA_OK;
 }
 
+int32_t vsa_attn_fwd_coalesced(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
+                               const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch, int32_t seqlen,
+                               int32_t heads, int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv,
+                               float scale, void* o, float* lse, void* stream) {
+    g_last_error[0] = 0;
+    VSA_REQUIRE(block_q == 64 || block_q == 128, VSA_ERR_UNSUPPORTED,
+                "vsa_attn_fwd_coalesced takes block_q 64 or 128 (got %d)", block_q);
+    int32_t rc = check_fwd(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld,
+                           block_q, block_kv, scale, o, lse);
+    if (rc != VSA_OK) return rc;
+    VSA_REQUIRE(idx_ld <= vsa::kWorklistMaxCnt, VSA_ERR_UNSUPPORTED, "idx_ld %d exceeds the work-list sort limit %d",
+                idx_ld, vsa::kWorklistMaxCnt);
+    if (seqlen % 256 != 0) {  // no 256-row tiles
+        if (block_q == 64)
+            return vsa_attn_fwd_paired(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim,
+                                       idx_ld, block_kv, scale, o, lse, stream);
+        return vsa_attn_fwd(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld,
+                            block_q, block_kv, scale, o, lse, stream);
+    }
+    const int nq = seqlen / block_q;
+    const int64_t n_items = (int64_t)batch * heads * nq;
+    const int64_t n128 = block_q == 64 ? n_items / 2 : n_items;  // 128-row tiles
+    const int64_t n256 = n128 / 2;                                // 256-row tiles
+    // [a, b, gate256, gate128, pad to 256 B][cnt128][idx128][cnt256][idx256][work256][work128][work64]
+    // (cnt128 / idx128 only when pairing from 64 rows)
+    const size_t words = 64 + (block_q == 64 ? (size_t)n128 * (1 + idx_ld) : 0) + (size_t)n256 * (1 + idx_ld) +
+                         (size_t)n256 + (size_t)n128 + (block_q == 64 ? (size_t)n_items : 0);
+    void* buf = nullptr;
+    rc = device_buffer(g_coal_bufs, words * sizeof(int32_t), &buf);
+    if (rc != VSA_OK) return rc;
+    int32_t* ctr_a = (int32_t*)buf;
+    int32_t* ctr_b = ctr_a + 1;
+    int32_t* gate256 = ctr_a + 2;
+    int32_t* gate128 = ctr_a + 3;
+    int32_t* w = ctr_a + 64;
+    const int32_t *idx128 = kv_block_idx, *cnt128 = kv_block_cnt;  // the 128-row CSR
+    if (block_q == 64) {
+        cnt128 = w;
+        idx128 = w + n128;
+        w += (size_t)n128 * (1 + idx_ld);
+    }
+    int32_t* cnt256 = w;
+    int32_t* idx256 = w + n256;
+    w += (size_t)n256 * (1 + idx_ld);
+    int32_t* work256 = w;
+    int32_t* work128 = work256 + n256;
+    int32_t* work64 = work128 + n128;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    if (block_q == 64) {
+        // level 1 (64 -> 128 rows) counts into a, level 2 (128 -> 256) into b
+        e = vsa::launch_pair_q_tiles(kv_block_idx, kv_block_cnt, (int)n128, idx_ld, (int32_t*)idx128,
+                                     (int32_t*)cnt128, ctr_a, st);
+        if (e != hipSuccess) return hip_fail(e, "pair_q_tiles launch");
+        e = vsa::launch_pair_q_tiles(idx128, cnt128, (int)n256, idx_ld, idx256, cnt256, ctr_b, st);
+        if (e != hipSuccess) return hip_fail(e, "pair_q_tiles launch");
+        e = vsa::launch_pair_gates(ctr_a, ctr_b, gate256, gate128, st);
+        if (e != hipSuccess) return hip_fail(e, "pair gates launch");
+    } else {
+        e = vsa::launch_pair_q_tiles(kv_block_idx, kv_block_cnt, (int)n256, idx_ld, idx256, cnt256, ctr_a, st);
+        if (e != hipSuccess) return hip_fail(e, "pair_q_tiles launch");
+    }
+    // exactly one schedule gets a non-empty work list
+    e = vsa::launch_build_worklist(cnt256, (int)n256, seqlen / 256, idx_ld, work256, st,
+                                   block_q == 64 ? gate256 : ctr_a, true);
+    if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
+    e = vsa::launch_build_worklist(cnt128, (int)n128, seqlen / 128, idx_ld, work128, st,
+                                   block_q == 64 ? gate128 : ctr_a, block_q == 64);
+    if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
+    if (block_q == 64) {
+        e = vsa::launch_build_worklist(kv_block_cnt, (int)n_items, nq, idx_ld, work64, st, ctr_a, false);
+        if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
+    }
+    vsa::FwdParams p256 = make_params(q, k, v, idx256, cnt256, kv_valid, batch, seqlen, heads, head_dim, idx_ld, 256,
+                                      block_kv, scale, work256, (int32_t)n256, o, lse);
+    e = vsa::launch_fwd(256, block_kv, head_dim, p256, st);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch (256-row tiles)");
+    vsa::FwdParams p128 = make_params(q, k, v, idx128, cnt128, kv_valid, batch, seqlen, heads, head_dim, idx_ld, 128,
+                                      block_kv, scale, work128, (int32_t)n128, o, lse);
+    e = vsa::launch_fwd(128, block_kv, head_dim, p128, st);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch (128-row tiles)");
+    if (block_q == 64) {
+        vsa::FwdParams p64 = make_params(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads,
+                                         head_dim, idx_ld, 64, block_kv, scale, work64, (int32_t)n_items, o, lse);
+        e = vsa::launch_fwd(64, block_kv, head_dim, p64, st);
+        if (e != hipSuccess) return hip_fail(e, "attention kernel launch (64-row tiles)");
+    }
+    return VSA_OK;
+}
+
 int32_t vsa_csr_transpose(const int32_t* kv_block_idx, const int32_t* kv_block_cnt, int32_t batch, int32_t heads,
                           int32_t nq, int32_t nkv, int32_t idx_ld, int32_t* q_block_idx, int32_t q_ld,
                           int32_t* q_block_cnt, int32_t* overflow, void* stream) {
@@ -493,7 +584,7 @@ int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 void vsa_release(void) {
     std::lock_guard<std::mutex> lock(g_buf_mutex);
-    for (auto* v : {&g_bufs, &g_bwd_bufs, &g_pair_bufs, &g_split_bufs, &g_bwd_split_bufs}) {
+    for (auto* v : {&g_bufs, &g_bwd_bufs, &g_pair_bufs, &g_coal_bufs, &g_split_bufs, &g_bwd_split_bufs}) {
         for (auto& b : *v) {
             if (b.ptr) (void)hipFree(b.ptr);
             b.ptr = nullptr;

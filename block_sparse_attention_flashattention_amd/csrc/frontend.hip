@@ -244,6 +244,15 @@ __global__ __launch_bounds__(256) void pair_q_tiles_kernel(const int32_t* __rest
 
 __global__ void zero_kernel(int32_t* p) { *p = 0; }
 
+// Gates of a two-level pairing from the mismatch counts of level 1 (a) and
+// level 2 (b): the 256-row list runs iff a + b == 0, the 128-row list iff
+// a == 0 and b != 0 (both as "run if the gate is zero").
+__global__ void pair_gates_kernel(const int32_t* a, const int32_t* b, int32_t* gate256, int32_t* gate128) {
+    const int32_t x = *a, y = *b;
+    *gate256 = (x == 0 && y == 0) ? 0 : 1;
+    *gate128 = (x == 0 && y != 0) ? 0 : 1;
+}
+
 // Valid keys per physical KV tile from valid tokens per logical KV block:
 // tile r of block T keeps clamp(vbs[T] - r*block_kv, 0, block_kv).
 __global__ void expand_valid_kernel(const int32_t* vbs, int n_out, int kv_ratio, int block_kv, int32_t* out) {
@@ -287,6 +296,12 @@ hipError_t launch_pair_q_tiles(const int32_t* idx, const int32_t* cnt, int n_pai
     if (e != hipSuccess || n_pairs <= 0) return e;
     hipLaunchKernelGGL(pair_q_tiles_kernel, dim3((n_pairs + 3) / 4), dim3(256), 0, stream, idx, cnt, n_pairs, ld,
                        out_idx, out_cnt, unpaired);
+    return hipGetLastError();
+}
+
+hipError_t launch_pair_gates(const int32_t* a, const int32_t* b, int32_t* gate256, int32_t* gate128,
+                             hipStream_t stream) {
+    hipLaunchKernelGGL(pair_gates_kernel, dim3(1), dim3(1), 0, stream, a, b, gate256, gate128);
     return hipGetLastError();
 }
 

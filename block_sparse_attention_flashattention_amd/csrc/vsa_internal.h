@@ -121,6 +121,8 @@ hipError_t launch_build_worklist(const int32_t* cnt, int n_items, int segment, i
                                  hipStream_t stream, const int32_t* gate = nullptr, bool run_if_zero = true);
 // Query tiles (2p, 2p+1) -> tile p of twice the height; *unpaired = number of
 // pairs whose lists differ (zeroed by the launch itself, in stream order).
+hipError_t launch_pair_gates(const int32_t* a, const int32_t* b, int32_t* gate256, int32_t* gate128,
+                             hipStream_t stream);
 hipError_t launch_pair_q_tiles(const int32_t* idx, const int32_t* cnt, int n_pairs, int ld, int32_t* out_idx,
                                int32_t* out_cnt, int32_t* unpaired, hipStream_t stream);
 // Q-direction CSR for the backward pass; nq must be <= 32 * kTransposeMaxWords.

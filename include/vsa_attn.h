@@ -251,6 +251,38 @@ int32_t vsa_attn_fwd_paired(const void* q, const void* k, const void* v, const i
                             float* lse, void* stream);
 
 /*
+ * vsa_attn_fwd_coalesced -- vsa_attn_fwd for a 64- or 128-row query tile CSR
+ * that runs adjacent tiles with identical lists as one tile up to 256 rows
+ * tall.
+ *
+ * Source: as vsa_pair_q_tiles (FastVideo page, fine-grained VSA kernels:
+ * the query-tile children of one Q256 logical row share their KV list and
+ * are paired onto taller physical tiles), applied level by level up to the
+ * Q256 row itself.
+ *
+ * Same arguments as vsa_attn_fwd, with block_q 64 or 128 (else
+ * VSA_ERR_UNSUPPORTED). Pairing levels: 64 -> 128 -> 256 rows for
+ * block_q = 64, 128 -> 256 for block_q = 128; a level applies only if every
+ * pair of that level has equal counts and equal stored entries in order
+ * (vsa_pair_q_tiles), so the selected token pairs never change. The levels
+ * and the choice of schedule are made on the device: exactly one of the
+ * 256-row, 128-row and (for block_q = 64) 64-row kernels gets a non-empty
+ * work list. O and LSE are those of the input CSR; the per-row arithmetic
+ * follows the kernel that runs (the 256-row and the many-entry 128-row
+ * kernels run the same steps per row). If seqlen is not a multiple of 256
+ * this is vsa_attn_fwd_paired (block_q 64) or vsa_attn_fwd (block_q 128).
+ * Partial tiles (kv_valid) are supported as in vsa_attn_fwd. Uses a
+ * library-owned device buffer of about 4*(batch*heads*seqlen/block_q)*
+ * (idx_ld + 3) bytes (grown on demand per device, released by
+ * vsa_release); calls on one device must not overlap in time on different
+ * streams. idx_ld must not exceed the work-list sort limit (8191).
+ */
+int32_t vsa_attn_fwd_coalesced(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
+                               const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch, int32_t seqlen,
+                               int32_t heads, int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv,
+                               float scale, void* o, float* lse, void* stream);
+
+/*
  * vsa_attn_bwd -- backward pass: dQ, dK and dV of vsa_attn_fwd.
  *
  * Source: the gradient of the FastVideo page's ref_masked_sdpa_fp32 (the function the

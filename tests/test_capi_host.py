@@ -36,7 +36,7 @@ def test_header_declares_the_binding_symbols():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.vsa_abi_version() == 5
+    assert lib.vsa_abi_version() == 6
 
 
 def test_set_max_splits_rounds_and_returns_previous(lib):
@@ -207,3 +207,16 @@ def test_attn_fwd_paired_validation(lib):
     assert f(A, A, A, A, A, None, 1, 1024, 2, 96, 16, 64, 0.1, A, A, None) == -2
     assert f(A, A, A, A, A, None, 1, 1024, 2, 128, 16, 256, 0.1, A, A, None) == -2
     assert f(A, A, A, A, A, None, 1, 1024, 2, 128, 9000, 64, 0.1, A, A, None) in (-1, -2)
+
+
+def test_attn_fwd_coalesced_validation(lib):
+    f = lib.vsa_attn_fwd_coalesced
+    # q, k, v, idx, cnt, kv_valid, B, S, H, D, ld, block_q, block_kv, scale, o, lse, stream
+    assert f(A, A, A, A, A, None, 1, 1024, 2, 128, 16, 256, 64, 0.1, A, A, None) == -2  # 256-row input: unsupported
+    assert "block_q 64 or 128" in lib.vsa_last_error().decode()
+    assert f(A, A, A, A, A, None, 1, 1024, 2, 128, 16, 32, 64, 0.1, A, A, None) == -2
+    assert f(A, A, A, A, A, None, 1, 1024, 2, 128, 16, 64, 64, 0.1, None, A, None) == -1  # null o
+    assert f(A, A, A, A, A, None, 1, 1000, 2, 128, 16, 64, 64, 0.1, A, A, None) == -1  # not a multiple of 64
+    assert f(A, A, A, A, A, None, 1, 1024, 2, 96, 16, 128, 64, 0.1, A, A, None) == -2  # head_dim
+    assert f(A, A, A, A, A, None, 1, 1024, 2, 128, 9000, 128, 64, 0.1, A, A, None) in (-1, -2)  # ld too large
+    assert f(A, A, A, A, A, None, 1, 1024, 2, 128, 16, 128, 64, 0.0, A, A, None) == -1  # scale

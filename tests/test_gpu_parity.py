@@ -572,3 +572,76 @@ def test_vsa256_paired_64x64_sampled(vsa):
     assert torch.equal(o, o2) and torch.equal(lse, l2)
     del o, lse, o2, l2
     torch.cuda.empty_cache()
+
+
+COALESCED = [(bq, bkv, D, partial) for bq in (64, 128) for bkv in (64, 128) for D, partial in ((128, False), (64, True))]
+
+
+@pytest.mark.parametrize("bq,bkv,D,partial", COALESCED,
+                         ids=[f"q{a}_kv{b}_d{c}{'_partial' if p else ''}" for a, b, c, p in COALESCED])
+def test_coalesced_forward_all_rows(vsa, bq, bkv, D, partial):
+    """Lists expanded from 256-row logical blocks run as 256-row tiles, from
+    128-row blocks as 128-row tiles, distinct lists natively: every row
+    against the oracle, and bitwise equal to the schedule that must run (the
+    unsplit kernel over the twice or once paired CSR, or over the input)."""
+    B, H, S = 2, 2, 2048
+    q, k, v = W.qkv(B, S, H, D, seed=bq + bkv + D + 91)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    scale = 1.0 / math.sqrt(D)
+    val = None
+    if partial:
+        val = W.ragged_block_sizes(S // bkv, bkv, seed=bq + bkv + D, p_full=0.4)
+        val[:2] = [0, 1]
+    vald = None if val is None else dev(val)
+
+    def expanded(lq, seed):
+        mask = np.stack([W.anchor_topk_mask(H, S // lq, S // 256, 3, seed=seed + b) for b in range(B)])
+        idx, cnt, _ = ofront.mask_to_csr(mask, (lq, 256), (bq, bkv), 3 * (256 // bkv))
+        return idx, cnt
+
+    cases = [("q256", expanded(256, D + bkv), 256), ("q128", expanded(128, D + bkv + 3), 128),
+             ("distinct", W.random_csr(B, H, S // bq, S // bkv, S // bkv, 0, S // bkv // 2, seed=D + bkv + bq), bq)]
+    for label, (idx, cnt), rows in cases:
+        idx = np.ascontiguousarray(idx[..., :max(1, int(cnt.max()))])
+        # the schedule the device must choose, from the oracle's pairing
+        ridx, rcnt, rbq = idx, cnt, bq
+        while rbq < 256:
+            pidx, pcnt, unp = ofront.pair_q_tiles(ridx, rcnt)
+            if unp != 0:
+                break
+            ridx, rcnt, rbq = pidx, pcnt, rbq * 2
+        assert rbq == (rows if rows >= bq else bq), f"{label}: unexpected pairing depth {rbq}"
+        say(f"coalesced forward q{bq} {label} kv{bkv} D={D} partial={partial}: runs {rbq}-row tiles")
+        o, lse = vsa.vsa_attn_fwd_coalesced(qd, kd, vd, dev(idx), dev(cnt), bq, bkv, scale, kv_valid=vald)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.attn_full(q, k, v, idx, cnt, bq, bkv, scale, kv_valid=val)
+        check_rows(o, lse, np.arange(B * H * S), o_ref.transpose(0, 2, 1, 3).reshape(-1, D), lse_ref.reshape(-1),
+                   S, H, f"coalesced q{bq} {label} kv{bkv} D={D}")
+        work = torch.arange(rcnt.size, dtype=torch.int32, device="cuda")
+        o2, l2 = vsa.vsa_attn_fwd_worklist(qd, kd, vd, dev(np.ascontiguousarray(ridx)), dev(rcnt), rbq, bkv, work,
+                                           scale, kv_valid=vald)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(lse, l2), f"{label}: not the {rbq}-row schedule's result"
+
+
+@pytest.mark.parametrize("tile", [(128, 64), (64, 64)], ids=["128x64", "64x64"])
+def test_vsa256_coalesced_sampled(vsa, tile):
+    """The VSA-256 mask at 128x64 or 64x64 runs as 256x64 tiles: sampled rows
+    against the oracle, bitwise equal to the 256x64 kernel's result."""
+    wl = W.VSA256_FINE
+    say(f"coalesced forward vsa256 {tile[0]}x{tile[1]}: generating inputs")
+    q, k, v = wl.qkv()
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    mask = dev(wl.logical_mask())
+    idx, cnt = vsa.vsa_mask_to_csr(mask, wl.logical_block, tile, 52)
+    o, lse = vsa.vsa_attn_fwd_coalesced(qd, kd, vd, idx, cnt, tile[0], tile[1], wl.scale)
+    torch.cuda.synchronize()
+    B, S, H, D = q.shape
+    rows = sample_rows(B, H, S, tile[0], 2, seed=tile[0] + 1)
+    o_ref, lse_ref = oracle.attn_rows(q, k, v, idx.cpu().numpy(), cnt.cpu().numpy(), tile[0], tile[1], wl.scale, rows)
+    check_rows(o, lse, rows, o_ref, lse_ref, S, H, f"vsa256 coalesced {tile[0]}x{tile[1]}")
+    idx2, cnt2 = vsa.vsa_mask_to_csr(mask, wl.logical_block, (256, 64), 52)
+    o2, l2 = _run_fwd(vsa, qd, kd, vd, idx2, cnt2, 256, 64, wl.scale)
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+    del o, lse, o2, l2
+    torch.cuda.empty_cache()

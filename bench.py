@@ -82,7 +82,7 @@ def parse_args():
 def main():
     args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (sharding is a design note).",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (how it would shard is a design note).",
               file=sys.stderr)
         return 2
 

@@ -645,3 +645,26 @@ def test_vsa256_coalesced_sampled(vsa, tile):
     assert torch.equal(o, o2) and torch.equal(lse, l2)
     del o, lse, o2, l2
     torch.cuda.empty_cache()
+
+
+def test_coalesced_forward_without_256_row_tiles(vsa):
+    """seqlen a multiple of 128 but not of 256: 64-row input falls back to the
+    64 -> 128 pairing, 128-row input to vsa_attn_fwd; every row against the
+    oracle and bitwise equal to those entry points."""
+    B, H, S, D, bkv = 1, 2, 1152, 64, 64
+    say("coalesced forward, seqlen 1152")
+    q, k, v = W.qkv(B, S, H, D, seed=17)
+    qd, kd, vd = dev(q), dev(k), dev(v)
+    for bq in (64, 128):
+        idx, cnt = W.random_csr(B, H, S // bq, S // bkv, 6, 0, 6, seed=18 + bq)
+        o, lse = vsa.vsa_attn_fwd_coalesced(qd, kd, vd, dev(idx), dev(cnt), bq, bkv, 0.125)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle.attn_full(q, k, v, idx, cnt, bq, bkv, 0.125)
+        check_rows(o, lse, np.arange(B * H * S), o_ref.transpose(0, 2, 1, 3).reshape(-1, D), lse_ref.reshape(-1),
+                   S, H, f"coalesced q{bq} seqlen {S}")
+        if bq == 64:
+            o2, l2 = vsa.vsa_attn_fwd_paired(qd, kd, vd, dev(idx), dev(cnt), bkv, 0.125)
+        else:
+            o2, l2 = vsa.vsa_attn_fwd(qd, kd, vd, dev(idx), dev(cnt), bq, bkv, 0.125)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(lse, l2)

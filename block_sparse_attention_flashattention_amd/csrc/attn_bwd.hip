@@ -121,6 +121,36 @@ __device__ __forceinline__ bf16x8 tr_operand(const char* smem, int base, const O
     return __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// OperandOffsets in one register per kind, for kernels short of registers.
+// The row-read offsets of chunk pairs c and the transposing-read offsets of
+// d blocks db differ from the first ones only in chunk bits (c << 5 and
+// db << 6: the chunk index is 2c ^ hi, and the swizzles and row terms leave
+// those bits alone), so each is formed by an XOR onto the tile base, which
+// must be a multiple of 256 bytes.
+template <int D>
+struct CompactOffsets {
+    static constexpr int ROW_BYTES = D * 2;
+    int row0, trl0, trh0;
+    template <int LAYOUT>
+    __device__ __forceinline__ void init(int lane) {
+        OperandOffsets<D> full;
+        full.template init<LAYOUT>(lane);
+        row0 = full.row[0];
+        trl0 = full.trl[0];
+        trh0 = full.trh[0];
+    }
+    // byte offset of the row read of chunk pair c in the tile at `base`
+    __device__ __forceinline__ int row(int base, int c) const { return (base + row0) ^ (c << 5); }
+};
+
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const char* smem, int base, const CompactOffsets<D>& off, int db, int g) {
+    const char* p = smem + g * 16 * CompactOffsets<D>::ROW_BYTES;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + ((base + off.trl0) ^ (db << 6))));
+    const bf16x4 up = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + ((base + off.trh0) ^ (db << 6))));
+    return __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // B operand registers of 32 token rows: lane l holds row l%32, d = 16c + 8*hi + (0..7).
 template <int DC>
 __device__ __forceinline__ void load_rows(bf16x8 (&reg)[DC], const uint16_t* row_ptr, int hi) {
@@ -429,7 +459,9 @@ __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) 
     wait_global_loads();
     lds_barrier();
 
-    OO qo;
+    // compact offsets: the full set left this kernel a few registers short,
+    // and the spill reload inside the step waited on the next step's tile loads
+    CompactOffsets<D> qo;
     qo.template init<kLayoutD>(lane);
     const F fetch(smem, wave, lane, tok_bytes);
     const char* qbase = (const char*)(prm.q + (int64_t)b * S * tok_stride + (int64_t)h * D);
@@ -478,9 +510,9 @@ __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) 
         for (int c = 0; c < DC; ++c)
 #pragma unroll
             for (int qs = 0; qs < QS / 32; ++qs) {
-                const bf16x8 qa = *(const bf16x8*)(smem + qb + qo.row[c] + qs * 32 * OO::ROW_BYTES);
+                const bf16x8 qa = *(const bf16x8*)(smem + qo.row(qb, c) + qs * 32 * OO::ROW_BYTES);
                 s[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kreg[c], s[qs], 0, 0, 0);
-                const bf16x8 oa = *(const bf16x8*)(smem + ob + qo.row[c] + qs * 32 * OO::ROW_BYTES);
+                const bf16x8 oa = *(const bf16x8*)(smem + qo.row(ob, c) + qs * 32 * OO::ROW_BYTES);
                 dp[qs] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(oa, vreg[c], dp[qs], 0, 0, 0);
             }
         __builtin_amdgcn_s_setprio(0);

@@ -270,3 +270,47 @@ def test_maximum_list_stride_and_empty_head(vsa, bq, bkv):
     for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
         check(name, got.float().cpu().numpy(), ref, f"max stride {bq}x{bkv}")
         assert np.all(got.float().cpu().numpy()[0, :, 1] == 0.0)
+
+
+def test_backward_tensors_past_2gib_sampled(vsa):
+    """B=12, S=32k, H=24, D=128 (Q, K, V, dO and the gradients 2.4 GB each):
+    sampled dQ and dK/dV rows of the last batch, past 2^31 bytes, against
+    the oracle (inputs drawn on the device with a seeded generator)."""
+    B, S, H, D, bq, bkv = 12, 32768, 24, 128, 256, 128
+    say("backward past 2 GiB: inputs")
+    g = torch.Generator(device="cuda").manual_seed(4048)
+
+    def draw():
+        x = torch.empty((B, S, H, D), dtype=torch.bfloat16, device="cuda")
+        for b in range(B):
+            x[b] = torch.randn((S, H, D), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        return x
+
+    q, k, v, do = draw(), draw(), draw(), draw()
+    nq, nkv = S // bq, S // bkv
+    idx, cnt = W.random_csr(B, H, nq, nkv, 12, 1, 12, seed=4049)
+    scale = 1.0 / math.sqrt(D)
+    idxd, cntd = dev(idx), dev(cnt)
+    say("backward past 2 GiB: kernels")
+    o, lse = vsa.vsa_attn_fwd(q, k, v, idxd, cntd, bq, bkv, scale)
+    q_idx, q_cnt = vsa.vsa_csr_transpose(idxd, cntd, nkv, nq)
+    dq, dk, dv = vsa.vsa_attn_bwd(q, k, v, o, lse, do, idxd, cntd, q_idx, q_cnt, bq, bkv, scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    b = B - 1
+    qrows = np.array([(b * H + h) * S + r for h in (0, 23) for r in rng.integers(0, S, size=16)], dtype=np.int64)
+    krows = np.array([(b * H + h) * S + r for h in (0, 23) for r in rng.integers(0, S, size=3)], dtype=np.int64)
+    qc, kc, vc, doc = q.cpu(), k.cpu(), v.cpu(), do.cpu()
+    say("backward past 2 GiB: oracle rows")
+    rq = oracle.bwd_dq_rows(qc, kc, vc, doc, idx, cnt, bq, bkv, scale, qrows)
+    rk, rv = oracle.bwd_dkv_rows(qc, kc, vc, doc, idx, cnt, bq, bkv, scale, krows)
+
+    def pick(t, rows):
+        bh, i = rows // S, rows % S
+        return t[torch.as_tensor(bh // H), torch.as_tensor(i), torch.as_tensor(bh % H)].float().cpu().numpy()
+
+    check("dQ", pick(dq, qrows), rq, "past 2 GiB")
+    check("dK", pick(dk, krows), rk, "past 2 GiB")
+    check("dV", pick(dv, krows), rv, "past 2 GiB")
+    del q, k, v, do, o, lse, dq, dk, dv, qc, kc, vc, doc
+    torch.cuda.empty_cache()

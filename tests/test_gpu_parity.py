@@ -674,3 +674,33 @@ def test_coalesced_forward_without_256_row_tiles(vsa):
             o2, l2 = vsa.vsa_attn_fwd(qd, kd, vd, dev(idx), dev(cnt), bq, bkv, 0.125)
         torch.cuda.synchronize()
         assert torch.equal(o, o2) and torch.equal(lse, l2)
+
+
+def test_tensors_past_2gib_sampled(vsa):
+    """B=12, S=32k, H=24, D=128: Q, K, V and O are 2.4 GB each, so the rows of
+    the last batches sit past 2^31 bytes. Sampled rows of the first and last
+    batch against the oracle (inputs drawn on the device with a seeded
+    generator and copied back for the oracle)."""
+    B, S, H, D, bq, bkv = 12, 32768, 24, 128, 256, 128
+    say("forward past 2 GiB: generating inputs")
+    g = torch.Generator(device="cuda").manual_seed(2024)
+
+    def draw():
+        x = torch.empty((B, S, H, D), dtype=torch.bfloat16, device="cuda")
+        for b in range(B):  # one batch at a time keeps the fp32 temporary small
+            x[b] = torch.randn((S, H, D), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        return x
+
+    q, k, v = draw(), draw(), draw()
+    assert q.numel() * 2 > 2 ** 31
+    nq, nkv = S // bq, S // bkv
+    idx, cnt = W.random_csr(B, H, nq, nkv, 12, 1, 12, seed=2025)
+    scale = 1.0 / math.sqrt(D)
+    say("forward past 2 GiB: kernel")
+    o, lse = _run_fwd(vsa, q, k, v, dev(idx), dev(cnt), bq, bkv, scale)
+    rows = [r for r in sample_rows(B, H, S, bq, 1, seed=7) if r // (S * H) in (0, B - 1)]
+    qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+    o_ref, lse_ref = oracle.attn_rows(qc, kc, vc, idx, cnt, bq, bkv, scale, rows)
+    check_rows(o, lse, rows, o_ref, lse_ref, S, H, "past 2 GiB")
+    del q, k, v, o, lse, qc, kc, vc
+    torch.cuda.empty_cache()

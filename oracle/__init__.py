@@ -231,17 +231,3 @@ def probs_row(q, k, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, flat_r
                                       int(flat_row), _ptr(p))
     _check(rc)
     return p
-
-
-def selected_pairs(kv_block_cnt, block_q, block_kv, kv_block_idx=None, kv_valid=None) -> int:
-    """Number of selected (query token, key token) pairs of a block CSR; with
-    kv_valid, only the valid keys of each selected tile count."""
-    if kv_valid is None:
-        return int(np.asarray(kv_block_cnt, dtype=np.int64).sum()) * block_q * block_kv
-    idx = np.asarray(kv_block_idx)
-    cnt = np.asarray(kv_block_cnt)
-    val = np.asarray(kv_valid, dtype=np.int64)
-    total = 0
-    for pos in np.ndindex(cnt.shape):
-        total += int(val[idx[pos][:cnt[pos]]].sum())
-    return total * block_q

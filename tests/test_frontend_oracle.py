@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from oracle import frontend
-from workloads import anchor_count_mask, anchor_topk_mask
+from workloads import anchor_count_mask, anchor_uniform_mask
 
 
 def _selected_by_logical(mask, lblock, S):
@@ -95,16 +95,46 @@ def test_segmented_worklist_sorts_within_segments_only():
 
 
 def test_page_mask_generator_invariants():
-    m = anchor_topk_mask(3, 16, 16, 8, seed=1566)
+    m = anchor_uniform_mask(3, 16, 16, 8, seed=1566)
     assert m.shape == (3, 16, 16)
     assert np.all(m.sum(-1) == 8)
     rows = np.arange(16)
     assert np.all(m[:, rows, rows] == 1)  # anchor floor(q*nkv/nq) = q on a square grid
-    m2 = anchor_topk_mask(3, 16, 16, 8, seed=1566)
+    m2 = anchor_uniform_mask(3, 16, 16, 8, seed=1566)
     assert np.array_equal(m, m2)
     # rectangular grid anchor
-    m3 = anchor_topk_mask(2, 8, 32, 3, seed=5)
+    m3 = anchor_uniform_mask(2, 8, 32, 3, seed=5)
     assert np.all(m3[:, np.arange(8), np.arange(8) * 4] == 1)
+    assert np.all(m3.sum(-1) == 3)
+    # keep = nkv selects every block; keep = 1 only the anchor
+    assert np.all(anchor_uniform_mask(1, 4, 4, 4, seed=0) == 1)
+    assert np.array_equal(anchor_uniform_mask(1, 4, 4, 1, seed=0)[0], np.eye(4, dtype=np.uint8))
+    with pytest.raises(ValueError):
+        anchor_uniform_mask(1, 4, 4, 5, seed=0)
+
+
+def test_mask_generator_is_uniform_off_the_anchor():
+    """Off the anchor every block is kept with probability (keep-1)/(NKV-1),
+    and pairs of blocks are kept together with the without-replacement
+    probability (keep-1)(keep-2)/((NKV-1)(NKV-2)), not the independent one."""
+    H, NQ, NKV, keep = 64, 64, 16, 5
+    m = anchor_uniform_mask(H, NQ, NKV, keep, seed=7).astype(np.float64)
+    anchor = (np.arange(NQ) * NKV) // NQ
+    off = np.ones((NQ, NKV), dtype=bool)
+    off[np.arange(NQ), anchor] = False
+    n = H * NQ
+    p1 = (keep - 1) / (NKV - 1)
+    overall = m[:, off].mean()
+    assert abs(overall - p1) < 4 * np.sqrt(p1 * (1 - p1) / (n * (NKV - 1)))
+    # per-column frequency, pooled over rows: no block favoured
+    col = np.array([m[:, off[:, j], j].mean() for j in range(NKV)])
+    sd = np.sqrt(p1 * (1 - p1) / (H * off.sum(0)))
+    assert np.all(np.abs(col - p1) < 5 * sd)
+    # joint frequency of two fixed non-anchor blocks in rows where both are off-anchor
+    both = off[:, 1] & off[:, 2]
+    joint = (m[:, both, 1] * m[:, both, 2]).mean()
+    p2 = (keep - 1) * (keep - 2) / ((NKV - 1) * (NKV - 2))
+    assert abs(joint - p2) < 5 * np.sqrt(p2 * (1 - p2) / (H * both.sum()))
 
 
 def test_count_mask_generator_invariants():
@@ -112,6 +142,8 @@ def test_count_mask_generator_invariants():
     c = m.sum(-1)
     assert c.min() >= 10 and c.max() <= 92
     assert abs(c.mean() - 51) < 1.0
+    # every count in 10..92 occurs, none outside
+    assert set(np.unique(c).tolist()) == set(range(10, 93))
     rows = np.arange(512)
     assert np.all(m[:, rows, rows] == 1)
 
@@ -164,7 +196,7 @@ def test_pairing_of_exact_expanded_q64_rows_gives_the_q128_csr(lblock, pkv):
     and it selects the same token pairs as the Q64 CSR."""
     S = 1024
     nql, nkvl = S // lblock[0], S // lblock[1]
-    mask = anchor_topk_mask(3, nql, nkvl, max(1, nkvl // 3), seed=17)[None]
+    mask = anchor_uniform_mask(3, nql, nkvl, max(1, nkvl // 3), seed=17)[None]
     ld = nkvl * (lblock[1] // pkv)
     idx64, cnt64, _ = frontend.mask_to_csr(mask, lblock, (64, pkv), ld)
     idx128, cnt128, _ = frontend.mask_to_csr(mask, lblock, (128, pkv), ld)
@@ -178,7 +210,7 @@ def test_pairing_counts_each_kind_of_differing_pair():
     """Starting from a fully paired CSR, each planted difference (one entry
     changed, two entries swapped, a count changed, a difference only past the
     stored prefix) is counted exactly when it changes the stored list."""
-    mask = anchor_topk_mask(2, 4, 16, 5, seed=3)[None]
+    mask = anchor_uniform_mask(2, 4, 16, 5, seed=3)[None]
     idx, cnt, _ = frontend.mask_to_csr(mask, (256, 64), (64, 64), 16)
     assert frontend.pair_q_tiles(idx, cnt)[2] == 0
     idx, cnt = idx.copy(), cnt.copy()

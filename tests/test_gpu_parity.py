@@ -459,7 +459,7 @@ def test_vsa256_ragged_blocks_sampled_and_cross_shape(vsa):
 # ------------------------------------------- Q64 pairing onto Q128 tiles
 
 def _exact_expanded_q64(B, H, S, lblock, bkv, keep, seed):
-    mask = np.stack([W.anchor_topk_mask(H, S // lblock[0], S // lblock[1], keep, seed=seed + b) for b in range(B)])
+    mask = np.stack([W.anchor_uniform_mask(H, S // lblock[0], S // lblock[1], keep, seed=seed + b) for b in range(B)])
     ld = keep * (lblock[1] // bkv)
     idx, cnt, _ = ofront.mask_to_csr(mask, lblock, (64, bkv), ld)
     return idx, cnt
@@ -601,7 +601,7 @@ def test_coalesced_forward_all_rows(vsa, bq, bkv, D, partial):
     vald = None if val is None else dev(val)
 
     def expanded(lq, seed):
-        mask = np.stack([W.anchor_topk_mask(H, S // lq, S // 256, 3, seed=seed + b) for b in range(B)])
+        mask = np.stack([W.anchor_uniform_mask(H, S // lq, S // 256, 3, seed=seed + b) for b in range(B)])
         idx, cnt, _ = ofront.mask_to_csr(mask, (lq, 256), (bq, bkv), 3 * (256 // bkv))
         return idx, cnt
 

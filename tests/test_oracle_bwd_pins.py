@@ -119,12 +119,12 @@ def test_key_gradients_sum_to_zero_per_head():
 
 
 def test_row_subsets_match_full_and_tile_shapes_agree_bitwise():
-    from workloads import anchor_topk_mask
+    from workloads import anchor_uniform_mask
 
     B, H, S, D = 1, 1, 512, 32
     q, k, v = qkv(B, S, H, D, seed=31)
     do = qkv(B, S, H, D, seed=32)[0]
-    base = anchor_topk_mask(H, S // 256, S // 256, 1, seed=33)[None]
+    base = anchor_uniform_mask(H, S // 256, S // 256, 1, seed=33)[None]
     vbs = np.array([256, 150], dtype=np.int32)
     res = []
     for shape in ((256, 256), (128, 64), (64, 64)):

@@ -142,11 +142,11 @@ def test_partial_tiles_zero_keys_closed_form():
 
 def test_partial_tiles_are_bitwise_identical_across_tile_shapes():
     """Ragged logical blocks expanded to finer tiles select the same key tokens."""
-    from workloads import anchor_topk_mask
+    from workloads import anchor_uniform_mask
 
     B, H, S, D = 1, 2, 1024, 64
     q, k, v = qkv(B, S, H, D, seed=33)
-    base = anchor_topk_mask(H, S // 256, S // 256, 2, seed=34)[None]
+    base = anchor_uniform_mask(H, S // 256, S // 256, 2, seed=34)[None]
     vbs = np.array([256, 200, 129, 64], dtype=np.int32)
     results = []
     for shape in ((256, 256), (256, 128), (128, 64), (64, 64)):
@@ -229,11 +229,11 @@ def test_idx_order_does_not_change_result_bitwise():
 
 
 def test_exact_expansion_is_bitwise_identical_across_tile_shapes():
-    from workloads import anchor_topk_mask
+    from workloads import anchor_uniform_mask
 
     B, H, S, D = 1, 2, 1024, 64
     q, k, v = qkv(B, S, H, D, seed=31)
-    base = anchor_topk_mask(H, S // 256, S // 256, 2, seed=32)[None]
+    base = anchor_uniform_mask(H, S // 256, S // 256, 2, seed=32)[None]
     results = []
     for shape in ((256, 256), (256, 128), (128, 64), (64, 64)):
         ld = S // shape[1]

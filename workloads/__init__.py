@@ -14,8 +14,8 @@ file ``benchmarks/bench_vsa_blackwell.py``:
   values do not depend on the GPU vendor's RNG stream.
 * A logical block mask keeps, in every Q-block row, the "diagonal anchor"
   KV block floor(q*NKV/NQ) plus ``keep-1`` further blocks chosen uniformly
-  without replacement, by taking the top-k of i.i.d. U(0,1) scores with the
-  anchor's score forced above every other (function ``make_logical_mask``).
+  without replacement (what the page's ``make_logical_mask`` selects; drawn
+  here with numpy's ``Generator.choice``, one call per row).
 * The mask seed is ``seed + seq_len + int(keep_fraction*1000)``, plus
   ``q_block*1_000_003 + kv_block*9_176`` when a shape is sampled natively
   rather than expanded from a 256x256 base (section ``main``).
@@ -31,18 +31,6 @@ import torch
 
 DEFAULT_SEED = 42
 
-# Keep fractions by sparsity label (bench_vsa_blackwell.py, table KEEP_FRAC).
-KEEP_FRAC = {
-    "dense": 1.0,
-    "50": 0.5,
-    "60": 0.4,
-    "70": 0.3,
-    "75": 0.25,
-    "80": 0.2,
-    "87.5": 0.125,
-    "90": 0.1,
-}
-
 
 def qkv(batch: int, seqlen: int, heads: int, head_dim: int, seed: int = DEFAULT_SEED):
     """Return bf16 CPU tensors q, k, v of shape [B, S, H, D], i.i.d. N(0,1)."""
@@ -54,47 +42,50 @@ def qkv(batch: int, seqlen: int, heads: int, head_dim: int, seed: int = DEFAULT_
     return tuple(out)
 
 
-def anchor_topk_mask(heads: int, nq: int, nkv: int, keep: int, seed: int) -> np.ndarray:
-    """[H, NQ, NKV] uint8 mask: diagonal anchor plus keep-1 uniform others.
+def _anchor_plus_uniform(rng: np.random.Generator, nq: int, nkv: int, counts: np.ndarray) -> np.ndarray:
+    """Rows of a logical block mask, one per entry of ``counts`` [H, NQ].
 
-    Mirrors the sampling of ``make_logical_mask`` on the FastVideo page: one
-    U(0,1) score per block on a seeded CPU generator, the anchor
-    floor(q*NKV/NQ) forced to score 2, and the top ``keep`` scores per row.
+    Row (h, r) keeps its diagonal anchor block a = floor(r*NKV/NQ) and
+    counts[h, r] - 1 further blocks drawn uniformly without replacement from
+    the NKV - 1 blocks other than a (one ``Generator.choice`` per row, rows in
+    (h, r) order).
     """
-    if not 1 <= keep <= nkv:
-        raise ValueError(f"keep must be in [1, {nkv}], got {keep}")
-    g = torch.Generator(device="cpu").manual_seed(seed)
-    scores = torch.rand(heads, nq, nkv, generator=g)
-    rows = torch.arange(nq)
-    anchor = torch.div(rows * nkv, nq, rounding_mode="floor").clamp_max(nkv - 1)
-    scores[:, rows, anchor] = 2.0
-    sel = torch.topk(scores, keep, dim=-1).indices
-    m = torch.zeros(heads, nq, nkv, dtype=torch.bool)
-    m.scatter_(-1, sel, True)
-    return m.to(torch.uint8).numpy()
+    heads = counts.shape[0]
+    m = np.zeros((heads, nq, nkv), dtype=np.uint8)
+    for h in range(heads):
+        for r in range(nq):
+            a = (r * nkv) // nq
+            picks = rng.choice(nkv - 1, size=int(counts[h, r]) - 1, replace=False)
+            picks = picks + (picks >= a)  # positions 0..NKV-2 of the non-anchor blocks
+            m[h, r, a] = 1
+            m[h, r, picks] = 1
+    return m
+
+
+def anchor_uniform_mask(heads: int, nq: int, nkv: int, keep: int, seed: int) -> np.ndarray:
+    """[H, NQ, NKV] uint8 mask: every row keeps ``keep`` blocks, its diagonal
+    anchor and keep-1 others chosen uniformly without replacement (the
+    selection the FastVideo page's ``make_logical_mask`` describes: anchor
+    always kept, the rest a uniform draw)."""
+    if keep < 1 or keep > nkv:
+        raise ValueError(f"cannot keep {keep} blocks in a row of {nkv}")
+    rng = np.random.default_rng(seed)
+    return _anchor_plus_uniform(rng, nq, nkv, np.full((heads, nq), keep, dtype=np.int64))
 
 
 def anchor_count_mask(heads: int, nq: int, nkv: int, lo: int, hi: int, seed: int) -> np.ndarray:
     """[H, NQ, NKV] uint8 mask whose per-row kept count is U{lo..hi}.
 
     The count of every (head, Q-block) row is drawn independently and
-    uniformly from the integers lo..hi inclusive; the row then keeps its
-    diagonal anchor plus count-1 further blocks chosen uniformly without
-    replacement (the anchor/top-k mechanism above with a per-row keep).
-    Ties among equal U(0,1) scores are broken by block index (stable sort).
+    uniformly from the integers lo..hi inclusive (one draw of all counts
+    first); the row then keeps its diagonal anchor plus count-1 further
+    blocks chosen uniformly without replacement, as in anchor_uniform_mask.
     """
     if not 1 <= lo <= hi <= nkv:
-        raise ValueError(f"need 1 <= lo <= hi <= {nkv}, got {lo}..{hi}")
-    g = torch.Generator(device="cpu").manual_seed(seed)
-    counts = torch.randint(lo, hi + 1, (heads, nq), generator=g)
-    scores = torch.rand(heads, nq, nkv, generator=g)
-    rows = torch.arange(nq)
-    anchor = torch.div(rows * nkv, nq, rounding_mode="floor").clamp_max(nkv - 1)
-    scores[:, rows, anchor] = 2.0
-    order = torch.sort(scores, dim=-1, descending=True, stable=True).indices
-    rank = torch.empty_like(order)
-    rank.scatter_(-1, order, torch.arange(nkv).expand_as(order).contiguous())
-    return (rank < counts[..., None]).to(torch.uint8).numpy()
+        raise ValueError(f"row counts {lo}..{hi} do not fit rows of {nkv} blocks")
+    rng = np.random.default_rng(seed)
+    counts = rng.integers(lo, hi + 1, size=(heads, nq))
+    return _anchor_plus_uniform(rng, nq, nkv, counts)
 
 
 def mask_seed(seed: int, seqlen: int, keep_fraction: float, native_shape=None) -> int:
@@ -149,7 +140,7 @@ class Workload:
         if self.mask_kind == "dense":
             m = np.ones((self.heads, nq, nkv), dtype=np.uint8)
         elif self.mask_kind == "topk":
-            m = anchor_topk_mask(self.heads, nq, nkv, self.keep, self.mask_seed(seed))
+            m = anchor_uniform_mask(self.heads, nq, nkv, self.keep, self.mask_seed(seed))
         elif self.mask_kind == "count":
             lo, hi = self.count_range
             m = anchor_count_mask(self.heads, nq, nkv, lo, hi, self.mask_seed(seed))

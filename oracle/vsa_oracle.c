@@ -476,11 +476,16 @@ int vsa_oracle_bwd_dkv_rows(const uint16_t* q, const uint16_t* k, const uint16_t
 
 
 /*
- * All three gradients for every row: one head at a time (OpenMP over heads),
- * query rows in ascending order; each row's dS row is added into the dK and
- * dV rows of the keys it sees, so every dK/dV sum runs over queries in
- * ascending order, the same order as vsa_oracle_bwd_dkv_rows (whose results
- * this reproduces bit for bit, only faster). dq, dk, dv: [B, S, H, D] fp32.
+ * All three gradients for every row, one head at a time, in two passes that
+ * are each parallel over rows:
+ *   1. every query row i (ascending keys j): P_ij, D_i, dS_ij and dQ_i;
+ *      P_ij and dS_ij are kept for the keys the row sees;
+ *   2. every key row j: dK_j = scale * sum_i dS_ij q_i and dV_j =
+ *      sum_i P_ij dO_i over the query rows i that see j, in ascending i.
+ * These are the same sums, in the same order and with the same fp32
+ * operations, as vsa_oracle_bwd_dq_rows and vsa_oracle_bwd_dkv_rows (whose
+ * results this reproduces bit for bit, only faster). dq, dk, dv:
+ * [B, S, H, D] fp32.
  */
 int vsa_oracle_bwd_full(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
                         const int32_t* kv_block_idx, const int32_t* kv_block_cnt, const int32_t* kv_valid, int B, int S,
@@ -490,72 +495,128 @@ int vsa_oracle_bwd_full(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     if (S % block_q || S % block_kv) return ORACLE_ERR_ARG;
     const int nq = S / block_q, nkv = S / block_kv;
     if (check_valid(kv_valid, nkv, block_kv) != ORACLE_OK) return ORACLE_ERR_ARG;
-    int status = ORACLE_OK;
 #ifdef _OPENMP
     if (n_threads <= 0) n_threads = omp_get_max_threads();
 #else
     (void)n_threads;
 #endif
+    const int64_t tok = (int64_t)H * D;
+    /* per query tile p: allow[p*nkv + t] keys of tile t it sees, first[p*nkv + t]
+     * the position of tile t's first key among the keys the row sees (ascending) */
+    int32_t* allow = (int32_t*)malloc(sizeof(int32_t) * (size_t)nq * nkv);
+    int64_t* first = (int64_t*)malloc(sizeof(int64_t) * (size_t)nq * nkv);
+    int64_t* row_off = (int64_t*)malloc(sizeof(int64_t) * ((size_t)S + 1));
+    if (!allow || !first || !row_off) {
+        free(allow);
+        free(first);
+        free(row_off);
+        return ORACLE_ERR_NOMEM;
+    }
+    float* pst = NULL; /* P_ij of every (row, seen key), rows back to back */
+    float* dst = NULL; /* dS_ij, same layout */
+    size_t cap = 0;
+    int status = ORACLE_OK;
+    for (int bh = 0; bh < B * H && status == ORACLE_OK; ++bh) {
+        const int b = bh / H, h = bh % H;
+        for (int p = 0; p < nq && status == ORACLE_OK; ++p) {
+            const int64_t crow = ((int64_t)b * H + h) * nq + p;
+            status = mark_tiles(kv_block_idx + crow * ld, kv_block_cnt[crow], ld, nkv, kv_valid, block_kv,
+                                allow + (size_t)p * nkv);
+            int64_t acc = 0;
+            for (int t = 0; t < nkv; ++t) {
+                first[(size_t)p * nkv + t] = acc;
+                acc += allow[(size_t)p * nkv + t];
+            }
+        }
+        if (status != ORACLE_OK) break;
+        row_off[0] = 0;
+        for (int i = 0; i < S; ++i) {
+            const int p = i / block_q;
+            row_off[i + 1] = row_off[i] + first[(size_t)p * nkv + nkv - 1] + allow[(size_t)p * nkv + nkv - 1];
+        }
+        const size_t need = (size_t)row_off[S];
+        if (need > cap) {
+            free(pst);
+            free(dst);
+            cap = need;
+            pst = (float*)malloc(sizeof(float) * (cap ? cap : 1));
+            dst = (float*)malloc(sizeof(float) * (cap ? cap : 1));
+            if (!pst || !dst) {
+                status = ORACLE_ERR_NOMEM;
+                break;
+            }
+        }
+        /* pass 1: query rows */
 #pragma omp parallel num_threads(n_threads)
-    {
-        float* s = (float*)malloc(sizeof(float) * (size_t)S);
-        float* qf = (float*)malloc(sizeof(float) * (size_t)D);
-        float* o = (float*)malloc(sizeof(float) * (size_t)D);
-        float* dof = (float*)malloc(sizeof(float) * (size_t)D);
-        int32_t* allow = (int32_t*)malloc(sizeof(int32_t) * (size_t)nkv);
-        if (!s || !qf || !o || !dof || !allow) {
+        {
+            float* s = (float*)malloc(sizeof(float) * (size_t)S);
+            float* qf = (float*)malloc(sizeof(float) * (size_t)D);
+            float* o = (float*)malloc(sizeof(float) * (size_t)D);
+            float* dof = (float*)malloc(sizeof(float) * (size_t)D);
+            if (!s || !qf || !o || !dof) {
 #pragma omp critical
-            status = ORACLE_ERR_NOMEM;
-        } else {
-#pragma omp for schedule(dynamic, 1)
-            for (int bh = 0; bh < B * H; ++bh) {
-                const int b = bh / H, h = bh % H;
-                const int64_t tok = (int64_t)H * D;
-                for (int j = 0; j < S; ++j)
-                    for (int d = 0; d < D; ++d) {
-                        dk[((int64_t)b * S + j) * tok + (int64_t)h * D + d] = 0.0f;
-                        dv[((int64_t)b * S + j) * tok + (int64_t)h * D + d] = 0.0f;
-                    }
+                status = ORACLE_ERR_NOMEM;
+            } else {
+#pragma omp for schedule(dynamic, 16)
                 for (int i = 0; i < S; ++i) {
-                    int64_t crow = ((int64_t)b * H + h) * nq + i / block_q;
+                    const int32_t* al = allow + (size_t)(i / block_q) * nkv;
                     float* dqrow = dq + ((int64_t)b * S + i) * tok + (int64_t)h * D;
-                    int rc = mark_tiles(kv_block_idx + crow * ld, kv_block_cnt[crow], ld, nkv, kv_valid, block_kv,
-                                        allow);
-                    if (rc != ORACLE_OK) {
-#pragma omp critical
-                        status = rc;
-                        break;
-                    }
                     float di;
-                    row_prob_out(q, k, v, dout, S, H, D, b, h, i, allow, nkv, block_kv, scale, qf, s, o, &di);
+                    row_prob_out(q, k, v, dout, S, H, D, b, h, i, al, nkv, block_kv, scale, qf, s, o, &di);
                     const uint16_t* drow = dout + ((int64_t)b * S + i) * tok + (int64_t)h * D;
                     for (int d = 0; d < D; ++d) dof[d] = bf16_to_f32(drow[d]);
                     for (int d = 0; d < D; ++d) dqrow[d] = 0.0f;
+                    int64_t pos = row_off[i];
                     for (int j = 0; j < S; ++j) {
-                        if (!allowed(allow, block_kv, j)) continue;
+                        if (!allowed(al, block_kv, j)) continue;
                         const uint16_t* vrow = v + ((int64_t)b * S + j) * tok + (int64_t)h * D;
                         const uint16_t* krow = k + ((int64_t)b * S + j) * tok + (int64_t)h * D;
-                        float* dkrow = dk + ((int64_t)b * S + j) * tok + (int64_t)h * D;
-                        float* dvrow = dv + ((int64_t)b * S + j) * tok + (int64_t)h * D;
                         float dp = 0.0f;
                         for (int d = 0; d < D; ++d) dp += dof[d] * bf16_to_f32(vrow[d]);
                         const float pij = s[j];
                         const float ds = pij * (dp - di);
                         for (int d = 0; d < D; ++d) dqrow[d] += ds * bf16_to_f32(krow[d]);
-                        for (int d = 0; d < D; ++d) dkrow[d] += ds * qf[d];
-                        for (int d = 0; d < D; ++d) dvrow[d] += pij * dof[d];
+                        pst[pos] = pij;
+                        dst[pos] = ds;
+                        ++pos;
                     }
                     for (int d = 0; d < D; ++d) dqrow[d] *= scale;
                 }
-                for (int j = 0; j < S; ++j)
-                    for (int d = 0; d < D; ++d) dk[((int64_t)b * S + j) * tok + (int64_t)h * D + d] *= scale;
             }
+            free(s);
+            free(qf);
+            free(o);
+            free(dof);
         }
-        free(s);
-        free(qf);
-        free(o);
-        free(dof);
-        free(allow);
+        if (status != ORACLE_OK) break;
+        /* pass 2: key rows, summing over the query rows that see them in
+         * ascending order (query tiles ascending, rows within a tile ascending) */
+#pragma omp parallel for schedule(dynamic, 16) num_threads(n_threads)
+        for (int j = 0; j < S; ++j) {
+            const int t = j / block_kv, r = j % block_kv;
+            float* dkrow = dk + ((int64_t)b * S + j) * tok + (int64_t)h * D;
+            float* dvrow = dv + ((int64_t)b * S + j) * tok + (int64_t)h * D;
+            for (int d = 0; d < D; ++d) dkrow[d] = 0.0f;
+            for (int d = 0; d < D; ++d) dvrow[d] = 0.0f;
+            for (int p = 0; p < nq; ++p) {
+                if (r >= allow[(size_t)p * nkv + t]) continue;
+                const int64_t at = first[(size_t)p * nkv + t] + r;
+                for (int i = p * block_q; i < (p + 1) * block_q; ++i) {
+                    const uint16_t* qrow = q + ((int64_t)b * S + i) * tok + (int64_t)h * D;
+                    const uint16_t* drow = dout + ((int64_t)b * S + i) * tok + (int64_t)h * D;
+                    const float pij = pst[row_off[i] + at];
+                    const float ds = dst[row_off[i] + at];
+                    for (int d = 0; d < D; ++d) dkrow[d] += ds * bf16_to_f32(qrow[d]);
+                    for (int d = 0; d < D; ++d) dvrow[d] += pij * bf16_to_f32(drow[d]);
+                }
+            }
+            for (int d = 0; d < D; ++d) dkrow[d] *= scale;
+        }
     }
+    free(pst);
+    free(dst);
+    free(allow);
+    free(first);
+    free(row_off);
     return status;
 }

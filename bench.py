@@ -41,11 +41,18 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="vsa256_b1h24s32768d128_keep13")
     ap.add_argument("--tile", default=None, help="physical QxKV tile, e.g. 128x64 (default: workload's first)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU leg (the oracle timing and the parity checks of the timed outputs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the headline workload (skip the `configs` object: dense, the VSA-256 mask "
+                         "on finer tiles natively and coalesced, and the native Q64 masks)")
+    ap.add_argument("--config-cpu-seconds", type=float, default=2.5,
+                    help="target CPU time of the oracle sample that checks each entry of `configs`")
     ap.add_argument("--traffic", default=None,
                     help="JSON file with measured HBM bytes per kernel launch (default: the one under profiles/ "
-                         "for this kernel and workload, used only if the kernel sources are unchanged)")
+                         "for this kernel and workload, written by the profiling module's `summarize` and used "
+                         "only if the kernel sources are unchanged)")
     ap.add_argument("--prewarm-seconds", type=float, default=0.5,
                     help="run steps back to back for this long before the warmup steps, so that the timed "
                          "steps see the sustained clock rather than the ramp out of idle")
@@ -70,10 +77,6 @@ def parse_args():
                          "work list and splits lists when there are few work items (all of it is timed)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward leg (dQ, dK, dV of the same workload; reported beside the headline)")
-    ap.add_argument("--traffic-from-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
-                                                                  "COPY_WRITE_DIR"), default=None,
-                    help="write the traffic JSON from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE output directories "
-                         "of this workload and of --copy-calibration, then exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter calibration)")
     return ap.parse_args()
@@ -85,9 +88,6 @@ def main():
         print("bench.py measures one GPU only: the library has no multi-GPU path (how it would shard is a design note).",
               file=sys.stderr)
         return 2
-
-    if args.traffic_from_counters:
-        return write_traffic(args)
 
     import torch
 
@@ -200,6 +200,8 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+    # the outputs of the last timed step, checked against the oracle below
+    o_timed, lse_timed = o.clone(), lse.clone()
     kernel_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in events]))
     value = flops / (ms_step * 1e-3) / 1e12
     kernel_tflops = flops / (kernel_ms * 1e-3) / 1e12
@@ -302,12 +304,132 @@ def main():
         },
     }
 
+    ok = True
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, q_cpu, k_cpu, v_cpu, idx, cnt, bq, bkv, ld, args.cpu_seconds,
-                                              None if kv_valid is None else kv_valid.cpu().numpy())
+        base, sample = cpu_baseline(wl, q_cpu, k_cpu, v_cpu, idx, cnt, bq, bkv, args.cpu_seconds,
+                                    None if kv_valid is None else kv_valid.cpu().numpy())
+        result["cpu_baseline"] = base
+        result["parity"] = compare_rows(o_timed, lse_timed, sample, S, H)
+        result["parity"]["scope"] = "outputs of the last timed step against the oracle rows of cpu_baseline"
+        ok = result["parity"]["pass"]
+    del o_timed, lse_timed
+
+    if not args.no_configs:
+        result["configs"] = time_configs(vsa, W, wl, (bq, bkv), args, stream, q, k, v, q_cpu, k_cpu, v_cpu, mask_cpu,
+                                         kernel_tflops)
+        ok = ok and all(c.get("parity", {}).get("pass", True) for c in result["configs"].values()
+                        if isinstance(c, dict) and "kernel" in c)
 
     print(json.dumps(result), flush=True)
-    return 0
+    return 0 if ok else 1
+
+
+# The other workloads and tile shapes timed beside the headline (kernel
+# scope unless noted): dense S=4k, the VSA-256 mask on 128x64 and 64x64 tiles
+# natively and coalesced to 256-row tiles, the native Q64 masks.
+CONFIGS = [
+    ("dense 128x128", "dense_b1h8s4096d128", (128, 128), "kernel"),
+    ("vsa256 128x64", "vsa256_fine_b1h24s32768d128_keep13", (128, 64), "kernel"),
+    ("vsa256 64x64", "vsa256_fine_b1h24s32768d128_keep13", (64, 64), "kernel"),
+    ("vsa256 128x64 coalesced", "vsa256_fine_b1h24s32768d128_keep13", (128, 64), "coalesce"),
+    ("vsa256 64x64 coalesced", "vsa256_fine_b1h24s32768d128_keep13", (64, 64), "coalesce"),
+    ("native64 64x64", "native64_b1h24s32768d128_cnt10to92", (64, 64), "kernel"),
+]
+
+
+def coalesced_rows(vsa, idx, cnt, bq, S):
+    """Query-tile height the coalesced entry point runs for this CSR (the
+    device makes the same pairing test level by level)."""
+    run_bq, ri, rc = bq, idx, cnt
+    while run_bq < 256 and S % 256 == 0:
+        pi, pc, un = vsa.vsa_pair_q_tiles(ri, rc)
+        if int(un.item()) != 0:
+            break
+        ri, rc, run_bq = pi, pc, run_bq * 2
+    return run_bq
+
+
+def time_configs(vsa, W, head_wl, head_tile, args, stream, q0, k0, v0, q0_cpu, k0_cpu, v0_cpu, mask0_cpu,
+                 head_kernel_tflops):
+    """Kernel time, sparse-aware TFLOP/s and (with the CPU leg) sampled parity
+    of every entry of CONFIGS, each on its own synthetic inputs resident in
+    HBM; the entry equal to the headline is skipped."""
+    import torch
+
+    out = {}
+    dev = q0.device
+    for label, wname, tile, scope in CONFIGS:
+        wl = W.WORKLOADS[wname]
+        if tile == head_tile and scope == "kernel" and wl.mask_kind == head_wl.mask_kind and \
+                wl.mask_seed() == head_wl.mask_seed() and wl.seqlen == head_wl.seqlen:
+            continue
+        B, H, S, D = wl.batch, wl.heads, wl.seqlen, wl.head_dim
+        same_inputs = (B, S, H, D) == tuple(q0_cpu.shape)
+        if same_inputs:
+            q, k, v, q_cpu, k_cpu, v_cpu = q0, k0, v0, q0_cpu, k0_cpu, v0_cpu
+        else:
+            q_cpu, k_cpu, v_cpu = wl.qkv()
+            q, k, v = (t.to(dev) for t in (q_cpu, k_cpu, v_cpu))
+        same_mask = wl.mask_kind == head_wl.mask_kind and wl.mask_seed() == head_wl.mask_seed() and \
+            wl.logical_block == head_wl.logical_block and same_inputs
+        mask_cpu = mask0_cpu if same_mask else wl.logical_mask()
+        mask = torch.from_numpy(np.ascontiguousarray(mask_cpu).copy()).to(dev)
+        lq, lkv = wl.logical_block
+        bq, bkv = tile
+        nq = S // bq
+        ld = int(mask_cpu.sum(-1).max()) * (lkv // bkv)
+        idx, cnt = vsa.vsa_mask_to_csr(mask, wl.logical_block, tile, ld, stream=stream)
+        work = vsa.vsa_build_worklist(cnt, ld, segment=nq, stream=stream)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+
+        def attention():
+            if scope == "coalesce":
+                vsa.vsa_attn_fwd_coalesced(q, k, v, idx, cnt, bq, bkv, wl.scale, o, lse, stream=stream)
+            else:
+                vsa.vsa_attn_fwd_worklist(q, k, v, idx, cnt, bq, bkv, work, wl.scale, o, lse, stream=stream)
+
+        for _ in range(max(args.warmup, 3)):
+            attention()
+        events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in events:
+            e0.record(stream)
+            attention()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in events]))
+        pairs = selected_pairs(idx, cnt, bq, bkv)
+        tflops = 4.0 * D * pairs / (ms * 1e-3) / 1e12
+        run_bq = coalesced_rows(vsa, idx, cnt, bq, S) if scope == "coalesce" else bq
+        entry = {
+            "workload": wl.name, "tile": f"{bq}x{bkv}",
+            "runs_as": f"{run_bq}x{bkv}",
+            "timed_scope": "vsa_attn_fwd_coalesced" if scope == "coalesce" else "vsa_attn_fwd_worklist",
+            "kernel": kernel_name(run_bq, bkv, D, n_items=B * H * (S // run_bq)),
+            "kernel_ms": round(ms, 4), "tflops": round(tflops, 2),
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "selected_pairs": pairs,
+            "vs_headline_kernel": round(tflops / head_kernel_tflops, 4),
+        }
+        if not args.no_cpu_baseline and args.config_cpu_seconds > 0:
+            _, sample = cpu_baseline(wl, q_cpu, k_cpu, v_cpu, idx, cnt, bq, bkv, args.config_cpu_seconds)
+            entry["parity"] = compare_rows(o, lse, sample, S, H)
+        out[label] = entry
+        print(f"[bench] {label}: {ms:.4f} ms {tflops:.1f} TFLOP/s"
+              + (f" parity {'ok' if entry['parity']['pass'] else 'FAILED'}" if "parity" in entry else ""),
+              file=sys.stderr, flush=True)
+        del o, lse, idx, cnt, work, mask
+        if not same_inputs:
+            del q, k, v
+        torch.cuda.empty_cache()
+    out["relative_efficiency"] = {
+        "basis": "kernel TFLOP/s of each entry over the headline kernel's (the FastVideo page's efficiency "
+                 "relative to the 256-row arm)",
+        **{lbl: e["vs_headline_kernel"] for lbl, e in out.items() if isinstance(e, dict) and "vs_headline_kernel" in e},
+    }
+    return out
 
 
 def selected_pairs(idx, cnt, bq, bkv, kv_valid=None):
@@ -422,53 +544,6 @@ def read_traffic(path, kname):
     return t.get("bytes_per_launch")
 
 
-def _counter_mean(d, counter, kernel_prefix):
-    """Mean of one counter over the dispatches whose kernel name contains
-    `kernel_prefix` (spaces ignored, so a full template name such as
-    vsa_fwd_iw_kernel<128,128,false> selects one instantiation)."""
-    import csv
-    vals = []
-    want = kernel_prefix.replace(" ", "")
-    with open(os.path.join(d, "run_counter_collection.csv")) as f:
-        for r in csv.DictReader(f):
-            if r["Counter_Name"] == counter and want in r["Kernel_Name"].replace(" ", ""):
-                vals.append(float(r["Counter_Value"]))
-    if not vals:
-        raise SystemExit(f"no {counter} rows for {kernel_prefix!r} in {d}")
-    return sum(vals) / len(vals)
-
-
-def write_traffic(args):
-    """Traffic JSON from FETCH_SIZE / WRITE_SIZE passes (KiB per dispatch),
-    each scaled by what the same counter reads for a plain copy of known size."""
-    import workloads as W
-    wl = W.WORKLOADS[args.workload]
-    bq, bkv = (int(x) for x in args.tile.lower().split("x")) if args.tile else wl.physical[0]
-    # (the schedule an exact-expanded mask runs on)
-    run_bq = 128 if args.paired else (256 if args.coalesce else bq)
-    kname = kernel_name(run_bq, bkv, wl.head_dim, partial=args.ragged is not None,
-                        n_items=wl.batch * wl.heads * (wl.seqlen // run_bq), entry=args.scope == "entry")
-    fetch_dir, write_dir, cfetch_dir, cwrite_dir = args.traffic_from_counters
-    copy_bytes = 1 << 30
-    fetch_scale = copy_bytes / (1024.0 * _counter_mean(cfetch_dir, "FETCH_SIZE", "copy"))
-    write_scale = copy_bytes / (1024.0 * _counter_mean(cwrite_dir, "WRITE_SIZE", "copy"))
-    fetch = _counter_mean(fetch_dir, "FETCH_SIZE", kname) * 1024.0 * fetch_scale
-    write = _counter_mean(write_dir, "WRITE_SIZE", kname) * 1024.0 * write_scale
-    out = {
-        "kernel": kname, "workload": wl.name, "tile": f"{bq}x{bkv}",
-        "bytes_per_launch": round(fetch + write),
-        "fetch_bytes": round(fetch), "write_bytes": round(write),
-        "fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4),
-        "source_hash": kernel_source_hash(kname),
-    }
-    path = args.traffic or default_traffic_path(kname, wl.name, run_bq, bkv)
-    with open(path, "w") as f:
-        json.dump(out, f, indent=1)
-        f.write("\n")
-    print(json.dumps(out))
-    return 0
-
-
 def sample_clock(step, seconds):
     """Run steps back to back for about `seconds` while amd-smi reads the gfx
     clock of every XCD once, half-way through."""
@@ -510,12 +585,21 @@ def sample_clock(step, seconds):
             "source": "amd-smi metric --clock, sampled while steps ran back to back"}
 
 
-def cpu_baseline(wl, q, k, v, idx, cnt, bq, bkv, ld, seconds, kv_valid=None):
-    """Time the CPU oracle on a bounded sample of query rows of this workload."""
+O_MAX_ABS, O_MEAN_ABS, LSE_REL = 2e-2, 2e-3, 1e-3  # forward tolerances (bf16 O, fp32 LSE)
+
+
+def oracle_threads():
+    """Host threads for the oracle: OMP_NUM_THREADS if set, else every CPU."""
+    return int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+
+
+def cpu_baseline(wl, q, k, v, idx, cnt, bq, bkv, seconds, kv_valid=None):
+    """Time the CPU oracle on a bounded sample of whole query tiles of this
+    workload (a fixed pseudo-random order, sized to about `seconds`); returns
+    the timing and the sample (rows and the oracle's O and LSE for them)."""
     import oracle
 
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
-    threads = min(threads, 16)
+    threads = oracle_threads()
     idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
     B, S, H, D = q.shape
     nq = S // bq
@@ -532,27 +616,61 @@ def cpu_baseline(wl, q, k, v, idx, cnt, bq, bkv, ld, seconds, kv_valid=None):
     def run(n_tiles):
         rows, items = rows_for(n_tiles)
         t0 = time.perf_counter()
-        oracle.attn_rows(q, k, v, idx_h, cnt_h, bq, bkv, wl.scale, rows, threads, kv_valid=kv_valid)
+        o_ref, lse_ref = oracle.attn_rows(q, k, v, idx_h, cnt_h, bq, bkv, wl.scale, rows, threads, kv_valid=kv_valid)
         dt = time.perf_counter() - t0
         if kv_valid is None:
             flops = 4.0 * D * float(cnt_h.reshape(-1)[items].sum()) * bq * bkv
         else:
             flat_idx, flat_cnt = idx_h.reshape(-1, idx_h.shape[-1]), cnt_h.reshape(-1)
             flops = 4.0 * D * bq * float(sum(kv_valid[flat_idx[i, :flat_cnt[i]]].sum() for i in items))
-        return dt, flops, rows.size
+        return dt, flops, rows, o_ref, lse_ref
 
-    dt, fl, _ = run(max(1, threads // 4))
-    n_tiles = max(1, min(B * H * nq, int(max(1, threads // 4) * seconds / max(dt, 1e-3))))
-    dt, fl, n_rows = run(n_tiles)
-    return {
+    probe = max(1, threads // 4)
+    dt, fl, *_ = run(probe)
+    n_tiles = max(1, min(B * H * nq, int(probe * seconds / max(dt, 1e-3))))
+    dt, fl, rows, o_ref, lse_ref = run(n_tiles)
+    base = {
         "value": round(fl / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{n_tiles} of {B * H * nq} query tiles ({n_rows} rows, {fl:.3e} sparse-aware flops) "
+        "sample": f"{n_tiles} of {B * H * nq} query tiles ({rows.size} rows, {fl:.3e} sparse-aware flops) "
                   f"in {dt:.1f} s",
         "cpu_model": cpu_model(),
         "host_cpus": os.cpu_count(),
+        "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+    }
+    return base, {"rows": rows, "o": o_ref, "lse": lse_ref, "tiles": n_tiles}
+
+
+def compare_rows(o_gpu, lse_gpu, sample, S, H):
+    """GPU O [B,S,H,D] / LSE [B,H,S] at the sample's flat rows (b*H + h)*S + i
+    against the oracle's: max-abs and mean-abs of O, relative LSE error (floor
+    1), and the FastVideo page's gate max(1e-2, 8 x the bf16 rounding floor of
+    the reference)."""
+    import torch
+
+    rows = sample["rows"]
+    i, h, b = rows % S, (rows // S) % H, rows // (S * H)
+    ti, th, tb = (torch.from_numpy(x).to(o_gpu.device) for x in (i, h, b))
+    og = o_gpu[tb, ti, th].float().cpu().numpy()
+    lg = lse_gpu[tb, th, ti].cpu().numpy()
+    o_ref, lse_ref = sample["o"], sample["lse"]
+    fin = np.isfinite(lse_ref)
+    d = np.abs(og - o_ref)
+    max_abs, mean_abs = float(d.max()), float(d.mean())
+    lse_rel = float((np.abs(lg[fin] - lse_ref[fin]) / np.maximum(1.0, np.abs(lse_ref[fin]))).max()) if fin.any() else 0.0
+    ref32 = torch.from_numpy(np.ascontiguousarray(o_ref, dtype=np.float32))
+    floor = float((ref32 - ref32.to(torch.bfloat16).float()).abs().max())
+    gate = max(1e-2, 8.0 * floor)
+    finite_ok = bool(np.array_equal(fin, np.isfinite(lg)) and np.isfinite(og).all())
+    ok = finite_ok and max_abs <= O_MAX_ABS and mean_abs <= O_MEAN_ABS and lse_rel <= LSE_REL and max_abs <= gate
+    return {
+        "rows": int(rows.size), "query_tiles": int(sample["tiles"]),
+        "max_abs_o": max_abs, "mean_abs_o": mean_abs, "lse_rel": lse_rel,
+        "page_gate": round(gate, 6), "tolerances": {"max_abs_o": O_MAX_ABS, "mean_abs_o": O_MEAN_ABS,
+                                                    "lse_rel": LSE_REL},
+        "pass": bool(ok),
     }
 
 

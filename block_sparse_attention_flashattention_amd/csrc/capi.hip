@@ -5,7 +5,9 @@
 #include <stdio.h>
 
 #include <atomic>
+#include <map>
 #include <mutex>
+#include <tuple>
 #include <vector>
 
 #include "vsa_attn.h"
@@ -95,78 +97,127 @@ vsa::FwdParams make_params(const void* q, const void* k, const void* v, const in
     return p;
 }
 
-// Library-owned work-list buffer, one per device, grown on demand.
+// Library-owned device buffers, one per (device, stream, purpose), grown on
+// demand. Keying by stream lets calls on different streams run at the same
+// time; calls on one stream are ordered by it. A buffer that is too small is
+// replaced by a larger one, and the old one is kept until vsa_release
+// (freeing it here would wait for the device).
+enum BufKind : int { kBufWork = 0, kBufBwd, kBufPair, kBufCoal, kBufSplit, kBufBwdSplit };
 struct DeviceBuffer {
     void* ptr = nullptr;
     size_t bytes = 0;
     size_t zeroed = 0;  // split workspaces: leading bytes known to hold zero counters
 };
 std::mutex g_buf_mutex;
-std::vector<DeviceBuffer> g_bufs;      // forward work list
-std::vector<DeviceBuffer> g_bwd_bufs;  // backward scratch (D, LSE*log2 e, two work lists)
-std::vector<DeviceBuffer> g_pair_bufs; // paired forward: counter, paired CSR, two work lists
-std::vector<DeviceBuffer> g_coal_bufs; // coalesced forward: counters, gates, paired CSRs, three work lists
+std::map<std::tuple<int, uintptr_t, int>, DeviceBuffer> g_bufs;
+std::vector<void*> g_retired;  // superseded buffers, freed by vsa_release
 
-int32_t device_buffer(std::vector<DeviceBuffer>& bufs, size_t bytes, void** out) {
+int32_t stream_buffer_locked(int kind, hipStream_t stream, size_t bytes, DeviceBuffer** out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    std::lock_guard<std::mutex> lock(g_buf_mutex);
-    if ((int)bufs.size() <= dev) bufs.resize(dev + 1);
-    DeviceBuffer& b = bufs[dev];
+    DeviceBuffer& b = g_bufs[std::make_tuple(dev, (uintptr_t)stream, kind)];
     if (b.bytes < bytes) {
-        if (b.ptr) {
-            e = hipFree(b.ptr);  // implicitly waits for work still using it
-            b.ptr = nullptr;
-            b.bytes = 0;
-            if (e != hipSuccess) return hip_fail(e, "hipFree");
-        }
-        e = hipMalloc(&b.ptr, bytes);
+        // grow by at least a quarter, in 64 KiB steps, so that slowly growing
+        // calls do not replace the buffer every time
+        size_t want = bytes > b.bytes + b.bytes / 4 ? bytes : b.bytes + b.bytes / 4;
+        want = (want + 65535) / 65536 * 65536;
+        void* p = nullptr;
+        e = hipMalloc(&p, want);
         if (e != hipSuccess) return hip_fail(e, "hipMalloc(library buffer)");
-        b.bytes = bytes;
+        if (b.ptr) g_retired.push_back(b.ptr);
+        b.ptr = p;
+        b.bytes = want;
         b.zeroed = 0;
     }
-    *out = b.ptr;
+    *out = &b;
     return VSA_OK;
+}
+
+int32_t stream_buffer(int kind, hipStream_t stream, size_t bytes, void** out) {
+    std::lock_guard<std::mutex> lock(g_buf_mutex);
+    DeviceBuffer* b = nullptr;
+    const int32_t rc = stream_buffer_locked(kind, stream, bytes, &b);
+    if (rc == VSA_OK) *out = b->ptr;
+    return rc;
 }
 
 // Workspace of a split-list launch: counter_bytes of per-item counters
 // followed by the partial states. The kernels return every counter they use
 // to 0, but the bytes past the previous call's counters held partial states,
-// so the counters are cleared whenever they reach beyond the bytes known to
-// be zero (a new buffer holds none).
-std::atomic<int32_t> g_max_splits{4};        // vsa_set_max_splits
-std::vector<DeviceBuffer> g_split_bufs;      // forward
-std::vector<DeviceBuffer> g_bwd_split_bufs;  // backward
-int32_t split_buffer(std::vector<DeviceBuffer>& bufs, size_t counter_bytes, size_t bytes, hipStream_t stream,
-                     void** out) {
-    int32_t rc = device_buffer(bufs, bytes, out);
-    if (rc != VSA_OK) return rc;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+// so the counters are cleared (by a kernel, on the stream) whenever they
+// reach beyond the bytes known to be zero (a new buffer holds none).
+std::atomic<int32_t> g_max_splits{4};  // vsa_set_max_splits
+int32_t split_buffer(int kind, size_t counter_bytes, size_t bytes, hipStream_t stream, void** out) {
     std::lock_guard<std::mutex> lock(g_buf_mutex);
-    DeviceBuffer& b = bufs[dev];
-    if (b.zeroed < counter_bytes) {
-        e = hipMemsetAsync(*out, 0, counter_bytes, stream);
-        if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(split counters)");
+    DeviceBuffer* b = nullptr;
+    int32_t rc = stream_buffer_locked(kind, stream, bytes, &b);
+    if (rc != VSA_OK) return rc;
+    if (b->zeroed < counter_bytes) {
+        const hipError_t e = vsa::launch_fill_zero((int32_t*)b->ptr, (int64_t)(counter_bytes / 4), stream);
+        if (e != hipSuccess) return hip_fail(e, "split counter clear launch");
     }
-    b.zeroed = counter_bytes;  // past them the partial states are written
+    b->zeroed = counter_bytes;  // past them the partial states are written
+    *out = b->ptr;
     return VSA_OK;
 }
 
-int32_t worklist_buffer(size_t bytes, int32_t** out) {
-    void* p = nullptr;
-    int32_t rc = device_buffer(g_bufs, bytes, &p);
-    *out = (int32_t*)p;
-    return rc;
+// Split choice and workspace layout of one vsa_attn_fwd call: with too few
+// work items to occupy every compute unit, each list is split over 2 or 4
+// workgroups (partial states merged by the last one). 256-row tiles run one
+// workgroup per compute unit; 64-row tiles go to the independent-wave
+// kernel, four per compute unit. (128-row tiles with few items measured
+// faster on the two-stream kernel unsplit.)
+struct FwdSplit {
+    int splits = 1;
+    size_t counter_bytes = 0;  // one int32 per item, padded to 256 bytes
+    size_t partial_bytes = 0;  // partial (O, max, sum) states of every part
+};
+FwdSplit plan_split(int64_t n_items, int block_q, int head_dim, int max_splits) {
+    FwdSplit f;
+    const int cus = vsa::device_cu_count();
+    if (block_q == 256) {
+        while (f.splits < max_splits && n_items * f.splits * 2 <= cus) f.splits *= 2;
+    } else if (block_q == 64 && n_items < (int64_t)vsa::kIwItemsPerCu * cus) {
+        while (f.splits < max_splits && n_items * f.splits < 4LL * cus) f.splits *= 2;
+    }
+    if (f.splits > 1) {
+        f.counter_bytes = ((size_t)n_items * sizeof(int32_t) + 255) / 256 * 256;
+        const size_t state_words = (size_t)(head_dim / 32 * 16 + 2) * 64;  // per wave
+        f.partial_bytes = (size_t)n_items * f.splits * (block_q / 32) * state_words * sizeof(float);
+    }
+    return f;
+}
+
+// The body of vsa_attn_fwd: the work list
+// (count-sorted within each batch and head) into `work`, then the kernel,
+// with split lists over `counters` / `partial` when splits > 1.
+int32_t run_fwd(const void* q, const void* k, const void* v, const int32_t* idx, const int32_t* cnt,
+                const int32_t* kv_valid, int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim,
+                int32_t idx_ld, int32_t block_q, int32_t block_kv, float scale, void* o, float* lse, hipStream_t st,
+                int32_t* work, int splits, int32_t* counters, float* partial) {
+    const int32_t n_items = batch * heads * (seqlen / block_q);
+    // one segment per (batch, head): heads stay contiguous in the list
+    hipError_t e = vsa::launch_build_worklist(cnt, n_items, seqlen / block_q, idx_ld, work, st);
+    if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
+    vsa::FwdParams p = make_params(q, k, v, idx, cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld, block_q,
+                                   block_kv, scale, work, n_items, o, lse);
+    if (splits > 1) {
+        p.splits = splits;
+        p.ws_counter = counters;
+        p.ws_partial = partial;
+        p.n_work = n_items * splits;
+    }
+    e = vsa::launch_fwd(block_q, block_kv, head_dim, p, st);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    return VSA_OK;
 }
 
 }  // namespace
 
 extern "C" {
 
-int32_t vsa_abi_version(void) { return 6; }
+int32_t vsa_abi_version(void) { return 7; }
 
 int32_t vsa_set_max_splits(int32_t max_splits) {
     const int32_t m = max_splits >= 4 ? 4 : (max_splits >= 2 ? 2 : 1);
@@ -261,42 +312,20 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
     VSA_REQUIRE(idx_ld <= vsa::kWorklistMaxCnt, VSA_ERR_UNSUPPORTED,
                 "idx_ld %d exceeds the work-list sort limit %d; use vsa_attn_fwd_worklist", idx_ld,
                 vsa::kWorklistMaxCnt);
+    hipStream_t st = (hipStream_t)stream;
     const int32_t n_items = batch * heads * (seqlen / block_q);
     int32_t* work = nullptr;
-    rc = worklist_buffer((size_t)n_items * sizeof(int32_t), &work);
+    rc = stream_buffer(kBufWork, st, (size_t)n_items * sizeof(int32_t), (void**)&work);
     if (rc != VSA_OK) return rc;
-    // one segment per (batch, head): heads stay contiguous in the list
-    hipError_t e = vsa::launch_build_worklist(kv_block_cnt, n_items, seqlen / block_q, idx_ld, work,
-                                              (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
-    vsa::FwdParams p = make_params(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim,
-                                   idx_ld, block_q, block_kv, scale, work, n_items, o, lse);
-    // Too few work items to occupy every compute unit: split each list over
-    // 2 or 4 workgroups (partial states merged by the last one). 256-row
-    // tiles run one workgroup per compute unit; 64-row tiles go to the
-    // independent-wave kernel, four per compute unit. (128-row tiles with few
-    // items measured faster on the two-stream kernel unsplit.)
-    const int cus = vsa::device_cu_count();
-    const int max_splits = g_max_splits.load();
-    if (block_q == 256) {
-        while (p.splits < max_splits && (int64_t)n_items * p.splits * 2 <= cus) p.splits *= 2;
-    } else if (block_q == 64 && (int64_t)n_items < (int64_t)vsa::kIwItemsPerCu * cus) {
-        while (p.splits < max_splits && (int64_t)n_items * p.splits < 4LL * cus) p.splits *= 2;
-    }
-    if (p.splits > 1) {
-        const size_t counters = ((size_t)n_items * sizeof(int32_t) + 255) / 256 * 256;
-        const size_t state_words = (size_t)(head_dim / 32 * 16 + 2) * 64;  // per wave
-        const size_t bytes = counters + (size_t)n_items * p.splits * (block_q / 32) * state_words * sizeof(float);
-        void* ws = nullptr;
-        rc = split_buffer(g_split_bufs, counters, bytes, (hipStream_t)stream, &ws);
+    const FwdSplit f = plan_split(n_items, block_q, head_dim, g_max_splits.load());
+    void* ws = nullptr;
+    if (f.splits > 1) {
+        rc = split_buffer(kBufSplit, f.counter_bytes, f.counter_bytes + f.partial_bytes, st, &ws);
         if (rc != VSA_OK) return rc;
-        p.ws_counter = (int32_t*)ws;
-        p.ws_partial = (float*)((char*)ws + counters);
-        p.n_work = n_items * p.splits;
     }
-    e = vsa::launch_fwd(block_q, block_kv, head_dim, p, (hipStream_t)stream);
-    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
-    return VSA_OK;
+    return run_fwd(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld, block_q,
+                   block_kv, scale, o, lse, st, work, f.splits, (int32_t*)ws,
+                   ws ? (float*)((char*)ws + f.counter_bytes) : nullptr);
 }
 
 int32_t vsa_pair_q_tiles(const int32_t* kv_block_idx, const int32_t* kv_block_cnt, int32_t batch, int32_t heads,
@@ -336,7 +365,7 @@ int32_t vsa_attn_fwd_paired(const void* q, const void* k, const void* v, const i
     // [unpaired, pad to 256 B][paired cnt][work 128][work 64][paired idx]
     const size_t words = 64 + (size_t)n_pairs * 2 + (size_t)n_items + (size_t)n_pairs * idx_ld;
     void* buf = nullptr;
-    rc = device_buffer(g_pair_bufs, words * sizeof(int32_t), &buf);
+    rc = stream_buffer(kBufPair, (hipStream_t)stream, words * sizeof(int32_t), &buf);
     if (rc != VSA_OK) return rc;
     int32_t* unpaired = (int32_t*)buf;
     int32_t* pcnt = unpaired + 64;
@@ -391,7 +420,7 @@ int32_t vsa_attn_fwd_coalesced(const void* q, const void* k, const void* v, cons
     const size_t words = 64 + (block_q == 64 ? (size_t)n128 * (1 + idx_ld) : 0) + (size_t)n256 * (1 + idx_ld) +
                          (size_t)n256 + (size_t)n128 + (block_q == 64 ? (size_t)n_items : 0);
     void* buf = nullptr;
-    rc = device_buffer(g_coal_bufs, words * sizeof(int32_t), &buf);
+    rc = stream_buffer(kBufCoal, (hipStream_t)stream, words * sizeof(int32_t), &buf);
     if (rc != VSA_OK) return rc;
     int32_t* ctr_a = (int32_t*)buf;
     int32_t* ctr_b = ctr_a + 1;
@@ -516,7 +545,7 @@ int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o,
     const int32_t nq = seqlen / block_q, nkv = seqlen / block_kv;
     const int32_t items_q = batch * heads * nq, items_kv = batch * heads * nkv;
     void* buf = nullptr;
-    rc = device_buffer(g_bwd_bufs, (size_t)rows * 2 * sizeof(float) + ((size_t)items_q + items_kv) * sizeof(int32_t),
+    rc = stream_buffer(kBufBwd, (hipStream_t)stream, (size_t)rows * 2 * sizeof(float) + ((size_t)items_q + items_kv) * sizeof(int32_t),
                        &buf);
     if (rc != VSA_OK) return rc;
     float* aux = (float*)buf;
@@ -570,7 +599,7 @@ int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                                                  vsa::bwd_split_words_kv(head_dim) * sizeof(float)
                                            : 0;
         void* ws = nullptr;
-        rc = split_buffer(g_bwd_split_bufs, cq + ckv, cq + ckv + wq + wkv, st, &ws);
+        rc = split_buffer(kBufBwdSplit, cq + ckv, cq + ckv + wq + wkv, st, &ws);
         if (rc != VSA_OK) return rc;
         a.ws_counter_q = (int32_t*)ws;
         a.ws_counter_kv = (int32_t*)((char*)ws + cq);
@@ -584,13 +613,11 @@ int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 void vsa_release(void) {
     std::lock_guard<std::mutex> lock(g_buf_mutex);
-    for (auto* v : {&g_bufs, &g_bwd_bufs, &g_pair_bufs, &g_coal_bufs, &g_split_bufs, &g_bwd_split_bufs}) {
-        for (auto& b : *v) {
-            if (b.ptr) (void)hipFree(b.ptr);
-            b.ptr = nullptr;
-            b.bytes = 0;
-        }
-    }
+    for (auto& kv : g_bufs)
+        if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+    g_bufs.clear();
+    for (void* p : g_retired) (void)hipFree(p);
+    g_retired.clear();
 }
 
 }  // extern "C"

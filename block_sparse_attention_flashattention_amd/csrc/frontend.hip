@@ -244,6 +244,12 @@ __global__ __launch_bounds__(256) void pair_q_tiles_kernel(const int32_t* __rest
 
 __global__ void zero_kernel(int32_t* p) { *p = 0; }
 
+// p[0, n) = 0, grid-stride (clears split counters without a memset node, so
+// that a captured graph replays it like any other kernel).
+__global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0;
+}
+
 // Gates of a two-level pairing from the mismatch counts of level 1 (a) and
 // level 2 (b): the 256-row list runs iff a + b == 0, the 128-row list iff
 // a == 0 and b != 0 (both as "run if the gate is zero").
@@ -310,6 +316,13 @@ hipError_t launch_csr_transpose(const int32_t* idx, const int32_t* cnt, int batc
     if (batch_heads <= 0 || nkv <= 0) return hipSuccess;
     hipLaunchKernelGGL(csr_transpose_kernel, dim3(batch_heads), dim3(1024), 0, stream, idx, cnt, nq, nkv, ld, q_idx,
                        q_ld, q_cnt, overflow);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream, p, n);
     return hipGetLastError();
 }
 

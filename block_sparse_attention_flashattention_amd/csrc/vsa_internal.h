@@ -129,6 +129,8 @@ hipError_t launch_pair_q_tiles(const int32_t* idx, const int32_t* cnt, int n_pai
 hipError_t launch_csr_transpose(const int32_t* idx, const int32_t* cnt, int batch_heads, int nq, int nkv, int ld,
                                 int32_t* q_idx, int q_ld, int32_t* q_cnt, int32_t* overflow, hipStream_t stream);
 constexpr int kTransposeMaxWords = 16384;
+// p[0, n) = 0 by a kernel (no memset node).
+hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t stream);
 hipError_t launch_expand_valid(const int32_t* vbs, int nkv_logical, int kv_ratio, int block_kv, int32_t* kv_valid,
                                hipStream_t stream);
 

@@ -31,6 +31,14 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream). All
  *    GPU work is enqueued asynchronously on it; no call synchronises the
  *    host with the device.
+ *  - Library-owned scratch (work lists, split workspaces, the backward's
+ *    per-row terms) is kept per device AND per stream: calls on different
+ *    streams never share it and may run at the same time; calls on one
+ *    stream are ordered by it. A buffer that must grow is replaced with
+ *    hipMalloc; the old one is not freed (hipFree would wait for the device)
+ *    but kept until vsa_release. Buffers are keyed by the stream handle, so
+ *    a stream destroyed while its work still runs must not be followed by a
+ *    new stream that reuses its handle before that work ends.
  *  - Arguments are validated on the host before anything is launched. A
  *    call returns VSA_OK, or a negative vsa_status_t and enqueues nothing.
  *    vsa_last_error() then returns a message naming the failed check.
@@ -176,9 +184,9 @@ int32_t vsa_expand_valid(const int32_t* vbs, int32_t nkv_logical, int32_t logica
  *   kv_valid: NULL or per-tile valid key counts (see the conventions above).
  *   Kernels read the whole CSR row [0, idx_ld) of every listed query tile.
  *   Builds the work list (count-sorted within each batch and head, segment
- *   = seqlen/block_q) in a library-owned device buffer (grown on demand per
- *   device, released by vsa_release) and then runs the kernel in that
- *   order; see vsa_attn_fwd_worklist for the kernel alone.
+ *   = seqlen/block_q) in a library-owned device buffer (one per device and
+ *   stream, grown on demand, released by vsa_release) and then runs the
+ *   kernel in that order; see vsa_attn_fwd_worklist for the kernel alone.
  *   With block_q = 256 and fewer than half as many query tiles as the GPU
  *   has compute units, or block_q = 64 and fewer than 8 query tiles per
  *   compute unit, each tile's list is split over 2 or 4 workgroups
@@ -186,7 +194,7 @@ int32_t vsa_expand_valid(const int32_t* vbs, int32_t nkv_logical, int32_t logica
  *   "BlackwellMultiHeadLatentAttentionForwardFP8", split-KV reduction):
  *   the last workgroup of a tile to finish merges all parts in part order,
  *   so results stay deterministic. This uses another library-owned buffer
- *   of about 17 KB per 32 rows and part.
+ *   (per device and stream) of about 17 KB per 32 rows and part.
  */
 int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
                      const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch, int32_t seqlen,
@@ -240,10 +248,8 @@ int32_t vsa_pair_q_tiles(const int32_t* kv_block_idx, const int32_t* kv_block_cn
  * work list. Either way O and LSE are those of the input CSR (the 128-row
  * kernel splits each list over two streams instead of four, so the
  * rounding order differs). If seqlen is not a multiple of 128 this is
- * vsa_attn_fwd. Uses a library-owned device buffer of about
- * 4*(batch*heads*seqlen/64)*(idx_ld/2 + 2) bytes (grown on demand per
- * device, released by vsa_release); calls on one device must not overlap
- * in time on different streams.
+ * vsa_attn_fwd. Uses a library-owned device buffer (per device and stream)
+ * of about 4*(batch*heads*seqlen/64)*(idx_ld/2 + 2) bytes.
  */
 int32_t vsa_attn_fwd_paired(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
                             const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch, int32_t seqlen,
@@ -272,10 +278,9 @@ int32_t vsa_attn_fwd_paired(const void* q, const void* k, const void* v, const i
  * kernels run the same steps per row). If seqlen is not a multiple of 256
  * this is vsa_attn_fwd_paired (block_q 64) or vsa_attn_fwd (block_q 128).
  * Partial tiles (kv_valid) are supported as in vsa_attn_fwd. Uses a
- * library-owned device buffer of about 4*(batch*heads*seqlen/block_q)*
- * (idx_ld + 3) bytes (grown on demand per device, released by
- * vsa_release); calls on one device must not overlap in time on different
- * streams. idx_ld must not exceed the work-list sort limit (8191).
+ * library-owned device buffer (per device and stream) of about
+ * 4*(batch*heads*seqlen/block_q)*(idx_ld + 3) bytes. idx_ld must not
+ * exceed the work-list sort limit (8191).
  */
 int32_t vsa_attn_fwd_coalesced(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
                                const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch, int32_t seqlen,
@@ -308,10 +313,8 @@ int32_t vsa_attn_fwd_coalesced(const void* q, const void* k, const void* v, cons
  *   Same shape limits as vsa_attn_fwd; q_ld, idx_ld <= 8191. Uses a
  *   library-owned device buffer of 8*batch*heads*seqlen bytes plus the work
  *   lists, and with split lists another of 4*head_dim bytes per token row and
- *   part for dQ and twice that for dK and dV (both grown on demand per
- *   device, released by vsa_release); calls that
- *   share a device must not overlap in time on different streams. Padding
- *   tokens of partial tiles must hold finite values.
+ *   part for dQ and twice that for dK and dV (both per device and stream).
+ *   Padding tokens of partial tiles must hold finite values.
  */
 int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                      const int32_t* kv_block_idx, const int32_t* kv_block_cnt, int32_t idx_ld,
@@ -319,8 +322,9 @@ int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim, int32_t block_q,
                      int32_t block_kv, float scale, void* dq, void* dk, void* dv, void* stream);
 
-/* Free the library-owned work-list buffers on every device. Not thread-safe
- * with concurrent vsa_attn_fwd calls. */
+/* Free the library-owned buffers (every device and stream, including the
+ * ones superseded by growth). Must not run while library work is in flight
+ * or another thread is inside a library call. */
 void vsa_release(void);
 
 /*

@@ -36,7 +36,7 @@ def test_header_declares_the_binding_symbols():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.vsa_abi_version() == 6
+    assert lib.vsa_abi_version() == 7
 
 
 def test_set_max_splits_rounds_and_returns_previous(lib):

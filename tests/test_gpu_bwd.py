@@ -171,66 +171,47 @@ def test_backward_is_deterministic(vsa, max_splits):
         assert torch.equal(x, y)
 
 
-def test_dense_backward_split_lists_sampled(vsa):
+def test_dense_backward_split_lists_every_row(vsa):
     """Dense S=4k at 128x128 (256 query and 256 KV tiles: split in two on a
-    256-CU GPU): sampled dQ and dK/dV rows against the oracle."""
+    256-CU GPU): dQ, dK and dV of every row against the oracle."""
     wl = W.DENSE
     say("dense backward 128x128: inputs")
     q, k, v = wl.qkv()
     do = W.qkv(wl.batch, wl.seqlen, wl.heads, wl.head_dim, seed=4243)[0]
     idx, cnt, _ = ofront.mask_to_csr(wl.logical_mask(), wl.logical_block, (128, 128), 32)
     dq, dk, dv = _run_bwd(vsa, q, k, v, do, idx, cnt, 128, 128, wl.scale)
-    B, S, H, D = q.shape
-    rng = np.random.default_rng(6)
-    qrows = np.array([h * S + r for h in range(H) for r in rng.integers(0, S, size=8)], dtype=np.int64)
-    krows = np.array([h * S + r for h in range(H) for r in rng.integers(0, S, size=4)], dtype=np.int64)
-    say("dense backward 128x128: oracle rows")
-    rq = oracle.bwd_dq_rows(q, k, v, do, idx, cnt, 128, 128, wl.scale, qrows)
-    rk, rv = oracle.bwd_dkv_rows(q, k, v, do, idx, cnt, 128, 128, wl.scale, krows)
-
-    def pick(t, rows):
-        h, i = rows // S, rows % S
-        return t.float().cpu().numpy()[0, i, h]
-
-    check("dQ", pick(dq, qrows), rq, "dense split sampled")
-    check("dK", pick(dk, krows), rk, "dense split sampled")
-    check("dV", pick(dv, krows), rv, "dense split sampled")
+    say("dense backward 128x128: oracle, every row")
+    rq, rk, rv = oracle.bwd_full(q, k, v, do, idx, cnt, 128, 128, wl.scale)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check(name, got.float().cpu().numpy(), ref, "dense split every row")
 
 
 FULL_SIZE = [
-    ("vsa256 256x128", W.VSA256, (256, 128), 26),
-    ("vsa256 64x64", W.VSA256_FINE, (64, 64), 52),
-    ("native64 64x64", W.NATIVE64, (64, 64), 92),
+    # label, workload, tile, idx_ld, heads compared on every row
+    ("vsa256 256x128", W.VSA256, (256, 128), 26, (0, 23)),
+    ("vsa256 64x64", W.VSA256_FINE, (64, 64), 52, (7,)),
+    ("native64 64x64", W.NATIVE64, (64, 64), 92, (16,)),
 ]
 
 
-@pytest.mark.parametrize("label,wl,tile,ld", FULL_SIZE, ids=[c[0] for c in FULL_SIZE])
-def test_backward_full_size_sampled_rows(vsa, label, wl, tile, ld):
-    """Full-size workloads (B1 H24 S32768 D128): sampled dQ rows and sampled
-    dK/dV rows against the oracle."""
+@pytest.mark.parametrize("label,wl,tile,ld,heads", FULL_SIZE, ids=[c[0] for c in FULL_SIZE])
+def test_backward_full_size_whole_heads(vsa, label, wl, tile, ld, heads):
+    """Full-size workloads (B1 H24 S32768 D128): the GPU runs every head; dQ,
+    dK and dV of whole heads (every one of their 32768 query and key rows)
+    are compared with the oracle run on those heads alone (heads are
+    independent, so this is the same computation)."""
     say(f"backward {label}: inputs")
     q, k, v = wl.qkv()
     do = W.qkv(wl.batch, wl.seqlen, wl.heads, wl.head_dim, seed=4242)[0]
     idx, cnt, _ = ofront.mask_to_csr(wl.logical_mask(), wl.logical_block, tile, ld)
     say(f"backward {label}: kernels")
     dq, dk, dv = _run_bwd(vsa, q, k, v, do, idx, cnt, tile[0], tile[1], wl.scale)
-    B, S, H, D = q.shape
-    rng = np.random.default_rng(5)
-    heads = [0, 11, 23]
-    qrows = np.array([h * S + r for h in heads for r in rng.integers(0, S, size=24)], dtype=np.int64)
-    krows = np.array([h * S + r for h in heads for r in rng.integers(0, S, size=3)], dtype=np.int64)
-    say(f"backward {label}: oracle dQ rows")
-    rq = oracle.bwd_dq_rows(q, k, v, do, idx, cnt, tile[0], tile[1], wl.scale, qrows)
-    say(f"backward {label}: oracle dK/dV rows")
-    rk, rv = oracle.bwd_dkv_rows(q, k, v, do, idx, cnt, tile[0], tile[1], wl.scale, krows)
-
-    def pick(t, rows):
-        h, i = rows // S, rows % S
-        return t.float().cpu().numpy()[0, i, h]
-
-    check("dQ", pick(dq, qrows), rq, f"{label} sampled")
-    check("dK", pick(dk, krows), rk, f"{label} sampled")
-    check("dV", pick(dv, krows), rv, f"{label} sampled")
+    for h in heads:
+        say(f"backward {label}: oracle, head {h}, every row")
+        sl = [t[:, :, h:h + 1].contiguous() for t in (q, k, v, do)]
+        rq, rk, rv = oracle.bwd_full(*sl, idx[:, h:h + 1], cnt[:, h:h + 1], tile[0], tile[1], wl.scale)
+        for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+            check(name, got[:, :, h:h + 1].float().cpu().numpy(), ref, f"{label} head {h} every row")
     del dq, dk, dv
     torch.cuda.empty_cache()
 

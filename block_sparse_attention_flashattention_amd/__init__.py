@@ -38,6 +38,7 @@ SYMBOLS = (
     "vsa_csr_transpose",
     "vsa_pair_q_tiles",
     "vsa_attn_fwd",
+    "vsa_attn_fwd_noalloc",
     "vsa_attn_fwd_paired",
     "vsa_attn_fwd_coalesced",
     "vsa_attn_fwd_worklist",
@@ -80,6 +81,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vsa_build_worklist.restype = i32
     lib.vsa_attn_fwd.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p, p, p]
     lib.vsa_attn_fwd.restype = i32
+    lib.vsa_attn_fwd_noalloc.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p, p, p]
+    lib.vsa_attn_fwd_noalloc.restype = i32
     lib.vsa_attn_fwd_worklist.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p, i32, p,
                                           p, p]
     lib.vsa_attn_fwd_worklist.restype = i32
@@ -181,6 +184,24 @@ def vsa_attn_fwd(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale=N
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     rc = load_library().vsa_attn_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(),
+        _valid_ptr(kv_valid, S, block_kv, q.device), B, S, H, D,
+        kv_block_idx.shape[3], block_q, block_kv, float(scale), o.data_ptr(), lse.data_ptr(),
+        _stream_ptr(stream, q.device))
+    _check(rc)
+    return o, lse
+
+
+def vsa_attn_fwd_noalloc(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale=None, o=None, lse=None,
+                         stream=None, kv_valid=None):
+    """vsa_attn_fwd without device allocation in the library: the work list
+    and split workspace live in the library's fixed per-GPU array (calls that
+    overlap in time on one GPU race). Pass ``o`` and ``lse`` to keep the
+    call itself free of allocation; returns (o, lse)."""
+    B, S, H, D, o, lse = _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = load_library().vsa_attn_fwd_noalloc(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(),
         _valid_ptr(kv_valid, S, block_kv, q.device), B, S, H, D,
         kv_block_idx.shape[3], block_q, block_kv, float(scale), o.data_ptr(), lse.data_ptr(),

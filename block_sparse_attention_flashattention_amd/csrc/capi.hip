@@ -189,7 +189,47 @@ FwdSplit plan_split(int64_t n_items, int block_q, int head_dim, int max_splits) 
     return f;
 }
 
-// The body of vsa_attn_fwd: the work list
+// Scratch of vsa_attn_fwd_noalloc: one copy per device, held until the
+// process ends. Layout: [counters | work list | partial states]; the counter
+// region is only ever written by split launches, which leave every counter
+// they use at zero, so it is cleared once per device.
+constexpr size_t kScratchBytes = 16u << 20;
+constexpr size_t kScratchCounterBytes = 256u << 10;
+static __device__ __align__(256) char scratch[kScratchBytes];
+struct ScratchState {
+    char* ptr = nullptr;        // device address of this device's copy of `scratch`
+    bool counters_zero = false; // a clearing launch has been enqueued outside graph capture
+};
+std::vector<ScratchState> g_scratch;  // per device, under g_buf_mutex
+
+int32_t scratch_for_device(hipStream_t stream, char** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_buf_mutex);
+    if ((int)g_scratch.size() <= dev) g_scratch.resize(dev + 1);
+    ScratchState& s = g_scratch[dev];
+    if (s.ptr == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        s.ptr = (char*)p;
+    }
+    if (!s.counters_zero) {
+        // Under graph capture the clearing kernel becomes part of the graph
+        // (and runs at every replay), so it is enqueued again next time.
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(stream, &cap);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+        e = vsa::launch_fill_zero((int32_t*)s.ptr, (int64_t)(kScratchCounterBytes / 4), stream);
+        if (e != hipSuccess) return hip_fail(e, "scratch counter clear launch");
+        if (cap == hipStreamCaptureStatusNone) s.counters_zero = true;
+    }
+    *out = s.ptr;
+    return VSA_OK;
+}
+
+// The body shared by vsa_attn_fwd and vsa_attn_fwd_noalloc: the work list
 // (count-sorted within each batch and head) into `work`, then the kernel,
 // with split lists over `counters` / `partial` when splits > 1.
 int32_t run_fwd(const void* q, const void* k, const void* v, const int32_t* idx, const int32_t* cnt,
@@ -217,7 +257,7 @@ int32_t run_fwd(const void* q, const void* k, const void* v, const int32_t* idx,
 
 extern "C" {
 
-int32_t vsa_abi_version(void) { return 7; }
+int32_t vsa_abi_version(void) { return 8; }
 
 int32_t vsa_set_max_splits(int32_t max_splits) {
     const int32_t m = max_splits >= 4 ? 4 : (max_splits >= 2 ? 2 : 1);
@@ -326,6 +366,40 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
     return run_fwd(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld, block_q,
                    block_kv, scale, o, lse, st, work, f.splits, (int32_t*)ws,
                    ws ? (float*)((char*)ws + f.counter_bytes) : nullptr);
+}
+
+int32_t vsa_attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
+                             const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch, int32_t seqlen,
+                             int32_t heads, int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv,
+                             float scale, void* o, float* lse, void* stream) {
+    g_last_error[0] = 0;
+    int32_t rc = check_fwd(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld,
+                           block_q, block_kv, scale, o, lse);
+    if (rc != VSA_OK) return rc;
+    VSA_REQUIRE(idx_ld <= vsa::kWorklistMaxCnt, VSA_ERR_UNSUPPORTED,
+                "idx_ld %d exceeds the work-list sort limit %d", idx_ld, vsa::kWorklistMaxCnt);
+    const int64_t n_items = (int64_t)batch * heads * (seqlen / block_q);
+    const size_t work_bytes = ((size_t)n_items * sizeof(int32_t) + 255) / 256 * 256;
+    const size_t room = kScratchBytes - kScratchCounterBytes;
+    VSA_REQUIRE(work_bytes <= room, VSA_ERR_UNSUPPORTED,
+                "%lld work items need %zu bytes of scratch; vsa_attn_fwd_noalloc holds %zu (at most %zu items)",
+                (long long)n_items, work_bytes, room, room / sizeof(int32_t));
+    hipStream_t st = (hipStream_t)stream;
+    char* base = nullptr;
+    rc = scratch_for_device(st, &base);
+    if (rc != VSA_OK) return rc;
+    // Split as vsa_attn_fwd would, with fewer parts (or none) where the
+    // partial states would not fit beside the work list.
+    FwdSplit f = plan_split(n_items, block_q, head_dim, g_max_splits.load());
+    while (f.splits > 1 && (f.counter_bytes > kScratchCounterBytes || f.partial_bytes > room - work_bytes)) {
+        const int parts = f.splits / 2;
+        f = plan_split(n_items, block_q, head_dim, parts);
+    }
+    int32_t* work = (int32_t*)(base + kScratchCounterBytes);
+    float* partial = (float*)(base + kScratchCounterBytes + work_bytes);
+    return run_fwd(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld, block_q,
+                   block_kv, scale, o, lse, st, work, f.splits, f.splits > 1 ? (int32_t*)base : nullptr,
+                   f.splits > 1 ? partial : nullptr);
 }
 
 int32_t vsa_pair_q_tiles(const int32_t* kv_block_idx, const int32_t* kv_block_cnt, int32_t batch, int32_t heads,

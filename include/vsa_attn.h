@@ -202,6 +202,30 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
                      float scale, void* o, float* lse, void* stream);
 
 /*
+ * vsa_attn_fwd_noalloc -- vsa_attn_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc during a step.
+ *
+ * Same arguments, result and kernels as vsa_attn_fwd, but it never calls
+ * hipMalloc or hipFree: the work list and split-list workspace live in a
+ * fixed 16 MiB device array of the library (one copy per GPU, held until
+ * the process ends). Limits: at most 4,128,768 work items
+ * (batch*heads*seqlen/block_q), else VSA_ERR_UNSUPPORTED; a launch that
+ * vsa_attn_fwd would split over more parts than the array's room for
+ * partial states allows is split over fewer parts, or not at all (results
+ * then differ from vsa_attn_fwd's by rounding only). Every call on one GPU
+ * shares that GPU's array, whatever the stream: calls that overlap in time
+ * on one GPU race and must be ordered by the caller (one stream, or events).
+ * The first call on a GPU (outside graph capture) also enqueues a small
+ * kernel that clears the array's counters; under capture that kernel is
+ * part of the captured work.
+ */
+int32_t vsa_attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,
+                             const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch, int32_t seqlen,
+                             int32_t heads, int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv,
+                             float scale, void* o, float* lse, void* stream);
+
+/*
  * vsa_attn_fwd_worklist -- the attention kernel alone, over a caller-built
  * work list (for example from vsa_build_worklist). Each entry is a flat
  * index (b*heads + h)*(seqlen/block_q) + p in [0, batch*heads*seqlen/block_q);
@@ -324,7 +348,8 @@ int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /* Free the library-owned buffers (every device and stream, including the
  * ones superseded by growth). Must not run while library work is in flight
- * or another thread is inside a library call. */
+ * or another thread is inside a library call. The no-alloc array of
+ * vsa_attn_fwd_noalloc is not affected. */
 void vsa_release(void);
 
 /*

@@ -36,7 +36,7 @@ def test_header_declares_the_binding_symbols():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.vsa_abi_version() == 7
+    assert lib.vsa_abi_version() == 8
 
 
 def test_set_max_splits_rounds_and_returns_previous(lib):
@@ -92,6 +92,25 @@ def _fwd(lib, **kw):
 ])
 def test_attn_fwd_rejects_invalid_arguments(lib, kw, status, needle):
     assert _fwd(lib, **kw) == status
+    assert needle in lib.vsa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), -1, "null"),
+    (dict(S=1000), -1, "divisible"),
+    (dict(D=96), -2, "head_dim"),
+    (dict(ld=9000), -2, "maximum"),
+    # 64 * 64 * 65536/64 = 4,194,304 work items: above what the fixed array holds
+    (dict(B=64, H=64, S=65536, bq=64, bkv=64), -2, "scratch"),
+])
+def test_attn_fwd_noalloc_rejects_before_touching_the_device(lib, kw, status, needle):
+    args = dict(q=A, k=A, v=A, idx=A, cnt=A, valid=None, B=1, S=1024, H=2, D=128, ld=16, bq=128, bkv=64, scale=0.1,
+                o=A, lse=A)
+    args.update(kw)
+    rc = lib.vsa_attn_fwd_noalloc(args["q"], args["k"], args["v"], args["idx"], args["cnt"], args["valid"],
+                                  args["B"], args["S"], args["H"], args["D"], args["ld"], args["bq"], args["bkv"],
+                                  args["scale"], args["o"], args["lse"], None)
+    assert rc == status
     assert needle in lib.vsa_last_error().decode()
 
 

@@ -157,11 +157,12 @@ def main():
                                       kv_valid=kv_valid)
 
     def step(ev0=None, ev1=None):
-        vsa.vsa_mask_to_csr(mask, (lq, lkv), (bq, bkv), ld, idx, cnt, stream=stream)
-        if not (args.paired or args.coalesce) and args.scope == "kernel":
-            vsa.vsa_build_worklist(cnt, ld, work, segment=nq, stream=stream)
         if vbs is not None:
             vsa.vsa_expand_valid(vbs, lkv, bkv, kv_valid, stream=stream)
+        # tiles without a valid key are left out of the lists
+        vsa.vsa_mask_to_csr(mask, (lq, lkv), (bq, bkv), ld, idx, cnt, stream=stream, kv_valid=kv_valid)
+        if not (args.paired or args.coalesce) and args.scope == "kernel":
+            vsa.vsa_build_worklist(cnt, ld, work, segment=nq, stream=stream)
         if ev0 is not None:
             ev0.record(stream)
         attention()
@@ -209,9 +210,9 @@ def main():
     # Wrapper scope: mask front-end + the entry point that builds its own
     # work list (what a caller without a cached work list pays).
     def wrapper():
-        vsa.vsa_mask_to_csr(mask, (lq, lkv), (bq, bkv), ld, idx, cnt, stream=stream)
         if vbs is not None:
             vsa.vsa_expand_valid(vbs, lkv, bkv, kv_valid, stream=stream)
+        vsa.vsa_mask_to_csr(mask, (lq, lkv), (bq, bkv), ld, idx, cnt, stream=stream, kv_valid=kv_valid)
         if args.paired or args.coalesce:
             attention()
         else:

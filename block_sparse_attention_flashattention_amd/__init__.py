@@ -75,7 +75,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vsa_status_string.restype = ctypes.c_char_p
     lib.vsa_last_error.argtypes = []
     lib.vsa_last_error.restype = ctypes.c_char_p
-    lib.vsa_mask_to_csr.argtypes = [p, i32, i32, i32, i32, i32, i32, i32, i32, p, i32, p, p, p]
+    lib.vsa_mask_to_csr.argtypes = [p, i32, i32, i32, i32, i32, i32, i32, i32, p, p, i32, p, p, p]
     lib.vsa_mask_to_csr.restype = i32
     lib.vsa_build_worklist.argtypes = [p, i32, i32, i32, p, p]
     lib.vsa_build_worklist.restype = i32
@@ -287,12 +287,14 @@ def vsa_attn_fwd_worklist(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv
 
 
 def vsa_mask_to_csr(mask, logical_block, block, idx_ld, kv_block_idx=None, kv_block_cnt=None, overflow=None,
-                    stream=None):
+                    stream=None, kv_valid=None):
     """Exact expansion of a logical mask to ``block`` tiles + block CSR.
 
     Returns (kv_block_idx, kv_block_cnt). Slots past a row's count are left
     as allocated (zero when allocated here). ``overflow`` (optional int32
     [1] GPU tensor) is set to 1 if some row holds more than ``idx_ld`` tiles.
+    ``kv_valid`` (optional int32 [S/block_kv]): valid keys per physical KV
+    tile; tiles without a valid key are left out of the lists.
     """
     _dev(mask, "mask", torch.uint8, 4)
     B, H, NQL, NKVL = mask.shape
@@ -314,6 +316,7 @@ def vsa_mask_to_csr(mask, logical_block, block, idx_ld, kv_block_idx=None, kv_bl
         _dev(overflow, "overflow", torch.int32, 1)
         ovf_ptr = overflow.data_ptr()
     rc = load_library().vsa_mask_to_csr(mask.data_ptr(), B, H, NQL, NKVL, lq, lkv, pq, pkv,
+                                        _valid_ptr(kv_valid, NQL * lq, pkv, mask.device),
                                         kv_block_idx.data_ptr(), idx_ld, kv_block_cnt.data_ptr(), ovf_ptr,
                                         _stream_ptr(stream, mask.device))
     _check(rc)

@@ -257,7 +257,7 @@ int32_t run_fwd(const void* q, const void* k, const void* v, const int32_t* idx,
 
 extern "C" {
 
-int32_t vsa_abi_version(void) { return 8; }
+int32_t vsa_abi_version(void) { return 9; }
 
 int32_t vsa_set_max_splits(int32_t max_splits) {
     const int32_t m = max_splits >= 4 ? 4 : (max_splits >= 2 ? 2 : 1);
@@ -278,8 +278,8 @@ const char* vsa_last_error(void) { return g_last_error; }
 
 int32_t vsa_mask_to_csr(const uint8_t* mask, int32_t batch, int32_t heads, int32_t nq_logical, int32_t nkv_logical,
                         int32_t logical_block_q, int32_t logical_block_kv, int32_t block_q, int32_t block_kv,
-                        int32_t* kv_block_idx, int32_t idx_ld, int32_t* kv_block_cnt, int32_t* overflow,
-                        void* stream) {
+                        const int32_t* kv_valid, int32_t* kv_block_idx, int32_t idx_ld, int32_t* kv_block_cnt,
+                        int32_t* overflow, void* stream) {
     g_last_error[0] = 0;
     VSA_REQUIRE(mask && kv_block_idx && kv_block_cnt, VSA_ERR_INVALID_ARG, "null pointer");
     VSA_REQUIRE(batch >= 1 && heads >= 1 && nq_logical >= 1 && nkv_logical >= 1, VSA_ERR_INVALID_ARG,
@@ -292,15 +292,15 @@ int32_t vsa_mask_to_csr(const uint8_t* mask, int32_t batch, int32_t heads, int32
     VSA_REQUIRE((int64_t)nq_logical * logical_block_q == (int64_t)nkv_logical * logical_block_kv,
                 VSA_ERR_INVALID_ARG, "query and key sequence lengths differ");
     VSA_REQUIRE(idx_ld >= 1, VSA_ERR_INVALID_ARG, "idx_ld must be >= 1");
-    VSA_REQUIRE(aligned(kv_block_idx, 4) && aligned(kv_block_cnt, 4) && aligned(overflow, 4), VSA_ERR_INVALID_ARG,
-                "index buffers must be 4-byte aligned");
+    VSA_REQUIRE(aligned(kv_block_idx, 4) && aligned(kv_block_cnt, 4) && aligned(overflow, 4) && aligned(kv_valid, 4),
+                VSA_ERR_INVALID_ARG, "index buffers and kv_valid must be 4-byte aligned");
     const int64_t q_ratio = logical_block_q / block_q, kv_ratio = logical_block_kv / block_kv;
     const int64_t nq_phys = (int64_t)nq_logical * q_ratio;
     const int64_t rows = (int64_t)batch * heads * nq_phys;
     VSA_REQUIRE(rows <= INT32_MAX / 4 && (int64_t)nkv_logical * kv_ratio <= INT32_MAX, VSA_ERR_INVALID_ARG,
                 "problem too large");
     hipError_t e = vsa::launch_mask_to_csr(mask, batch, heads, nq_logical, nkv_logical, (int)q_ratio, (int)kv_ratio,
-                                           (int)nq_phys, kv_block_idx, idx_ld, kv_block_cnt, overflow,
+                                           (int)nq_phys, kv_valid, kv_block_idx, idx_ld, kv_block_cnt, overflow,
                                            (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "mask_to_csr launch");
     return VSA_OK;

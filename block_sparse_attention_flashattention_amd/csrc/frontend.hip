@@ -13,11 +13,17 @@ namespace vsa {
 namespace {
 
 // One wave per physical CSR row: 64 mask bytes per step, ballot + prefix
-// popcount to place each selected cell.
+// popcount to place each selected cell. With valid key counts per physical
+// KV tile (VALID), a tile with no valid key is left out of the list: each
+// lane counts the non-empty tiles of its cell and a wave prefix sum places
+// them.
+template <bool VALID>
 __global__ __launch_bounds__(256) void mask_to_csr_kernel(const uint8_t* __restrict__ mask, int n_rows,
                                                           int nq_logical, int nkv_logical, int q_ratio,
-                                                          int kv_ratio, int nq_physical, int32_t* __restrict__ idx,
-                                                          int ld, int32_t* __restrict__ cnt,
+                                                          int kv_ratio, int nq_physical,
+                                                          const int32_t* __restrict__ kv_valid,
+                                                          int32_t* __restrict__ idx, int ld,
+                                                          int32_t* __restrict__ cnt,
                                                           int32_t* __restrict__ overflow) {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -27,20 +33,40 @@ __global__ __launch_bounds__(256) void mask_to_csr_kernel(const uint8_t* __restr
     const uint8_t* mrow = mask + ((int64_t)bh * nq_logical + p / q_ratio) * nkv_logical;
     int32_t* orow = idx + (int64_t)row * ld;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int running = 0;  // selected logical cells so far
+    int running = 0;  // physical tiles listed so far
     for (int base = 0; base < nkv_logical; base += 64) {
         const int t = base + lane;
         const bool sel = t < nkv_logical && mrow[t] != 0;
-        const uint64_t bal = __ballot(sel);
-        if (sel) {
-            const int pos = (running + __popcll(bal & below)) * kv_ratio;
+        if constexpr (!VALID) {
+            const uint64_t bal = __ballot(sel);
+            if (sel) {
+                const int pos = (running + __popcll(bal & below)) * kv_ratio;
+                for (int r = 0; r < kv_ratio; ++r)
+                    if (pos + r < ld) orow[pos + r] = t * kv_ratio + r;
+            }
+            running += __popcll(bal);
+        } else {
+            unsigned keep = 0;  // bit r: physical tile t*kv_ratio + r has a valid key
+            if (sel)
+                for (int r = 0; r < kv_ratio; ++r) keep |= (kv_valid[t * kv_ratio + r] > 0 ? 1u : 0u) << r;
+            const int m = __popc(keep);
+            int x = m;  // inclusive prefix sum of m over the wave
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(x, off);
+                if (lane >= off) x += y;
+            }
+            int pos = running + x - m;
             for (int r = 0; r < kv_ratio; ++r)
-                if (pos + r < ld) orow[pos + r] = t * kv_ratio + r;
+                if ((keep >> r) & 1u) {
+                    if (pos < ld) orow[pos] = t * kv_ratio + r;
+                    ++pos;
+                }
+            running += __shfl(x, 63);
         }
-        running += __popcll(bal);
     }
     if (lane == 0) {
-        const int c = running * kv_ratio;
+        const int c = VALID ? running : running * kv_ratio;
         cnt[row] = c;
         if (c > ld && overflow) *overflow = 1;
     }
@@ -272,12 +298,16 @@ __global__ void expand_valid_kernel(const int32_t* vbs, int n_out, int kv_ratio,
 }  // namespace
 
 hipError_t launch_mask_to_csr(const uint8_t* mask, int batch, int heads, int nq_logical, int nkv_logical,
-                              int q_ratio, int kv_ratio, int nq_physical, int32_t* idx, int ld, int32_t* cnt,
-                              int32_t* overflow, hipStream_t stream) {
+                              int q_ratio, int kv_ratio, int nq_physical, const int32_t* kv_valid, int32_t* idx,
+                              int ld, int32_t* cnt, int32_t* overflow, hipStream_t stream) {
     const int n_rows = batch * heads * nq_physical;
     if (n_rows <= 0) return hipSuccess;
-    hipLaunchKernelGGL(mask_to_csr_kernel, dim3((n_rows + 3) / 4), dim3(256), 0, stream, mask, n_rows, nq_logical,
-                       nkv_logical, q_ratio, kv_ratio, nq_physical, idx, ld, cnt, overflow);
+    if (kv_valid)
+        hipLaunchKernelGGL(mask_to_csr_kernel<true>, dim3((n_rows + 3) / 4), dim3(256), 0, stream, mask, n_rows,
+                           nq_logical, nkv_logical, q_ratio, kv_ratio, nq_physical, kv_valid, idx, ld, cnt, overflow);
+    else
+        hipLaunchKernelGGL(mask_to_csr_kernel<false>, dim3((n_rows + 3) / 4), dim3(256), 0, stream, mask, n_rows,
+                           nq_logical, nkv_logical, q_ratio, kv_ratio, nq_physical, kv_valid, idx, ld, cnt, overflow);
     return hipGetLastError();
 }
 

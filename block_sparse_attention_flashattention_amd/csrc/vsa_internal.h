@@ -112,9 +112,11 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 bool bwd_supported(int block_q, int block_kv, int head_dim);
 
 // Front-end launches (frontend.hip).
+// kv_valid (may be null): valid keys per physical KV tile; tiles without one
+// are left out of the lists.
 hipError_t launch_mask_to_csr(const uint8_t* mask, int batch, int heads, int nq_logical, int nkv_logical,
-                              int q_ratio, int kv_ratio, int nq_physical, int32_t* idx, int ld, int32_t* cnt,
-                              int32_t* overflow, hipStream_t stream);
+                              int q_ratio, int kv_ratio, int nq_physical, const int32_t* kv_valid, int32_t* idx,
+                              int ld, int32_t* cnt, int32_t* overflow, hipStream_t stream);
 // With a gate, the list is built only if (*gate == 0) == run_if_zero, and
 // is all -1 (skipped by the kernels) otherwise.
 hipError_t launch_build_worklist(const int32_t* cnt, int n_items, int segment, int max_cnt, int32_t* work,

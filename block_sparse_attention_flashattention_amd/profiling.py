@@ -116,6 +116,7 @@ def collect(out, tag, workload, tile, extra=(), timeout=240):
 def collect_copy(out, timeout=120):
     """FETCH_SIZE and WRITE_SIZE of a plain 1 GiB device copy (the scale)."""
     out = os.path.abspath(out)
+    os.makedirs(out, exist_ok=True)
     for name, ctr in (("copy_fetch", "FETCH_SIZE"), ("copy_write", "WRITE_SIZE")):
         cmd = ["rocprofv3", "--pmc", ctr, "--output-format", "csv", "-d", os.path.join(out, name), "-o", "run", "--",
                sys.executable, BENCH, "--copy-calibration"]

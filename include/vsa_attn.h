@@ -98,10 +98,16 @@ const char* vsa_last_error(void);
  *   block_q/kv     physical tile shape; must divide the logical block sizes.
  *                  seqlen = nq_logical*logical_block_q must equal
  *                  nkv_logical*logical_block_kv.
+ *   kv_valid       optional [seqlen/block_kv] int32 (may be NULL): valid
+ *                  key tokens per physical KV tile, as passed to the forward
+ *                  (see vsa_expand_valid). A selected tile with no valid key
+ *                  (kv_valid <= 0) is left out of the list, so no kernel
+ *                  fetches or multiplies it; the selected token pairs are
+ *                  unchanged (such a tile has none).
  *   kv_block_idx   out [batch, heads, seqlen/block_q, idx_ld]: ascending
  *                  physical KV tile indices; slots past the count are not
  *                  written.
- *   kv_block_cnt   out [batch, heads, seqlen/block_q]: number of selected
+ *   kv_block_cnt   out [batch, heads, seqlen/block_q]: number of listed
  *                  physical KV tiles (the true count, even if > idx_ld).
  *   overflow       optional out (device int32, may be NULL): set to 1 if
  *                  any row's count exceeds idx_ld (that row then keeps only
@@ -109,8 +115,8 @@ const char* vsa_last_error(void);
  */
 int32_t vsa_mask_to_csr(const uint8_t* mask, int32_t batch, int32_t heads, int32_t nq_logical,
                         int32_t nkv_logical, int32_t logical_block_q, int32_t logical_block_kv,
-                        int32_t block_q, int32_t block_kv, int32_t* kv_block_idx, int32_t idx_ld,
-                        int32_t* kv_block_cnt, int32_t* overflow, void* stream);
+                        int32_t block_q, int32_t block_kv, const int32_t* kv_valid, int32_t* kv_block_idx,
+                        int32_t idx_ld, int32_t* kv_block_cnt, int32_t* overflow, void* stream);
 
 /*
  * vsa_build_worklist -- mask front-end, step 2: count-sorted work list.

@@ -46,7 +46,7 @@ from __future__ import annotations
 import numpy as np
 
 
-def mask_to_csr(logical_mask, logical_block, physical_block, ld, fill=-1):
+def mask_to_csr(logical_mask, logical_block, physical_block, ld, fill=-1, kv_valid=None):
     """Expand a logical mask and list its selected KV tiles per Q tile.
 
     logical_mask: [B, H, NQ_l, NKV_l], nonzero = selected.
@@ -55,6 +55,8 @@ def mask_to_csr(logical_mask, logical_block, physical_block, ld, fill=-1):
     Returns (idx [B, H, NQ_p, ld] int32, cnt [B, H, NQ_p] int32, overflow).
     cnt is the true count; a row with cnt > ld keeps only its first ld
     entries and sets ``overflow``. Slots past a row's count hold ``fill``.
+    kv_valid [NKV_p] (optional): valid keys per physical KV tile; a tile
+    with none holds no selectable key, so it is not listed.
     """
     m = np.asarray(logical_mask) != 0
     lq, lkv = logical_block
@@ -62,6 +64,11 @@ def mask_to_csr(logical_mask, logical_block, physical_block, ld, fill=-1):
     if lq % pq or lkv % pkv:
         raise ValueError("physical tile sizes must divide the logical block sizes")
     phys = np.repeat(np.repeat(m, lq // pq, axis=2), lkv // pkv, axis=3)
+    if kv_valid is not None:
+        has_key = np.asarray(kv_valid).reshape(-1) > 0
+        if has_key.size != phys.shape[3]:
+            raise ValueError("kv_valid must hold one count per physical KV tile")
+        phys = phys & has_key[None, None, None, :]
     B, H, NQ, NKV = phys.shape
     idx = np.full((B, H, NQ, ld), fill, dtype=np.int32)
     cnt = np.zeros((B, H, NQ), dtype=np.int32)

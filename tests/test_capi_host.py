@@ -36,7 +36,7 @@ def test_header_declares_the_binding_symbols():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.vsa_abi_version() == 8
+    assert lib.vsa_abi_version() == 9
 
 
 def test_set_max_splits_rounds_and_returns_previous(lib):
@@ -128,13 +128,16 @@ def test_attn_fwd_worklist_rejects_bad_work_list(lib):
 
 def test_mask_to_csr_rejects_invalid_arguments(lib):
     f = lib.vsa_mask_to_csr
-    assert f(None, 1, 1, 4, 4, 256, 256, 128, 64, A, 8, A, None, None) == -1
+    # mask, B, H, NQl, NKVl, LQ, LKV, PQ, PKV, kv_valid, idx, ld, cnt, overflow, stream
+    assert f(None, 1, 1, 4, 4, 256, 256, 128, 64, None, A, 8, A, None, None) == -1
     # physical tile must divide the logical block
-    assert f(A, 1, 1, 4, 4, 256, 256, 96, 64, A, 8, A, None, None) == -1
+    assert f(A, 1, 1, 4, 4, 256, 256, 96, 64, None, A, 8, A, None, None) == -1
     assert "divide" in lib.vsa_last_error().decode()
     # query and key lengths must agree
-    assert f(A, 1, 1, 4, 8, 256, 256, 128, 64, A, 8, A, None, None) == -1
-    assert f(A, 1, 1, 4, 4, 256, 256, 128, 64, A, 0, A, None, None) == -1
+    assert f(A, 1, 1, 4, 8, 256, 256, 128, 64, None, A, 8, A, None, None) == -1
+    assert f(A, 1, 1, 4, 4, 256, 256, 128, 64, None, A, 0, A, None, None) == -1
+    assert f(A, 1, 1, 4, 4, 256, 256, 128, 64, A + 2, A, 8, A, None, None) == -1  # misaligned kv_valid
+    assert "kv_valid" in lib.vsa_last_error().decode()
 
 
 def test_build_worklist_validation(lib):

@@ -47,6 +47,33 @@ def test_csr_selects_exactly_the_logical_token_pairs(lblock, pblock):
     assert np.all(cnt % e == 0)
 
 
+@pytest.mark.parametrize("lblock,pblock", [((256, 256), (256, 128)), ((256, 256), (128, 64)),
+                                           ((256, 256), (64, 64)), ((128, 64), (32, 16))])
+def test_csr_with_valid_counts_selects_exactly_the_valid_token_pairs(lblock, pblock):
+    """With valid keys per physical tile, the listed tiles' valid keys are
+    exactly the logical mask's pairs restricted to valid key tokens, and no
+    listed tile is empty (the tiles left out held no valid key)."""
+    S = 1024
+    rng = np.random.default_rng(lblock[1] + pblock[0])
+    mask = (rng.random((2, 2, S // lblock[0], S // lblock[1])) < 0.5).astype(np.uint8)
+    vbs = rng.integers(0, lblock[1] + 1, size=S // lblock[1])
+    vbs[:2] = [0, lblock[1]]
+    val = frontend.expand_valid(vbs, lblock[1], pblock[1])
+    ld = S // pblock[1]
+    idx, cnt, ovf = frontend.mask_to_csr(mask, lblock, pblock, ld, kv_valid=val)
+    assert not ovf
+    key_exists = np.concatenate([np.arange(lblock[1]) < n for n in vbs])  # per key token
+    want = _selected_by_logical(mask, lblock, S) & key_exists[None, None, None, :]
+    got = _selected_by_csr(idx, cnt, pblock, S) & key_exists[None, None, None, :]
+    assert np.array_equal(got, want)
+    for pos in np.ndindex(cnt.shape):
+        row = idx[pos][:cnt[pos]]
+        assert np.all(val[row] > 0) and np.all(np.diff(row) > 0)
+    # without valid counts the same rows list at least as many tiles
+    _, cnt_all, _ = frontend.mask_to_csr(mask, lblock, pblock, ld)
+    assert np.all(cnt <= cnt_all) and cnt.sum() < cnt_all.sum()
+
+
 def test_overflow_truncates_and_flags():
     mask = np.ones((1, 1, 2, 8), dtype=np.uint8)
     idx, cnt, ovf = frontend.mask_to_csr(mask, (64, 64), (64, 32), ld=10)

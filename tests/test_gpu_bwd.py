@@ -216,6 +216,31 @@ def test_backward_full_size_whole_heads(vsa, label, wl, tile, ld, heads):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("tile", [(256, 128), (64, 64)], ids=["256x128", "64x64"])
+def test_backward_with_empty_tiles_dropped(vsa, tile):
+    """Ragged KV blocks with tiles left out of the lists by the front-end:
+    dQ, dK, dV of every row against the oracle (which lists every selected
+    tile; keys of a dropped tile get zero gradients)."""
+    B, H, S, D = 1, 2, 2048, 128
+    say(f"backward, empty tiles dropped, {tile}")
+    q, k, v = W.qkv(B, S, H, D, seed=510 + tile[0])
+    do = W.qkv(B, S, H, D, seed=511 + tile[0])[0]
+    mask = W.anchor_uniform_mask(H, S // 256, S // 256, 4, seed=512)[None]
+    vbs = W.ragged_block_sizes(S // 256, 256, seed=513)
+    vbs[:2] = [0, 100]
+    val = ofront.expand_valid(vbs, 256, tile[1])
+    ld = 4 * (256 // tile[1])
+    idx, cnt, _ = ofront.mask_to_csr(mask, (256, 256), tile, ld)
+    didx, dcnt = vsa.vsa_mask_to_csr(dev(mask), (256, 256), tile, ld, kv_valid=dev(val))
+    torch.cuda.synchronize()
+    assert int(dcnt.sum()) < int(cnt.sum())
+    scale = 1.0 / math.sqrt(D)
+    dq, dk, dv = _run_bwd(vsa, q, k, v, do, didx.cpu().numpy(), dcnt.cpu().numpy(), tile[0], tile[1], scale, val)
+    rq, rk, rv = oracle.bwd_full(q, k, v, do, idx, cnt, tile[0], tile[1], scale, kv_valid=val)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        check(name, got.float().cpu().numpy(), ref, f"dropped {tile}")
+
+
 @pytest.mark.parametrize("bq,bkv", [(256, 128), (128, 64), (64, 64)])
 def test_maximum_list_stride_and_empty_head(vsa, bq, bkv):
     """idx_ld = q_ld = 8191 (the largest accepted; the kernels stage whole

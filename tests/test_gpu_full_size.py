@@ -209,31 +209,47 @@ def test_native64_every_element(vsa, native64_ref, entry):
 @pytest.fixture(scope="module")
 def ragged_ref(vsa):
     """VSA-256 with ragged logical KV blocks (valid tokens per 256-token block
-    in [128, 256], 30% full): the oracle over every row at 256x128."""
+    uniform in [0, 256], 30% full): the oracle over every row at 256x128."""
     wl = W.VSA256
     t0 = time.perf_counter()
     q, k, v = wl.qkv()
     mask = wl.logical_mask()
-    vbs = W.ragged_block_sizes(wl.seqlen // 256, 256, seed=2026, lo=128)
+    vbs = W.ragged_block_sizes(wl.seqlen // 256, 256, seed=2026)
+    vbs[:3] = [0, 128, 1]
     idx, cnt, _ = ofront.mask_to_csr(mask, wl.logical_block, (256, 128), 26)
     val = ofront.expand_valid(vbs, 256, 128)
     o, lse = oracle.attn_full(q, k, v, idx, cnt, 256, 128, wl.scale, kv_valid=val)
     say(f"oracle ragged vsa256 at 256x128, every row: {time.perf_counter() - t0:.1f} s")
-    return dict(qd=dev(q), kd=dev(k), vd=dev(v), mask=dev(mask), vbs=dev(vbs), o=o, lse=lse)
+    return dict(qd=dev(q), kd=dev(k), vd=dev(v), mask=dev(mask), mask_h=mask, vbs=dev(vbs), vbs_h=vbs, o=o,
+                lse=lse)
 
 
-@pytest.mark.parametrize("tile,ld", [((256, 128), 26), ((128, 64), 52), ((64, 64), 52)],
-                         ids=["256x128", "128x64", "64x64"])
-def test_vsa256_ragged_every_element(vsa, ragged_ref, tile, ld):
+RAGGED_RUNS = [((256, 128), 26, False), ((256, 128), 26, True), ((128, 64), 52, True), ((64, 64), 52, True)]
+
+
+@pytest.mark.parametrize("tile,ld,drop", RAGGED_RUNS,
+                         ids=[f"{t[0]}x{t[1]}{'_dropped' if d else ''}" for t, _, d in RAGGED_RUNS])
+def test_vsa256_ragged_every_element(vsa, ragged_ref, tile, ld, drop):
     """Partial KV tiles at full size: the valid counts per physical tile are
     expanded on the device from the per-block counts; every element against
     the one oracle run (the token-level selection is the same at every tile
-    shape)."""
+    shape). With `drop`, the front-end leaves tiles without a valid key out of
+    the lists (their counts shrink; the CSR is bit-exact against the
+    oracle's front-end)."""
     r = ragged_ref
-    idx, cnt = vsa.vsa_mask_to_csr(r["mask"], (256, 256), tile, ld)
     val = vsa.vsa_expand_valid(r["vbs"], 256, tile[1])
+    idx, cnt = vsa.vsa_mask_to_csr(r["mask"], (256, 256), tile, ld, kv_valid=val if drop else None)
+    if drop:
+        ridx, rcnt, _ = ofront.mask_to_csr(r["mask_h"], (256, 256), tile, ld,
+                                           kv_valid=ofront.expand_valid(r["vbs_h"], 256, tile[1]))
+        torch.cuda.synchronize()
+        assert np.array_equal(cnt.cpu().numpy(), rcnt)
+        listed = np.arange(ld)[None, None, None, :] < rcnt[..., None]
+        assert np.array_equal(np.where(listed, idx.cpu().numpy(), -1), np.where(listed, ridx, -1))
+        full = ofront.mask_to_csr(r["mask_h"], (256, 256), tile, ld)[1]
+        say(f"ragged {tile}: {int(full.sum() - rcnt.sum())} of {int(full.sum())} listed tiles dropped")
     o, lse = vsa.vsa_attn_fwd(r["qd"], r["kd"], r["vd"], idx, cnt, tile[0], tile[1], W.VSA256.scale, kv_valid=val)
     torch.cuda.synchronize()
-    check_all(o, lse, r["o"], r["lse"], f"ragged vsa256 {tile[0]}x{tile[1]}")
+    check_all(o, lse, r["o"], r["lse"], f"ragged vsa256 {tile[0]}x{tile[1]}{' dropped' if drop else ''}")
     del o, lse
     torch.cuda.empty_cache()

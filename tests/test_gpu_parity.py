@@ -119,6 +119,36 @@ def test_mask_to_csr_bit_exact(vsa, label, wl, shape, ld):
     assert bool(ovf.item()) == ovf_ref
 
 
+@pytest.mark.parametrize("lblock,shape", [((256, 256), (256, 128)), ((256, 256), (64, 64)), ((128, 64), (32, 16)),
+                                          ((256, 256), (128, 256))])
+def test_mask_to_csr_drops_empty_tiles_bit_exact(vsa, lblock, shape):
+    """With valid keys per physical tile, tiles without one are left out:
+    counts and lists bit-exact against the oracle's front-end (rows of more
+    than 64 logical cells exercise the wave prefix sum across steps)."""
+    say(f"mask_to_csr with valid counts {lblock} -> {shape}")
+    S = 32768 if lblock[1] == 256 else 8192  # 128 logical cells per row
+    rng = np.random.default_rng(shape[0] + shape[1])
+    mask = (rng.random((2, 3, S // lblock[0], S // lblock[1])) < 0.6).astype(np.uint8)
+    vbs = W.ragged_block_sizes(S // lblock[1], lblock[1], seed=shape[1], p_full=0.2)
+    vbs[:4] = [0, 1, lblock[1], 0]
+    val = ofront.expand_valid(vbs, lblock[1], shape[1])
+    ld = S // shape[1]
+    ridx, rcnt, _ = ofront.mask_to_csr(mask, lblock, shape, ld, kv_valid=val)
+    idx, cnt = vsa.vsa_mask_to_csr(dev(mask), lblock, shape, ld, kv_valid=dev(val))
+    torch.cuda.synchronize()
+    assert np.array_equal(cnt.cpu().numpy(), rcnt)
+    listed = np.arange(ld)[None, None, None, :] < rcnt[..., None]
+    assert np.array_equal(np.where(listed, idx.cpu().numpy(), -1), np.where(listed, ridx, -1))
+    # a compact row length truncates and keeps the true count
+    small = max(1, int(rcnt.max()) - 3)
+    ovf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    i2, c2 = vsa.vsa_mask_to_csr(dev(mask), lblock, shape, small, overflow=ovf, kv_valid=dev(val))
+    torch.cuda.synchronize()
+    assert np.array_equal(c2.cpu().numpy(), rcnt) and ovf.item() == 1
+    keep = np.arange(small)[None, None, None, :] < np.minimum(rcnt, small)[..., None]
+    assert np.array_equal(np.where(keep, i2.cpu().numpy(), -1), np.where(keep, ridx[..., :small], -1))
+
+
 def test_mask_to_csr_overflow_flag(vsa):
     say("mask_to_csr overflow")
     rng = np.random.default_rng(5)

@@ -296,6 +296,7 @@ def summarize(out, tag, workload, tile, extra=(), profiles=PROFILES, write_files
               f"- Waves per launch: {sq['waves']:.0f}.", ""]
     text = "\n".join(lines)
     if write_files:
+        os.makedirs(profiles, exist_ok=True)
         stem = kname.split("<")[0] + ("_partial" if kname.endswith("true>") else "")
         suffix = "_paired" if "--paired" in extra else ("_coalesced" if "--coalesce" in extra else "")
         with open(os.path.join(profiles, f"{stem}{suffix}_{tile}_{workload}.md"), "w") as f:

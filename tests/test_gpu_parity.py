@@ -330,6 +330,42 @@ def test_invalid_entries_are_skipped_and_counts_clamped(vsa):
                S, H, "invalid entries")
 
 
+UNSPLIT_CASES = [(bkv, D) for bkv in (64, 128) for D in (128, 64)]
+
+
+@pytest.mark.parametrize("bkv,D", UNSPLIT_CASES, ids=[f"256x{a}_d{b}" for a, b in UNSPLIT_CASES])
+def test_256_row_tiles_unsplit_all_rows(vsa, bkv, D):
+    """256-row tiles through the work-list entry point (lists never split):
+    lists of lengths 0, 1, 2, 3, all tiles and all but one, in shuffled
+    order, with out-of-range entries that must be skipped and a work list in
+    reverse order; every row against the oracle."""
+    B, H, S = 2, 3, 4096
+    nq, nkv = S // 256, S // bkv
+    say(f"256-row tiles unsplit 256x{bkv} D={D}")
+    q, k, v = W.qkv(B, S, H, D, seed=bkv + D + 300)
+    idx, cnt = W.random_csr(B, H, nq, nkv, nkv, 0, nkv, seed=bkv * 5 + D)
+    lens = [0, 1, 2, 3, nkv, nkv - 1, 5]
+    for i, c in enumerate(lens):
+        cnt[0, 0, i] = c
+        idx[0, 0, i, :c] = np.random.default_rng(i).permutation(nkv)[:c]
+    idx[1, 2, 3, 1] = -4          # skipped
+    idx[1, 2, 4, 0] = nkv + 2     # skipped
+    cnt[1, 2, 4] = max(cnt[1, 2, 4], 1)
+    idx_clean = np.full_like(idx, -1)
+    cnt_clean = np.zeros_like(cnt)
+    for pos in np.ndindex(cnt.shape):
+        ent = [t for t in idx[pos][:cnt[pos]] if 0 <= t < nkv]
+        idx_clean[pos][:len(ent)] = ent
+        cnt_clean[pos] = len(ent)
+    scale = 1.0 / math.sqrt(D)
+    o_ref, lse_ref = oracle.attn_full(q, k, v, idx_clean, cnt_clean, 256, bkv, scale)
+    work = torch.arange(B * H * nq, dtype=torch.int32, device="cuda").flip(0)
+    o, lse = vsa.vsa_attn_fwd_worklist(dev(q), dev(k), dev(v), dev(idx), dev(cnt), 256, bkv, work, scale)
+    torch.cuda.synchronize()
+    check_rows(o, lse, np.arange(B * H * S), o_ref.transpose(0, 2, 1, 3).reshape(-1, D), lse_ref.reshape(-1), S, H,
+               f"256x{bkv} D={D} unsplit")
+
+
 def test_worklist_subset_writes_only_listed_tiles(vsa):
     B, H, S, D, bq, bkv = 1, 2, 512, 64, 64, 64
     say("forward work-list subset")

@@ -38,6 +38,7 @@ SYMBOLS = (
     "vsa_csr_transpose",
     "vsa_pair_q_tiles",
     "vsa_attn_fwd",
+    "vsa_attn_fwd_strided",
     "vsa_attn_fwd_noalloc",
     "vsa_attn_fwd_paired",
     "vsa_attn_fwd_coalesced",
@@ -81,6 +82,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vsa_build_worklist.restype = i32
     lib.vsa_attn_fwd.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p, p, p]
     lib.vsa_attn_fwd.restype = i32
+    lib.vsa_attn_fwd_strided.argtypes = [p, p, p, ctypes.POINTER(ctypes.c_int64), p, p, p, i32, i32, i32, i32, i32,
+                                         i32, i32, f32, p, p, p]
+    lib.vsa_attn_fwd_strided.restype = i32
     lib.vsa_attn_fwd_noalloc.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p, p, p]
     lib.vsa_attn_fwd_noalloc.restype = i32
     lib.vsa_attn_fwd_worklist.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p, i32, p,
@@ -122,7 +126,9 @@ def _stream_ptr(stream, device) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int, views: bool = False) -> None:
+    """Checks a device tensor argument; ``views``: a strided view whose last
+    dimension is contiguous is accepted."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
@@ -131,13 +137,16 @@ def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
-    if not t.is_contiguous():
+    if views:
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name} must have a contiguous last dimension")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
 
-def _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse):
+def _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse, views=False):
     for name, t in (("q", q), ("k", k), ("v", v)):
-        _dev(t, name, torch.bfloat16, 4)
+        _dev(t, name, torch.bfloat16, 4, views)
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v must share the shape [B, S, H, D]")
     B, S, H, D = q.shape
@@ -178,13 +187,36 @@ def vsa_attn_fwd(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale=N
 
     Builds the count-sorted work list internally, then runs the fused
     kernel. ``scale`` defaults to 1/sqrt(D). ``kv_valid`` (int32
-    [S/block_kv], optional): valid leading keys of each KV tile.
+    [S/block_kv], optional): valid leading keys of each KV tile. q, k, v
+    that are strided views (last dimension contiguous) go through
+    vsa_attn_fwd_strided.
     """
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        return vsa_attn_fwd_strided(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale, o, lse, stream,
+                                    kv_valid)
     B, S, H, D, o, lse = _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     rc = load_library().vsa_attn_fwd(
         q.data_ptr(), k.data_ptr(), v.data_ptr(), kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(),
+        _valid_ptr(kv_valid, S, block_kv, q.device), B, S, H, D,
+        kv_block_idx.shape[3], block_q, block_kv, float(scale), o.data_ptr(), lse.data_ptr(),
+        _stream_ptr(stream, q.device))
+    _check(rc)
+    return o, lse
+
+
+def vsa_attn_fwd_strided(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale=None, o=None, lse=None,
+                         stream=None, kv_valid=None):
+    """vsa_attn_fwd reading q, k, v in place through their strides (each a
+    [B, S, H, D] view with a contiguous last dimension, e.g. slices of a
+    packed QKV projection); returns (o, lse)."""
+    B, S, H, D, o, lse = _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse, views=True)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    strides = (ctypes.c_int64 * 9)(*[t.stride(i) for t in (q, k, v) for i in range(3)])
+    rc = load_library().vsa_attn_fwd_strided(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), strides, kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(),
         _valid_ptr(kv_valid, S, block_kv, q.device), B, S, H, D,
         kv_block_idx.shape[3], block_q, block_kv, float(scale), o.data_ptr(), lse.data_ptr(),
         _stream_ptr(stream, q.device))

@@ -63,8 +63,7 @@ __global__ __launch_bounds__(512) void vsa_fwd_2t_kernel(FwdParams prm) {
     const int h = bh % prm.H;
     const int b = bh / prm.H;
     const int S = prm.S;
-    const int64_t tok_stride = (int64_t)prm.H * D;
-    const int tok_bytes = (int)(tok_stride * 2);
+    const int64_t tok_stride = (int64_t)prm.H * D;  // o is contiguous
     const int32_t* irow = prm.idx + (int64_t)item * prm.ld;
     const int ldc = prm.ld < kIdxCap2t ? prm.ld : kIdxCap2t;
     int n = prm.cnt[item];
@@ -77,18 +76,19 @@ __global__ __launch_bounds__(512) void vsa_fwd_2t_kernel(FwdParams prm) {
 
     E e;
     e.init(smem, lane, prm.scale_log2);
-    e.load_q(prm.q + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D);
+    e.load_q(prm.q + (int64_t)b * prm.qs[0] + (int64_t)(q0 + l32) * prm.qs[1] + (int64_t)h * prm.qs[2]);
 
     int* lidx = (int*)(smem + 2 * GROUP_LDS);
     for (int i = tid; i < ldc; i += 512) lidx[i] = stage_entry<PARTIAL>(irow[i], nkv, BKV, prm.kv_valid);
     e.q_ready();
 
     auto valid = [&](int t) { return t >= 0 && t < nkv; };
-    const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
-    const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
-    const F fetch(smem, wave & 3, lane, tok_bytes);
-    auto tile_at = [&](const char* base, int t) {
-        return uniform_ptr(base + (int64_t)(valid(t) ? t : 0) * BKV * tok_bytes);
+    const char* kbase = (const char*)(prm.k + (int64_t)b * prm.ks[0] + (int64_t)h * prm.ks[2]);
+    const char* vbase = (const char*)(prm.v + (int64_t)b * prm.vs[0] + (int64_t)h * prm.vs[2]);
+    const int kt_bytes = (int)(prm.ks[1] * 2), vt_bytes = (int)(prm.vs[1] * 2);  // K and V row strides
+    const F fetch(smem, wave & 3, lane, kt_bytes, vt_bytes);
+    auto tile_at = [&](const char* base, int row_bytes, int t) {
+        return uniform_ptr(base + (int64_t)(valid(t) ? t : 0) * BKV * row_bytes);
     };
     // buffers of group g
     auto kbuf = [](int g) { return g * GROUP_LDS; };
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(512) void vsa_fwd_2t_kernel(FwdParams prm) {
     // tile index is read from the CSR row in global memory, since the staged
     // copy is not visible to every wave before the barrier
     if (ng > 0)
-        fetch.all(kbuf(grp), tile_at(kbase, __builtin_amdgcn_readfirstlane(irow[grp ? N0 : 0])), tok_bytes, kLayoutK);
+        fetch.all(kbuf(grp), tile_at(kbase, kt_bytes, __builtin_amdgcn_readfirstlane(irow[grp ? N0 : 0])), kt_bytes, kLayoutK);
     wait_global_loads();
     lds_barrier();
 
@@ -116,15 +116,15 @@ __global__ __launch_bounds__(512) void vsa_fwd_2t_kernel(FwdParams prm) {
     // has the slack for its loads.
     auto k_loads = [&](int g, int kj) {  // BPW hooks: K_kj of group g, if it exists
         const bool dk = kj < (g ? N1 : N0);
-        const char* kt = dk ? tile_at(kbase, tile_of(g, kj)) : nullptr;
+        const char* kt = dk ? tile_at(kbase, kt_bytes, tile_of(g, kj)) : nullptr;
         const int kd = kbuf(g);
-        return [=, &fetch](int i) { if (dk) fetch.block(kd, kt, tok_bytes, kLayoutK, i); };
+        return [=, &fetch](int i) { if (dk) fetch.block(kd, kt, kt_bytes, kLayoutK, i); };
     };
     auto v_loads = [&](int g, int vj) {  // BPW hooks: V_vj of group g, if it exists
         const bool dv = vj >= 0 && vj < (g ? N1 : N0);
-        const char* vt = dv ? tile_at(vbase, tile_of(g, vj)) : nullptr;
+        const char* vt = dv ? tile_at(vbase, vt_bytes, tile_of(g, vj)) : nullptr;
         const int vd = vbuf(g);
-        return [=, &fetch](int i) { if (dv) fetch.block(vd, vt, tok_bytes, kLayoutV, i); };
+        return [=, &fetch](int i) { if (dv) fetch.block(vd, vt, vt_bytes, kLayoutV, i); };
     };
     auto issue = [](const auto& hooks) {
 #pragma unroll

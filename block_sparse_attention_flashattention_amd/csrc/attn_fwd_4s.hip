@@ -59,8 +59,7 @@ __global__ __launch_bounds__(512) void vsa_fwd_4s_kernel(FwdParams prm) {
     const int h = bh % prm.H;
     const int b = bh / prm.H;
     const int S = prm.S;
-    const int64_t tok_stride = (int64_t)prm.H * D;
-    const int tok_bytes = (int)(tok_stride * 2);
+    const int64_t tok_stride = (int64_t)prm.H * D;  // o is contiguous
     // The count, the CSR row and Q are fetched at once; the row is read up
     // to its allocated length ld, so it does not wait for the count.
     const int32_t* irow = prm.idx + (int64_t)item * prm.ld;
@@ -81,7 +80,7 @@ __global__ __launch_bounds__(512) void vsa_fwd_4s_kernel(FwdParams prm) {
 
     E e;
     e.init(smem, lane, prm.scale_log2);
-    e.load_q(prm.q + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D);
+    e.load_q(prm.q + (int64_t)b * prm.qs[0] + (int64_t)(q0 + l32) * prm.qs[1] + (int64_t)h * prm.qs[2]);
 
     int* lidx = (int*)(smem + NSTREAM * STREAM_LDS);
     for (int i = tid; i < ldc; i += 512) lidx[i] = stage_entry<PARTIAL>(irow[i], nkv, block_kv, prm.kv_valid);
@@ -96,36 +95,37 @@ __global__ __launch_bounds__(512) void vsa_fwd_4s_kernel(FwdParams prm) {
                        ((first + j) % R) * SUB;
         return nv < 0 ? 0 : (nv > SUB ? SUB : nv);
     };
-    const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
-    const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    const char* kbase = (const char*)(prm.k + (int64_t)b * prm.ks[0] + (int64_t)h * prm.ks[2]);
+    const char* vbase = (const char*)(prm.v + (int64_t)b * prm.vs[0] + (int64_t)h * prm.vs[2]);
+    const int kt_bytes = (int)(prm.ks[1] * 2), vt_bytes = (int)(prm.vs[1] * 2);  // K and V row strides
     using F = TileFetch<SUB, D, 2>;
     const int fw = rb;  // this wave's index among the waves fetching its stream's tiles
-    const F fetch(smem, fw, lane, tok_bytes);
+    const F fetch(smem, fw, lane, kt_bytes, vt_bytes);
     // sub-tile j of this stream in CSR tile t; out-of-range tiles load tile 0
     // and contribute nothing
-    auto sub_ptr = [&](const char* base, int t, int j) {
+    auto sub_ptr = [&](const char* base, int row_bytes, int t, int j) {
         const int64_t row0 = (int64_t)(valid(t) ? t : 0) * block_kv + ((first + j) % R) * SUB;
-        return uniform_ptr(base + row0 * tok_bytes);
+        return uniform_ptr(base + row0 * row_bytes);
     };
-    auto tile_ptr = [&](const char* base, int j) { return sub_ptr(base, tile_of(j), j); };
+    auto tile_ptr = [&](const char* base, int row_bytes, int j) { return sub_ptr(base, row_bytes, tile_of(j), j); };
     const int sbase = st * STREAM_LDS;
     auto kbuf = [&](int j) { return sbase + (j & 1) * G::TILE; };
     auto vbuf = [&](int j) { return sbase + (2 + (j & 1)) * G::TILE; };
     // The loads of M_j (K_{j+1} if it exists, then V_j) are spread over the
     // MFMA phase, one 1 KB block per hook.
     auto loads = [&](int j) {
-        const char* kt = tile_ptr(kbase, j + 1);
-        const char* vt = tile_ptr(vbase, j);
+        const char* kt = tile_ptr(kbase, kt_bytes, j + 1);
+        const char* vt = tile_ptr(vbase, vt_bytes, j);
         const int kd = kbuf(j + 1), vd = vbuf(j);
         return [=, &fetch](int i) {
-            if (i < F::BPW) fetch.block(kd, kt, tok_bytes, false, i);
-            else fetch.block(vd, vt, tok_bytes, true, i - F::BPW);
+            if (i < F::BPW) fetch.block(kd, kt, kt_bytes, false, i);
+            else fetch.block(vd, vt, vt_bytes, true, i - F::BPW);
         };
     };
     auto v_loads = [&](int j) {
-        const char* vt = tile_ptr(vbase, j);
+        const char* vt = tile_ptr(vbase, vt_bytes, j);
         const int vd = vbuf(j);
-        return [=, &fetch](int i) { fetch.block(vd, vt, tok_bytes, true, i); };
+        return [=, &fetch](int i) { fetch.block(vd, vt, vt_bytes, true, i); };
     };
     auto pv = [&](int j) { e.template mfma_phase<true, false>(vbuf(j), 0); };
     auto softmax = [&](int j) {
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(512) void vsa_fwd_4s_kernel(FwdParams prm) {
     // barrier then publishes both it and the staged row.
     if (ng > 0) {
         const int t0 = __builtin_amdgcn_readfirstlane(irow[first / R]);
-        fetch.all(kbuf(0), sub_ptr(kbase, t0, 0), tok_bytes, false);
+        fetch.all(kbuf(0), sub_ptr(kbase, kt_bytes, t0, 0), kt_bytes, false);
     }
     wait_global_loads();
     bar();

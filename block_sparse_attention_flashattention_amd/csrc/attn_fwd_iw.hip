@@ -63,8 +63,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_fwd_iw_kernel(FwdParams prm) {
     const int h = bh % prm.H;
     const int b = bh / prm.H;
     const int S = prm.S;
-    const int64_t tok_stride = (int64_t)prm.H * D;
-    const int tok_bytes = (int)(tok_stride * 2);
+    const int64_t tok_stride = (int64_t)prm.H * D;  // o is contiguous
     // the count, the CSR row, Q and the first K sub-tile are fetched at once
     const int32_t* irow = prm.idx + (int64_t)item * prm.ld + part;
     const int ldp = prm.ld > part ? (prm.ld - part + SP - 1) / SP : 0;  // this part's slots of the row
@@ -78,23 +77,24 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_fwd_iw_kernel(FwdParams prm) {
     const int R = block_kv / SUB;  // sub-tiles per CSR tile
     const int q0 = p * BQ + wave * 32;
     auto valid = [&](int t) { return t >= 0 && t < nkv; };
-    const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
-    const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
-    const F fetch(smem, wave, lane, tok_bytes);
+    const char* kbase = (const char*)(prm.k + (int64_t)b * prm.ks[0] + (int64_t)h * prm.ks[2]);
+    const char* vbase = (const char*)(prm.v + (int64_t)b * prm.vs[0] + (int64_t)h * prm.vs[2]);
+    const int kt_bytes = (int)(prm.ks[1] * 2), vt_bytes = (int)(prm.vs[1] * 2);  // K and V row strides
+    const F fetch(smem, wave, lane, kt_bytes, vt_bytes);
     // sub-tile r of CSR tile t; out-of-range tiles load tile 0 and contribute nothing
-    auto sub_ptr = [&](const char* base, int t, int r) {
-        return uniform_ptr(base + ((int64_t)(valid(t) ? t : 0) * block_kv + r * SUB) * tok_bytes);
+    auto sub_ptr = [&](const char* base, int row_bytes, int t, int r) {
+        return uniform_ptr(base + ((int64_t)(valid(t) ? t : 0) * block_kv + r * SUB) * row_bytes);
     };
 
     E e;
     e.init(smem, lane, prm.scale_log2);
-    e.load_q(prm.q + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D);
+    e.load_q(prm.q + (int64_t)b * prm.qs[0] + (int64_t)(q0 + l32) * prm.qs[1] + (int64_t)h * prm.qs[2]);
 
     int* lidx = (int*)(smem + 4 * G::TILE);
     for (int i = tid; i < ldc; i += BQ * 2)
         lidx[i] = stage_entry<PARTIAL>(irow[(int64_t)i * SP], nkv, block_kv, prm.kv_valid);
     e.q_ready();
-    fetch.all(0, sub_ptr(kbase, first_tile, 0), tok_bytes, kLayoutK);
+    fetch.all(0, sub_ptr(kbase, kt_bytes, first_tile, 0), kt_bytes, kLayoutK);
     n = n < 0 ? 0 : (n > prm.ld ? prm.ld : n);
     n = n > part ? (n - part + SP - 1) / SP : 0;  // this part's entries
     n = n > ldc ? ldc : n;
@@ -103,7 +103,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_fwd_iw_kernel(FwdParams prm) {
     lds_barrier();
 
     auto entry = [&](int j) { return __builtin_amdgcn_readfirstlane(lidx[j / R]); };
-    auto src = [&](const char* base, int j) { return sub_ptr(base, entry_tile<PARTIAL>(entry(j)), j % R); };
+    auto src = [&](const char* base, int row_bytes, int j) {
+        return sub_ptr(base, row_bytes, entry_tile<PARTIAL>(entry(j)), j % R);
+    };
     auto keys = [&](int j) {
         const int nv = entry_keys<PARTIAL>(entry(j), block_kv) - (j % R) * SUB;
         return nv < 0 ? 0 : (nv > SUB ? SUB : nv);
@@ -112,14 +114,14 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_fwd_iw_kernel(FwdParams prm) {
     auto vbuf = [](int j) { return (2 + (j & 1)) * G::TILE; };
     // loads of step j: K_{j+1} (if dk) in hooks 0..BPW-1, V_j in hooks BPW..2*BPW-1
     auto loads = [&](int j, bool dk) {
-        const char* kt = dk ? src(kbase, j + 1) : nullptr;
-        const char* vt = src(vbase, j);
+        const char* kt = dk ? src(kbase, kt_bytes, j + 1) : nullptr;
+        const char* vt = src(vbase, vt_bytes, j);
         const int kd = kbuf(j + 1), vd = vbuf(j);
         return [=, &fetch](int i) {
             if (i < F::BPW) {
-                if (dk) fetch.block(kd, kt, tok_bytes, kLayoutK, i);
+                if (dk) fetch.block(kd, kt, kt_bytes, kLayoutK, i);
             } else {
-                fetch.block(vd, vt, tok_bytes, kLayoutV, i - F::BPW);
+                fetch.block(vd, vt, vt_bytes, kLayoutV, i - F::BPW);
             }
         };
     };

@@ -61,8 +61,7 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     const int h = bh % prm.H;
     const int b = bh / prm.H;
     const int S = prm.S;
-    const int64_t tok_stride = (int64_t)prm.H * D;
-    const int tok_bytes = (int)(tok_stride * 2);
+    const int64_t tok_stride = (int64_t)prm.H * D;  // o is contiguous
     // The count, the CSR row, Q and the first K tile are all fetched at once
     // (none of these loads waits for another; the row is read up to its
     // allocated length ld, so it does not need the count first).
@@ -76,18 +75,19 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     const int nkv = prm.nkv;
     const int q0 = p * BQ + wave * 32;
     auto valid = [&](int t) { return t >= 0 && t < nkv; };
-    const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
-    const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    const char* kbase = (const char*)(prm.k + (int64_t)b * prm.ks[0] + (int64_t)h * prm.ks[2]);
+    const char* vbase = (const char*)(prm.v + (int64_t)b * prm.vs[0] + (int64_t)h * prm.vs[2]);
+    const int kt_bytes = (int)(prm.ks[1] * 2), vt_bytes = (int)(prm.vs[1] * 2);  // K and V row strides
     using F = TileFetch<BKV, D, 4>;  // a tile is fetched by the four waves of one group
-    const F fetch(smem, wave & 3, lane, tok_bytes);
+    const F fetch(smem, wave & 3, lane, kt_bytes, vt_bytes);
     // out-of-range entries load tile 0 and contribute nothing
-    auto tile_at = [&](const char* base, int t) {
-        return uniform_ptr(base + (int64_t)(valid(t) ? t : 0) * BKV * tok_bytes);
+    auto tile_at = [&](const char* base, int row_bytes, int t) {
+        return uniform_ptr(base + (int64_t)(valid(t) ? t : 0) * BKV * row_bytes);
     };
 
     E e;
     e.init(smem, lane, prm.scale_log2);
-    e.load_q(prm.q + ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D);
+    e.load_q(prm.q + (int64_t)b * prm.qs[0] + (int64_t)(q0 + l32) * prm.qs[1] + (int64_t)h * prm.qs[2]);
 
     // Stage this tile's CSR row in LDS: list entries are then read with
     // uniform LDS loads, which do not wait on outstanding global loads.
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     for (int i = tid; i < ldc; i += 512) lidx[i] = stage_entry<PARTIAL>(irow[(int64_t)i * SP], nkv, BKV, prm.kv_valid);
     e.q_ready();
     // group 1 fetches K_0 (buffer 0 is free); an empty row fetches it too
-    if (grp == 1) fetch.all(0, tile_at(kbase, first_tile), tok_bytes, false);
+    if (grp == 1) fetch.all(0, tile_at(kbase, kt_bytes, first_tile), kt_bytes, false);
     n = n < 0 ? 0 : (n > prm.ld ? prm.ld : n);
     n = n > part ? (n - part + SP - 1) / SP : 0;  // this part's entries
     n = n > ldc ? ldc : n;
@@ -106,19 +106,19 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
     // the entry is out of range).
     auto tile_of = [&](int j) { return entry_tile<PARTIAL>(__builtin_amdgcn_readfirstlane(lidx[j])); };
     auto keys_of = [&](int j) { return entry_keys<PARTIAL>(__builtin_amdgcn_readfirstlane(lidx[j]), BKV); };
-    auto tile_ptr = [&](const char* base, int j) { return tile_at(base, tile_of(j)); };
+    auto tile_ptr = [&](const char* base, int row_bytes, int j) { return tile_at(base, row_bytes, tile_of(j)); };
     // LDS byte offsets of the K and V buffers used for list entry j
     auto kbuf = [](int j) { return (j & 1) * G::TILE; };
     auto vbuf = [](int j) { return (2 + (j & 1)) * G::TILE; };
     // Tile loads are spread over a phase (one 1 KB block per hook) so that
     // the eight waves' loads do not queue up at the start of the phase.
     auto v_loads = [&](int j) {
-        const char* tile = tile_ptr(vbase, j);
-        return [=, &fetch](int i) { fetch.block(vbuf(j), tile, tok_bytes, true, i); };
+        const char* tile = tile_ptr(vbase, vt_bytes, j);
+        return [=, &fetch](int i) { fetch.block(vbuf(j), tile, vt_bytes, true, i); };
     };
     auto k_loads = [&](int j) {
-        const char* tile = tile_ptr(kbase, j);
-        return [=, &fetch](int i) { fetch.block(kbuf(j), tile, tok_bytes, false, i); };
+        const char* tile = tile_ptr(kbase, kt_bytes, j);
+        return [=, &fetch](int i) { fetch.block(kbuf(j), tile, kt_bytes, false, i); };
     };
     auto pv = [&](int j) { e.template mfma_phase<true, false>(vbuf(j), 0); };
     // softmax of list entry j, masking a partial tile's missing keys first
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(512) void vsa_fwd_pp_kernel(FwdParams prm) {
         lds_barrier();
     } else {
         if (n > 0) {
-            if (n > 1) fetch.all(kbuf(1), tile_ptr(kbase, 1), tok_bytes, false);
+            if (n > 1) fetch.all(kbuf(1), tile_ptr(kbase, kt_bytes, 1), kt_bytes, false);
             lds_barrier();
             e.template mfma_phase<false, true>(0, kbuf(0));                                    // M_0
             wait_global_loads();

@@ -71,7 +71,6 @@ vsa::FwdParams make_params(const void* q, const void* k, const void* v, const in
                            const int32_t* kv_valid, int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim,
                            int32_t idx_ld, int32_t block_q, int32_t block_kv, float scale, const int32_t* work,
                            int32_t n_work, void* o, float* lse) {
-    (void)head_dim;
     vsa::FwdParams p;
     p.q = (const uint16_t*)q;
     p.k = (const uint16_t*)k;
@@ -94,7 +93,40 @@ vsa::FwdParams make_params(const void* q, const void* k, const void* v, const in
     p.splits = 1;
     p.ws_counter = nullptr;
     p.ws_partial = nullptr;
+    // contiguous [B, S, H, D]
+    const int64_t hs = head_dim, ts = (int64_t)heads * head_dim, bs = (int64_t)seqlen * ts;
+    for (int64_t* x : {p.qs, p.ks, p.vs}) {
+        x[0] = bs;
+        x[1] = ts;
+        x[2] = hs;
+    }
     return p;
+}
+
+// Strides of vsa_attn_fwd_strided (q, k, v: batch, token, head, in elements):
+// every row must start on a 16-byte boundary, a row stride must fit the
+// kernels' 32-bit row offsets, and rows of one tensor must not overlap.
+int32_t check_strides(const int64_t* s, int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim) {
+    VSA_REQUIRE(s, VSA_ERR_INVALID_ARG, "null stride array");
+    const char* name[3] = {"q", "k", "v"};
+    for (int t = 0; t < 3; ++t) {
+        const int64_t bs = s[3 * t], ts = s[3 * t + 1], hs = s[3 * t + 2];
+        VSA_REQUIRE(bs >= 0 && ts >= 0 && hs >= 0, VSA_ERR_INVALID_ARG, "%s strides must be >= 0", name[t]);
+        VSA_REQUIRE(bs % 8 == 0 && ts % 8 == 0 && hs % 8 == 0, VSA_ERR_INVALID_ARG,
+                    "%s strides (%lld, %lld, %lld) must be multiples of 8 elements (16 bytes)", name[t],
+                    (long long)bs, (long long)ts, (long long)hs);
+        VSA_REQUIRE(ts <= ((int64_t)1 << 24), VSA_ERR_UNSUPPORTED, "%s token stride %lld exceeds 2^24", name[t],
+                    (long long)ts);
+        // rows (b, r, h) are distinct and their head_dim elements do not overlap:
+        // heads of a token side by side, tokens beyond the heads, batches beyond the tokens
+        VSA_REQUIRE(heads == 1 || hs >= head_dim, VSA_ERR_INVALID_ARG, "%s head stride %lld below head_dim %d",
+                    name[t], (long long)hs, head_dim);
+        VSA_REQUIRE(seqlen == 1 || ts >= (int64_t)(heads - 1) * hs + head_dim, VSA_ERR_INVALID_ARG,
+                    "%s token stride %lld overlaps its heads", name[t], (long long)ts);
+        VSA_REQUIRE(batch == 1 || bs >= (int64_t)(seqlen - 1) * ts + (int64_t)(heads - 1) * hs + head_dim,
+                    VSA_ERR_INVALID_ARG, "%s batch stride %lld overlaps its tokens", name[t], (long long)bs);
+    }
+    return VSA_OK;
 }
 
 // Library-owned device buffers, one per (device, stream, purpose), grown on
@@ -235,13 +267,20 @@ int32_t scratch_for_device(hipStream_t stream, char** out) {
 int32_t run_fwd(const void* q, const void* k, const void* v, const int32_t* idx, const int32_t* cnt,
                 const int32_t* kv_valid, int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim,
                 int32_t idx_ld, int32_t block_q, int32_t block_kv, float scale, void* o, float* lse, hipStream_t st,
-                int32_t* work, int splits, int32_t* counters, float* partial) {
+                int32_t* work, int splits, int32_t* counters, float* partial, const int64_t* strides = nullptr) {
     const int32_t n_items = batch * heads * (seqlen / block_q);
     // one segment per (batch, head): heads stay contiguous in the list
     hipError_t e = vsa::launch_build_worklist(cnt, n_items, seqlen / block_q, idx_ld, work, st);
     if (e != hipSuccess) return hip_fail(e, "build_worklist launch");
     vsa::FwdParams p = make_params(q, k, v, idx, cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld, block_q,
                                    block_kv, scale, work, n_items, o, lse);
+    if (strides) {
+        for (int i = 0; i < 3; ++i) {
+            p.qs[i] = strides[i];
+            p.ks[i] = strides[3 + i];
+            p.vs[i] = strides[6 + i];
+        }
+    }
     if (splits > 1) {
         p.splits = splits;
         p.ws_counter = counters;
@@ -257,7 +296,7 @@ int32_t run_fwd(const void* q, const void* k, const void* v, const int32_t* idx,
 
 extern "C" {
 
-int32_t vsa_abi_version(void) { return 9; }
+int32_t vsa_abi_version(void) { return 10; }
 
 int32_t vsa_set_max_splits(int32_t max_splits) {
     const int32_t m = max_splits >= 4 ? 4 : (max_splits >= 2 ? 2 : 1);
@@ -345,10 +384,22 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
                      const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch, int32_t seqlen,
                      int32_t heads, int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv, float scale,
                      void* o, float* lse, void* stream) {
+    return vsa_attn_fwd_strided(q, k, v, nullptr, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads,
+                                head_dim, idx_ld, block_q, block_kv, scale, o, lse, stream);
+}
+
+int32_t vsa_attn_fwd_strided(const void* q, const void* k, const void* v, const int64_t* qkv_strides,
+                             const int32_t* kv_block_idx, const int32_t* kv_block_cnt, const int32_t* kv_valid,
+                             int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim, int32_t idx_ld,
+                             int32_t block_q, int32_t block_kv, float scale, void* o, float* lse, void* stream) {
     g_last_error[0] = 0;
     int32_t rc = check_fwd(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld,
                            block_q, block_kv, scale, o, lse);
     if (rc != VSA_OK) return rc;
+    if (qkv_strides) {
+        rc = check_strides(qkv_strides, batch, seqlen, heads, head_dim);
+        if (rc != VSA_OK) return rc;
+    }
     VSA_REQUIRE(idx_ld <= vsa::kWorklistMaxCnt, VSA_ERR_UNSUPPORTED,
                 "idx_ld %d exceeds the work-list sort limit %d; use vsa_attn_fwd_worklist", idx_ld,
                 vsa::kWorklistMaxCnt);
@@ -365,7 +416,7 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
     }
     return run_fwd(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld, block_q,
                    block_kv, scale, o, lse, st, work, f.splits, (int32_t*)ws,
-                   ws ? (float*)((char*)ws + f.counter_bytes) : nullptr);
+                   ws ? (float*)((char*)ws + f.counter_bytes) : nullptr, qkv_strides);
 }
 
 int32_t vsa_attn_fwd_noalloc(const void* q, const void* k, const void* v, const int32_t* kv_block_idx,

@@ -22,6 +22,10 @@ struct FwdParams {
     const int32_t* kv_valid; // [nkv] valid leading keys per KV tile; null = all tiles full
     uint16_t* o;             // [B, S, H, D] bf16 bits
     float* lse;              // [B, H, S]
+    // element strides of q, k and v between batches, tokens and heads (row r
+    // of head h in batch b starts at b*s[0] + r*s[1] + h*s[2]; head_dim is
+    // contiguous); o and lse are contiguous
+    int64_t qs[3], ks[3], vs[3];
     int32_t n_work;
     int32_t n_items;         // B * H * nq
     int32_t S, H, nq, nkv, ld;

@@ -102,7 +102,7 @@ struct TileGeom {
 // waves that fetch it (wave gw takes blocks [gw*BPW, (gw+1)*BPW)); each block
 // is one direct-to-LDS 16-byte-per-lane load from a uniform row base plus a
 // 32-bit per-lane offset. `tile` points at row 0 of the tile for this head;
-// consecutive rows are tok_bytes apart.
+// consecutive rows are tok_bytes apart (v_tok_bytes for the V layout).
 //
 // A lane's offset within its block depends on the block only through the
 // swizzle, which repeats every KP blocks for K and is the same for every
@@ -122,8 +122,9 @@ struct TileFetch {
     uint32_t doff[KP];
     uint32_t voff;
 
-    __device__ __forceinline__ TileFetch(const char* smem, int gw_, int lane, int tok_bytes)
+    __device__ __forceinline__ TileFetch(const char* smem, int gw_, int lane, int tok_bytes, int v_tok_bytes = -1)
         : gw(gw_), lds0(lds_addr(smem)) {
+        if (v_tok_bytes < 0) v_tok_bytes = tok_bytes;
         const int rl = lane / G::NC, pos = lane % G::NC;
 #pragma unroll
         for (int k = 0; k < KP; ++k) {
@@ -131,7 +132,7 @@ struct TileFetch {
             koff[k] = (uint32_t)(rl * tok_bytes + ((pos ^ swz_k<G::NC>(row)) << 4));
             doff[k] = (uint32_t)(rl * tok_bytes + ((pos ^ swz_d<G::NC>(row)) << 4));
         }
-        voff = (uint32_t)(rl * tok_bytes + ((pos ^ swz_v<G::NC>(rl)) << 4));
+        voff = (uint32_t)(rl * v_tok_bytes + ((pos ^ swz_v<G::NC>(rl)) << 4));
     }
     // block i (0 <= i < BPW) of this wave's share; dst is the tile buffer's
     // byte offset from the base; layout is a TileLayout

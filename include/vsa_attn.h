@@ -17,7 +17,8 @@
  *
  * Conventions shared by all entry points
  * --------------------------------------
- *  - Tensors are dense, row-major and contiguous:
+ *  - Tensors are dense, row-major and contiguous (vsa_attn_fwd_strided also
+ *    takes q, k, v as strided views):
  *      q, k, v, o      [batch, seqlen, heads, head_dim]  bf16 (raw 16-bit)
  *      lse             [batch, heads, seqlen]            fp32
  *      kv_block_idx    [batch, heads, seqlen/block_q, idx_ld]  int32
@@ -206,6 +207,32 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
                      const int32_t* kv_block_cnt, const int32_t* kv_valid, int32_t batch, int32_t seqlen,
                      int32_t heads, int32_t head_dim, int32_t idx_ld, int32_t block_q, int32_t block_kv,
                      float scale, void* o, float* lse, void* stream);
+
+/*
+ * vsa_attn_fwd_strided -- vsa_attn_fwd with q, k and v given as strided views
+ * (for example the three slices of a packed QKV projection), read in place.
+ *
+ * Source: FastVideo page, arm_fa4 / the _flash_attn_fwd call, whose q, k, v
+ * are tensors with their own strides.
+ *
+ *   qkv_strides: host array of 9 int64, the strides in elements of q, k and
+ *   v in that order, each as (batch, token, head): row r of head h in batch
+ *   b of q starts at element b*s[0] + r*s[1] + h*s[2], and its head_dim
+ *   elements are contiguous. NULL = contiguous [B, S, H, D] (vsa_attn_fwd).
+ *   Every stride is >= 0 and a multiple of 8 elements (rows start on 16-byte
+ *   boundaries, as q, k, v must); the token stride is at most 2^24 elements;
+ *   the rows of one tensor do not overlap (head stride >= head_dim, token
+ *   stride >= (heads-1)*head stride + head_dim, and the same for the batch
+ *   stride); VSA_ERR_INVALID_ARG / VSA_ERR_UNSUPPORTED otherwise. q, k and v
+ *   may overlap one another (they are only read); o and lse stay contiguous
+ *   and must not overlap the inputs. Otherwise as vsa_attn_fwd: same kernels,
+ *   work list, splits and buffers, and results bitwise equal to vsa_attn_fwd
+ *   on contiguous copies of the same values.
+ */
+int32_t vsa_attn_fwd_strided(const void* q, const void* k, const void* v, const int64_t* qkv_strides,
+                             const int32_t* kv_block_idx, const int32_t* kv_block_cnt, const int32_t* kv_valid,
+                             int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim, int32_t idx_ld,
+                             int32_t block_q, int32_t block_kv, float scale, void* o, float* lse, void* stream);
 
 /*
  * vsa_attn_fwd_noalloc -- vsa_attn_fwd for callers that cannot allocate

@@ -36,7 +36,7 @@ def test_header_declares_the_binding_symbols():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.vsa_abi_version() == 9
+    assert lib.vsa_abi_version() == 10
 
 
 def test_set_max_splits_rounds_and_returns_previous(lib):
@@ -112,6 +112,39 @@ def test_attn_fwd_noalloc_rejects_before_touching_the_device(lib, kw, status, ne
                                   args["scale"], args["o"], args["lse"], None)
     assert rc == status
     assert needle in lib.vsa_last_error().decode()
+
+
+def _packed(B=1, S=1024, H=2, D=128):
+    """Strides (elements) of q, k, v sliced from a packed [B, S, 3, H, D] projection."""
+    one = [S * 3 * H * D, 3 * H * D, D]
+    return one * 3
+
+
+@pytest.mark.parametrize("edit,status,needle", [
+    ({1: 3 * 2 * 128 + 4}, -1, "multiples of 8"),       # q token stride not a 16-byte multiple
+    ({5: 64}, -1, "below head_dim"),                      # k heads overlap
+    ({7: 128}, -1, "overlaps its heads"),                 # v tokens overlap its two heads
+    ({0: 1024}, -1, "overlaps its tokens"),               # q batches overlap (needs B > 1)
+    ({4: -8}, -1, ">= 0"),
+    ({4: (1 << 24) + 8}, -2, "2^24"),
+])
+def test_attn_fwd_strided_rejects_bad_strides(lib, edit, status, needle):
+    strides = _packed()
+    for i, x in edit.items():
+        strides[i] = x
+    arr = (ctypes.c_int64 * 9)(*strides)
+    B = 2 if 0 in edit else 1
+    rc = lib.vsa_attn_fwd_strided(A, A, A, arr, A, A, None, B, 1024, 2, 128, 16, 128, 64, 0.1, A, A, None)
+    assert rc == status
+    assert needle in lib.vsa_last_error().decode()
+
+
+def test_attn_fwd_strided_checks_the_common_arguments_first(lib):
+    arr = (ctypes.c_int64 * 9)(*_packed())
+    rc = lib.vsa_attn_fwd_strided(A, A, A, arr, A, A, None, 1, 1000, 2, 128, 16, 128, 64, 0.1, A, A, None)
+    assert rc == -1 and "divisible" in lib.vsa_last_error().decode()
+    rc = lib.vsa_attn_fwd_strided(A + 8, A, A, arr, A, A, None, 1, 1024, 2, 128, 16, 128, 64, 0.1, A, A, None)
+    assert rc == -1 and "aligned" in lib.vsa_last_error().decode()
 
 
 def test_attn_fwd_worklist_rejects_bad_work_list(lib):

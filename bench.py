@@ -404,15 +404,23 @@ def time_configs(vsa, W, head_wl, head_tile, args, stream, q0, k0, v0, q0_cpu, k
         pairs = selected_pairs(idx, cnt, bq, bkv)
         tflops = 4.0 * D * pairs / (ms * 1e-3) / 1e12
         run_bq = coalesced_rows(vsa, idx, cnt, bq, S) if scope == "coalesce" else bq
+        kname = kernel_name(run_bq, bkv, D, n_items=B * H * (S // run_bq))
+        # HBM bytes per launch from the committed counters (a workload with the
+        # headline's mask shares the headline workload's profiles)
+        traffic = read_traffic(default_traffic_path(kname, wl.name, run_bq, bkv), kname)
+        if traffic is None and same_mask:
+            traffic = read_traffic(default_traffic_path(kname, head_wl.name, run_bq, bkv), kname)
         entry = {
             "workload": wl.name, "tile": f"{bq}x{bkv}",
             "runs_as": f"{run_bq}x{bkv}",
             "timed_scope": "vsa_attn_fwd_coalesced" if scope == "coalesce" else "vsa_attn_fwd_worklist",
-            "kernel": kernel_name(run_bq, bkv, D, n_items=B * H * (S // run_bq)),
+            "kernel": kname,
             "kernel_ms": round(ms, 4), "tflops": round(tflops, 2),
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
             "selected_pairs": pairs,
             "vs_headline_kernel": round(tflops / head_kernel_tflops, 4),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": kname},
         }
         if not args.no_cpu_baseline and args.config_cpu_seconds > 0:
             _, sample = cpu_baseline(wl, q_cpu, k_cpu, v_cpu, idx, cnt, bq, bkv, args.config_cpu_seconds)

@@ -59,7 +59,9 @@ def bench_common(workload, tile, extra=()):
 def passes(workload, tile, extra=()):
     """(name, rocprofv3 options, bench flags) of the four passes, in order."""
     common = bench_common(workload, tile, extra)
-    short = [*common, "--no-backward", "--steps", "2", "--warmup", "1"]
+    # the counter passes keep the bench's backward leg, whose kernels get a
+    # section of their own (a few launches of each)
+    short = [*common, "--steps", "2", "--warmup", "1"]
     return [
         ("trace", ["--kernel-trace", "--stats"], [*common, "--steps", "20", "--warmup", "5"]),
         ("fetch", ["--pmc", "FETCH_SIZE"], short),
@@ -226,6 +228,35 @@ def traffic(fetch_csv, write_csv, copy_fetch_dir, copy_write_dir, kernel):
             "fetch_scale": round(fs, 4), "write_scale": round(ws, 4)}
 
 
+def backward_kernel_lines(out, d, ours):
+    """Per backward kernel of the counter passes (if they ran the backward
+    leg): trace average, executed MFMA flops and their rate, MFMA busy, LDS
+    conflicts and HBM bytes per launch; no lines if the counters hold none."""
+    sq_csv = os.path.join(d, "sq", "run_counter_collection.csv")
+    rows = []
+    for r in sorted((r for r in ours if r["short"].startswith(("vsa_bwd_", "bwd_prep"))), key=lambda r: r["short"]):
+        kname = _norm(r["short"])
+        if not counter_values(sq_csv, "SQ_INSTS_VALU_MFMA_MOPS_BF16", kname) and not r["short"].startswith("bwd_prep"):
+            continue
+        try:
+            sq = sq_summary(sq_csv, kname)
+            tr = traffic(os.path.join(d, "fetch", "run_counter_collection.csv"),
+                         os.path.join(d, "write", "run_counter_collection.csv"),
+                         os.path.join(out, "copy_fetch"), os.path.join(out, "copy_write"), kname)
+        except ValueError:
+            continue
+        rate = sq["mfma_flops"] / (r["avg_us"] * 1e-6) / 1e12
+        rows.append(f"| {r['short']} | {r['avg_us']:.1f} | {sq['mfma_flops']:.4g} | {rate:.1f} | "
+                    f"{100 * sq['mfma_busy']:.1f}% | {100 * sq['lds_conflict_rate']:.2f}% | "
+                    f"{tr['fetch_bytes'] / 1e9:.3f} + {tr['write_bytes'] / 1e9:.3f} |")
+    if not rows:
+        return []
+    return ["", "Backward kernels (trace average; counters per working dispatch, reduced as below; the flops are "
+            "what the MFMAs executed, S and dP included in both kernels):", "",
+            "| kernel | avg us | MFMA flop | executed TFLOP/s | MFMA busy | LDS conflicts | HBM GB (fetch + write) |",
+            "|---|---|---|---|---|---|---|", *rows]
+
+
 def summarize(out, tag, workload, tile, extra=(), profiles=PROFILES, write_files=True):
     """Write profiles/<kernel>_<tile>_<workload>.md and the traffic JSON from
     out/tag (collect) and out/copy_{fetch,write} (collect-copy); returns the
@@ -280,6 +311,7 @@ def summarize(out, tag, workload, tile, extra=(), profiles=PROFILES, write_files
         lines += ["", "## Backward leg of the traced run (`vsa_csr_transpose` + `vsa_attn_bwd`)", "",
                   f"{bw['ms'] * 1e3:.1f} us per backward = {bw['tflops']:.1f} TFLOP/s at {bw['flops_per_pair']} "
                   f"flops per selected pair ({bw['pct_of_bf16_peak']:.1f}% of peak)."]
+        lines += backward_kernel_lines(out, d, ours)
     lines += ["", "## Counters (mean per working dispatch of this kernel)", "",
               f"- MFMA: SQ_INSTS_VALU_MFMA_MOPS_BF16 x {FLOPS_PER_MOP} = {sq['mfma_flops']:.4g} flop "
               f"(sparse-aware algorithmic {flops:.4g}"

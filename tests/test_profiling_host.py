@@ -99,3 +99,46 @@ def test_pass_commands_keep_counters_apart_from_tracing():
         assert "--no-configs" in flags and "--no-cpu-baseline" in flags
         cmd = P.command("/tmp/x", opts, flags)
         assert cmd[cmd.index("--") + 1] == sys.executable  # the program itself follows "--"
+
+
+def _write_counters(path, kernel, values):
+    """A rocprofv3 counter CSV with one row per (dispatch, counter)."""
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    head = ("Correlation_Id,Dispatch_Id,Agent_Id,Queue_Id,Process_Id,Thread_Id,Grid_Size,Kernel_Id,Kernel_Name,"
+            "Workgroup_Size,LDS_Block_Size,Scratch_Size,VGPR_Count,Accum_VGPR_Count,SGPR_Count,Counter_Name,"
+            "Counter_Value,Start_Timestamp,End_Timestamp")
+    with open(path, "w") as f:
+        f.write(head + "\n")
+        for disp, per in enumerate(values, start=1):
+            for counter, val in per.items():
+                f.write(f'{disp},{disp},Agent 1,1,1,1,1,1,"void vsa::(anonymous namespace)::{kernel}(vsa::BwdParams)",'
+                        f"256,0,0,4,0,16,{counter},{val},0,1\n")
+
+
+def test_backward_kernel_section_from_counters(tmp_path):
+    """The backward section reduces each backward kernel's counters like the
+    forward's: executed MFMA flops = MOPS x 512, their rate over the trace
+    average, busy fraction and HBM bytes scaled by the copy."""
+    import shutil
+    out = str(tmp_path)
+    shutil.copytree(os.path.join(DATA, "copy_fetch"), os.path.join(out, "copy_fetch"))
+    shutil.copytree(os.path.join(DATA, "copy_write"), os.path.join(out, "copy_write"))
+    d = os.path.join(out, "t")
+    k = "vsa_bwd_dq_kernel<256, 128, false, false>"
+    sq = {"SQ_VALU_MFMA_BUSY_CYCLES": 4.0e8, "SQ_INSTS_VALU_MFMA_MOPS_BF16": 4.0e9, "SQ_LDS_BANK_CONFLICT": 0.0,
+          "SQ_ACTIVE_INST_LDS": 1.0e7, "SQ_BUSY_CYCLES": 1.0e7, "SQ_WAVES": 24576.0, "GRBM_GUI_ACTIVE": 8.0e6}
+    _write_counters(os.path.join(d, "sq", "run_counter_collection.csv"), k, [sq, sq])
+    _write_counters(os.path.join(d, "fetch", "run_counter_collection.csv"), k, [{"FETCH_SIZE": 1.0e6}] * 2)
+    _write_counters(os.path.join(d, "write", "run_counter_collection.csv"), k, [{"WRITE_SIZE": 2.0e5}] * 2)
+    ours = [{"name": f"void vsa::{k}(vsa::BwdParams)", "short": k, "calls": 2, "avg_us": 2000.0, "min_us": 1.0,
+             "max_us": 3.0}]
+    lines = P.backward_kernel_lines(out, d, ours)
+    row = [ln for ln in lines if ln.startswith(f"| {k} |")]
+    assert len(row) == 1
+    flops = 4.0e9 * 512
+    busy = 4.0e8 / (8.0e6 / 8 * 1024)
+    assert f"| {flops:.4g} | {flops / 2000e-6 / 1e12:.1f} | {100 * busy:.1f}% |" in row[0]
+    fs = P.copy_scale(os.path.join(out, "copy_fetch"), "FETCH_SIZE")
+    assert f"{1.0e6 * 1024 * fs / 1e9:.3f} + " in row[0]
+    # no backward dispatches in the counters: no section
+    assert P.backward_kernel_lines(out, os.path.join(DATA, "c2"), ours) == []

@@ -77,6 +77,10 @@ def parse_args():
                          "work list and splits lists when there are few work items (all of it is timed)")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the backward leg (dQ, dK, dV of the same workload; reported beside the headline)")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="skip the MFMA rate measurement reported beside the roofline (what the matrix cores "
+                         "sustain on random bf16 operands, alone and beside softmax-shaped vector work, and on "
+                         "zero operands; vsa_measure_mfma, about 0.3 s after the timed steps)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter calibration)")
     return ap.parse_args()
@@ -321,8 +325,29 @@ def main():
         ok = ok and all(c.get("parity", {}).get("pass", True) for c in result["configs"].values()
                         if isinstance(c, dict) and "kernel" in c)
 
+    if not args.no_mfma_ceiling:
+        result["mfma_ceiling"] = mfma_ceiling(vsa, kernel_tflops)
+
     print(json.dumps(result), flush=True)
     return 0 if ok else 1
+
+
+def mfma_ceiling(vsa, kernel_tflops, iters=200000):
+    """What the matrix cores sustain on v_mfma_f32_32x32x16_bf16 when every
+    compute unit runs it back to back (vsa_measure_mfma): on operands drawn
+    like Q, K, V (bf16 N(0,1)), on the same beside softmax-shaped vector work
+    on the other wave of each SIMD (the forward kernels' phase split), and on
+    zero operands. The published peak assumes the top clock, which a long run
+    keeps only on zero operands; the fractions say how far the kernel is from
+    what this part sustains on data like its own."""
+    vsa.vsa_measure_mfma("random", iters=iters // 4)  # out of the idle clock state
+    out = {"unit": "TFLOP/s", "mfma": "v_mfma_f32_32x32x16_bf16", "iters": iters}
+    for mode in ("random", "pingpong_softmax", "zero"):
+        r = vsa.vsa_measure_mfma(mode, iters=iters)
+        out[mode] = {"value": round(r["tflops"], 1), "clock_mhz": round(r["clock_mhz"])}
+    out["kernel_frac_of_random"] = round(kernel_tflops / out["random"]["value"], 4)
+    out["kernel_frac_of_pingpong_softmax"] = round(kernel_tflops / out["pingpong_softmax"]["value"], 4)
+    return out
 
 
 # The other workloads and tile shapes timed beside the headline (kernel

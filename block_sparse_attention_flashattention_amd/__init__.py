@@ -46,6 +46,7 @@ SYMBOLS = (
     "vsa_attn_bwd",
     "vsa_release",
     "vsa_set_max_splits",
+    "vsa_measure_mfma",
 )
 
 
@@ -107,6 +108,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vsa_release.restype = None
     lib.vsa_set_max_splits.argtypes = [i32]
     lib.vsa_set_max_splits.restype = i32
+    lib.vsa_measure_mfma.argtypes = [i32, i32, ctypes.POINTER(f32), ctypes.POINTER(f32), p]
+    lib.vsa_measure_mfma.restype = i32
     _lib = lib
     return lib
 
@@ -468,3 +471,18 @@ def vsa_set_max_splits(max_splits: int) -> int:
     """Most parts (1, 2 or 4) a work item's list may be split into when a
     launch has too few items; returns the previous value."""
     return int(load_library().vsa_set_max_splits(int(max_splits)))
+
+
+MFMA_MODES = {"random": 0, "zero": 1, "pingpong_softmax": 2}
+
+
+def vsa_measure_mfma(mode: str = "random", iters: int = 200000, stream=None, device=None) -> dict:
+    """What the matrix cores sustain on v_mfma_f32_32x32x16_bf16 with the
+    given operands ("random": bf16 N(0,1), "zero", or "pingpong_softmax":
+    random operands beside softmax-shaped vector work on the other wave of
+    each SIMD): {"tflops": ..., "clock_mhz": ...}. Synchronises."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    t, c = ctypes.c_float(0.0), ctypes.c_float(0.0)
+    _check(load_library().vsa_measure_mfma(MFMA_MODES[mode], int(iters), ctypes.byref(t), ctypes.byref(c),
+                                           _stream_ptr(stream, dev)))
+    return {"tflops": float(t.value), "clock_mhz": float(c.value)}

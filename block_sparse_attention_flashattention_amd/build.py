@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvsa_attn.so")
 SOURCES = ["attn_fwd.hip", "attn_fwd_pp.hip", "attn_fwd_iw.hip", "attn_fwd_2t.hip", "attn_fwd_2s.hip", "attn_fwd_4s.hip", "attn_bwd.hip", "frontend.hip",
-           "capi.hip"]
+           "measure.hip", "capi.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -294,13 +294,29 @@ int32_t run_fwd(const void* q, const void* k, const void* v, const int32_t* idx,
 
 }  // namespace
 
+namespace vsa {
+// Sustained MFMA rate and shader clock on random / zero operands, or beside
+// softmax-shaped vector work (mode 0 / 1 / 2; measure.hip). Synchronises.
+hipError_t measure_mfma(int mode, int iters, hipStream_t stream, float* tflops, float* clock_mhz);
+}  // namespace vsa
+
 extern "C" {
 
-int32_t vsa_abi_version(void) { return 10; }
+int32_t vsa_abi_version(void) { return 11; }
 
 int32_t vsa_set_max_splits(int32_t max_splits) {
     const int32_t m = max_splits >= 4 ? 4 : (max_splits >= 2 ? 2 : 1);
     return g_max_splits.exchange(m);
+}
+
+int32_t vsa_measure_mfma(int32_t mode, int32_t iters, float* tflops, float* clock_mhz, void* stream) {
+    g_last_error[0] = 0;
+    VSA_REQUIRE(tflops && clock_mhz, VSA_ERR_INVALID_ARG, "null pointer");
+    VSA_REQUIRE(mode >= 0 && mode <= 2, VSA_ERR_INVALID_ARG, "mode must be 0, 1 or 2");
+    VSA_REQUIRE(iters >= 1 && iters <= 2000000, VSA_ERR_INVALID_ARG, "iters must be in [1, 2000000]");
+    const hipError_t e = vsa::measure_mfma(mode, iters, (hipStream_t)stream, tflops, clock_mhz);
+    if (e != hipSuccess) return hip_fail(e, "MFMA rate measurement");
+    return VSA_OK;
 }
 
 const char* vsa_status_string(int32_t status) {

@@ -51,8 +51,9 @@ COPY_BYTES = 1 << 30   # bench.py --copy-calibration
 
 def bench_common(workload, tile, extra=()):
     """bench.py flags shared by every pass: the workload, no CPU leg, no other
-    configs, no clock sampling or flush launches, a short pre-warm."""
-    return ["--no-cpu-baseline", "--no-configs", "--clock-seconds", "0", "--flush-steps", "0",
+    configs, no MFMA rate measurement, no clock sampling or flush launches, a
+    short pre-warm."""
+    return ["--no-cpu-baseline", "--no-configs", "--no-mfma-ceiling", "--clock-seconds", "0", "--flush-steps", "0",
             "--prewarm-seconds", "0.3", "--workload", workload, "--tile", tile, *extra]
 
 

@@ -397,6 +397,30 @@ void vsa_release(void);
  */
 int32_t vsa_set_max_splits(int32_t max_splits);
 
+/*
+ * vsa_measure_mfma -- a measurement aid for the roofline the forward is
+ * reported against, not part of the attention operation: what this device's
+ * matrix cores sustain on v_mfma_f32_32x32x16_bf16 when every compute unit
+ * runs it back to back. Under such a load the shader clock is set by the
+ * power the chip draws, which depends on the operand bits, so the published
+ * dense peak (top clock) is not what bf16 data drawn like Q, K and V gets.
+ *   mode 0: operands drawn from N(0,1) in bf16, two MFMA waves per SIMD;
+ *   mode 1: all-zero operands, otherwise as mode 0;
+ *   mode 2: per SIMD one wave issues the MFMAs of mode 0 while the other
+ *           issues softmax-shaped vector work (fma, exp2, add, max, bf16
+ *           pack; about 4.5 instructions per MFMA of its partner), the phase
+ *           split of the forward kernels.
+ * iters (1 .. 2,000,000) is the number of 8-MFMA iterations per MFMA wave
+ * (200,000 take about 60 ms). Host outputs: *tflops = MFMA flops / elapsed
+ * time between HIP events around the launch; *clock_mhz = the mean over
+ * waves of shader cycles (s_memtime) per real time (s_memrealtime, 100 MHz).
+ * Unlike every other entry point this call synchronises: it allocates and
+ * frees two small device buffers and waits for the kernel on `stream`.
+ * Returns VSA_OK, VSA_ERR_INVALID_ARG (null output, mode or iters out of
+ * range) or VSA_ERR_HIP.
+ */
+int32_t vsa_measure_mfma(int32_t mode, int32_t iters, float* tflops, float* clock_mhz, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

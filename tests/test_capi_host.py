@@ -36,7 +36,7 @@ def test_header_declares_the_binding_symbols():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.vsa_abi_version() == 10
+    assert lib.vsa_abi_version() == 11
 
 
 def test_set_max_splits_rounds_and_returns_previous(lib):
@@ -275,3 +275,14 @@ def test_attn_fwd_coalesced_validation(lib):
     assert f(A, A, A, A, A, None, 1, 1024, 2, 96, 16, 128, 64, 0.1, A, A, None) == -2  # head_dim
     assert f(A, A, A, A, A, None, 1, 1024, 2, 128, 9000, 128, 64, 0.1, A, A, None) in (-1, -2)  # ld too large
     assert f(A, A, A, A, A, None, 1, 1024, 2, 128, 16, 128, 64, 0.0, A, A, None) == -1  # scale
+
+
+def test_measure_mfma_rejects_invalid_arguments(lib):
+    t, c = ctypes.c_float(0.0), ctypes.c_float(0.0)
+    assert lib.vsa_measure_mfma(3, 100, ctypes.byref(t), ctypes.byref(c), None) == -1
+    assert "mode" in lib.vsa_last_error().decode()
+    assert lib.vsa_measure_mfma(0, 0, ctypes.byref(t), ctypes.byref(c), None) == -1
+    assert "iters" in lib.vsa_last_error().decode()
+    assert lib.vsa_measure_mfma(0, 2000001, ctypes.byref(t), ctypes.byref(c), None) == -1
+    assert lib.vsa_measure_mfma(0, 100, None, ctypes.byref(c), None) == -1
+    assert "null" in lib.vsa_last_error().decode()

@@ -155,7 +155,7 @@ hipError_t measure_mfma(int mode, int iters, hipStream_t stream, float* tflops, 
     hipEvent_t e0 = nullptr, e1 = nullptr;
     hipError_t e = hipMalloc((void**)&frag, host.size() * 2);
     if (e == hipSuccess) e = hipMalloc((void**)&out, (size_t)waves * 3 * sizeof(unsigned long long));
-    if (e == hipSuccess) e = hipMemcpyAsync(frag, host.data(), host.size() * 2, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipMemcpy(frag, host.data(), host.size() * 2, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipEventCreate(&e0);
     if (e == hipSuccess) e = hipEventCreate(&e1);
     if (e == hipSuccess) e = hipEventRecord(e0, stream);

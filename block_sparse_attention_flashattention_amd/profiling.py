@@ -154,8 +154,12 @@ def kernel_stats(path):
     return rows
 
 
+MEASUREMENT_KERNELS = ("mfma_rate_kernel", "mfma_pingpong_kernel")  # vsa_measure_mfma, not the attention path
+
+
 def is_ours(row):
-    return "at::" not in row["name"] and not row["name"].startswith("__amd")
+    name = row["name"]
+    return "at::" not in name and not name.startswith("__amd") and not any(k in name for k in MEASUREMENT_KERNELS)
 
 
 def counter_values(path, counter, kernel):

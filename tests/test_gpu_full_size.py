@@ -50,7 +50,7 @@ def vsa():
 
 def dev(x):
     if isinstance(x, np.ndarray):
-        x = torch.from_numpy(np.ascontiguousarray(x))
+        x = torch.from_numpy(np.array(x, copy=True, order="C"))  # a writable copy (cached oracle arrays are read-only)
     return x.contiguous().to("cuda")
 
 

@@ -38,6 +38,8 @@ def test_short_names_and_stats():
     assert len(main) == 1 and main[0]["calls"] == 313
     assert main[0]["avg_us"] == pytest.approx(1115.216619808)
     assert not any(P.is_ours(r) for r in stats if "at::native" in r["name"] or r["name"].startswith("__amd"))
+    assert not P.is_ours({"name": "void vsa::(anonymous namespace)::mfma_rate_kernel<false>(...)"})
+    assert P.is_ours({"name": "void vsa::(anonymous namespace)::vsa_fwd_pp_kernel<128, 128, false>(vsa::FwdParams)"})
 
 
 def test_sq_reduction_by_hand():

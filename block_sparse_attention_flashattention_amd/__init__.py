@@ -161,7 +161,7 @@ def _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse, vi
     if tuple(kv_block_idx.shape[:3]) != (B, H, nq) or tuple(kv_block_cnt.shape) != (B, H, nq):
         raise ValueError(f"kv_block_idx must be [B,H,{nq},ld] and kv_block_cnt [B,H,{nq}]")
     if o is None:
-        o = torch.empty_like(q)
+        o = torch.empty((B, S, H, D), dtype=torch.bfloat16, device=q.device)  # contiguous, whatever q's strides
     if lse is None:
         lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     _dev(o, "o", torch.bfloat16, 4)
@@ -446,7 +446,7 @@ def vsa_attn_bwd(q, k, v, o, lse, dout, kv_block_idx, kv_block_cnt, q_block_idx,
     grads = []
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         if t is None:
-            t = torch.empty_like(q)
+            t = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
         _dev(t, name, torch.bfloat16, 4)
         if t.shape != q.shape:
             raise ValueError(f"{name} must match q")

@@ -220,12 +220,16 @@ int32_t vsa_attn_fwd(const void* q, const void* k, const void* v, const int32_t*
  *   b of q starts at element b*s[0] + r*s[1] + h*s[2], and its head_dim
  *   elements are contiguous. NULL = contiguous [B, S, H, D] (vsa_attn_fwd).
  *   Every stride is >= 0 and a multiple of 8 elements (rows start on 16-byte
- *   boundaries, as q, k, v must); the token stride is at most 2^24 elements;
- *   the rows of one tensor do not overlap (head stride >= head_dim, token
- *   stride >= (heads-1)*head stride + head_dim, and the same for the batch
- *   stride); VSA_ERR_INVALID_ARG / VSA_ERR_UNSUPPORTED otherwise. q, k and v
- *   may overlap one another (they are only read); o and lse stay contiguous
- *   and must not overlap the inputs. Otherwise as vsa_attn_fwd: same kernels,
+ *   boundaries, as q, k, v must) and the token stride is at most 2^24
+ *   elements; VSA_ERR_INVALID_ARG / VSA_ERR_UNSUPPORTED otherwise. The
+ *   strides need no particular order and rows may coincide, since q, k and
+ *   v are only read: a [batch, heads, seqlen, head_dim] buffer viewed as
+ *   [B, S, H, D] (token stride head_dim, head stride seqlen*head_dim), and
+ *   k, v broadcast over the heads (head stride 0: every query head attends
+ *   to the same keys and values, as in multi-query attention) are both
+ *   valid. Every row addressed must lie inside the caller's allocation. q, k
+ *   and v may overlap one another; o and lse stay contiguous and must not
+ *   overlap the inputs. Otherwise as vsa_attn_fwd: same kernels,
  *   work list, splits and buffers, and results bitwise equal to vsa_attn_fwd
  *   on contiguous copies of the same values.
  */

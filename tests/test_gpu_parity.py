@@ -245,9 +245,15 @@ def test_every_tile_shape_all_rows(vsa, bq, bkv, D):
 def _strided_views(q, k, v, layout):
     """q, k, v [B, S, H, D] (device) copied into the buffers of ``layout`` and
     returned as views of them: packed [B,S,3,H,D] projection, heads
-    interleaved [B,S,H,3,D], q alone with k, v from a packed [B,S,2,H,D], or
-    each tensor in a token-padded buffer [B,S+64,H,D] at token 32."""
+    interleaved [B,S,H,3,D], q alone with k, v from a packed [B,S,2,H,D],
+    [B,H,S,D] buffers seen as [B,S,H,D], k and v of head 0 broadcast over the
+    heads (head stride 0), or each tensor in a token-padded buffer
+    [B,S+64,H,D] at token 32."""
     B, S, H, D = q.shape
+    if layout == "bhsd":
+        return tuple(t.transpose(1, 2).contiguous().transpose(1, 2) for t in (q, k, v))
+    if layout == "kv_broadcast":
+        return q, k[:, :, :1].expand(B, S, H, D), v[:, :, :1].expand(B, S, H, D)
     if layout == "qkv_packed":
         buf = torch.stack((q, k, v), dim=2).contiguous()
         return buf[:, :, 0], buf[:, :, 1], buf[:, :, 2]
@@ -266,16 +272,19 @@ def _strided_views(q, k, v, layout):
 
 
 STRIDED = [(bq, bkv, D, "qkv_packed") for bq, bkv, D in SHAPES] + \
-          [(256, 128, 128, lay) for lay in ("heads_interleaved", "kv_packed", "token_padded")] + \
-          [(64, 64, 64, lay) for lay in ("heads_interleaved", "kv_packed", "token_padded")]
+          [(bq, bkv, D, "bhsd") for bq, bkv, D in SHAPES] + \
+          [(256, 128, 128, lay) for lay in ("heads_interleaved", "kv_packed", "token_padded", "kv_broadcast")] + \
+          [(64, 64, 64, lay) for lay in ("heads_interleaved", "kv_packed", "token_padded", "kv_broadcast")] + \
+          [(128, 64, 128, "kv_broadcast")]
 
 
 @pytest.mark.parametrize("bq,bkv,D,layout", STRIDED, ids=[f"{a}x{b}_d{c}_{l}" for a, b, c, l in STRIDED])
 def test_strided_views_bitwise_equal_to_contiguous(vsa, bq, bkv, D, layout):
     """q, k, v read in place through their strides (vsa_attn_fwd_strided, the
     route vsa_attn_fwd takes for views) give the result of the contiguous
-    call bitwise, for every tile shape (splits included at these sizes); the
-    packed 256x128 case is also checked against the oracle on every row."""
+    call on copies of the same views bitwise, for every tile shape (splits
+    included at these sizes); the packed 256x128 case and a broadcast case
+    are also checked against the oracle on every row."""
     B, H, S = 2, 2, 1024
     say(f"strided views {layout} {bq}x{bkv} D={D}")
     q, k, v = W.qkv(B, S, H, D, seed=bq + bkv + D + 11)
@@ -285,13 +294,15 @@ def test_strided_views_bitwise_equal_to_contiguous(vsa, bq, bkv, D, layout):
     qd, kd, vd = dev(q), dev(k), dev(v)
     qs, ks, vs = _strided_views(qd, kd, vd, layout)
     assert not (qs.is_contiguous() and ks.is_contiguous() and vs.is_contiguous())
-    o1, l1 = _run_fwd(vsa, qd, kd, vd, dev(idx), dev(cnt), bq, bkv, scale)
+    qc, kc, vc = qs.contiguous(), ks.contiguous(), vs.contiguous()
+    o1, l1 = _run_fwd(vsa, qc, kc, vc, dev(idx), dev(cnt), bq, bkv, scale)
     o2, l2 = _run_fwd(vsa, qs, ks, vs, dev(idx), dev(cnt), bq, bkv, scale)
     assert torch.equal(o1, o2) and torch.equal(l1, l2), f"{layout} {bq}x{bkv}: strided result differs"
-    if (bq, bkv, D, layout) == (256, 128, 128, "qkv_packed"):
+    if (bq, bkv, D, layout) in ((256, 128, 128, "qkv_packed"), (128, 64, 128, "kv_broadcast")):
+        q, k, v = qc.cpu(), kc.cpu(), vc.cpu()
         o_ref, lse_ref = oracle.attn_full(q, k, v, idx, cnt, bq, bkv, scale)
         check_rows(o2, l2, np.arange(B * H * S), o_ref.transpose(0, 2, 1, 3).reshape(-1, D), lse_ref.reshape(-1), S,
-                   H, "strided packed 256x128")
+                   H, f"strided {layout} {bq}x{bkv}")
 
 
 @pytest.mark.parametrize("bq,bkv,D", SHAPES, ids=[f"{a}x{b}_d{c}" for a, b, c in SHAPES])

@@ -241,13 +241,16 @@ def test_backward_with_empty_tiles_dropped(vsa, tile):
         check(name, got.float().cpu().numpy(), ref, f"dropped {tile}")
 
 
-@pytest.mark.parametrize("bq,bkv", [(256, 128), (128, 64), (64, 64)])
-def test_maximum_list_stride_and_empty_head(vsa, bq, bkv):
+@pytest.mark.parametrize("bq,bkv,D", [(256, 128, 64), (128, 64, 64), (64, 64, 64), (256, 128, 128), (128, 128, 128),
+                                      (64, 128, 128)])
+def test_maximum_list_stride_and_empty_head(vsa, bq, bkv, D):
     """idx_ld = q_ld = 8191 (the largest accepted; the kernels stage whole
-    rows, and the backward then needs more than 64 KB of LDS), with every row
-    of head 1 empty: forward and backward against the oracle on all rows."""
-    B, H, S, D = 1, 2, 1024, 64
-    say(f"maximum list stride {bq}x{bkv}")
+    rows, and the backward then needs more than 64 KB of LDS; at D=128 the
+    256-row forward fills the whole 160 KB of a compute unit's LDS), with
+    every row of head 1 empty: forward and backward against the oracle on all
+    rows."""
+    B, H, S = 1, 2, 1024
+    say(f"maximum list stride {bq}x{bkv} D={D}")
     q, k, v = W.qkv(B, S, H, D, seed=bq + bkv + 3)
     do = W.qkv(B, S, H, D, seed=bq + bkv + 4)[0]
     nq, nkv = S // bq, S // bkv
@@ -274,7 +277,7 @@ def test_maximum_list_stride_and_empty_head(vsa, bq, bkv):
     torch.cuda.synchronize()
     rq, rk, rv = oracle.bwd_full(q, k, v, do, idx_c, cnt, bq, bkv, scale)
     for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
-        check(name, got.float().cpu().numpy(), ref, f"max stride {bq}x{bkv}")
+        check(name, got.float().cpu().numpy(), ref, f"max stride {bq}x{bkv} D={D}")
         assert np.all(got.float().cpu().numpy()[0, :, 1] == 0.0)
 
 

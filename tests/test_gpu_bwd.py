@@ -49,7 +49,7 @@ def vsa():
 
 def dev(x):
     if isinstance(x, np.ndarray):
-        x = torch.from_numpy(np.ascontiguousarray(x))
+        x = torch.from_numpy(np.array(x, copy=True, order="C"))  # writable (oracle arrays may be read-only)
     return x.contiguous().to("cuda")
 
 

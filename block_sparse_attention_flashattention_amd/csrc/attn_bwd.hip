@@ -13,6 +13,8 @@
 // the page's FA4 block_sparsity.py backward) and accumulates in registers;
 // dQ comes from one workgroup per query tile that walks the forward list, as
 // the split-dQ form of the FlashAttention backward does. Both recompute P.
+// The dQ kernel runs first: it also forms D and LSE * log2(e) for its rows
+// (it holds dO already), which the dK/dV kernel then reads.
 //
 // Operand layouts follow the forward (wave_engine.h): 32x32x16 bf16 MFMA,
 // lane l / register r of a result holds row 8*(r/4) + 4*(l/32) + r%4 and
@@ -42,43 +44,6 @@ constexpr int dq_stage_bytes() { return 2 * dq_sub<BQ>() * D * 2; }
 constexpr int kDkvQs = 32;  // query rows per dK/dV step
 template <int D>
 constexpr int dkv_stage_bytes() { return 2 * kDkvQs * D * 2 + 2 * kDkvQs * 4; }
-
-// ---------------------------------------------------------------- preprocess
-// aux[0][(b*H + h)*S + i] = D_i = dO_i . O_i;  aux[1][...] = LSE_i * log2(e)
-// (+inf for an empty row, so that exp2(s - lse2) = 0).
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-                                                       const float* __restrict__ lse, float* __restrict__ aux,
-                                                       int n_rows, int S, int H) {
-    constexpr int LPR = D / 8;     // lanes per token row (16 bytes each)
-    constexpr int RPW = 64 / LPR;  // rows per wave
-    const int lane = threadIdx.x & 63;
-    const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;  // (b*S + i)*H + h
-    float acc = 0.0f;
-    if (row < n_rows) {
-        const int64_t off = row * D + (lane % LPR) * 8;
-        const u32x4 a = *(const u32x4*)(o + off);
-        const u32x4 g = *(const u32x4*)(dout + off);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float a0 = __builtin_bit_cast(float, a[e] << 16), a1 = __builtin_bit_cast(float, a[e] & 0xffff0000u);
-            const float g0 = __builtin_bit_cast(float, g[e] << 16), g1 = __builtin_bit_cast(float, g[e] & 0xffff0000u);
-            acc = fmaf(a0, g0, acc);
-            acc = fmaf(a1, g1, acc);
-        }
-    }
-#pragma unroll
-    for (int w = LPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w);
-    if (row < n_rows && lane % LPR == 0) {
-        const int h = (int)(row % H);
-        const int64_t bi = row / H;  // b*S + i
-        const int64_t i = bi % S, b = bi / S;
-        const int64_t dst = (b * H + h) * S + i;
-        aux[dst] = acc;
-        const float l = lse[dst];
-        aux[(int64_t)n_rows + dst] = l == -__builtin_inff() ? __builtin_inff() : l * 1.4426950408889634f;
-    }
-}
 
 // Per-lane LDS offsets for the operand reads of one tile layout.
 template <int D>
@@ -219,8 +184,9 @@ __device__ __forceinline__ bool merge_parts(f32x16 (&acc)[NA], float* mine, cons
 }
 
 struct BwdParams {
-    const uint16_t *q, *k, *v, *dout;
-    const float* aux;         // [2][B*H*S]: D, then LSE*log2(e)
+    const uint16_t *q, *k, *v, *o, *dout;
+    const float* lse;         // forward LSE [B,H,S]
+    float* aux;               // [2][B*H*S]: D, then LSE*log2(e); written by the dQ kernel
     const int32_t* idx;       // forward CSR [B,H,nq,ld]
     const int32_t* cnt;
     const int32_t* qidx;      // Q-direction CSR [B,H,nkv,q_ld]
@@ -289,8 +255,26 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_bwd_dq_kernel(BwdParams prm) {
     load_rows<DC>(qreg, prm.q + qrow, hi);
     load_rows<DC>(doreg, prm.dout + qrow, hi);
     const int64_t arow = (int64_t)bh * S + q0 + l32;
-    const float dval = prm.aux[arow];
-    const float lse2 = prm.aux[(int64_t)prm.n_rows + arow];
+    // D_i = dO_i . O_i (this lane's half of the row, then both half-waves) and
+    // LSE_i * log2(e) (+inf for a row without keys, so that exp2(s - lse2) = 0);
+    // part 0 also writes both to aux for the dK/dV kernel, launched after this one
+    float dval, lse2;
+    {
+        bf16x8 oreg[DC];
+        load_rows<DC>(oreg, prm.o + qrow, hi);
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = fmaf((float)oreg[c][e], (float)doreg[c][e], acc);
+        dval = halfwave_sum(acc);
+        const float l = prm.lse[arow];
+        lse2 = l == -__builtin_inff() ? __builtin_inff() : l * 1.4426950408889634f;
+        if (part == 0 && hi == 0) {
+            prm.aux[arow] = dval;
+            prm.aux[(int64_t)prm.n_rows + arow] = lse2;
+        }
+    }
 
     int* lidx = (int*)(smem + 2 * STAGE);
     for (int i = tid; i < ldc; i += BQ * 2)
@@ -580,16 +564,6 @@ __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) 
     store_rows<DB>(prm.dv + krow, dv, 1.0f, hi);
 }
 
-template <int D>
-hipError_t launch_prep(const uint16_t* o, const uint16_t* dout, const float* lse, float* aux, int n_rows, int S, int H,
-                       hipStream_t stream) {
-    constexpr int RPW = 64 / (D / 8);
-    const int rows_per_block = 4 * RPW;
-    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((n_rows + rows_per_block - 1) / rows_per_block), dim3(256), 0, stream,
-                       o, dout, lse, aux, n_rows, S, H);
-    return hipGetLastError();
-}
-
 // Launch with `lds` bytes of dynamic LDS (allowing more than the default
 // limit once per kernel when needed).
 template <typename K>
@@ -656,6 +630,8 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.k = a.k;
     p.v = a.v;
     p.dout = a.dout;
+    p.o = a.o;
+    p.lse = a.lse;
     p.aux = a.aux;
     p.idx = a.idx;
     p.cnt = a.cnt;
@@ -686,18 +662,17 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.ws_counter_kv = a.ws_counter_kv;
     p.ws_q = a.ws_q;
     p.ws_kv = a.ws_kv;
-    hipError_t e = a.D == 128 ? launch_prep<128>(a.o, a.dout, a.lse, a.aux, p.n_rows, a.S, a.H, stream)
-                              : launch_prep<64>(a.o, a.dout, a.lse, a.aux, p.n_rows, a.S, a.H, stream);
-    if (e != hipSuccess) return e;
+    // the dQ kernel forms D and LSE*log2(e) for every row, which the dK/dV kernel reads
     const bool partial = a.kv_valid != nullptr;
+    hipError_t e;
     if (a.D == 128) {
-        e = partial ? launch_dkv_d<128, true>(p, stream) : launch_dkv_d<128, false>(p, stream);
+        e = partial ? launch_dq_d<128, true>(p, stream) : launch_dq_d<128, false>(p, stream);
         if (e != hipSuccess) return e;
-        return partial ? launch_dq_d<128, true>(p, stream) : launch_dq_d<128, false>(p, stream);
+        return partial ? launch_dkv_d<128, true>(p, stream) : launch_dkv_d<128, false>(p, stream);
     }
-    e = partial ? launch_dkv_d<64, true>(p, stream) : launch_dkv_d<64, false>(p, stream);
+    e = partial ? launch_dq_d<64, true>(p, stream) : launch_dq_d<64, false>(p, stream);
     if (e != hipSuccess) return e;
-    return partial ? launch_dq_d<64, true>(p, stream) : launch_dq_d<64, false>(p, stream);
+    return partial ? launch_dkv_d<64, true>(p, stream) : launch_dkv_d<64, false>(p, stream);
 }
 
 }  // namespace vsa

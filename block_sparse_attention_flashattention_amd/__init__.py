@@ -44,6 +44,7 @@ SYMBOLS = (
     "vsa_attn_fwd_coalesced",
     "vsa_attn_fwd_worklist",
     "vsa_attn_bwd",
+    "vsa_attn_bwd_strided",
     "vsa_release",
     "vsa_set_max_splits",
     "vsa_measure_mfma",
@@ -104,6 +105,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vsa_attn_bwd.argtypes = [p, p, p, p, p, p, p, p, i32, p, p, i32, p, i32, i32, i32, i32, i32, i32, f32, p, p,
                                  p, p]
     lib.vsa_attn_bwd.restype = i32
+    lib.vsa_attn_bwd_strided.argtypes = [p, p, p, p, p, p, ctypes.POINTER(ctypes.c_int64), p, p, i32, p, p, i32, p,
+                                         i32, i32, i32, i32, i32, i32, f32, p, p, p, p]
+    lib.vsa_attn_bwd_strided.restype = i32
     lib.vsa_release.argtypes = []
     lib.vsa_release.restype = None
     lib.vsa_set_max_splits.argtypes = [i32]
@@ -433,9 +437,29 @@ def vsa_attn_bwd(q, k, v, o, lse, dout, kv_block_idx, kv_block_cnt, q_block_idx,
     """Backward pass of vsa_attn_fwd; returns (dq, dk, dv), bf16 [B, S, H, D].
 
     ``o`` and ``lse`` are the forward's outputs; ``q_block_idx`` /
-    ``q_block_cnt`` the transposed CSR from ``vsa_csr_transpose``."""
-    B, S, H, D, o, lse = _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse)
-    _dev(dout, "dout", torch.bfloat16, 4)
+    ``q_block_cnt`` the transposed CSR from ``vsa_csr_transpose``. q, k, v
+    and dout that are strided views (last dimension contiguous) go through
+    vsa_attn_bwd_strided."""
+    if not all(t.is_contiguous() for t in (q, k, v, dout)):
+        return vsa_attn_bwd_strided(q, k, v, o, lse, dout, kv_block_idx, kv_block_cnt, q_block_idx, q_block_cnt,
+                                    block_q, block_kv, scale, dq, dk, dv, stream, kv_valid)
+    return _bwd(q, k, v, o, lse, dout, kv_block_idx, kv_block_cnt, q_block_idx, q_block_cnt, block_q, block_kv, scale,
+                dq, dk, dv, stream, kv_valid, views=False)
+
+
+def vsa_attn_bwd_strided(q, k, v, o, lse, dout, kv_block_idx, kv_block_cnt, q_block_idx, q_block_cnt, block_q,
+                         block_kv, scale=None, dq=None, dk=None, dv=None, stream=None, kv_valid=None):
+    """vsa_attn_bwd reading q, k, v and dout in place through their strides
+    (each a [B, S, H, D] view with a contiguous last dimension); o, lse and
+    the gradients are contiguous. Returns (dq, dk, dv)."""
+    return _bwd(q, k, v, o, lse, dout, kv_block_idx, kv_block_cnt, q_block_idx, q_block_cnt, block_q, block_kv, scale,
+                dq, dk, dv, stream, kv_valid, views=True)
+
+
+def _bwd(q, k, v, o, lse, dout, kv_block_idx, kv_block_cnt, q_block_idx, q_block_cnt, block_q, block_kv, scale, dq,
+         dk, dv, stream, kv_valid, views):
+    B, S, H, D, o, lse = _fwd_args(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, o, lse, views=views)
+    _dev(dout, "dout", torch.bfloat16, 4, views=views)
     if dout.shape != q.shape:
         raise ValueError("dout must match q")
     nkv = S // block_kv
@@ -453,12 +477,17 @@ def vsa_attn_bwd(q, k, v, o, lse, dout, kv_block_idx, kv_block_cnt, q_block_idx,
         grads.append(t)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    rc = load_library().vsa_attn_bwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-        kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(), kv_block_idx.shape[3], q_block_idx.data_ptr(),
-        q_block_cnt.data_ptr(), q_block_idx.shape[3], _valid_ptr(kv_valid, S, block_kv, q.device), B, S, H, D,
-        block_q, block_kv, float(scale), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
-        _stream_ptr(stream, q.device))
+    lib = load_library()
+    tail = (kv_block_idx.data_ptr(), kv_block_cnt.data_ptr(), kv_block_idx.shape[3], q_block_idx.data_ptr(),
+            q_block_cnt.data_ptr(), q_block_idx.shape[3], _valid_ptr(kv_valid, S, block_kv, q.device), B, S, H, D,
+            block_q, block_kv, float(scale), grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(),
+            _stream_ptr(stream, q.device))
+    head = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr())
+    if views:
+        strides = (ctypes.c_int64 * 12)(*[t.stride(i) for t in (q, k, v, dout) for i in range(3)])
+        rc = lib.vsa_attn_bwd_strided(*head, strides, *tail)
+    else:
+        rc = lib.vsa_attn_bwd(*head, *tail)
     _check(rc)
     return tuple(grads)
 

@@ -185,6 +185,11 @@ __device__ __forceinline__ bool merge_parts(f32x16 (&acc)[NA], float* mine, cons
 
 struct BwdParams {
     const uint16_t *q, *k, *v, *o, *dout;
+    // element strides between batches, tokens and heads of q, k, v and dout
+    // (row r of head h in batch b starts at b*s[0] + r*s[1] + h*s[2]); o, dq,
+    // dk, dv and the per-row terms are contiguous
+    int64_t qs[3], ks[3], vs[3], ds[3];
+    int32_t strided;  // any of them not the contiguous [B, S, H, D] layout
     const float* lse;         // forward LSE [B,H,S]
     float* aux;               // [2][B*H*S]: D, then LSE*log2(e); written by the dQ kernel
     const int32_t* idx;       // forward CSR [B,H,nq,ld]
@@ -237,8 +242,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_bwd_dq_kernel(BwdParams prm) {
     if (item < 0 || item >= prm.n_items_q) return;
     const int p = item % prm.nq, bh = item / prm.nq, h = bh % prm.H, b = bh / prm.H;
     const int S = prm.S, nkv = prm.nkv, block_kv = prm.block_kv;
-    const int64_t tok_stride = (int64_t)prm.H * D;
-    const int tok_bytes = (int)(tok_stride * 2);
+    const int64_t tok_stride = (int64_t)prm.H * D;  // o and dq are contiguous
     const int32_t* irow = prm.idx + (int64_t)item * prm.ld + part;
     const int ldp = prm.ld > part ? (prm.ld - part + SP - 1) / SP : 0;  // this part's slots of the row
     const int ldc = ldp < kIdxCapBwd ? ldp : kIdxCapBwd;
@@ -249,11 +253,13 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_bwd_dq_kernel(BwdParams prm) {
     const int R = block_kv / SUB;
     const int steps = n * R;
     const int q0 = p * BQ + wave * 32;
-    const int64_t qrow = ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D;
+    const int64_t qrow = ((int64_t)b * S + q0 + l32) * tok_stride + (int64_t)h * D;  // o, dq
+    const int64_t qin = (int64_t)b * prm.qs[0] + (int64_t)(q0 + l32) * prm.qs[1] + (int64_t)h * prm.qs[2];
+    const int64_t doin = (int64_t)b * prm.ds[0] + (int64_t)(q0 + l32) * prm.ds[1] + (int64_t)h * prm.ds[2];
 
     bf16x8 qreg[DC], doreg[DC];
-    load_rows<DC>(qreg, prm.q + qrow, hi);
-    load_rows<DC>(doreg, prm.dout + qrow, hi);
+    load_rows<DC>(qreg, prm.q + qin, hi);
+    load_rows<DC>(doreg, prm.dout + doin, hi);
     const int64_t arow = (int64_t)bh * S + q0 + l32;
     // D_i = dO_i . O_i (this lane's half of the row, then both half-waves) and
     // LSE_i * log2(e) (+inf for a row without keys, so that exp2(s - lse2) = 0);
@@ -290,19 +296,20 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_bwd_dq_kernel(BwdParams prm) {
     OO ko, vo;
     ko.template init<kLayoutD>(lane);
     vo.template init<kLayoutK>(lane);
-    const F fetch(smem, wave, lane, tok_bytes);
-    const char* kbase = (const char*)(prm.k + (int64_t)b * S * tok_stride + (int64_t)h * D);
-    const char* vbase = (const char*)(prm.v + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    const int kt_bytes = (int)(prm.ks[1] * 2), vt_bytes = (int)(prm.vs[1] * 2);  // K and V row strides
+    const F kfetch(smem, wave, lane, kt_bytes), vfetch(smem, wave, lane, vt_bytes);
+    const char* kbase = (const char*)(prm.k + (int64_t)b * prm.ks[0] + (int64_t)h * prm.ks[2]);
+    const char* vbase = (const char*)(prm.v + (int64_t)b * prm.vs[0] + (int64_t)h * prm.vs[2]);
     auto entry = [&](int j) { return __builtin_amdgcn_readfirstlane(lidx[j / R]); };
-    auto step_ptr = [&](const char* base, int j) {
+    auto step_ptr = [&](const char* base, int row_bytes, int j) {
         const int t = entry_tile<PARTIAL>(entry(j));
         const int64_t row0 = (int64_t)(t >= 0 && t < nkv ? t : 0) * block_kv + (j % R) * SUB;
-        return uniform_ptr(base + row0 * tok_bytes);
+        return uniform_ptr(base + row0 * row_bytes);
     };
     auto fetch_step = [&](int j) {
         const int st = (j & 1) * STAGE;
-        fetch.all(st, step_ptr(kbase, j), tok_bytes, kLayoutD);
-        fetch.all(st + G::TILE, step_ptr(vbase, j), tok_bytes, kLayoutK);
+        kfetch.all(st, step_ptr(kbase, kt_bytes, j), kt_bytes, kLayoutD);
+        vfetch.all(st + G::TILE, step_ptr(vbase, vt_bytes, j), vt_bytes, kLayoutK);
     };
 
     f32x16 dq[DB];
@@ -385,7 +392,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void vsa_bwd_dq_kernel(BwdParams prm) {
 // 32-row steps keep a 128-key workgroup within 256 registers per wave, so two
 // workgroups share a compute unit and each SIMD has a second wave whose MFMAs
 // can run while this one computes exponentials.
-template <int BKV, int D, bool PARTIAL, bool SPLIT>
+template <int BKV, int D, bool PARTIAL, bool SPLIT, bool STRIDED>
 __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) {
     constexpr int NW = BKV / 32;
     constexpr int QS = kDkvQs;  // query rows per step
@@ -408,8 +415,7 @@ __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) 
     if (item < 0 || item >= prm.n_items_kv) return;
     const int nt = item % prm.nkv, bh = item / prm.nkv, h = bh % prm.H, b = bh / prm.H;
     const int S = prm.S, nq = prm.nq, block_q = prm.block_q;
-    const int64_t tok_stride = (int64_t)prm.H * D;
-    const int tok_bytes = (int)(tok_stride * 2);
+    const int64_t tok_stride = (int64_t)prm.H * D;  // dk and dv are contiguous
     const int32_t* qrow_list = prm.qidx + (int64_t)item * prm.q_ld + part;
     const int ldp = prm.q_ld > part ? (prm.q_ld - part + SP - 1) / SP : 0;  // this part's slots of the row
     const int ldc = ldp < kIdxCapBwd ? ldp : kIdxCapBwd;
@@ -420,7 +426,13 @@ __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) 
     const int RQ = block_q / QS;
     const int steps = n * RQ;
     const int kv0 = nt * BKV + wave * 32;
-    const int64_t krow = ((int64_t)b * S + kv0 + l32) * tok_stride + (int64_t)h * D;
+    const int64_t krow = ((int64_t)b * S + kv0 + l32) * tok_stride + (int64_t)h * D;  // dk, dv
+    // (built apart for contiguous inputs, where Q and dO share one row stride
+    // and one set of tile-fetch offsets)
+    const int64_t kin =
+        STRIDED ? (int64_t)b * prm.ks[0] + (int64_t)(kv0 + l32) * prm.ks[1] + (int64_t)h * prm.ks[2] : krow;
+    const int64_t vin =
+        STRIDED ? (int64_t)b * prm.vs[0] + (int64_t)(kv0 + l32) * prm.vs[1] + (int64_t)h * prm.vs[2] : krow;
     // valid keys of this wave's column (partial tiles)
     int nv_tile = BKV;
     if constexpr (PARTIAL) {
@@ -430,8 +442,8 @@ __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) 
     const bool key_ok = wave * 32 + l32 < nv_tile;
 
     bf16x8 kreg[DC], vreg[DC];
-    load_rows<DC>(kreg, prm.k + krow, hi);
-    load_rows<DC>(vreg, prm.v + krow, hi);
+    load_rows<DC>(kreg, prm.k + kin, hi);
+    load_rows<DC>(vreg, prm.v + vin, hi);
 
     int* lq = (int*)(smem + 2 * STAGE);
     for (int i = tid; i < ldc; i += BKV * 2) {
@@ -447,9 +459,14 @@ __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) 
     // and the spill reload inside the step waited on the next step's tile loads
     CompactOffsets<D> qo;
     qo.template init<kLayoutD>(lane);
-    const F fetch(smem, wave, lane, tok_bytes);
-    const char* qbase = (const char*)(prm.q + (int64_t)b * S * tok_stride + (int64_t)h * D);
-    const char* dbase = (const char*)(prm.dout + (int64_t)b * S * tok_stride + (int64_t)h * D);
+    // Q and dO row strides
+    const int qt_bytes = STRIDED ? (int)(prm.qs[1] * 2) : (int)(tok_stride * 2);
+    const int dt_bytes = STRIDED ? (int)(prm.ds[1] * 2) : qt_bytes;
+    const F qfetch(smem, wave, lane, qt_bytes), dfetch(smem, wave, lane, dt_bytes);
+    const int64_t qb0 = STRIDED ? (int64_t)b * prm.qs[0] + (int64_t)h * prm.qs[2] : (int64_t)b * S * tok_stride + h * D;
+    const int64_t db0 = STRIDED ? (int64_t)b * prm.ds[0] + (int64_t)h * prm.ds[2] : qb0;
+    const char* qbase = (const char*)(prm.q + qb0);
+    const char* dbase = (const char*)(prm.dout + db0);
     const float* dvec = prm.aux + (int64_t)bh * S;
     const float* lvec = prm.aux + (int64_t)prm.n_rows + (int64_t)bh * S;
     auto entry = [&](int j) { return __builtin_amdgcn_readfirstlane(lq[j / RQ]); };
@@ -457,11 +474,11 @@ __global__ __launch_bounds__(BKV * 2, 2) void vsa_bwd_dkv_kernel(BwdParams prm) 
         const int m = entry(j);
         const int r0 = (m >= 0 ? m : 0) * block_q + (j % RQ) * QS;  // first query row of the step
         const int st = (j & 1) * STAGE;
-        fetch.all(st, uniform_ptr(qbase + (int64_t)r0 * tok_bytes), tok_bytes, kLayoutD);
-        fetch.all(st + G::TILE, uniform_ptr(dbase + (int64_t)r0 * tok_bytes), tok_bytes, kLayoutD);
+        qfetch.all(st, uniform_ptr(qbase + (int64_t)r0 * qt_bytes), qt_bytes, kLayoutD);
+        dfetch.all(st + G::TILE, uniform_ptr(dbase + (int64_t)r0 * dt_bytes), dt_bytes, kLayoutD);
         if (wave == 0 && lane < QS / 4) {
             // D and lse2 of the step's rows: 256 bytes each, 16 bytes per lane
-            const uint32_t dst = fetch.lds0 + (uint32_t)(st + 2 * G::TILE);
+            const uint32_t dst = qfetch.lds0 + (uint32_t)(st + 2 * G::TILE);
             lds_dma16(dvec + r0, (uint32_t)(lane * 16), dst);
             lds_dma16(lvec + r0, (uint32_t)(lane * 16), dst + QS * 4);
         }
@@ -600,13 +617,13 @@ hipError_t launch_dq_d(const BwdParams& p, hipStream_t stream) {
     return p.splits_q > 1 ? launch_dq_s<D, PARTIAL, true>(p, stream) : launch_dq_s<D, PARTIAL, false>(p, stream);
 }
 
-template <int D, bool PARTIAL, bool SPLIT>
+template <int D, bool PARTIAL, bool SPLIT, bool STRIDED>
 hipError_t launch_dkv_s(const BwdParams& p, hipStream_t stream) {
     const int lds = 2 * dkv_stage_bytes<D>() + 4 * (p.q_ld < kIdxCapBwd ? p.q_ld : kIdxCapBwd);
     const int grid = p.n_items_kv * p.splits_kv;
     switch (p.block_kv) {
-        case 64: return launch_dyn(vsa_bwd_dkv_kernel<64, D, PARTIAL, SPLIT>, grid, 128, lds, p, stream);
-        case 128: return launch_dyn(vsa_bwd_dkv_kernel<128, D, PARTIAL, SPLIT>, grid, 256, lds, p, stream);
+        case 64: return launch_dyn(vsa_bwd_dkv_kernel<64, D, PARTIAL, SPLIT, STRIDED>, grid, 128, lds, p, stream);
+        case 128: return launch_dyn(vsa_bwd_dkv_kernel<128, D, PARTIAL, SPLIT, STRIDED>, grid, 256, lds, p, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -614,7 +631,11 @@ hipError_t launch_dkv_s(const BwdParams& p, hipStream_t stream) {
 template <int D, bool PARTIAL>
 hipError_t launch_dkv_d(const BwdParams& p, hipStream_t stream) {
     if (p.n_items_kv <= 0) return hipSuccess;
-    return p.splits_kv > 1 ? launch_dkv_s<D, PARTIAL, true>(p, stream) : launch_dkv_s<D, PARTIAL, false>(p, stream);
+    if (p.strided)
+        return p.splits_kv > 1 ? launch_dkv_s<D, PARTIAL, true, true>(p, stream)
+                               : launch_dkv_s<D, PARTIAL, false, true>(p, stream);
+    return p.splits_kv > 1 ? launch_dkv_s<D, PARTIAL, true, false>(p, stream)
+                           : launch_dkv_s<D, PARTIAL, false, false>(p, stream);
 }
 
 }  // namespace
@@ -632,6 +653,19 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     p.dout = a.dout;
     p.o = a.o;
     p.lse = a.lse;
+    for (int i = 0; i < 3; ++i) {
+        const int64_t contiguous[3] = {(int64_t)a.S * a.H * a.D, (int64_t)a.H * a.D, (int64_t)a.D};
+        p.qs[i] = a.strides ? a.strides[i] : contiguous[i];
+        p.ks[i] = a.strides ? a.strides[3 + i] : contiguous[i];
+        p.vs[i] = a.strides ? a.strides[6 + i] : contiguous[i];
+        p.ds[i] = a.strides ? a.strides[9 + i] : contiguous[i];
+    }
+    p.strided = 0;
+    for (int i = 0; i < 3; ++i) {
+        const int64_t contiguous[3] = {(int64_t)a.S * a.H * a.D, (int64_t)a.H * a.D, (int64_t)a.D};
+        if (p.qs[i] != contiguous[i] || p.ks[i] != contiguous[i] || p.vs[i] != contiguous[i] || p.ds[i] != contiguous[i])
+            p.strided = 1;
+    }
     p.aux = a.aux;
     p.idx = a.idx;
     p.cnt = a.cnt;

@@ -106,10 +106,11 @@ vsa::FwdParams make_params(const void* q, const void* k, const void* v, const in
 // Strides of vsa_attn_fwd_strided (q, k, v: batch, token, head, in elements):
 // every row must start on a 16-byte boundary, a row stride must fit the
 // kernels' 32-bit row offsets, and rows of one tensor must not overlap.
-int32_t check_strides(const int64_t* s, int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim) {
+int32_t check_strides(const int64_t* s, int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim,
+                      int n_tensors = 3) {
     VSA_REQUIRE(s, VSA_ERR_INVALID_ARG, "null stride array");
-    const char* name[3] = {"q", "k", "v"};
-    for (int t = 0; t < 3; ++t) {
+    const char* name[4] = {"q", "k", "v", "dout"};
+    for (int t = 0; t < n_tensors; ++t) {
         const int64_t bs = s[3 * t], ts = s[3 * t + 1], hs = s[3 * t + 2];
         VSA_REQUIRE(bs >= 0 && ts >= 0 && hs >= 0, VSA_ERR_INVALID_ARG, "%s strides must be >= 0", name[t]);
         VSA_REQUIRE(bs % 8 == 0 && ts % 8 == 0 && hs % 8 == 0, VSA_ERR_INVALID_ARG,
@@ -302,7 +303,7 @@ hipError_t measure_mfma(int mode, int iters, hipStream_t stream, float* tflops, 
 
 extern "C" {
 
-int32_t vsa_abi_version(void) { return 11; }
+int32_t vsa_abi_version(void) { return 12; }
 
 int32_t vsa_set_max_splits(int32_t max_splits) {
     const int32_t m = max_splits >= 4 ? 4 : (max_splits >= 2 ? 2 : 1);
@@ -667,10 +668,25 @@ int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const int32_t* q_block_idx, const int32_t* q_block_cnt, int32_t q_ld, const int32_t* kv_valid,
                      int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim, int32_t block_q,
                      int32_t block_kv, float scale, void* dq, void* dk, void* dv, void* stream) {
+    return vsa_attn_bwd_strided(q, k, v, o, lse, dout, nullptr, kv_block_idx, kv_block_cnt, idx_ld, q_block_idx,
+                                q_block_cnt, q_ld, kv_valid, batch, seqlen, heads, head_dim, block_q, block_kv, scale,
+                                dq, dk, dv, stream);
+}
+
+int32_t vsa_attn_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, const int64_t* strides, const int32_t* kv_block_idx,
+                             const int32_t* kv_block_cnt, int32_t idx_ld, const int32_t* q_block_idx,
+                             const int32_t* q_block_cnt, int32_t q_ld, const int32_t* kv_valid, int32_t batch,
+                             int32_t seqlen, int32_t heads, int32_t head_dim, int32_t block_q, int32_t block_kv,
+                             float scale, void* dq, void* dk, void* dv, void* stream) {
     g_last_error[0] = 0;
     int32_t rc = check_fwd(q, k, v, kv_block_idx, kv_block_cnt, kv_valid, batch, seqlen, heads, head_dim, idx_ld,
                            block_q, block_kv, scale, o, lse);
     if (rc != VSA_OK) return rc;
+    if (strides) {
+        rc = check_strides(strides, batch, seqlen, heads, head_dim, 4);
+        if (rc != VSA_OK) return rc;
+    }
     VSA_REQUIRE(dout && dq && dk && dv && q_block_idx && q_block_cnt, VSA_ERR_INVALID_ARG, "null pointer");
     VSA_REQUIRE(aligned(dout, 16) && aligned(dq, 16) && aligned(dk, 16) && aligned(dv, 16), VSA_ERR_INVALID_ARG,
                 "dout, dq, dk, dv must be 16-byte aligned");
@@ -703,6 +719,7 @@ int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o,
     a.v = (const uint16_t*)v;
     a.o = (const uint16_t*)o;
     a.dout = (const uint16_t*)dout;
+    a.strides = strides;
     a.lse = lse;
     a.aux = aux;
     a.idx = kv_block_idx;

@@ -95,6 +95,10 @@ bool fwd_supported(int block_q, int block_kv, int head_dim);
 // scratch (D, LSE*log2 e); work lists as for the forward.
 struct BwdArgs {
     const uint16_t *q, *k, *v, *o, *dout;
+    // element strides of q, k, v and dout as (batch, token, head), 12 values
+    // (head_dim contiguous); null: all four contiguous [B, S, H, D]. o, dq, dk
+    // and dv are contiguous.
+    const int64_t* strides = nullptr;
     const float* lse;
     float* aux;
     const int32_t *idx, *cnt;    // forward CSR

@@ -17,8 +17,8 @@
  *
  * Conventions shared by all entry points
  * --------------------------------------
- *  - Tensors are dense, row-major and contiguous (vsa_attn_fwd_strided also
- *    takes q, k, v as strided views):
+ *  - Tensors are dense, row-major and contiguous (vsa_attn_fwd_strided and
+ *    vsa_attn_bwd_strided also take q, k, v and dout as strided views):
  *      q, k, v, o      [batch, seqlen, heads, head_dim]  bf16 (raw 16-bit)
  *      lse             [batch, heads, seqlen]            fp32
  *      kv_block_idx    [batch, heads, seqlen/block_q, idx_ld]  int32
@@ -382,6 +382,31 @@ int32_t vsa_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const int32_t* q_block_idx, const int32_t* q_block_cnt, int32_t q_ld, const int32_t* kv_valid,
                      int32_t batch, int32_t seqlen, int32_t heads, int32_t head_dim, int32_t block_q,
                      int32_t block_kv, float scale, void* dq, void* dk, void* dv, void* stream);
+
+/*
+ * vsa_attn_bwd_strided -- vsa_attn_bwd with q, k, v and dout given as
+ * strided views (for example the slices of a packed QKV projection, or
+ * [batch, heads, seqlen, head_dim] tensors), read in place.
+ *
+ * Source: as vsa_attn_bwd; the pages' interface takes tensors with their own
+ * strides (FastVideo page, arm_fa4 / _flash_attn_fwd).
+ *
+ *   strides: host array of 12 int64, the element strides of q, k, v and dout
+ *   in that order, each as (batch, token, head), with the same meaning and
+ *   limits as in vsa_attn_fwd_strided (>= 0, multiples of 8, token stride at
+ *   most 2^24, any order, rows may coincide); NULL = all four contiguous
+ *   (vsa_attn_bwd). o, lse, dq, dk and dv stay contiguous. Otherwise as
+ *   vsa_attn_bwd: same kernels, buffers and split lists, and results bitwise
+ *   equal to vsa_attn_bwd on contiguous copies of the same values. With k, v
+ *   broadcast over the heads (head stride 0), dk and dv hold each head's
+ *   gradient; their sum over the heads is the gradient of the shared tensor.
+ */
+int32_t vsa_attn_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, const int64_t* strides, const int32_t* kv_block_idx,
+                             const int32_t* kv_block_cnt, int32_t idx_ld, const int32_t* q_block_idx,
+                             const int32_t* q_block_cnt, int32_t q_ld, const int32_t* kv_valid, int32_t batch,
+                             int32_t seqlen, int32_t heads, int32_t head_dim, int32_t block_q, int32_t block_kv,
+                             float scale, void* dq, void* dk, void* dv, void* stream);
 
 /* Free the library-owned buffers (every device and stream, including the
  * ones superseded by growth). Must not run while library work is in flight

@@ -36,7 +36,7 @@ def test_header_declares_the_binding_symbols():
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.vsa_abi_version() == 11
+    assert lib.vsa_abi_version() == 12
 
 
 def test_set_max_splits_rounds_and_returns_previous(lib):
@@ -285,3 +285,19 @@ def test_measure_mfma_rejects_invalid_arguments(lib):
     assert lib.vsa_measure_mfma(0, 2000001, ctypes.byref(t), ctypes.byref(c), None) == -1
     assert lib.vsa_measure_mfma(0, 100, None, ctypes.byref(c), None) == -1
     assert "null" in lib.vsa_last_error().decode()
+
+
+@pytest.mark.parametrize("edit,status,needle", [
+    ({10: 3 * 2 * 128 + 4}, -1, "multiples of 8"),      # dout token stride not a 16-byte multiple
+    ({9: -1024}, -1, ">= 0"),                            # dout batch stride negative
+    ({4: (1 << 24) + 8}, -2, "2^24"),                    # k token stride too large
+])
+def test_attn_bwd_strided_rejects_bad_strides(lib, edit, status, needle):
+    strides = _packed() + [1024 * 2 * 128, 2 * 128, 128]  # q, k, v from a packed projection, dout contiguous
+    for i, x in edit.items():
+        strides[i] = x
+    arr = (ctypes.c_int64 * 12)(*strides)
+    rc = lib.vsa_attn_bwd_strided(A, A, A, A, A, A, arr, A, A, 16, A, A, 16, None, 1, 1024, 2, 128, 128, 64, 0.1,
+                                  A, A, A, None)
+    assert rc == status
+    assert needle in lib.vsa_last_error().decode()

@@ -323,3 +323,54 @@ def test_backward_tensors_past_2gib_sampled(vsa):
     check("dV", pick(dv, krows), rv, "past 2 GiB")
     del q, k, v, do, o, lse, dq, dk, dv, qc, kc, vc, doc
     torch.cuda.empty_cache()
+
+
+def _views(t, layout):
+    """A [B, S, H, D] device tensor's values as a strided view: sliced from a
+    packed [B, S, 3, H, D] buffer, from a [B, H, S, D] buffer, or head 0
+    broadcast over the heads (head stride 0)."""
+    B, S, H, D = t.shape
+    if layout == "packed":
+        buf = torch.zeros((B, S, 3, H, D), dtype=t.dtype, device=t.device)
+        buf[:, :, 1] = t
+        return buf[:, :, 1]
+    if layout == "bhsd":
+        return t.transpose(1, 2).contiguous().transpose(1, 2)
+    assert layout == "broadcast"
+    return t[:, :, :1].expand(B, S, H, D)
+
+
+STRIDED_BWD = [(256, 128, 128, "packed", "packed", "bhsd"), (128, 64, 64, "bhsd", "bhsd", "packed"),
+               (64, 64, 128, "packed", "broadcast", "bhsd"), (256, 64, 64, "bhsd", "broadcast", "packed"),
+               (128, 128, 128, "packed", "packed", "packed")]
+
+
+@pytest.mark.parametrize("bq,bkv,D,qlay,kvlay,dolay", STRIDED_BWD,
+                         ids=[f"{a}x{b}_d{c}_{q}_{kv}_{d}" for a, b, c, q, kv, d in STRIDED_BWD])
+@pytest.mark.parametrize("max_splits", [4, 1], ids=["split", "unsplit"], indirect=True)
+def test_strided_backward_bitwise_equal_to_contiguous(vsa, bq, bkv, D, qlay, kvlay, dolay, max_splits):
+    """q, k, v and dout read in place through their strides
+    (vsa_attn_bwd_strided, the route vsa_attn_bwd takes for views) give the
+    gradients of the contiguous call on copies of the same values bitwise;
+    one case per tile shape family is also checked against the oracle."""
+    B, H, S = 2, 2, 768
+    say(f"strided backward {bq}x{bkv} D={D} q:{qlay} kv:{kvlay} dout:{dolay} max_splits={max_splits}")
+    q, k, v = (dev(t) for t in W.qkv(B, S, H, D, seed=bq + bkv + D + 300))
+    do = dev(W.qkv(B, S, H, D, seed=bq + bkv + D + 301)[0])
+    qs, ks, vs, dos = _views(q, qlay), _views(k, kvlay), _views(v, kvlay), _views(do, dolay)
+    qc, kc, vc, doc = qs.contiguous(), ks.contiguous(), vs.contiguous(), dos.contiguous()
+    nq, nkv = S // bq, S // bkv
+    idx, cnt = W.random_csr(B, H, nq, nkv, nkv, 0, nkv, seed=bq * 9 + bkv + D)
+    idxd, cntd = dev(idx), dev(cnt)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = vsa.vsa_attn_fwd(qc, kc, vc, idxd, cntd, bq, bkv, scale)
+    q_idx, q_cnt = vsa.vsa_csr_transpose(idxd, cntd, nkv, nq)
+    ref = vsa.vsa_attn_bwd(qc, kc, vc, o, lse, doc, idxd, cntd, q_idx, q_cnt, bq, bkv, scale)
+    got = vsa.vsa_attn_bwd(qs, ks, vs, o, lse, dos, idxd, cntd, q_idx, q_cnt, bq, bkv, scale)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
+        assert torch.equal(a, b), f"strided {name} differs from the contiguous call"
+    if max_splits == 4 and (qlay, kvlay) in (("packed", "packed"), ("packed", "broadcast")):
+        rq, rk, rv = oracle.bwd_full(qc.cpu(), kc.cpu(), vc.cpu(), doc.cpu(), idx, cnt, bq, bkv, scale)
+        for name, g, r in (("dQ", got[0], rq), ("dK", got[1], rk), ("dV", got[2], rv)):
+            check(name, g.float().cpu().numpy(), r, f"strided {bq}x{bkv}")

@@ -340,21 +340,25 @@ def _views(t, layout):
     return t[:, :, :1].expand(B, S, H, D)
 
 
-STRIDED_BWD = [(256, 128, 128, "packed", "packed", "bhsd"), (128, 64, 64, "bhsd", "bhsd", "packed"),
-               (64, 64, 128, "packed", "broadcast", "bhsd"), (256, 64, 64, "bhsd", "broadcast", "packed"),
-               (128, 128, 128, "packed", "packed", "packed")]
+STRIDED_BWD = [(256, 128, 128, "packed", "packed", "bhsd", False), (128, 64, 64, "bhsd", "bhsd", "packed", False),
+               (64, 64, 128, "packed", "broadcast", "bhsd", False), (256, 64, 64, "bhsd", "broadcast", "packed", False),
+               (128, 128, 128, "packed", "packed", "packed", False), (256, 128, 64, "packed", "bhsd", "bhsd", True),
+               (64, 64, 64, "bhsd", "packed", "packed", True)]
 
 
-@pytest.mark.parametrize("bq,bkv,D,qlay,kvlay,dolay", STRIDED_BWD,
-                         ids=[f"{a}x{b}_d{c}_{q}_{kv}_{d}" for a, b, c, q, kv, d in STRIDED_BWD])
+@pytest.mark.parametrize("bq,bkv,D,qlay,kvlay,dolay,partial", STRIDED_BWD,
+                         ids=[f"{a}x{b}_d{c}_{q}_{kv}_{d}{'_partial' if pt else ''}"
+                              for a, b, c, q, kv, d, pt in STRIDED_BWD])
 @pytest.mark.parametrize("max_splits", [4, 1], ids=["split", "unsplit"], indirect=True)
-def test_strided_backward_bitwise_equal_to_contiguous(vsa, bq, bkv, D, qlay, kvlay, dolay, max_splits):
+def test_strided_backward_bitwise_equal_to_contiguous(vsa, bq, bkv, D, qlay, kvlay, dolay, partial, max_splits):
     """q, k, v and dout read in place through their strides
     (vsa_attn_bwd_strided, the route vsa_attn_bwd takes for views) give the
-    gradients of the contiguous call on copies of the same values bitwise;
-    one case per tile shape family is also checked against the oracle."""
+    gradients of the contiguous call on copies of the same values bitwise,
+    with full and partial tiles; some cases are also checked against the
+    oracle."""
     B, H, S = 2, 2, 768
-    say(f"strided backward {bq}x{bkv} D={D} q:{qlay} kv:{kvlay} dout:{dolay} max_splits={max_splits}")
+    say(f"strided backward {bq}x{bkv} D={D} q:{qlay} kv:{kvlay} dout:{dolay} partial={partial} "
+        f"max_splits={max_splits}")
     q, k, v = (dev(t) for t in W.qkv(B, S, H, D, seed=bq + bkv + D + 300))
     do = dev(W.qkv(B, S, H, D, seed=bq + bkv + D + 301)[0])
     qs, ks, vs, dos = _views(q, qlay), _views(k, kvlay), _views(v, kvlay), _views(do, dolay)
@@ -362,15 +366,17 @@ def test_strided_backward_bitwise_equal_to_contiguous(vsa, bq, bkv, D, qlay, kvl
     nq, nkv = S // bq, S // bkv
     idx, cnt = W.random_csr(B, H, nq, nkv, nkv, 0, nkv, seed=bq * 9 + bkv + D)
     idxd, cntd = dev(idx), dev(cnt)
+    val = W.ragged_block_sizes(nkv, bkv, seed=bq + bkv + D + 7, p_full=0.4) if partial else None
+    vd = None if val is None else dev(val)
     scale = 1.0 / math.sqrt(D)
-    o, lse = vsa.vsa_attn_fwd(qc, kc, vc, idxd, cntd, bq, bkv, scale)
+    o, lse = vsa.vsa_attn_fwd(qc, kc, vc, idxd, cntd, bq, bkv, scale, kv_valid=vd)
     q_idx, q_cnt = vsa.vsa_csr_transpose(idxd, cntd, nkv, nq)
-    ref = vsa.vsa_attn_bwd(qc, kc, vc, o, lse, doc, idxd, cntd, q_idx, q_cnt, bq, bkv, scale)
-    got = vsa.vsa_attn_bwd(qs, ks, vs, o, lse, dos, idxd, cntd, q_idx, q_cnt, bq, bkv, scale)
+    ref = vsa.vsa_attn_bwd(qc, kc, vc, o, lse, doc, idxd, cntd, q_idx, q_cnt, bq, bkv, scale, kv_valid=vd)
+    got = vsa.vsa_attn_bwd(qs, ks, vs, o, lse, dos, idxd, cntd, q_idx, q_cnt, bq, bkv, scale, kv_valid=vd)
     torch.cuda.synchronize()
     for name, a, b in zip(("dQ", "dK", "dV"), got, ref):
         assert torch.equal(a, b), f"strided {name} differs from the contiguous call"
-    if max_splits == 4 and (qlay, kvlay) in (("packed", "packed"), ("packed", "broadcast")):
-        rq, rk, rv = oracle.bwd_full(qc.cpu(), kc.cpu(), vc.cpu(), doc.cpu(), idx, cnt, bq, bkv, scale)
+    if max_splits == 4 and (partial or (qlay, kvlay) in (("packed", "packed"), ("packed", "broadcast"))):
+        rq, rk, rv = oracle.bwd_full(qc.cpu(), kc.cpu(), vc.cpu(), doc.cpu(), idx, cnt, bq, bkv, scale, kv_valid=val)
         for name, g, r in (("dQ", got[0], rq), ("dK", got[1], rk), ("dV", got[2], rv)):
             check(name, g.float().cpu().numpy(), r, f"strided {bq}x{bkv}")

@@ -57,7 +57,7 @@ def parse_args():
                     help="run steps back to back for this long before the warmup steps, so that the timed "
                          "steps see the sustained clock rather than the ramp out of idle")
     ap.add_argument("--clock-seconds", type=float, default=2.0,
-                    help="seconds of extra steps during which amd-smi samples the gfx clock (0: skip)")
+                    help="seconds of extra steps during which amd-smi samples the gfx clock and socket power (0: skip)")
     ap.add_argument("--flush-steps", type=int, default=10,
                     help="kernel launches timed after writing a buffer larger than the last-level cache")
     ap.add_argument("--ragged", type=int, default=None, metavar="SEED",
@@ -580,7 +580,9 @@ def read_traffic(path, kname):
 
 def sample_clock(step, seconds):
     """Run steps back to back for about `seconds` while amd-smi reads the gfx
-    clock of every XCD once, half-way through."""
+    clock of every XCD and the socket power once, half-way through. The
+    socket power shows whether the step runs at the board's power limit
+    (1,400 W on MI355X), where its time follows its energy per step."""
     import subprocess
     import threading
 
@@ -589,12 +591,15 @@ def sample_clock(step, seconds):
 
     def query():
         try:
-            r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True, text=True,
-                               timeout=30)
+            r = subprocess.run(["amd-smi", "metric", "--clock", "--power", "--json"], capture_output=True,
+                               text=True, timeout=30)
             d = json.loads(r.stdout)
             d = d["gpu_data"][0] if isinstance(d, dict) and "gpu_data" in d else d[0]
             clk = d["clock"]
             box["mhz"] = [float(clk[k]["clk"]["value"]) for k in sorted(clk) if k.startswith("gfx_")]
+            pw = (d.get("power") or {}).get("socket_power")
+            if isinstance(pw, dict) and isinstance(pw.get("value"), (int, float)):
+                box["watts"] = float(pw["value"])
         except Exception as e:  # best effort: the tool may be missing or print another layout
             box["error"] = f"{type(e).__name__}: {e}"[:200]
 
@@ -615,8 +620,8 @@ def sample_clock(step, seconds):
     if "mhz" not in box:
         return {"gfx_mhz_mean": None, "error": box.get("error", "no sample")}
     mhz = box["mhz"]
-    return {"gfx_mhz_mean": round(sum(mhz) / len(mhz), 1), "gfx_mhz": mhz,
-            "source": "amd-smi metric --clock, sampled while steps ran back to back"}
+    return {"gfx_mhz_mean": round(sum(mhz) / len(mhz), 1), "gfx_mhz": mhz, "socket_power_w": box.get("watts"),
+            "source": "amd-smi metric --clock --power, sampled while steps ran back to back"}
 
 
 O_MAX_ABS, O_MEAN_ABS, LSE_REL = 2e-2, 2e-3, 1e-3  # forward tolerances (bf16 O, fp32 LSE)

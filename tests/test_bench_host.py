@@ -1,6 +1,6 @@
 """Host-side logic of bench.py (no GPU): the kernel it names for the roofline,
-the staleness check of measured traffic, the sparse-aware pair count, and the
-refusal of more than one GPU."""
+the staleness check of measured traffic, the sparse-aware pair count, the
+refusal of more than one GPU, and the parsing of the clock and power sample."""
 
 import json
 import os
@@ -67,3 +67,32 @@ def test_more_than_one_gpu_is_refused(argv, env):
                        env={**os.environ, **env}, timeout=120)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+def _smi_json(watts):
+    clock = {f"gfx_{i}": {"clk": {"value": 1600 + 10 * i, "unit": "MHz"}} for i in range(8)}
+    clock["mem_0"] = {"clk": {"value": 2000, "unit": "MHz"}}
+    power = {"socket_power": {"value": watts, "unit": "W"} if watts is not None else "N/A", "gfx_voltage": "N/A"}
+    return json.dumps({"gpu_data": [{"gpu": 0, "clock": clock, "power": power}]})
+
+
+@pytest.mark.parametrize("watts", [1400, None])
+def test_clock_sample_reads_gfx_clocks_and_socket_power(monkeypatch, watts):
+    """sample_clock parses the gfx clock of every XCD and the socket power
+    from amd-smi's JSON (layout as the tool prints it on MI355X); a missing
+    power reading leaves the field empty rather than failing the bench."""
+    calls = []
+
+    def fake_run(cmd, **kw):
+        calls.append(cmd)
+        return subprocess.CompletedProcess(cmd, 0, stdout=_smi_json(watts), stderr="")
+
+    monkeypatch.setattr(subprocess, "run", fake_run)
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: None)
+    steps = []
+    out = bench.sample_clock(lambda: steps.append(1), 0.05)
+    assert calls and calls[0][:2] == ["amd-smi", "metric"] and "--power" in calls[0] and "--clock" in calls[0]
+    assert out["gfx_mhz"] == [1600.0 + 10 * i for i in range(8)]
+    assert out["gfx_mhz_mean"] == pytest.approx(1635.0)
+    assert out["socket_power_w"] == (None if watts is None else float(watts))
+    assert steps  # steps ran while the sample was taken

@@ -510,7 +510,7 @@ def time_backward(vsa, q, k, v, o, lse, idx, cnt, bq, bkv, scale, D, pairs, step
     ms = e0.elapsed_time(e1) / steps
     tflops = 10.0 * D * pairs / (ms * 1e-3) / 1e12
     return {"ms": round(ms, 4), "tflops": round(tflops, 2), "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-            "flops_per_pair": f"10*D={10 * D}", "scope": "vsa_csr_transpose + vsa_attn_bwd (prep, dK/dV, dQ)"}
+            "flops_per_pair": f"10*D={10 * D}", "scope": "vsa_csr_transpose + vsa_attn_bwd (dQ with D and LSE, then dK/dV)"}
 
 
 IW_ITEMS_PER_CU = 8  # the library's switch to the independent-wave kernel

@@ -239,9 +239,9 @@ def backward_kernel_lines(out, d, ours):
     conflicts and HBM bytes per launch; no lines if the counters hold none."""
     sq_csv = os.path.join(d, "sq", "run_counter_collection.csv")
     rows = []
-    for r in sorted((r for r in ours if r["short"].startswith(("vsa_bwd_", "bwd_prep"))), key=lambda r: r["short"]):
+    for r in sorted((r for r in ours if r["short"].startswith("vsa_bwd_")), key=lambda r: r["short"]):
         kname = _norm(r["short"])
-        if not counter_values(sq_csv, "SQ_INSTS_VALU_MFMA_MOPS_BF16", kname) and not r["short"].startswith("bwd_prep"):
+        if not counter_values(sq_csv, "SQ_INSTS_VALU_MFMA_MOPS_BF16", kname):
             continue
         try:
             sq = sq_summary(sq_csv, kname)

@@ -27,8 +27,8 @@ pytestmark = pytest.mark.gpu
 O_MAX_ABS = 2e-2
 O_MEAN_ABS = 2e-3
 LSE_REL = 1e-3
-N_CASES = 120
-N_BWD_CASES = 40
+N_CASES = 400
+N_BWD_CASES = 120
 G_MAX = 2e-2
 G_MEAN = 2e-3
 

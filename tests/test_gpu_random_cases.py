@@ -8,8 +8,8 @@ point (vsa_attn_fwd, the work-list kernel, strided q/k/v views, the no-alloc
 entry, the paired and coalesced entries where the tile shape allows), so that
 combinations no hand-written case names still meet the oracle. The backward
 cases draw the same way and run the transposed lists and vsa_attn_bwd on the
-GPU forward's O and LSE. Tolerances as in test_gpu_parity.py and
-test_gpu_bwd.py.
+GPU forward's O and LSE (on strided views of packed buffers where the case draws
+the strided entry). Tolerances as in test_gpu_parity.py and test_gpu_bwd.py.
 """
 
 import math
@@ -135,6 +135,12 @@ def test_random_backward_case_every_row(vsa, i):
         valid = W.ragged_block_sizes(nkv, bkv, seed=c["seed"] + 2, p_full=0.3)
     dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to("cuda")  # noqa: E731
     qd, kd, vd, dod = q.to("cuda"), k.to("cuda"), v.to("cuda"), do.to("cuda")
+    if c["entry"] == "strided":
+        # q, k, v as slices of a packed [B, S, 3, H, D] buffer and dO as one of a [B, S, 2, H, D]
+        # buffer: both passes read them in place through their strides
+        buf = torch.stack((qd, kd, vd), dim=2).contiguous()
+        qd, kd, vd = buf[:, :, 0], buf[:, :, 1], buf[:, :, 2]
+        dod = torch.stack((dod, torch.zeros_like(dod)), dim=2).contiguous()[:, :, 0]
     idxd, cntd = dev(idx), dev(cnt)
     vv = None if valid is None else dev(valid)
     o, lse = vsa.vsa_attn_fwd(qd, kd, vd, idxd, cntd, bq, bkv, c["scale"], kv_valid=vv)

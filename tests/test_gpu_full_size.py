@@ -11,6 +11,7 @@ to fp32) and all B*H*S rows of LSE: max |dO| <= 2e-2, mean |dO| <= 2e-3,
 within max(1e-2, 8 x the largest bf16 rounding error of the reference).
 """
 
+import dataclasses
 import os
 import time
 
@@ -112,6 +113,15 @@ def vsa256_ref(vsa):
     return Reference(W.VSA256, (256, 128), 26)
 
 
+# the VSA-256 mask at head_dim 64 with twice the heads (the same flops as at head_dim 128)
+VSA256_D64 = dataclasses.replace(W.VSA256, name="vsa256_b1h48s32768d64_keep13", heads=48, head_dim=64)
+
+
+@pytest.fixture(scope="module")
+def vsa256_d64_ref(vsa):
+    return Reference(VSA256_D64, (256, 128), 26)
+
+
 @pytest.fixture(scope="module")
 def native64_ref(vsa):
     return Reference(W.NATIVE64, (64, 64), 92)
@@ -186,6 +196,21 @@ def test_vsa256_cross_shape_agreement(vsa, vsa256_ref):
         say(f"cross-shape {tile}: max|dO|={d.max().item():.3e} mean|dO|={d.mean().item():.3e} LSE rel={lrel:.3e}")
         assert d.max().item() <= O_MAX_ABS and d.mean().item() <= O_MEAN_ABS and lrel <= LSE_REL
         del o1, l1, d
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("tile,ld", [((256, 128), 26), ((128, 64), 52), ((64, 64), 52)],
+                         ids=["256x128", "128x64", "64x64"])
+def test_vsa256_head_dim_64_every_element(vsa, vsa256_d64_ref, tile, ld):
+    """The VSA-256 mask at head_dim 64 (B1 H48 S32768): the 256-row, 128-row
+    and 64-row kernels built for head_dim 64, every element against one
+    oracle run."""
+    r = vsa256_d64_ref
+    idx, cnt = r.csr(vsa, tile, ld)
+    o, lse = vsa.vsa_attn_fwd(r.qd, r.kd, r.vd, idx, cnt, tile[0], tile[1], r.wl.scale)
+    torch.cuda.synchronize()
+    check_all(o, lse, r.o, r.lse, f"vsa256 d64 {tile[0]}x{tile[1]}")
+    del o, lse
     torch.cuda.empty_cache()
 
 

@@ -191,12 +191,13 @@ FULL_SIZE = [
     ("vsa256 256x128", W.VSA256, (256, 128), 26, (0, 23)),
     ("vsa256 64x64", W.VSA256_FINE, (64, 64), 52, (7,)),
     ("native64 64x64", W.NATIVE64, (64, 64), 92, (16,)),
+    ("vsa256 d64 256x128", W.VSA256_D64, (256, 128), 26, (40,)),
 ]
 
 
 @pytest.mark.parametrize("label,wl,tile,ld,heads", FULL_SIZE, ids=[c[0] for c in FULL_SIZE])
 def test_backward_full_size_whole_heads(vsa, label, wl, tile, ld, heads):
-    """Full-size workloads (B1 H24 S32768 D128): the GPU runs every head; dQ,
+    """Full-size workloads (B1 S32768, H24 at D128, H48 at D64): the GPU runs every head; dQ,
     dK and dV of whole heads (every one of their 32768 query and key rows)
     are compared with the oracle run on those heads alone (heads are
     independent, so this is the same computation)."""

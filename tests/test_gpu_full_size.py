@@ -11,7 +11,6 @@ to fp32) and all B*H*S rows of LSE: max |dO| <= 2e-2, mean |dO| <= 2e-3,
 within max(1e-2, 8 x the largest bf16 rounding error of the reference).
 """
 
-import dataclasses
 import os
 import time
 
@@ -113,13 +112,9 @@ def vsa256_ref(vsa):
     return Reference(W.VSA256, (256, 128), 26)
 
 
-# the VSA-256 mask at head_dim 64 with twice the heads (the same flops as at head_dim 128)
-VSA256_D64 = dataclasses.replace(W.VSA256, name="vsa256_b1h48s32768d64_keep13", heads=48, head_dim=64)
-
-
 @pytest.fixture(scope="module")
 def vsa256_d64_ref(vsa):
-    return Reference(VSA256_D64, (256, 128), 26)
+    return Reference(W.VSA256_D64, (256, 128), 26)
 
 
 @pytest.fixture(scope="module")

@@ -152,8 +152,10 @@ class Workload:
         return qkv(self.batch, self.seqlen, self.heads, self.head_dim, seed)
 
 
-# The five workloads of the block-sparse forward (tiny, dense, VSA-256 on its
-# own tiles and on finer tiles, native Q64/KV64 with skewed counts).
+# The workloads of the block-sparse forward (tiny, dense, VSA-256 on its own
+# tiles and on finer tiles, native Q64/KV64 with skewed counts), and the
+# VSA-256 mask at head_dim 64 with twice the heads (the flops of VSA-256),
+# a parity and throughput case for the head_dim-64 kernels.
 TINY = Workload("tiny_64x64_b1h2s1024d64", 1, 2, 1024, 64, (64, 64), ((64, 64),),
                 "topk", keep=8, keep_fraction=0.5)
 DENSE = Workload("dense_b1h8s4096d128", 1, 8, 4096, 128, (256, 256), ((128, 128), (256, 128)),
@@ -165,7 +167,10 @@ VSA256_FINE = Workload("vsa256_fine_b1h24s32768d128_keep13", 1, 24, 32768, 128, 
 NATIVE64 = Workload("native64_b1h24s32768d128_cnt10to92", 1, 24, 32768, 128, (64, 64),
                     ((64, 64),), "count", count_range=(10, 92), keep_fraction=0.1)
 
-WORKLOADS = {w.name: w for w in (TINY, DENSE, VSA256, VSA256_FINE, NATIVE64)}
+VSA256_D64 = Workload("vsa256_b1h48s32768d64_keep13", 1, 48, 32768, 64, (256, 256),
+                      ((256, 128), (128, 64), (64, 64)), "topk", keep=13, keep_fraction=0.1)
+
+WORKLOADS = {w.name: w for w in (TINY, DENSE, VSA256, VSA256_FINE, NATIVE64, VSA256_D64)}
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:

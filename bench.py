@@ -252,7 +252,7 @@ def main():
 
     clock = sample_clock(step, args.clock_seconds) if args.clock_seconds > 0 else None
     backward = None if args.no_backward else time_backward(vsa, q, k, v, o, lse, idx, cnt, bq, bkv, scale, D, pairs,
-                                                           args.steps, stream, kv_valid)
+                                                           args.steps, stream, kv_valid, args.clock_seconds)
 
     # Algorithmic HBM bytes of one kernel launch: Q, K, V read once, O and
     # LSE written once, CSR indices and counts read once.
@@ -478,11 +478,14 @@ def selected_pairs(idx, cnt, bq, bkv, kv_valid=None):
     return int((keys * listed).sum().item()) * bq
 
 
-def time_backward(vsa, q, k, v, o, lse, idx, cnt, bq, bkv, scale, D, pairs, steps, stream, kv_valid=None):
+def time_backward(vsa, q, k, v, o, lse, idx, cnt, bq, bkv, scale, D, pairs, steps, stream, kv_valid=None,
+                  clock_seconds=0.0):
     """Backward leg: the Q-direction CSR plus dQ, dK, dV of this workload,
     timed like the forward (HIP events on the launch stream). Throughput uses
     the usual 10*D flops per selected pair (QK^T, dO V^T, P^T dO, dS K,
-    dS^T Q); the kernels recompute QK^T and dO V^T once more (14*D executed)."""
+    dS^T Q); the kernels recompute QK^T and dO V^T once more (14*D executed).
+    With clock_seconds > 0 the gfx clock and socket power are sampled while
+    backward steps run back to back, as for the forward."""
     import torch
 
     B, S, H, _ = q.shape
@@ -509,8 +512,10 @@ def time_backward(vsa, q, k, v, o, lse, idx, cnt, bq, bkv, scale, D, pairs, step
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     tflops = 10.0 * D * pairs / (ms * 1e-3) / 1e12
+    clock = sample_clock(run, clock_seconds) if clock_seconds > 0 else None
     return {"ms": round(ms, 4), "tflops": round(tflops, 2), "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-            "flops_per_pair": f"10*D={10 * D}", "scope": "vsa_csr_transpose + vsa_attn_bwd (dQ with D and LSE, then dK/dV)"}
+            "flops_per_pair": f"10*D={10 * D}", "scope": "vsa_csr_transpose + vsa_attn_bwd (dQ with D and LSE, then dK/dV)",
+            "clock": clock}
 
 
 IW_ITEMS_PER_CU = 8  # the library's switch to the independent-wave kernel

@@ -512,6 +512,7 @@ def vsa_measure_mfma(mode: str = "random", iters: int = 200000, stream=None, dev
     each SIMD): {"tflops": ..., "clock_mhz": ...}. Synchronises."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     t, c = ctypes.c_float(0.0), ctypes.c_float(0.0)
-    _check(load_library().vsa_measure_mfma(MFMA_MODES[mode], int(iters), ctypes.byref(t), ctypes.byref(c),
-                                           _stream_ptr(stream, dev)))
+    with torch.cuda.device(dev):  # the library measures on the current device
+        _check(load_library().vsa_measure_mfma(MFMA_MODES[mode], int(iters), ctypes.byref(t), ctypes.byref(c),
+                                               _stream_ptr(stream, dev)))
     return {"tflops": float(t.value), "clock_mhz": float(c.value)}

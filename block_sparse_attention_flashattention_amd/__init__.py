@@ -14,6 +14,7 @@ kv_block_idx ``[B, H, S/block_q, ld]`` int32; kv_block_cnt
 from __future__ import annotations
 
 import ctypes
+import functools
 import math
 import os
 
@@ -188,6 +189,23 @@ def _valid_ptr(kv_valid, S, block_kv, device):
     return kv_valid.data_ptr()
 
 
+def _on_tensor_device(fn):
+    """Run a binding function with the device of its first tensor argument
+    current: every library call works on the calling thread's current HIP
+    device, whose stream and memory the call's pointers must belong to."""
+    @functools.wraps(fn)
+    def wrapped(*args, **kwargs):
+        for a in (*args, *kwargs.values()):
+            if isinstance(a, torch.Tensor):
+                if a.is_cuda:
+                    with torch.cuda.device(a.device):
+                        return fn(*args, **kwargs)
+                break
+        return fn(*args, **kwargs)
+    return wrapped
+
+
+@_on_tensor_device
 def vsa_attn_fwd(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale=None, o=None, lse=None,
                  stream=None, kv_valid=None):
     """Block-sparse attention forward; returns (o, lse).
@@ -213,6 +231,7 @@ def vsa_attn_fwd(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale=N
     return o, lse
 
 
+@_on_tensor_device
 def vsa_attn_fwd_strided(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale=None, o=None, lse=None,
                          stream=None, kv_valid=None):
     """vsa_attn_fwd reading q, k, v in place through their strides (each a
@@ -231,6 +250,7 @@ def vsa_attn_fwd_strided(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv,
     return o, lse
 
 
+@_on_tensor_device
 def vsa_attn_fwd_noalloc(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale=None, o=None, lse=None,
                          stream=None, kv_valid=None):
     """vsa_attn_fwd without device allocation in the library: the work list
@@ -249,6 +269,7 @@ def vsa_attn_fwd_noalloc(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv,
     return o, lse
 
 
+@_on_tensor_device
 def vsa_attn_fwd_paired(q, k, v, kv_block_idx, kv_block_cnt, block_kv, scale=None, o=None, lse=None, stream=None,
                         kv_valid=None):
     """Forward over a 64-row query tile CSR that runs adjacent tiles as one
@@ -265,6 +286,7 @@ def vsa_attn_fwd_paired(q, k, v, kv_block_idx, kv_block_cnt, block_kv, scale=Non
     return o, lse
 
 
+@_on_tensor_device
 def vsa_attn_fwd_coalesced(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, scale=None, o=None, lse=None,
                            stream=None, kv_valid=None):
     """Forward over a 64- or 128-row query tile CSR that runs adjacent tiles
@@ -282,6 +304,7 @@ def vsa_attn_fwd_coalesced(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_k
     return o, lse
 
 
+@_on_tensor_device
 def vsa_pair_q_tiles(kv_block_idx, kv_block_cnt, paired_idx=None, paired_cnt=None, unpaired=None, stream=None):
     """Pair query tiles (2p, 2p+1): returns (paired_idx [B,H,NQ/2,ld],
     paired_cnt [B,H,NQ/2], unpaired [1]) as GPU tensors; no host sync."""
@@ -309,6 +332,7 @@ def vsa_pair_q_tiles(kv_block_idx, kv_block_cnt, paired_idx=None, paired_cnt=Non
     return paired_idx, paired_cnt, unpaired
 
 
+@_on_tensor_device
 def vsa_attn_fwd_worklist(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv, work_list, scale=None, o=None,
                           lse=None, stream=None, kv_valid=None):
     """The fused kernel alone over a caller-built work list; returns (o, lse)."""
@@ -325,6 +349,7 @@ def vsa_attn_fwd_worklist(q, k, v, kv_block_idx, kv_block_cnt, block_q, block_kv
     return o, lse
 
 
+@_on_tensor_device
 def vsa_mask_to_csr(mask, logical_block, block, idx_ld, kv_block_idx=None, kv_block_cnt=None, overflow=None,
                     stream=None, kv_valid=None):
     """Exact expansion of a logical mask to ``block`` tiles + block CSR.
@@ -362,6 +387,7 @@ def vsa_mask_to_csr(mask, logical_block, block, idx_ld, kv_block_idx=None, kv_bl
     return kv_block_idx, kv_block_cnt
 
 
+@_on_tensor_device
 def vsa_build_worklist(kv_block_cnt, max_cnt, work_list=None, segment=None, stream=None):
     """Count-sorted work list as int32 [n]: largest count first (stable)
     within each segment of ``segment`` consecutive items. The default
@@ -385,6 +411,7 @@ def vsa_build_worklist(kv_block_cnt, max_cnt, work_list=None, segment=None, stre
     return work_list
 
 
+@_on_tensor_device
 def vsa_expand_valid(vbs, logical_block_kv, block_kv, kv_valid=None, stream=None):
     """Valid keys per physical KV tile (int32 [nkv_logical * LKV/PKV]) from the
     valid tokens per logical KV block ``vbs`` (int32 [nkv_logical] GPU tensor)."""
@@ -403,6 +430,7 @@ def vsa_expand_valid(vbs, logical_block_kv, block_kv, kv_valid=None, stream=None
     return kv_valid
 
 
+@_on_tensor_device
 def vsa_csr_transpose(kv_block_idx, kv_block_cnt, nkv, q_ld, q_block_idx=None, q_block_cnt=None, overflow=None,
                       stream=None):
     """Q-direction block CSR for the backward pass: (q_block_idx [B,H,nkv,q_ld],
@@ -432,6 +460,7 @@ def vsa_csr_transpose(kv_block_idx, kv_block_cnt, nkv, q_ld, q_block_idx=None, q
     return q_block_idx, q_block_cnt
 
 
+@_on_tensor_device
 def vsa_attn_bwd(q, k, v, o, lse, dout, kv_block_idx, kv_block_cnt, q_block_idx, q_block_cnt, block_q, block_kv,
                  scale=None, dq=None, dk=None, dv=None, stream=None, kv_valid=None):
     """Backward pass of vsa_attn_fwd; returns (dq, dk, dv), bf16 [B, S, H, D].
@@ -447,6 +476,7 @@ def vsa_attn_bwd(q, k, v, o, lse, dout, kv_block_idx, kv_block_cnt, q_block_idx,
                 dq, dk, dv, stream, kv_valid, views=False)
 
 
+@_on_tensor_device
 def vsa_attn_bwd_strided(q, k, v, o, lse, dout, kv_block_idx, kv_block_cnt, q_block_idx, q_block_cnt, block_q,
                          block_kv, scale=None, dq=None, dk=None, dv=None, stream=None, kv_valid=None):
     """vsa_attn_bwd reading q, k, v and dout in place through their strides

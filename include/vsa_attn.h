@@ -32,6 +32,8 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = default stream). All
  *    GPU work is enqueued asynchronously on it; no call synchronises the
  *    host with the device.
+ *  - Every call works on the calling thread's current HIP device
+ *    (hipSetDevice); the stream and every device pointer must belong to it.
  *  - Library-owned scratch (work lists, split workspaces, the backward's
  *    per-row terms) is kept per device AND per stream: calls on different
  *    streams never share it and may run at the same time; calls on one
